@@ -1,0 +1,260 @@
+"""Benchmark: OSCAR INT2 decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload (concurrent_28x100k_36l): 28 sequences of 100,000 tokens,
+32 query / 8 KV heads, head_dim 128, 36 layers, random permuted page tables
+(page 16), sinks 64 + recent 256 in BF16, the rest INT2.  One step = for each
+of the 36 layers: kv_write of each sequence's new token (position 99,999),
+then decode_attn over the 100,000 cached tokens.  value = decoded tokens/s
+(28 per step).  Inputs are seeded synthetic data already resident in HBM.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/sec + achieved HBM GB/s (% of peak), 100K ctx, 1 MI355X"
+PEAK_HBM_GBS = 8000.0
+SIG = 1.0 / math.sqrt(128)
+
+WORKLOADS = {
+    "concurrent_28x100k_36l": dict(batch=28, seq_len=100_000, q_heads=32, kv_heads=8, layers=36,
+                                   table="permuted", law="heavy"),
+    "qwen3_8b_layer_100k": dict(batch=1, seq_len=100_000, q_heads=32, kv_heads=8, layers=1,
+                                table="contiguous", law="heavy"),
+    "ragged_64x4k_128k": dict(batch=64, seq_len=(4096, 131072), q_heads=64, kv_heads=8, layers=1,
+                              table="permuted", law="outlier"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def int2_tokens(L, sink=64, recent=256):
+    return max(sink, L - recent) - sink if L > sink else 0
+
+
+def bf16_tokens(L, sink=64, recent=256):
+    return L if L <= sink else sink + (L - max(sink, L - recent))
+
+
+def decode_bytes(lens, H, Hq):
+    """Algorithmic HBM bytes of one decode_attn call: 80 B per INT2 token-head,
+    512 B per BF16 token-head, q and out, one page-table entry per INT2 page,
+    U_K and U_V."""
+    tot = 0
+    for L in lens:
+        ni = int2_tokens(int(L))
+        tot += H * (ni * 80 + bf16_tokens(int(L)) * 512)
+        tot += 4 * (math.ceil((64 + ni) / 16) - 4)
+    tot += len(lens) * Hq * 128 * 2 * 2
+    tot += 2 * H * 128 * 128 * 2
+    return tot
+
+
+def write_bytes(n_tokens, H):
+    """kv_write of n tokens (K and V): read 2x256 B per token-head, write 80 B
+    INT2 + 2x256 B ring copy per token-head, U_K and U_V."""
+    return n_tokens * H * (512 + 80 + 512) + 2 * H * 128 * 128 * 2
+
+
+def cpu_baseline(H, layers, seq_len, budget_s=20.0):
+    """The fp64 oracle's decode, timed on this host on a bounded sample: one
+    sequence x one KV head (4 query heads) at the full length; extrapolated to
+    the whole step (batch x KV heads x layers units)."""
+    import oracle as O
+    import synth
+    from threadpoolctl import threadpool_info
+    rng = np.random.default_rng(1234)
+    shape = O.Shape(num_kv_heads=1, num_q_heads=4)
+    law = synth.heavy_tail_law(rng, 1)
+    qc, kc, vc = synth.calibration_samples(rng, law, 4, 256)
+    cal = O.calibrate_layer(qc, kc, vc, SIG)
+    layer = O.Layer(cal["u_k"], cal["u_v"], cal["clip_k"], cal["clip_v"])
+    pages = math.ceil(seq_len / 16)
+    table = synth.contiguous_page_table(1, pages)
+    cache = O.new_cache(shape, pages, 1)
+    k = law.sample_bf16(rng, seq_len)
+    v = law.sample_bf16(rng, seq_len)
+    O.kv_write(shape, cache, layer, k, v, np.zeros(seq_len, int), np.arange(seq_len), table, [seq_len])
+    q = synth.decode_queries(rng, 1, 4)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start < budget_s and len(times) < 50):
+        t0 = time.perf_counter()
+        O.decode(shape, cache, layer, q, table, [seq_len], SIG)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > 3 * budget_s:
+            break
+    t_unit = statistics.median(times)
+    threads = sum(int(i.get("num_threads", 0)) for i in threadpool_info() if i.get("user_api") == "blas")
+    return t_unit, len(times), max(threads, 1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="concurrent_28x100k_36l", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build is single-GPU: the decode shards by sequence or KV head with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import int2_rotated_kv_write_amd as lib
+    import synth
+    from synth.device import sample_kv_device, sample_queries_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    lib.load()
+    wl = WORKLOADS[args.workload]
+    B, Hq, H, NL = wl["batch"], wl["q_heads"], wl["kv_heads"], wl["layers"]
+    rng = np.random.default_rng(args.seed)
+    if isinstance(wl["seq_len"], tuple):
+        lens = synth.ragged_lengths(rng, B, *wl["seq_len"])
+    else:
+        lens = np.full(B, wl["seq_len"], np.int32)
+    max_pages = int(math.ceil(lens.max() / 16))
+    shape = lib.CacheShape(H, Hq)
+    law = synth.heavy_tail_law(rng, H) if wl["law"] == "heavy" else synth.outlier_law(rng, H)
+
+    # ---- offline calibration (host, native library), one set replicated per layer ----
+    t0 = time.perf_counter()
+    qc, kc, vc = synth.calibration_samples(rng, law, Hq // H, 2048)
+    u_k, u_v, ck, cv = lib.calibrate_layer(qc, kc, vc, SIG, 0.999)
+    log(f"calibration: {time.perf_counter() - t0:.1f}s clip_k={ck:.3f} clip_v={cv:.3f}")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    u_k_d, u_v_d = bf(u_k), bf(u_v)
+
+    # ---- page tables (one per layer, like separate cache pools) ----
+    if wl["table"] == "permuted":
+        table = synth.permuted_page_table(rng, B, max_pages)
+    else:
+        table = synth.contiguous_page_table(B, max_pages)
+    num_pages = int(table.max()) + 1
+    table_d = torch.from_numpy(table).to(dev)
+
+    # ---- caches: prefill positions [0, L-1) of every sequence through kv_write ----
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    caches = []
+    t0 = time.perf_counter()
+    for layer in range(NL):
+        c = lib.allocate_cache(shape, num_pages, B, dev, u_k=u_k_d.clone(), u_v=u_v_d.clone(),
+                               clip_k=float(ck), clip_v=float(cv))
+        for b in range(B):
+            n = int(lens[b]) - 1
+            for s0 in range(0, n, 1 << 16):
+                m = min(1 << 16, n - s0)
+                k = sample_kv_device(law, m, gen, dev)
+                v = sample_kv_device(law, m, gen, dev)
+                idx = torch.full((m,), b, dtype=torch.int32, device=dev)
+                pos = torch.arange(s0, s0 + m, dtype=torch.int32, device=dev)
+                after = torch.from_numpy(np.maximum(lens - 1, 0).astype(np.int32)).to(dev)
+                lib.kv_write(shape, c, k, v, idx, pos, table_d, after)
+        caches.append(c)
+        if layer % 6 == 5 or layer == NL - 1:
+            torch.cuda.synchronize()
+            log(f"prefilled {layer + 1}/{NL} layers ({time.perf_counter() - t0:.1f}s)")
+
+    # ---- per-step inputs: the new token of every sequence and the queries ----
+    new_k = [sample_kv_device(law, B, gen, dev) for _ in range(NL)]
+    new_v = [sample_kv_device(law, B, gen, dev) for _ in range(NL)]
+    qs = [sample_queries_device(B, Hq, gen, dev) for _ in range(NL)]
+    seq_idx = torch.arange(B, dtype=torch.int32, device=dev)
+    new_pos = torch.from_numpy((lens - 1).astype(np.int32)).to(dev)
+    lens_d = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.decode_workspace_bytes(shape, B, max_pages), dtype=torch.uint8, device=dev)
+    writes = [lib.prepare_kv_write(shape, caches[l], new_k[l], new_v[l], seq_idx, new_pos, table_d, lens_d)
+              for l in range(NL)]
+    decodes = [lib.prepare_decode_attn(shape, caches[l], qs[l], table_d, lens_d, out, ws, SIG)
+               for l in range(NL)]
+    torch.cuda.synchronize()
+
+    # HIP events on the stream the library launches on (torch's current
+    # stream), around every decode_attn of the timed steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(NL)] for _ in range(args.steps)]
+
+    def step(events):
+        for l in range(NL):
+            writes[l]()
+            if events is not None:
+                events[l][0].record()
+            decodes[l]()
+            if events is not None:
+                events[l][1].record()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(ev[s_])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec_ms = [e0.elapsed_time(e1) for row in ev for e0, e1 in row]
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    tok_s = B * args.steps / elapsed
+    dbytes = decode_bytes(lens, H, Hq)
+    wbytes = write_bytes(B, H)
+    step_bytes = NL * (dbytes + wbytes)
+    dec_avg_ms = statistics.mean(dec_ms)
+    achieved = dbytes / (dec_avg_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step:.3f} ms, decode_attn avg {dec_avg_ms * 1e3:.1f} us/layer, "
+        f"{achieved:.0f} GB/s decode, {step_bytes / (elapsed / args.steps) / 1e9:.0f} GB/s step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t_unit, reps, threads = cpu_baseline(H, NL, int(lens.max()))
+        units = B * H * NL
+        cpu = {"value": B / (t_unit * units), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": (f"fp64 oracle decode of 1 sequence x 1 KV head (4 query heads) at "
+                          f"L={int(lens.max())}, median of {reps} runs = {t_unit:.3f}s, "
+                          f"extrapolated x{units} (batch x KV heads x layers)")}
+        log(f"cpu baseline: {t_unit:.3f}s per unit, {threads} threads")
+
+    rec = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int2 codes x f16 -> f32", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "seq_len": int(lens.max()) if B else 0,
+                   "seq_len_total": int(lens.sum()), "num_q_heads": Hq, "num_kv_heads": H,
+                   "head_dim": 128, "layers": NL, "page_size": 16, "page_table": wl["table"],
+                   "sink": 64, "recent": 256, "step": "per layer: kv_write(1 token/seq) + decode_attn"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "decode_attn (rotate_q + split + reduce), per layer",
+                     "bytes_per_launch": dbytes, "avg_launch_us": dec_avg_ms * 1e3},
+        "step_hbm_gbs": step_bytes / (elapsed / args.steps) / 1e9,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

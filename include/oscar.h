@@ -1,0 +1,181 @@
+/*
+ * oscar.h -- C ABI of the MI355X (gfx950) OSCAR INT2 KV-cache library.
+ *
+ * OSCAR stores each new key/value token rotated by R_K = U_Q . H_Had . P_br
+ * (keys) or R_V = U_S . H_Had . P_br (values), clipped and quantized to INT2,
+ * in a paged cache whose first `sink` tokens and last `recent` tokens stay in
+ * BF16; decode attention reads the mixed cache in one pass.
+ *
+ * Pages (title -> tag used below):
+ *   [it] "OSCAR: Come Together AI Comprime la KV Cache a 2-bit per LLM"
+ *   [ru] "Together AI vypustila ishodniki OSCAR - INT2-kvantovanie KV-kesha
+ *         dlya dolgih kontekstov LLM" (cited by paragraph)
+ *   [es] "Resumen Tecnico: OSCAR - Rotacion Consciente de la Covarianza
+ *         Espectral Offline para Cuantizacion de Cache KV de 2 bits"
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers unless the comment says host.
+ *     They are owned by the caller; the library never allocates, frees or
+ *     synchronises, keeps no state between calls and is re-entrant.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Return codes report argument errors found on the host
+ *     and launch errors; nothing checks device memory contents.
+ *   - bf16 values travel as uint16_t bit patterns; fp16 as uint16_t.
+ *   - Row-vector convention: a stored token is k' = k R.
+ *
+ * Page block format (one 1280-byte block per physical page id and KV head;
+ * `pages` is [num_pages][num_kv_heads][1280]):
+ *   [   0,  512) K codes, token-major: slot t at byte 32*t; post-rotation
+ *                channel j at byte j/4, bits 2*(j%4).
+ *   [ 512, 1024) V codes, channel-major: channel j is the little-endian uint32
+ *                at 512 + 4*j; slot t at bits 2*t.
+ *   [1024, 1152) K group parameters, slot t at 1024 + 8*t: fp16 s0, z0, s1, z1
+ *   [1152, 1280) V group parameters, slot t at 1152 + 8*t: fp16 s0, z0, s1, z1
+ * Group g covers post-rotation channels [64g, 64g+64); a code c decodes to
+ * z_g + s_g * c.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define OSCAR_OK 0
+#define OSCAR_EINVAL 1   /* bad argument (null pointer, unsupported shape, bad size) */
+#define OSCAR_ENOWS 2    /* workspace smaller than oscar_decode_workspace_bytes() */
+#define OSCAR_EHIP 3     /* a HIP call failed; oscar_last_error() has the detail */
+
+/* Cache geometry.  The Italian page's section "Architettura del Sistema di
+ * Serving e Layout di Memoria" gives 64 BF16 sink tokens and 256 BF16 recent
+ * tokens (also configurable server flags on that page); group = 64 channels
+ * with an fp16 scale and zero per token-group is this library's INT2 format.
+ * Supported: head_dim == 128, page_size == 16, group == 64,
+ * 1 <= num_kv_heads, num_q_heads % num_kv_heads == 0,
+ * 1 <= num_q_heads / num_kv_heads <= 8, 0 <= sink <= 1024 with
+ * sink % 16 == 0, 1 <= recent <= 4096. */
+typedef struct oscar_shape {
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t sink;
+  int32_t recent;
+  int32_t group;
+} oscar_shape_t;
+
+/* One layer's cache and rotation.  Sequence "slot" b indexes the sink and ring
+ * buffers; for decode, batch entry b uses slot b.
+ *   pages          [num_pages][H_kv][1280] bytes (format above)
+ *   k_sink, v_sink bf16 [num_slots][H_kv][sink][128]; row p holds position p
+ *   k_ring, v_ring bf16 [num_slots][H_kv][recent][128]; row p % recent holds
+ *                  position p while p is inside the recent window
+ *   u_k, u_v       bf16 [H_kv][128][128] row-major U (eigenvectors in columns:
+ *                  U[i][j], i = input channel), i.e. U_Q and U_S of the
+ *                  Spanish summary, section 2.2 A.2
+ *   clip_k, clip_v per-layer clip thresholds c: rotated values are clamped to
+ *                  [-c, c] before quantization ([es] 2.2 A.4); finite,
+ *                  0 < c <= 16384. */
+typedef struct oscar_layer {
+  uint8_t* pages;
+  uint16_t* k_sink;
+  uint16_t* v_sink;
+  uint16_t* k_ring;
+  uint16_t* v_ring;
+  const uint16_t* u_k;
+  const uint16_t* u_v;
+  float clip_k;
+  float clip_v;
+} oscar_layer_t;
+
+/* kv_write -- rotate, clip, quantize and pack new tokens into the cache.
+ * [it] "Architettura del Sistema di Serving e Layout di Memoria" (each token
+ * is rotated, clipped and quantized at write time; history is INT2, sink and
+ * recent tokens BF16); [es] 2.2 B; rotation composition [it] "I tre fattori
+ * della rotazione", [ru] paragraph 3.
+ *
+ *   k, v            bf16 [num_tokens][H_kv][128]; either may be NULL (that
+ *                   half of the cache is not written)
+ *   seq_idx, pos    int32 [num_tokens]: sequence slot and position of token t
+ *   page_table      int32 [num_slots][max_pages]: physical page of logical page
+ *   seq_lens_after  int32 [num_slots]: sequence length once this call's tokens
+ *                   are in (decides which tokens enter the recent ring)
+ * For every token with pos >= sink: INT2 codes and group parameters go to
+ * page_table[seq][pos/16], slot pos%16 (also while the token is still recent,
+ * so nothing is re-encoded when it leaves the window).  pos < sink: bf16 copy
+ * to the sink row.  pos >= max(sink, seq_lens_after[seq] - recent): bf16 copy
+ * to ring row pos % recent.
+ * The caller guarantees: no two tokens of one call share a (physical page,
+ * slot) or a (seq, pos); indices are in range.  Quantization: per 64-channel
+ * group s = fp16_rne((max-min)/3), z = fp16_rne(min), code =
+ * clamp(rne((w - z)/s), 0, 3), codes 0 when s == 0.
+ * Returns OSCAR_OK, OSCAR_EINVAL or OSCAR_EHIP.  num_tokens == 0 is a no-op. */
+int oscar_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer,
+                   const uint16_t* k, const uint16_t* v, const int32_t* seq_idx,
+                   const int32_t* pos, int32_t num_tokens, const int32_t* page_table,
+                   int32_t max_pages, const int32_t* seq_lens_after, hipStream_t stream);
+
+/* Bytes of device workspace oscar_decode_attn needs for `batch` sequences
+ * whose page_table rows hold `max_pages` entries.  0 on invalid arguments. */
+size_t oscar_decode_workspace_bytes(const oscar_shape_t* shape, int32_t batch, int32_t max_pages);
+
+/* decode_attn -- one decode step of attention over the mixed-precision paged
+ * cache: the read path of [it] "Architettura del Sistema di Serving e Layout
+ * di Memoria" and [es] 2.2 B (unpack, dequantize, inverse rotation and
+ * attention in one pass).  The inverse rotation is folded: q is rotated once
+ * by R_K and the accumulated INT2 output once by R_V^T.
+ *
+ *   q          bf16 [batch][num_q_heads][128]
+ *   page_table int32 [batch][max_pages]
+ *   seq_lens   int32 [batch], 0 <= L <= 16 * max_pages
+ *   sm_scale   softmax scale (1/sqrt(128) for standard attention)
+ *   out        bf16 [batch][num_q_heads][128] (written, round to nearest even)
+ *   workspace  device scratch of at least oscar_decode_workspace_bytes(shape,
+ *              batch, max_pages) bytes, 256-byte aligned; clobbered
+ * For batch entry b, query head h, KV head h / (num_q_heads/num_kv_heads),
+ * L = seq_lens[b]: out = softmax(sm_scale * q . K^T) V over positions [0, L)
+ * where positions < min(sink, L) come from the sink rows, positions >=
+ * max(sink, L - recent) from the ring, and the rest from the INT2 pages
+ * (dequantized and inverse-rotated).  L == 0 writes zeros.
+ * Returns OSCAR_OK, OSCAR_EINVAL, OSCAR_ENOWS or OSCAR_EHIP. */
+int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer,
+                      const uint16_t* q, const int32_t* page_table, int32_t max_pages,
+                      const int32_t* seq_lens, int32_t batch, float sm_scale, uint16_t* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* calibrate_layer -- HOST, offline: the calibration of [es] 2.2 A (steps 1-4)
+ * and [ru] paragraph 2 for one layer, in fp64 on host memory.
+ *   q_cal  host double [H_kv][gqa][num_samples][128] calibration queries
+ *   k_cal, v_cal host double [H_kv][num_samples][128]
+ * Per KV head: C_Q = (1/N) sum q^T q pooled over the gqa query heads,
+ * C_S = (1/N) sum (S V)^T (S V) with S the causal softmax(sm_scale q k^T) of
+ * each query head; U_Q, U_S = eigenvectors as columns, eigenvalues
+ * descending, each column signed so its largest-|.| entry is positive;
+ * written as bf16 (nearest even) to u_k_out, u_v_out (host uint16
+ * [H_kv][128][128]).  clip_k_out / clip_v_out (host float): the `quantile`
+ * (linear interpolation) of |x U H P| over all calibration tokens, channels
+ * and heads, with the bf16 U.  num_threads <= 0 uses the hardware count.
+ * Returns OSCAR_OK or OSCAR_EINVAL. */
+int oscar_calibrate_layer(int32_t num_kv_heads, int32_t gqa, int32_t num_samples,
+                          const double* q_cal, const double* k_cal, const double* v_cal,
+                          double sm_scale, double quantile, uint16_t* u_k_out,
+                          uint16_t* u_v_out, float* clip_k_out, float* clip_v_out,
+                          int32_t num_threads);
+
+/* Static description of a return code. */
+const char* oscar_status_string(int status);
+
+/* Detail of the last OSCAR_EHIP / OSCAR_EINVAL on the calling thread. */
+const char* oscar_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

@@ -1,0 +1,21 @@
+"""MI355X (gfx950) OSCAR INT2 KV cache: rotated INT2 KV write and
+mixed-precision paged decode attention.
+
+Thin Python binding over the C ABI in include/oscar.h (liboscar_gfx950.so,
+built in-tree by ``int2_rotated_kv_write_amd.build``).  PyTorch provides
+device memory and streams; every step of the write and decode paths runs in
+the library's HIP kernels.  Importing this package does not load the library;
+the first call does, and raises if the library is missing.
+"""
+from ._native import load, library_path
+from .api import (
+    CacheBuffers, CacheShape, OscarError, allocate_cache, calibrate_layer,
+    decode_attn, decode_workspace_bytes, kv_write, prepare_decode_attn, prepare_kv_write,
+    status_string,
+)
+
+__all__ = [
+    "load", "library_path", "CacheShape", "CacheBuffers", "OscarError",
+    "allocate_cache", "kv_write", "decode_attn", "decode_workspace_bytes",
+    "calibrate_layer", "status_string", "prepare_kv_write", "prepare_decode_attn",
+]

@@ -1,0 +1,234 @@
+"""Python face of the C ABI: argument marshalling only.
+
+Every function checks tensor dtypes, devices and shapes, passes raw pointers
+and the current HIP stream to the library, and raises OscarError on a
+non-zero status.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from ._native import OscarLayer, OscarShape, load
+
+HEAD_DIM = 128
+PAGE_BLOCK = 1280
+
+
+class OscarError(RuntimeError):
+    pass
+
+
+def status_string(code: int) -> str:
+    return load().oscar_status_string(code).decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load()
+        raise OscarError(f"{lib.oscar_status_string(rc).decode()} ({rc}): {lib.oscar_last_error().decode()}")
+
+
+@dataclass(frozen=True)
+class CacheShape:
+    num_kv_heads: int
+    num_q_heads: int
+    head_dim: int = HEAD_DIM
+    page_size: int = 16
+    sink: int = 64
+    recent: int = 256
+    group: int = 64
+
+    @property
+    def gqa(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def c(self) -> OscarShape:
+        return OscarShape(self.num_kv_heads, self.num_q_heads, self.head_dim, self.page_size,
+                          self.sink, self.recent, self.group)
+
+
+@dataclass
+class CacheBuffers:
+    """One layer's device buffers (layouts in include/oscar.h)."""
+    pages: "torch.Tensor"      # uint8 [num_pages][H_kv][1280]
+    k_sink: "torch.Tensor"     # bfloat16 [slots][H_kv][sink][128]
+    v_sink: "torch.Tensor"
+    k_ring: "torch.Tensor"     # bfloat16 [slots][H_kv][recent][128]
+    v_ring: "torch.Tensor"
+    u_k: "torch.Tensor"        # bfloat16 [H_kv][128][128]
+    u_v: "torch.Tensor"
+    clip_k: float
+    clip_v: float
+
+    def c(self) -> OscarLayer:
+        return OscarLayer(self.pages.data_ptr(), self.k_sink.data_ptr(), self.v_sink.data_ptr(),
+                          self.k_ring.data_ptr(), self.v_ring.data_ptr(), self.u_k.data_ptr(),
+                          self.u_v.data_ptr(), float(self.clip_k), float(self.clip_v))
+
+
+def allocate_cache(shape: CacheShape, num_pages: int, num_slots: int, device,
+                   u_k=None, u_v=None, clip_k: float = 1.0, clip_v: float = 1.0) -> CacheBuffers:
+    import torch
+    H = shape.num_kv_heads
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device=device)
+    if u_k is None:
+        u_k = z(H, HEAD_DIM, HEAD_DIM)
+    if u_v is None:
+        u_v = z(H, HEAD_DIM, HEAD_DIM)
+    return CacheBuffers(
+        pages=z(num_pages, H, PAGE_BLOCK, dt=torch.uint8),
+        k_sink=z(num_slots, H, max(shape.sink, 1), HEAD_DIM),
+        v_sink=z(num_slots, H, max(shape.sink, 1), HEAD_DIM),
+        k_ring=z(num_slots, H, shape.recent, HEAD_DIM),
+        v_ring=z(num_slots, H, shape.recent, HEAD_DIM),
+        u_k=u_k, u_v=u_v, clip_k=clip_k, clip_v=clip_v)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t, dtype, name, shape=None):
+    import torch
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise OscarError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise OscarError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise OscarError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise OscarError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _check_cache(shape: CacheShape, cache: CacheBuffers):
+    import torch
+    H = shape.num_kv_heads
+    if cache.pages.dim() != 3 or cache.pages.shape[1:] != (H, PAGE_BLOCK):
+        raise OscarError("pages must be [num_pages][H_kv][1280]")
+    _dev(cache.pages, torch.uint8, "pages")
+    for n in ("k_sink", "v_sink", "k_ring", "v_ring"):
+        _dev(getattr(cache, n), torch.bfloat16, n)
+    for n in ("u_k", "u_v"):
+        _dev(getattr(cache, n), torch.bfloat16, n, (H, HEAD_DIM, HEAD_DIM))
+
+
+def kv_write(shape: CacheShape, cache: CacheBuffers, k, v, seq_idx, pos, page_table,
+             seq_lens_after, stream=None) -> None:
+    """oscar_kv_write: rotate, clip, quantize and pack tokens (k and/or v:
+    bfloat16 [T][H_kv][128]) into the cache."""
+    import torch
+    _check_cache(shape, cache)
+    T = int(seq_idx.numel())
+    H = shape.num_kv_heads
+    kp = _dev(k, torch.bfloat16, "k", (T, H, HEAD_DIM))
+    vp = _dev(v, torch.bfloat16, "v", (T, H, HEAD_DIM))
+    if page_table.dim() != 2:
+        raise OscarError("page_table must be [num_slots][max_pages]")
+    rc = load().oscar_kv_write(
+        ctypes.byref(shape.c()), ctypes.byref(cache.c()), kp, vp,
+        _dev(seq_idx, torch.int32, "seq_idx", (T,)), _dev(pos, torch.int32, "pos", (T,)), T,
+        _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
+        _dev(seq_lens_after, torch.int32, "seq_lens_after"), _stream(stream))
+    _check(rc)
+
+
+def decode_workspace_bytes(shape: CacheShape, batch: int, max_pages: int) -> int:
+    return int(load().oscar_decode_workspace_bytes(ctypes.byref(shape.c()), batch, max_pages))
+
+
+def decode_attn(shape: CacheShape, cache: CacheBuffers, q, page_table, seq_lens, out, workspace,
+                sm_scale: float | None = None, stream=None) -> None:
+    """oscar_decode_attn: out (bfloat16 [B][Hq][128]) = attention of q over the
+    cache for sequence lengths seq_lens (int32 [B])."""
+    import torch
+    _check_cache(shape, cache)
+    B = int(seq_lens.numel())
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if page_table.dim() != 2 or page_table.shape[0] < B:
+        raise OscarError("page_table must be [>= batch][max_pages]")
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise OscarError("workspace must be a uint8 device tensor")
+    rc = load().oscar_decode_attn(
+        ctypes.byref(shape.c()), ctypes.byref(cache.c()),
+        _dev(q, torch.bfloat16, "q", (B, shape.num_q_heads, HEAD_DIM)),
+        _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens", (B,)), B, float(sm_scale),
+        _dev(out, torch.bfloat16, "out", (B, shape.num_q_heads, HEAD_DIM)),
+        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(rc)
+
+
+def calibrate_layer(q_cal: np.ndarray, k_cal: np.ndarray, v_cal: np.ndarray, sm_scale: float,
+                    quantile: float = 0.999, num_threads: int = 0):
+    """oscar_calibrate_layer (host, offline).  q_cal float64 [H][G][N][128],
+    k_cal / v_cal float64 [H][N][128].  Returns (u_k, u_v) as uint16 bf16 bits
+    [H][128][128] and (clip_k, clip_v) as float32."""
+    q_cal = np.ascontiguousarray(q_cal, np.float64)
+    k_cal = np.ascontiguousarray(k_cal, np.float64)
+    v_cal = np.ascontiguousarray(v_cal, np.float64)
+    H, G, N, D = q_cal.shape
+    if D != HEAD_DIM or k_cal.shape != (H, N, D) or v_cal.shape != (H, N, D):
+        raise OscarError("calibration arrays: q [H][G][N][128], k/v [H][N][128]")
+    u_k = np.zeros((H, D, D), np.uint16)
+    u_v = np.zeros((H, D, D), np.uint16)
+    ck, cv = ctypes.c_float(), ctypes.c_float()
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = load().oscar_calibrate_layer(
+        H, G, N, q_cal.ctypes.data_as(dp), k_cal.ctypes.data_as(dp), v_cal.ctypes.data_as(dp),
+        float(sm_scale), float(quantile), u_k.ctypes.data, u_v.ctypes.data,
+        ctypes.byref(ck), ctypes.byref(cv), int(num_threads))
+    _check(rc)
+    return u_k, u_v, np.float32(ck.value), np.float32(cv.value)
+
+
+class PreparedCall:
+    """A library call with its ctypes arguments built once (for tight loops);
+    calling it re-issues the same launch on the same stream."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def prepare_kv_write(shape: CacheShape, cache: CacheBuffers, k, v, seq_idx, pos, page_table,
+                     seq_lens_after, stream=None) -> PreparedCall:
+    import torch
+    _check_cache(shape, cache)
+    T = int(seq_idx.numel())
+    H = shape.num_kv_heads
+    cs, cl = shape.c(), cache.c()
+    args = (ctypes.byref(cs), ctypes.byref(cl),
+            _dev(k, torch.bfloat16, "k", (T, H, HEAD_DIM)), _dev(v, torch.bfloat16, "v", (T, H, HEAD_DIM)),
+            _dev(seq_idx, torch.int32, "seq_idx", (T,)), _dev(pos, torch.int32, "pos", (T,)), T,
+            _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
+            _dev(seq_lens_after, torch.int32, "seq_lens_after"), _stream(stream))
+    return PreparedCall(load().oscar_kv_write, args, (cs, cl, k, v, seq_idx, pos, page_table, seq_lens_after))
+
+
+def prepare_decode_attn(shape: CacheShape, cache: CacheBuffers, q, page_table, seq_lens, out, workspace,
+                        sm_scale: float | None = None, stream=None) -> PreparedCall:
+    import torch
+    _check_cache(shape, cache)
+    B = int(seq_lens.numel())
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    cs, cl = shape.c(), cache.c()
+    args = (ctypes.byref(cs), ctypes.byref(cl), _dev(q, torch.bfloat16, "q", (B, shape.num_q_heads, HEAD_DIM)),
+            _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
+            _dev(seq_lens, torch.int32, "seq_lens", (B,)), B, float(sm_scale),
+            _dev(out, torch.bfloat16, "out", (B, shape.num_q_heads, HEAD_DIM)),
+            workspace.data_ptr(), workspace.numel(), _stream(stream))
+    return PreparedCall(load().oscar_decode_attn, args, (cs, cl, q, page_table, seq_lens, out, workspace))

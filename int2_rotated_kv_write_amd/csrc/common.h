@@ -1,0 +1,112 @@
+// Device helpers shared by the OSCAR gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+constexpr int kBlockBytes = 1280;   // one page block per (physical page, KV head)
+constexpr int kKCodes = 0;          // K codes, token-major [16][32 B]
+constexpr int kVCodes = 512;        // V codes, channel-major [128] uint32, slot t at bits 2t
+constexpr int kKParams = 1024;      // [16] x {fp16 s0, z0, s1, z1}
+constexpr int kVParams = 1152;
+constexpr int kMaxGqa = 8;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef short short2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;   // v_cvt_f16_f32: round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xFFFFu));
+}
+
+// fp32 <- sum of two fp16 products plus c (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
+}
+
+// fp32 <- sum of two bf16 products plus c (v_dot2_f32_bf16); bf16 x bf16 is exact in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(short2v, a), __builtin_bit_cast(short2v, b), c,
+                                         false);
+}
+
+// ---------------------------------------------------------------------------
+// Code-pair unpacking.
+//
+// A 32-bit word holds 16 two-bit codes, code k at bits 2k.  unpack16 turns it
+// into 8 fp16 pairs without any integer->float conversion: a code placed in
+// fraction bits 6-7 of an fp16 whose exponent is 2^4 reads as 16 + code; in
+// bits 8-9 under exponent 2^2 it reads as 4 + code.  Pair i holds codes
+// (k_i, k_i + 8) from the low and high halves of the word, with the constant
+// kPairBase[i] added to both.  Consumers subtract sum(base * weight).
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int pair_k(int i) {   // k of pair i
+  return i == 0 ? 3 : i == 1 ? 4 : i == 2 ? 5 : i == 3 ? 6 : i == 4 ? 7 : i == 5 ? 1 : i == 6 ? 2 : 0;
+}
+__host__ __device__ constexpr int pair_base(int i) {
+  return (i == 1 || i == 3 || i == 6) ? 4 : 16;
+}
+__host__ __device__ constexpr int pair_of_k(int k) {  // inverse of pair_k (k in 0..7)
+  return k == 3 ? 0 : k == 4 ? 1 : k == 5 ? 2 : k == 6 ? 3 : k == 7 ? 4 : k == 1 ? 5 : k == 2 ? 6 : 7;
+}
+
+__device__ __forceinline__ void unpack16(uint32_t x, uint32_t e[8]) {
+  constexpr uint32_t m16 = 0x00C000C0u, b16 = 0x4C004C00u;   // bits 6-7 -> 16 + c
+  constexpr uint32_t m4 = 0x03000300u, b4 = 0x44004400u;     // bits 8-9 -> 4 + c
+  const uint32_t r4 = x >> 4, r8 = x >> 8, l4 = x << 4, l6 = x << 6;
+  e[0] = (x & m16) | b16;    // k = 3
+  e[1] = (x & m4) | b4;      // k = 4
+  e[2] = (r4 & m16) | b16;   // k = 5
+  e[3] = (r4 & m4) | b4;     // k = 6
+  e[4] = (r8 & m16) | b16;   // k = 7
+  e[5] = (l4 & m16) | b16;   // k = 1
+  e[6] = (l4 & m4) | b4;     // k = 2
+  e[7] = (l6 & m16) | b16;   // k = 0
+}
+
+// 7-bit / 3-bit index reversal.
+__host__ __device__ constexpr int bitrev3(int x) { return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1); }
+__host__ __device__ constexpr int bitrev7(int x) {
+  return ((x & 1) << 6) | ((x & 2) << 4) | ((x & 4) << 2) | (x & 8) | ((x >> 2) & 4) | ((x >> 4) & 2) |
+         ((x >> 6) & 1);
+}
+
+__device__ __forceinline__ float wave_sum_xor(float v, int from, int to) {
+  for (int m = from; m <= to; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
+  for (int m = from; m <= to; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_min_xor(float v, int from, int to) {
+  for (int m = from; m <= to; m <<= 1) v = fminf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// Make this wave's earlier LDS writes visible to its own other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+}  // namespace oscar

@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI (oscar_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oscar {
+
+struct KvWriteLaunch {
+  const uint16_t *k, *v, *u_k, *u_v;
+  float clip_k, clip_v;
+  uint16_t *k_sink, *v_sink, *k_ring, *v_ring;
+  uint8_t* pages;
+  const int32_t *seq_idx, *pos, *page_table, *seq_lens_after;
+  int32_t num_tokens, num_kv_heads, max_pages, sink, recent;
+};
+
+// Split-K plan of one decode call: the INT2 history of each (sequence, KV
+// head) is cut into `n_split` ranges of `pages_per_split` logical pages; the
+// BF16 sink+recent tokens into `n_bsplit` chunks of 64 tokens.  Every
+// (sequence, query head) owns n_bsplit + n_split partial records.
+struct DecodePlan {
+  int32_t pages_per_split, n_split, n_bsplit, n_total;
+  size_t qrot_off, part_off, bytes;
+};
+
+constexpr int kQrotBytes = 320;      // rotated-query record per (sequence, query head)
+constexpr int kPartFloats = 132;     // m, l, 2 pad, acc[128]
+constexpr int kBf16Chunk = 64;       // BF16 tokens per split item
+
+DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t recent,
+                            int32_t batch, int32_t max_pages);
+
+struct DecodeLaunch {
+  const uint8_t* pages;
+  const uint16_t *k_sink, *v_sink, *k_ring, *v_ring, *u_k, *u_v;
+  const uint16_t* q;
+  const int32_t *page_table, *seq_lens;
+  uint16_t* out;
+  uint8_t* workspace;
+  float sm_scale;
+  int32_t num_kv_heads, num_q_heads, max_pages, batch, sink, recent;
+  DecodePlan plan;
+};
+
+int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream);
+int launch_decode(const DecodeLaunch& L, hipStream_t stream);
+
+}  // namespace oscar

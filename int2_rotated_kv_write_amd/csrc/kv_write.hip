@@ -1,0 +1,292 @@
+// kv_write: rotate (x U on MFMA, then Walsh-Hadamard and bit reversal),
+// clip, quantize to INT2 and pack new K/V tokens into the paged cache.
+//
+// Method: the Italian page "OSCAR: Come Together AI Comprime la KV Cache a
+// 2-bit per LLM", sections "I tre fattori della rotazione" (R = U H_Had P_br)
+// and "Architettura del Sistema di Serving e Layout di Memoria" (each token is
+// rotated, clipped and quantized at write time; sink and recent tokens stay
+// BF16); the Spanish summary "Resumen Tecnico: OSCAR ...", section 2.2 B.
+//
+// Work decomposition: one 256-thread block per (chunk of 16-token tiles,
+// KV head, K-or-V).  The block stages U^T in LDS once; each wave keeps all 32
+// MFMA A-fragments of U^T in registers and walks its tiles.  Per tile of 16
+// tokens the wave computes y^T = U^T x^T with 32 v_mfma_f32_16x16x32_bf16;
+// lane l then owns token l%16 and channels 16*mt + 4*(l/16) + r (mt<8, r<4),
+// so five of the seven butterfly stages are in registers and two cross lanes.
+#include "common.h"
+#include "kernels.h"
+
+namespace oscar {
+
+namespace {
+
+constexpr int kTilesPerWave = 8;    // 4 waves x 8 tiles = 512 tokens per block
+
+struct KvWriteArgs {
+  const uint16_t* x[2];
+  const uint16_t* u[2];
+  float clip[2];
+  uint16_t* sink[2];
+  uint16_t* ring[2];
+  uint8_t* pages;
+  const int32_t* seq_idx;
+  const int32_t* pos;
+  const int32_t* page_table;
+  const int32_t* lens_after;
+  int32_t num_tokens, num_heads, max_pages, sink_len, recent, num_tiles;
+  int32_t kind_of_z[2];
+};
+
+__global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ut[kHeadDim * kHeadDim];   // U^T, 32 KB
+  __shared__ __attribute__((aligned(16))) uint8_t vbytes[4][kHeadDim][16];    // V transposition
+
+  const int kind = a.kind_of_z[blockIdx.z];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15;   // token within the tile (MFMA N index)
+  const int q = lane >> 4;   // channel quarter: channels 16mt + 4q + r
+
+  // ---- stage U^T: ut[j][i] = U[i][j] ----
+  const uint16_t* U = a.u[kind] + (size_t)h * kHeadDim * kHeadDim;
+  for (int e = tid; e < kHeadDim * kHeadDim / 8; e += 256) {
+    const uint4 v = reinterpret_cast<const uint4*>(U)[e];
+    const int i = e >> 4, j0 = (e & 15) * 8;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ut[(j0 + 2 * k) * kHeadDim + i] = (uint16_t)(w[k] & 0xFFFFu);
+      ut[(j0 + 2 * k + 1) * kHeadDim + i] = (uint16_t)(w[k] >> 16);
+    }
+  }
+  __syncthreads();
+
+  // A fragment (mt, ks): rows = output channel 16mt + n', cols = input channels
+  // 32ks + 8q' .. +7 (the same k mapping as the B fragment below).
+  bf16x8 afrag[8][4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      afrag[mt][ks] = *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kHeadDim + 32 * ks + 8 * q]);
+
+  const float clip = a.clip[kind];
+  const uint16_t* X = a.x[kind];
+  uint16_t* sink_buf = a.sink[kind];
+  uint16_t* ring_buf = a.ring[kind];
+  const int params_off = kind == 0 ? kKParams : kVParams;
+
+  for (int it = 0; it < kTilesPerWave; ++it) {
+    const int tile = (blockIdx.x * kTilesPerWave + it) * 4 + wave;
+    if (tile >= a.num_tiles) break;   // wave-uniform
+    const int t = tile * 16 + n;
+    const bool valid = t < a.num_tokens;
+    const int b = valid ? a.seq_idx[t] : 0;
+    const int p = valid ? a.pos[t] : 0;
+
+    // ---- B fragments: x[t][h][32ks + 8q .. +7] ----
+    bf16x8 bfrag[4];
+    uint4 xraw[4];
+    const uint16_t* xrow = X + ((size_t)(valid ? t : 0) * a.num_heads + h) * kHeadDim;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      xraw[ks] = valid ? *reinterpret_cast<const uint4*>(xrow + 32 * ks + 8 * q) : make_uint4(0, 0, 0, 0);
+      bfrag[ks] = __builtin_bit_cast(bf16x8, xraw[ks]);
+    }
+
+    // ---- bf16 copies (sink rows, recent ring) ----
+    if (valid) {
+      if (p < a.sink_len) {
+        uint16_t* row = sink_buf + (((size_t)b * a.num_heads + h) * a.sink_len + p) * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(row + 32 * ks + 8 * q) = xraw[ks];
+      }
+      const int L_after = a.lens_after[b];
+      if (p >= max(a.sink_len, L_after - a.recent)) {
+        uint16_t* row = ring_buf + (((size_t)b * a.num_heads + h) * a.recent + (p % a.recent)) * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(row + 32 * ks + 8 * q) = xraw[ks];
+      }
+    }
+
+    // ---- y^T = U^T x^T ----
+    float v[32];   // v[4*mt + r] = channel 16mt + 4q + r of token n
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[mt][ks], bfrag[ks], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * mt + r] = acc[r];
+    }
+
+    // ---- Walsh-Hadamard over the 128 channels (Sylvester order) ----
+    // in-register bits: index bits 0,1 (channel bits 0,1) and 2,3,4 (channel bits 4,5,6)
+#pragma unroll
+    for (int s = 1; s < 32; s <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i & s) continue;
+        const float x0 = v[i], x1 = v[i | s];
+        v[i] = x0 + x1;
+        v[i | s] = x0 - x1;
+      }
+    }
+    // cross-lane bits: channel bit 2 = lane bit 4, channel bit 3 = lane bit 5
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float o = __shfl_xor(v[i], m);
+        v[i] = upper ? (o - v[i]) : (v[i] + o);
+      }
+    }
+
+    // ---- scale, clip, group min/max ----
+    // channel c = 16mt + 4q + r goes to post-rotation index j = bitrev7(c),
+    // whose group j/64 is bit 0 of c, i.e. r & 1.
+    float mn[2] = {INFINITY, INFINITY}, mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float w = v[i] * 0.08838834764831845f;
+      w = fminf(fmaxf(w, -clip), clip);
+      v[i] = w;
+      mn[i & 1] = fminf(mn[i & 1], w);
+      mx[i & 1] = fmaxf(mx[i & 1], w);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      mn[g] = wave_min_xor(mn[g], 16, 32);
+      mx[g] = wave_max_xor(mx[g], 16, 32);
+    }
+    uint32_t sbits[2], zbits[2];
+    float sf[2], zf[2], inv[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      sbits[g] = f32_to_f16_bits((mx[g] - mn[g]) / 3.0f);
+      zbits[g] = f32_to_f16_bits(mn[g]);
+      sf[g] = f16_bits_to_f32(sbits[g]);
+      zf[g] = f16_bits_to_f32(zbits[g]);
+      inv[g] = sf[g] > 0.f ? 1.0f / sf[g] : 0.f;
+    }
+    uint32_t code[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float tq = (v[i] - zf[i & 1]) * inv[i & 1];
+      tq = fminf(fmaxf(__builtin_rintf(tq), 0.f), 3.f);
+      code[i] = (uint32_t)tq;
+    }
+
+    // ---- store INT2 ----
+    const bool is_int2 = valid && p >= a.sink_len;
+    // whole aligned page written by this tile?
+    const int b0 = __shfl(b, 0), p0 = __shfl(p, 0);
+    const bool full_page = __all(is_int2 && b == b0 && p == p0 + n && (p0 & 15) == 0);
+    uint8_t* blk = nullptr;
+    const int slot = p & 15;
+    if (is_int2) {
+      const int32_t pid = a.page_table[(size_t)b * a.max_pages + (p >> 4)];
+      blk = a.pages + ((size_t)pid * a.num_heads + h) * kBlockBytes;
+    }
+    if (kind == 0) {
+      // K, token-major: post-rotation channel j = 64 r0 + 32 r1 + 16 q0 + 8 q1 + bitrev3(mt)
+      // -> halfword (j / 8) = 8 r0 + 4 r1 + 2 q0 + q1, bit 2 * bitrev3(mt).
+      if (is_int2) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t hw = 0;
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt) hw |= code[4 * mt + r] << (2 * bitrev3(mt));
+          const int hidx = 8 * (r & 1) + 4 * (r >> 1) + 2 * (q & 1) + (q >> 1);
+          *reinterpret_cast<uint16_t*>(blk + kKCodes + 32 * slot + 2 * hidx) = (uint16_t)hw;
+        }
+      }
+    } else if (full_page) {
+      // V, channel-major, whole page: transpose through LDS, write whole words.
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int mt = i >> 2, r = i & 3;
+        const int j = 64 * (r & 1) + 32 * (r >> 1) + 16 * (q & 1) + 8 * (q >> 1) + bitrev3(mt);
+        vbytes[wave][j][n] = (uint8_t)code[i];
+      }
+      wave_lds_sync();
+      const uint8_t* page_blk = nullptr;
+      {
+        const int32_t pid = a.page_table[(size_t)b0 * a.max_pages + (p0 >> 4)];
+        page_blk = a.pages + ((size_t)pid * a.num_heads + h) * kBlockBytes;
+      }
+      uint32_t words[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 by = *reinterpret_cast<const uint4*>(&vbytes[wave][2 * lane + c][0]);
+        const uint32_t parts[4] = {by.x, by.y, by.z, by.w};
+        uint32_t wv = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t y = parts[k] | (parts[k] >> 6);
+          y = (y | (y >> 12)) & 0xFFu;   // 4 two-bit codes -> one byte
+          wv |= y << (8 * k);
+        }
+        words[c] = wv;
+      }
+      *reinterpret_cast<uint2*>(const_cast<uint8_t*>(page_blk) + kVCodes + 8 * lane) = make_uint2(words[0], words[1]);
+      wave_lds_sync();
+    } else if (is_int2) {
+      // V, partial page: merge this slot's two bits into each word atomically.
+      uint32_t* words = reinterpret_cast<uint32_t*>(blk + kVCodes);
+      const uint32_t clear = ~(3u << (2 * slot));
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int mt = i >> 2, r = i & 3;
+        const int j = 64 * (r & 1) + 32 * (r >> 1) + 16 * (q & 1) + 8 * (q >> 1) + bitrev3(mt);
+        atomicAnd(&words[j], clear);
+        if (code[i]) atomicOr(&words[j], code[i] << (2 * slot));
+      }
+    }
+    if (is_int2 && q == 0) {
+      const uint32_t lo = sbits[0] | (zbits[0] << 16), hi = sbits[1] | (zbits[1] << 16);
+      *reinterpret_cast<uint2*>(blk + params_off + 8 * slot) = make_uint2(lo, hi);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream) {
+  KvWriteArgs a{};
+  int nz = 0;
+  const uint16_t* xs[2] = {L.k, L.v};
+  for (int kind = 0; kind < 2; ++kind) {
+    a.x[kind] = xs[kind];
+    if (xs[kind]) a.kind_of_z[nz++] = kind;
+  }
+  if (nz == 0 || L.num_tokens == 0) return 0;
+  a.u[0] = L.u_k;
+  a.u[1] = L.u_v;
+  a.clip[0] = L.clip_k;
+  a.clip[1] = L.clip_v;
+  a.sink[0] = L.k_sink;
+  a.sink[1] = L.v_sink;
+  a.ring[0] = L.k_ring;
+  a.ring[1] = L.v_ring;
+  a.pages = L.pages;
+  a.seq_idx = L.seq_idx;
+  a.pos = L.pos;
+  a.page_table = L.page_table;
+  a.lens_after = L.seq_lens_after;
+  a.num_tokens = L.num_tokens;
+  a.num_heads = L.num_kv_heads;
+  a.max_pages = L.max_pages;
+  a.sink_len = L.sink;
+  a.recent = L.recent;
+  a.num_tiles = (L.num_tokens + 15) / 16;
+  const int tiles_per_block = 4 * kTilesPerWave;
+  dim3 grid((a.num_tiles + tiles_per_block - 1) / tiles_per_block, L.num_kv_heads, nz);
+  hipLaunchKernelGGL(kv_write_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace oscar

@@ -1,0 +1,145 @@
+// C ABI entry points (include/oscar.h): host-side argument checks, the
+// split-K plan and kernel launches.  No allocation, no synchronisation.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/oscar.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int code, const char* fmt, const char* detail = "") {
+  std::snprintf(g_last_error, sizeof(g_last_error), fmt, detail);
+  return code;
+}
+
+int check_shape(const oscar_shape_t* s) {
+  if (!s) return fail(OSCAR_EINVAL, "shape is NULL%s");
+  if (s->head_dim != 128) return fail(OSCAR_EINVAL, "head_dim must be 128%s");
+  if (s->page_size != 16) return fail(OSCAR_EINVAL, "page_size must be 16%s");
+  if (s->group != 64) return fail(OSCAR_EINVAL, "group must be 64%s");
+  if (s->num_kv_heads < 1) return fail(OSCAR_EINVAL, "num_kv_heads must be >= 1%s");
+  if (s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads != 0)
+    return fail(OSCAR_EINVAL, "num_q_heads must be a positive multiple of num_kv_heads%s");
+  if (s->num_q_heads / s->num_kv_heads > 8) return fail(OSCAR_EINVAL, "num_q_heads / num_kv_heads must be <= 8%s");
+  if (s->sink < 0 || s->sink > 1024 || s->sink % 16 != 0)
+    return fail(OSCAR_EINVAL, "sink must be a multiple of 16 in [0, 1024]%s");
+  if (s->recent < 1 || s->recent > 4096) return fail(OSCAR_EINVAL, "recent must be in [1, 4096]%s");
+  return OSCAR_OK;
+}
+
+bool clip_ok(float c) { return std::isfinite(c) && c > 0.f && c <= 16384.f; }
+
+int hip_fail(const char* what) {
+  const hipError_t e = hipGetLastError();
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
+  return OSCAR_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* oscar_status_string(int status) {
+  switch (status) {
+    case OSCAR_OK: return "ok";
+    case OSCAR_EINVAL: return "invalid argument";
+    case OSCAR_ENOWS: return "workspace too small";
+    case OSCAR_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* oscar_last_error(void) { return g_last_error; }
+
+int oscar_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* k, const uint16_t* v,
+                   const int32_t* seq_idx, const int32_t* pos, int32_t num_tokens, const int32_t* page_table,
+                   int32_t max_pages, const int32_t* seq_lens_after, hipStream_t stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (!layer) return fail(OSCAR_EINVAL, "layer is NULL%s");
+  if (num_tokens < 0) return fail(OSCAR_EINVAL, "num_tokens < 0%s");
+  if (max_pages < 1) return fail(OSCAR_EINVAL, "max_pages must be >= 1%s");
+  if (num_tokens == 0 || (!k && !v)) return OSCAR_OK;
+  if (!seq_idx || !pos || !page_table || !seq_lens_after || !layer->pages)
+    return fail(OSCAR_EINVAL, "NULL index array or pages%s");
+  if (k && (!layer->u_k || !layer->k_ring || (shape->sink > 0 && !layer->k_sink) || !clip_ok(layer->clip_k)))
+    return fail(OSCAR_EINVAL, "K half: NULL u_k/k_ring/k_sink or clip_k outside (0, 16384]%s");
+  if (v && (!layer->u_v || !layer->v_ring || (shape->sink > 0 && !layer->v_sink) || !clip_ok(layer->clip_v)))
+    return fail(OSCAR_EINVAL, "V half: NULL u_v/v_ring/v_sink or clip_v outside (0, 16384]%s");
+  oscar::KvWriteLaunch L{};
+  L.k = k;
+  L.v = v;
+  L.u_k = layer->u_k;
+  L.u_v = layer->u_v;
+  L.clip_k = layer->clip_k;
+  L.clip_v = layer->clip_v;
+  L.k_sink = layer->k_sink;
+  L.v_sink = layer->v_sink;
+  L.k_ring = layer->k_ring;
+  L.v_ring = layer->v_ring;
+  L.pages = layer->pages;
+  L.seq_idx = seq_idx;
+  L.pos = pos;
+  L.page_table = page_table;
+  L.seq_lens_after = seq_lens_after;
+  L.num_tokens = num_tokens;
+  L.num_kv_heads = shape->num_kv_heads;
+  L.max_pages = max_pages;
+  L.sink = shape->sink;
+  L.recent = shape->recent;
+  if (oscar::launch_kv_write(L, stream)) return hip_fail("kv_write launch");
+  return OSCAR_OK;
+}
+
+size_t oscar_decode_workspace_bytes(const oscar_shape_t* shape, int32_t batch, int32_t max_pages) {
+  if (check_shape(shape) || batch < 0 || max_pages < 1) return 0;
+  return oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink, shape->recent, batch,
+                                 max_pages)
+      .bytes;
+}
+
+int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q,
+                      const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                      float sm_scale, uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (!layer) return fail(OSCAR_EINVAL, "layer is NULL%s");
+  if (batch < 0) return fail(OSCAR_EINVAL, "batch < 0%s");
+  if (max_pages < 1) return fail(OSCAR_EINVAL, "max_pages must be >= 1%s");
+  if (!std::isfinite(sm_scale)) return fail(OSCAR_EINVAL, "sm_scale is not finite%s");
+  if (batch == 0) return OSCAR_OK;
+  if (!q || !page_table || !seq_lens || !out || !layer->pages || !layer->k_ring || !layer->v_ring || !layer->u_k ||
+      !layer->u_v || (shape->sink > 0 && (!layer->k_sink || !layer->v_sink)))
+    return fail(OSCAR_EINVAL, "NULL tensor pointer%s");
+  const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
+                                                         shape->recent, batch, max_pages);
+  if (!workspace || workspace_bytes < plan.bytes) return fail(OSCAR_ENOWS, "workspace smaller than required%s");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned%s");
+  oscar::DecodeLaunch L{};
+  L.pages = layer->pages;
+  L.k_sink = layer->k_sink;
+  L.v_sink = layer->v_sink;
+  L.k_ring = layer->k_ring;
+  L.v_ring = layer->v_ring;
+  L.u_k = layer->u_k;
+  L.u_v = layer->u_v;
+  L.q = q;
+  L.page_table = page_table;
+  L.seq_lens = seq_lens;
+  L.out = out;
+  L.workspace = static_cast<uint8_t*>(workspace);
+  L.sm_scale = sm_scale;
+  L.num_kv_heads = shape->num_kv_heads;
+  L.num_q_heads = shape->num_q_heads;
+  L.max_pages = max_pages;
+  L.batch = batch;
+  L.sink = shape->sink;
+  L.recent = shape->recent;
+  L.plan = plan;
+  if (oscar::launch_decode(L, stream)) return hip_fail("decode launch");
+  return OSCAR_OK;
+}
+
+}  // extern "C"

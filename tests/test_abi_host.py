@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/oscar.h declares, and rejects bad arguments before
+any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int2_rotated_kv_write_amd as lib
+from int2_rotated_kv_write_amd._native import OscarLayer, OscarShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "oscar.h")).read()
+    return sorted(set(re.findall(r"\b(oscar_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = lib.load()
+    names = header_functions()
+    assert len(names) >= 6
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert lib.status_string(0) == "ok"
+    assert lib.status_string(1) == "invalid argument"
+    assert lib.status_string(2) == "workspace too small"
+    assert lib.status_string(3) == "HIP error"
+
+
+def good_shape(**kw):
+    d = dict(num_kv_heads=8, num_q_heads=32, head_dim=128, page_size=16, sink=64, recent=256, group=64)
+    d.update(kw)
+    return OscarShape(**d)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(head_dim=64), dict(page_size=32), dict(group=128), dict(num_kv_heads=0),
+    dict(num_q_heads=30), dict(num_q_heads=8 * 9), dict(sink=10), dict(sink=2048),
+    dict(recent=0), dict(recent=5000),
+])
+def test_bad_shapes_rejected(bad):
+    L = lib.load()
+    s = good_shape(**bad)
+    layer = OscarLayer()
+    rc = L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), 1, 1, 1, 1, 4, 1, 8, 1, None)
+    assert rc == 1
+    assert L.oscar_decode_workspace_bytes(ctypes.byref(s), 2, 10) == 0
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), 1, 1, 8, 1, 2, 0.1, 1, 1, 1 << 30, None)
+    assert rc == 1
+    assert L.oscar_last_error()
+
+
+def test_null_and_range_arguments_rejected():
+    L = lib.load()
+    s = good_shape()
+    assert L.oscar_kv_write(None, None, 1, 1, 1, 1, 4, 1, 8, 1, None) == 1
+    layer = OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1,
+                       clip_k=4.0, clip_v=4.0)
+    # negative token count, zero max_pages, NULL index arrays
+    assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), 1, 1, 1, 1, -1, 1, 8, 1, None) == 1
+    assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), 1, 1, 1, 1, 4, 1, 0, 1, None) == 1
+    assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), 1, 1, None, 1, 4, 1, 8, 1, None) == 1
+    # clip thresholds must be finite and in (0, 16384]
+    for c in (0.0, -1.0, float("inf"), float("nan"), 20000.0):
+        bad = OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1, clip_k=c, clip_v=4.0)
+        assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(bad), 1, None, 1, 1, 4, 1, 8, 1, None) == 1
+    # zero tokens, or neither k nor v: nothing to do
+    assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), 1, 1, 1, 1, 0, 1, 8, 1, None) == 0
+    assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), None, None, 1, 1, 4, 1, 8, 1, None) == 0
+
+
+def test_decode_workspace_checks():
+    L = lib.load()
+    s = good_shape()
+    layer = OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1,
+                       clip_k=4.0, clip_v=4.0)
+    need = L.oscar_decode_workspace_bytes(ctypes.byref(s), 28, 6250)
+    assert need > 28 * 32 * 320
+    # too small -> ENOWS; misaligned -> EINVAL; batch 0 -> OK without touching anything
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), 1, 1, 6250, 1, 28, 0.088, 1, 256, need - 1, None)
+    assert rc == 2
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), 1, 1, 6250, 1, 28, 0.088, 1, 257, need, None)
+    assert rc == 1
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), 1, 1, 6250, 1, 0, 0.088, 1, None, 0, None)
+    assert rc == 0
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), None, 1, 6250, 1, 28, 0.088, 1, 256, need, None)
+    assert rc == 1
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), 1, 1, 6250, 1, 28, float("nan"), 1, 256, need,
+                             None)
+    assert rc == 1
+
+
+def test_workspace_grows_with_batch_and_pages():
+    L = lib.load()
+    s = good_shape()
+    a = L.oscar_decode_workspace_bytes(ctypes.byref(s), 1, 100)
+    b = L.oscar_decode_workspace_bytes(ctypes.byref(s), 2, 100)
+    c = L.oscar_decode_workspace_bytes(ctypes.byref(s), 2, 10000)
+    assert 0 < a < b < c

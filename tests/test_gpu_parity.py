@@ -1,0 +1,150 @@
+"""GPU parity: the HIP kv_write and decode_attn against the fp64 oracle on
+the same seeded inputs (rules in gpu_harness.py).
+
+Each case writes the same tokens through both paths and compares the caches,
+then runs decode (a) on an upload of the oracle-written cache, isolating the
+decode kernels, and (b) on the GPU-written cache, end to end."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from gpu_harness import (SIG, compare_kv_write, compare_outputs, device_cache, from_dev_bf16,
+                         host_cache, lib_shape, to_dev_bf16, to_dev_i32)
+
+pytestmark = pytest.mark.gpu
+
+
+def make_layer(rng, shape, law, n_cal):
+    qc, kc, vc = synth.calibration_samples(rng, law, shape.gqa, n_cal)
+    cal = O.calibrate_layer(qc, kc, vc, SIG)
+    return O.Layer(cal["u_k"], cal["u_v"], cal["clip_k"], cal["clip_v"])
+
+
+def run_scenario(device, shape, layer, law, lens, table, calls, rng, seed_q=0, check_each_call=True):
+    """calls: list of (seq_idx, pos) arrays; lens_after derived per call."""
+    import torch
+    import int2_rotated_kv_write_amd as lib
+    n_slots = len(lens)
+    num_pages = int(table.max()) + 1
+    H = shape.num_kv_heads
+    ref = O.new_cache(shape, num_pages, n_slots)
+    dc = device_cache(shape, ref, layer, device)
+    ls = lib_shape(shape)
+    # token values for every (slot, pos)
+    Lmax = max(max(lens), 1)
+    kvals = np.stack([law.sample_bf16(rng, Lmax) for _ in range(n_slots)])   # [S][L][H][128]
+    vvals = np.stack([law.sample_bf16(rng, Lmax) for _ in range(n_slots)])
+    written = np.zeros(n_slots, np.int64)
+    table_d = to_dev_i32(table, device)
+    stats_all = []
+    for seq_idx, pos in calls:
+        seq_idx = np.asarray(seq_idx, np.int64)
+        pos = np.asarray(pos, np.int64)
+        for s, p in zip(seq_idx, pos):
+            written[s] = max(written[s], p + 1)
+        lens_after = written.copy()
+        k = kvals[seq_idx, pos]
+        v = vvals[seq_idx, pos]
+        got_before = host_cache(dc) if check_each_call else None
+        info = O.kv_write(shape, ref, layer, k, v, seq_idx, pos, table, lens_after)
+        lib.kv_write(ls, dc, to_dev_bf16(k, device), to_dev_bf16(v, device), to_dev_i32(seq_idx, device),
+                     to_dev_i32(pos, device), table_d, to_dev_i32(lens_after, device))
+        torch.cuda.synchronize()
+        if check_each_call:
+            stats_all.append(compare_kv_write(shape, ref, host_cache(dc), info, got_before))
+    # decode at the final lengths
+    B = n_slots
+    q = synth.decode_queries(np.random.default_rng(seed_q), B, shape.num_q_heads)
+    out_ref = O.decode(shape, ref, layer, q, table, lens, SIG)
+    ws = torch.empty(lib.decode_workspace_bytes(ls, B, table.shape[1]), dtype=torch.uint8, device=device)
+    q_d = to_dev_bf16(q, device)
+    lens_d = to_dev_i32(lens, device)
+    results = {}
+    for name, cache in (("oracle-written", device_cache(shape, ref, layer, device)), ("gpu-written", dc)):
+        out = torch.empty((B, shape.num_q_heads, 128), dtype=torch.bfloat16, device=device)
+        out.fill_(float("nan"))
+        lib.decode_attn(ls, cache, q_d, table_d, lens_d, out, ws, SIG)
+        torch.cuda.synchronize()
+        results[name] = compare_outputs(from_dev_bf16(out), out_ref)
+    return stats_all, results
+
+
+def test_tiny_gqa4_1k_write_and_decode(gpu):
+    """1 sequence, 1 KV head, 4 query heads, 1024 tokens (64 sink / 704 INT2 /
+    256 recent), outlier law, calibration on 2048 samples, seed 0."""
+    rng = np.random.default_rng(0)
+    shape = O.Shape(num_kv_heads=1, num_q_heads=4)
+    law = synth.outlier_law(rng, 1)
+    layer = make_layer(rng, shape, law, 2048)
+    L = 1024
+    table = synth.contiguous_page_table(1, 64)
+    stats, res = run_scenario(gpu, shape, layer, law, [L], table, [(np.zeros(L), np.arange(L))], rng)
+    print("write stats", stats, "decode", res, flush=True)
+    assert stats[0]["codes"] == 2 * 960 * 128
+
+
+def test_chunked_and_single_token_writes(gpu):
+    """Unaligned prefill chunks and one-token decode steps (partial pages),
+    including tokens that enter and leave the recent ring."""
+    rng = np.random.default_rng(1)
+    shape = O.Shape(num_kv_heads=2, num_q_heads=8)
+    law = synth.outlier_law(rng, 2)
+    layer = make_layer(rng, shape, law, 256)
+    table = synth.permuted_page_table(rng, 1, 40)
+    calls = [(np.zeros(100), np.arange(100)), (np.zeros(257), np.arange(100, 357))]
+    calls += [([0], [p]) for p in range(357, 420)]
+    stats, res = run_scenario(gpu, shape, layer, law, [420], table, calls, rng)
+    print("decode", res, flush=True)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+def test_ragged_batch_permuted_pages(gpu, G):
+    """Lengths at every region edge in one batch; tokens of all sequences
+    interleaved in one write call; random disjoint page tables."""
+    rng = np.random.default_rng(10 + G)
+    shape = O.Shape(num_kv_heads=2, num_q_heads=2 * G)
+    law = synth.outlier_law(rng, 2)
+    layer = make_layer(rng, shape, law, 256)
+    lens = [0, 1, 63, 64, 65, 320, 321, 333, 1000, 2049]
+    max_pages = 130
+    table = synth.permuted_page_table(rng, len(lens), max_pages)
+    seq_idx = np.concatenate([np.full(L, s) for s, L in enumerate(lens)])
+    pos = np.concatenate([np.arange(L) for L in lens])
+    perm = rng.permutation(len(pos))
+    stats, res = run_scenario(gpu, shape, layer, law, lens, table, [(seq_idx[perm], pos[perm])], rng)
+    print("G", G, "decode", res, flush=True)
+
+
+@pytest.mark.parametrize("sink,recent", [(16, 32), (0, 1), (128, 100)])
+def test_other_sink_and_recent_sizes(gpu, sink, recent):
+    rng = np.random.default_rng(sink + recent)
+    shape = O.Shape(num_kv_heads=1, num_q_heads=4, sink=sink, recent=recent)
+    law = synth.heavy_tail_law(rng, 1)
+    layer = make_layer(rng, shape, law, 256)
+    lens = [5, sink + recent + 7, 700]
+    table = synth.permuted_page_table(rng, 3, 50)
+    calls = [(np.full(L, s), np.arange(L)) for s, L in enumerate(lens)]
+    stats, res = run_scenario(gpu, shape, layer, law, lens, table, calls, rng)
+    print(sink, recent, "decode", res, flush=True)
+
+
+def test_zero_length_and_empty_calls(gpu):
+    import torch
+    import int2_rotated_kv_write_amd as lib
+    shape = O.Shape(num_kv_heads=1, num_q_heads=2)
+    ls = lib_shape(shape)
+    layer = O.Layer(np.zeros((1, 128, 128), np.uint16), np.zeros((1, 128, 128), np.uint16),
+                    np.float32(1), np.float32(1))
+    dc = device_cache(shape, O.new_cache(shape, 4, 1), layer, gpu)
+    t = to_dev_i32(np.zeros((1, 4)), gpu)
+    e = torch.empty(0, dtype=torch.int32, device=gpu)
+    lib.kv_write(ls, dc, None, None, e, e, t, to_dev_i32([0], gpu))   # nothing to write
+    out = torch.full((1, 2, 128), 7.0, dtype=torch.bfloat16, device=gpu)
+    ws = torch.empty(lib.decode_workspace_bytes(ls, 1, 4), dtype=torch.uint8, device=gpu)
+    lib.decode_attn(ls, dc, torch.zeros((1, 2, 128), dtype=torch.bfloat16, device=gpu), t,
+                    to_dev_i32([0], gpu), out, ws)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all()
