@@ -188,6 +188,12 @@ def main():
     lens_d = torch.from_numpy(lens.astype(np.int32)).to(dev)
     out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(lib.decode_workspace_bytes(shape, B, max_pages), dtype=torch.uint8, device=dev)
+    # reference kernel of known size for calibrating HBM counters: reads and
+    # writes 256 MiB once (outside the timed region)
+    ref_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    ref_dst = torch.empty_like(ref_src)
+    torch.mul(ref_src, 1.0, out=ref_dst)
+    del ref_src, ref_dst
     writes = [lib.prepare_kv_write(shape, caches[l], new_k[l], new_v[l], seq_idx, new_pos, table_d, lens_d)
               for l in range(NL)]
     decodes = [lib.prepare_decode_attn(shape, caches[l], qs[l], table_d, lens_d, out, ws, SIG)

@@ -102,6 +102,45 @@ __device__ __forceinline__ float wave_min_xor(float v, int from, int to) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane reductions without LDS traffic: DPP inside a 16-lane row, the
+// gfx950 permlane swaps across rows.  "tok" reductions combine the lanes that
+// share lane%4 (stride 4), "quad" ones the 4 lanes of a quad.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+__device__ __forceinline__ float swap16(float x, bool is_max) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return is_max ? fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float swap32(float x, bool is_max) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return is_max ? fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp<kQuadXor1>(x);
+  return x + dpp<kQuadXor2>(x);
+}
+// reduce over the 16 lanes with the same lane%4 (all four rows, stride 4)
+__device__ __forceinline__ float tok_max(float x) {
+  x = fmaxf(x, dpp<kRowRor4>(x));
+  x = fmaxf(x, dpp<kRowRor8>(x));
+  return swap32(swap16(x, true), true);
+}
+__device__ __forceinline__ float tok_sum(float x) {
+  x += dpp<kRowRor4>(x);
+  x += dpp<kRowRor8>(x);
+  return swap32(swap16(x, false), false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Make this wave's earlier LDS writes visible to its own other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");

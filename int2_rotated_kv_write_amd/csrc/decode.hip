@@ -129,7 +129,10 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // split: block (item, KV head, sequence), 4 waves.
 // ---------------------------------------------------------------------------
+constexpr int kMaxPagesPerSplit = 128;
+
 struct __attribute__((aligned(16))) SplitSmem {
+  int32_t pid[kMaxPagesPerSplit];    // physical page ids of the item's page range
   uint32_t w[4][kMaxGqa][2][8];      // fp16 pairs of p*s per (wave, head, group, pair)
   float p[4][kMaxGqa][16];           // BF16 items: probabilities per token
   float m[4][kMaxGqa];
@@ -288,15 +291,37 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 #pragma unroll
   for (int jj = 0; jj < NJ; ++jj) zacc[jj][0] = zacc[jj][1] = oacc[jj][0] = oacc[jj][1] = 0.f;
 
-  const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+  // physical page ids of this item, once per block
+  {
+    const int32_t* ptab = a.page_table + (size_t)b * a.max_pages + first;
+    for (int i = threadIdx.x; i < end - first; i += 256) sm.pid[i] = ptab[i];
+    __syncthreads();
+  }
   uint16_t* wl = reinterpret_cast<uint16_t*>(&sm.w[wave][0][0][0]);
+  const size_t head_off = (size_t)h * kBlockBytes;
+  const size_t page_stride = (size_t)a.H * kBlockBytes;
 
-  for (int pg = first + wave; pg < end; pg += 4) {
-    const uint8_t* blk = a.pages + ((size_t)ptab[pg] * a.H + h) * kBlockBytes;
-    const uint2 kc = *reinterpret_cast<const uint2*>(blk + kKCodes + 32 * t + 8 * q);
-    const uint32_t kp = *reinterpret_cast<const uint32_t*>(blk + kKParams + 8 * t + 4 * (q >> 1));
-    const uint2 vc = *reinterpret_cast<const uint2*>(blk + kVCodes + 8 * lane);
-    const uint2 vp = *reinterpret_cast<const uint2*>(blk + kVParams + 8 * t);
+  struct PageRegs {
+    uint2 kc, vc, vp;
+    uint32_t kp;
+  };
+  auto load_page = [&](int pg) {
+    const uint8_t* blk = a.pages + (size_t)sm.pid[pg - first] * page_stride + head_off;
+    PageRegs r;
+    r.kc = *reinterpret_cast<const uint2*>(blk + kKCodes + 32 * t + 8 * q);
+    r.kp = *reinterpret_cast<const uint32_t*>(blk + kKParams + 8 * t + 4 * (q >> 1));
+    r.vc = *reinterpret_cast<const uint2*>(blk + kVCodes + 8 * lane);
+    r.vp = *reinterpret_cast<const uint2*>(blk + kVParams + 8 * t);
+    return r;
+  };
+
+  int pg = first + wave;
+  PageRegs cur = {}, nxt = {};
+  if (pg < end) cur = load_page(pg);
+  for (; pg < end; pg += 4) {
+    if (pg + 4 < end) nxt = load_page(pg + 4);   // keep the next page in flight
+    const uint2 kc = cur.kc, vc = cur.vc, vp = cur.vp;
+    const uint32_t kp = cur.kp;
 
     // ---- logits (base-2 units): exact integer dot of Q with the codes ----
     uint32_t bv[8];   // byte vectors: bv[4w + j] holds channels 16(2q+w) + 4b + j
@@ -317,9 +342,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
         dl = (int)__builtin_amdgcn_udot4(qlo[hh][k], bv[k], (uint32_t)dl, false);
       }
       const float d = (float)(dh * 256 + dl) * alpha_q[hh];
-      float x = fmaf(ks, d, kz * qsum[hh]);
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
+      const float x = quad_sum(fmaf(ks, d, kz * qsum[hh]));
       lg[hh] = tok_ok ? x : -INFINITY;
     }
 
@@ -327,9 +350,9 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     float alpha[G], pr[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float mn = fmaxf(m[hh], wave_max_xor(lg[hh], 4, 32));
-      alpha[hh] = exp2f(m[hh] - mn);
-      pr[hh] = tok_ok ? exp2f(lg[hh] - mn) : 0.f;
+      const float mn = fmaxf(m[hh], tok_max(lg[hh]));
+      alpha[hh] = fast_exp2(m[hh] - mn);
+      pr[hh] = tok_ok ? fast_exp2(lg[hh] - mn) : 0.f;
       m[hh] = mn;
       lp[hh] = fmaf(lp[hh], alpha[hh], pr[hh]);
     }
@@ -378,18 +401,17 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
       acc[hh][0] = a0;
       acc[hh][1] = a1;
     }
+    cur = nxt;
   }
 
   // ---- finish the wave: l, and acc += sum(p z) - sum(base * p s) ----
   float lsum[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) lsum[hh] = wave_sum_xor(lp[hh], 4, 32);
+  for (int hh = 0; hh < G; ++hh) lsum[hh] = tok_sum(lp[hh]);
 #pragma unroll
   for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      zacc[jj][g] = wave_sum_xor(zacc[jj][g] - oacc[jj][g], 4, 32);
-    }
+    for (int g = 0; g < 2; ++g) zacc[jj][g] = tok_sum(zacc[jj][g] - oacc[jj][g]);
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const float d0 = __shfl(zacc[hh / 4][0], hh % 4);
