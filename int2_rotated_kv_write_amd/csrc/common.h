@@ -68,9 +68,17 @@ __host__ __device__ constexpr int pair_of_k(int k) {  // inverse of pair_k (k in
   return k == 3 ? 0 : k == 4 ? 1 : k == 5 ? 2 : k == 6 ? 3 : k == 7 ? 4 : k == 1 ? 5 : k == 2 ? 6 : 7;
 }
 
-__device__ __forceinline__ void unpack16(uint32_t x, uint32_t e[8]) {
-  constexpr uint32_t m16 = 0x00C000C0u, b16 = 0x4C004C00u;   // bits 6-7 -> 16 + c
-  constexpr uint32_t m4 = 0x03000300u, b4 = 0x44004400u;     // bits 8-9 -> 4 + c
+// Masks and bases live in VGPRs so that (x & m) | b is one v_and_or_b32
+// (a VOP3 instruction cannot take two literal constants on gfx9).
+struct PairConsts {
+  uint32_t m16, b16, m4, b4;
+  __device__ __forceinline__ PairConsts() : m16(0x00C000C0u), b16(0x4C004C00u), m4(0x03000300u), b4(0x44004400u) {
+    asm volatile("" : "+v"(m16), "+v"(b16), "+v"(m4), "+v"(b4));
+  }
+};
+
+__device__ __forceinline__ void unpack16(uint32_t x, uint32_t e[8], const PairConsts& k) {
+  const uint32_t m16 = k.m16, b16 = k.b16, m4 = k.m4, b4 = k.b4;   // bits 6-7 -> 16 + c, 8-9 -> 4 + c
   const uint32_t r4 = x >> 4, r8 = x >> 8, l4 = x << 4, l6 = x << 6;
   e[0] = (x & m16) | b16;    // k = 3
   e[1] = (x & m4) | b4;      // k = 4

@@ -9,9 +9,12 @@
 // The inverse rotation is folded instead of applied per token: with
 // k_hat = k_hat' R_K^T, q . k_hat = (q R_K) . k_hat', and
 // sum_i p_i v_hat_i = (sum_i p_i v_hat'_i) R_V^T.  Three launches:
-//   rotate_q  q' = q U_K H P (times sm_scale*log2 e) once per (sequence, head)
-//   split     split-K over the pages: BF16 chunks with the plain q, INT2 page
-//             ranges with q' on the packed codes; online softmax in base 2
+//   rotate_q  q' = q U_K H P (times sm_scale*log2 e) once per (sequence, head),
+//             stored as fp16 hi/lo MFMA fragments
+//   split     split-K over the pages: BF16 chunks with the plain q; INT2 page
+//             ranges on v_mfma_f32_16x16x32_f16 -- logits = codes x q' (the
+//             G query heads of a KV head share every code) and acc = (p s) x
+//             codes; online softmax in base 2
 //   reduce    log-sum-exp merge, acc_rot R_V^T = ((acc_rot P) H) U_V^T, bf16 out
 #include "common.h"
 #include "kernels.h"
@@ -20,19 +23,17 @@ namespace oscar {
 
 namespace {
 
-// Rotated query of one (sequence, query head), as 16-bit fixed point:
-// q'_c = alpha * Q_c with Q_c = rne(q'_c / alpha) in [-32767, 32767] and
-// alpha = max|q'| / 32767; Q_c = 256 * hi_c + lo_c with hi_c a signed byte and
-// lo_c an unsigned byte.  For chunk q (post-rotation channels 32q .. 32q+31 =
-// code words d = 2q, 2q+1), limb[16q + 4w + j] (w = 0, 1) packs the hi bytes
-// of channels 16d + j, +4, +8, +12 (byte b holds channel 16d + 4b + j) and
-// limb[16q + 8 + 4w + j] the lo bytes, matching the byte vectors
-// (word >> 2j) & 0x03030303 of code word d.
+// Rotated query of one (sequence, query head) as B fragments of the logit
+// MFMA.  q' = hi + lo with hi = fp16(q'), lo = fp16(q' - hi) (about 22
+// significant bits).  frag[g][kh][limb][c] are the four registers that lane
+// (column = head, k-group c) feeds to the MFMA over group g, k-half kh: pair v
+// holds channels (64g + 16c + k_i, +8) with i = 4 kh + v and k_i = pair_k(i),
+// the same pairs unpack16 makes of code word c of group g.
 struct QrotRecord {
-  uint32_t limb[64];
-  float alpha;
-  float qsum[4];   // sum_c q'_c over each chunk (fp32)
-  float pad[11];
+  uint32_t frag[2][2][2][4][4];
+  float negc[2];   // -sum over the group of (hi + lo)_c * base(c): MFMA accumulator start
+  float qsum[2];   // sum over the group of q'_c (fp32), for the zero-point term
+  float pad[12];
 };
 static_assert(sizeof(QrotRecord) == kQrotBytes, "record size");
 
@@ -58,71 +59,57 @@ __device__ __forceinline__ int int2_end(int L, int sink, int recent) {   // INT2
 // ---------------------------------------------------------------------------
 // rotate_q: one block per (sequence, KV head); two query heads at a time.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
-  __shared__ float y[2][kHeadDim];
-  __shared__ float qs[2][kHeadDim];
-  __shared__ int32_t qi[2][kHeadDim];
-  __shared__ float amax[2][4];
-  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const int tid = threadIdx.x, hl = tid >> 7, j = tid & 127;
+__global__ __launch_bounds__(128) void rotate_q_kernel(DecodeArgs a) {
+  __shared__ float y[kHeadDim];
+  __shared__ float qs[kHeadDim];
+  __shared__ uint16_t qh[kHeadDim], ql[kHeadDim];
+  const int bq = blockIdx.x, b = bq / a.Hq, hq = bq % a.Hq, h = hq / a.G;
+  const int j = threadIdx.x;
   const uint16_t* U = a.u_k + (size_t)h * kHeadDim * kHeadDim;
-  for (int h0 = 0; h0 < a.G; h0 += 2) {
-    const int hh = h0 + hl;
-    const bool act = hh < a.G;
-    const int hq = h * a.G + hh;
-    if (act) {
-      const uint16_t* qv = a.q + ((size_t)b * a.Hq + hq) * kHeadDim;
-      float acc = 0.f;
-      for (int i = 0; i < kHeadDim; ++i)
-        acc = fmaf(bf16_bits_to_f32(qv[i]), bf16_bits_to_f32(U[i * kHeadDim + j]), acc);
-      y[hl][j] = acc;
+  const uint16_t* qv = a.q + (size_t)bq * kHeadDim;
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int i = 0; i < kHeadDim; i += 2) {
+    acc0 = fmaf(bf16_bits_to_f32(qv[i]), bf16_bits_to_f32(U[i * kHeadDim + j]), acc0);
+    acc1 = fmaf(bf16_bits_to_f32(qv[i + 1]), bf16_bits_to_f32(U[(i + 1) * kHeadDim + j]), acc1);
+  }
+  y[j] = acc0 + acc1;
+  __syncthreads();
+  for (int s = 1; s < kHeadDim; s <<= 1) {
+    if (j < 64) {
+      const int lo = ((j & ~(s - 1)) << 1) | (j & (s - 1)), hi = lo | s;
+      const float x0 = y[lo], x1 = y[hi];
+      y[lo] = x0 + x1;
+      y[hi] = x0 - x1;
     }
     __syncthreads();
-    for (int s = 1; s < kHeadDim; s <<= 1) {
-      if (act && j < 64) {
-        const int lo = ((j & ~(s - 1)) << 1) | (j & (s - 1)), hi = lo | s;
-        const float x0 = y[hl][lo], x1 = y[hl][hi];
-        y[hl][lo] = x0 + x1;
-        y[hl][hi] = x0 - x1;
-      }
-      __syncthreads();
+  }
+  {
+    const float w = y[bitrev7(j)] * 0.08838834764831845f * a.sl2e;   // (z P)_j = z_br(j)
+    const uint32_t hb = f32_to_f16_bits(w);
+    qs[j] = w;
+    qh[j] = (uint16_t)hb;
+    ql[j] = (uint16_t)f32_to_f16_bits(w - f16_bits_to_f32(hb));
+  }
+  __syncthreads();
+  QrotRecord* rec = a.qrot + bq;
+  {
+    // j = (((g*2 + kh)*2 + limb)*4 + c)*4 + v
+    const int v = j & 3, c = (j >> 2) & 3, limb = (j >> 4) & 1, kh = (j >> 5) & 1, g = (j >> 6) & 1;
+    const int ch = 64 * g + 16 * c + pair_k(4 * kh + v);
+    const uint16_t* src = limb ? ql : qh;
+    (&rec->frag[0][0][0][0][0])[j] = (uint32_t)src[ch] | ((uint32_t)src[ch + 8] << 16);
+  }
+  if (j < 4) {
+    const int g = j & 1;
+    float sum = 0.f;
+    for (int c = 64 * g; c < 64 * g + 64; ++c) {
+      if (j < 2)
+        sum -= (float)pair_base(pair_of_k(c & 7)) * (f16_bits_to_f32(qh[c]) + f16_bits_to_f32(ql[c]));
+      else
+        sum += qs[c];
     }
-    float w = 0.f;
-    if (act) {
-      w = y[hl][bitrev7(j)] * 0.08838834764831845f * a.sl2e;   // (z P)_j = z_br(j)
-      qs[hl][j] = w;
-    }
-    // max |q'| over the 128 channels of this head: 2 waves per head
-    float mx = wave_max_xor(fabsf(w), 1, 32);
-    if ((tid & 63) == 0) amax[hl][(tid >> 6) & 1] = mx;
-    __syncthreads();
-    const float qmax = fmaxf(amax[hl][0], amax[hl][1]);
-    const float alpha = qmax > 0.f ? qmax / 32767.0f : 1.0f;
-    if (act) qi[hl][j] = (int32_t)fminf(fmaxf(__builtin_rintf(w / alpha), -32767.f), 32767.f);
-    __syncthreads();
-    if (act) {
-      QrotRecord* rec = a.qrot + ((size_t)b * a.Hq + hq);
-      if (j < 64) {
-        // j = 16 q + 8 lohi + 4 w + jj  ->  word d = 2q + w, byte b: channel 16d + 4b + jj
-        const int qq = j >> 4, lohi = (j >> 3) & 1, w2 = (j >> 2) & 1, jj = j & 3, d = 2 * qq + w2;
-        uint32_t packed = 0;
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int Q = qi[hl][16 * d + 4 * bb + jj];
-          const uint32_t byte = lohi ? (uint32_t)(Q & 0xFF) : (uint32_t)((Q >> 8) & 0xFF);
-          packed |= byte << (8 * bb);
-        }
-        rec->limb[j] = packed;
-      } else if (j < 68) {
-        const int ch = j - 64;
-        float sum = 0.f;
-        for (int c = 32 * ch; c < 32 * ch + 32; ++c) sum += qs[hl][c];
-        rec->qsum[ch] = sum;
-      } else if (j == 68) {
-        rec->alpha = alpha;
-      }
-    }
-    __syncthreads();
+    if (j < 2) rec->negc[g] = sum;
+    else rec->qsum[g] = sum;
   }
 }
 
@@ -130,14 +117,21 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(DecodeArgs a) {
 // split: block (item, KV head, sequence), 4 waves.
 // ---------------------------------------------------------------------------
 constexpr int kMaxPagesPerSplit = 128;
+constexpr int kRing = 8;   // pages in flight per wave (LDS ring, even: pages go in pairs)
+// while pages j, j+1 are read, the DMAs of pages j+2 .. j+kRing-1 (two instructions each) may be in flight
+static_assert(2 * (kRing - 2) == 12, "s_waitcnt vmcnt immediate below assumes kRing == 8");
 
 struct __attribute__((aligned(16))) SplitSmem {
   int32_t pid[kMaxPagesPerSplit];    // physical page ids of the item's page range
-  uint32_t w[4][kMaxGqa][2][8];      // fp16 pairs of p*s per (wave, head, group, pair)
-  float p[4][kMaxGqa][16];           // BF16 items: probabilities per token
-  float m[4][kMaxGqa];
-  float l[4][kMaxGqa];
-  float acc[4][kMaxGqa][kHeadDim];
+  union {
+    uint8_t ring[4][kRing][kBlockBytes];   // INT2 items: per-wave ring of page blocks
+    struct {
+      float p[4][kMaxGqa][16];             // BF16 items: probabilities per token
+      float m[4][kMaxGqa];
+      float l[4][kMaxGqa];
+      float acc[4][kMaxGqa][kHeadDim];
+    };
+  };
 };
 
 template <int G>
@@ -250,187 +244,231 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
   merge_waves_and_store<G>(a, b, h, chunk, sm);
 }
 
-// INT2 history pages [first, end): wave w takes pages first + w, + 4, ...
-// K stage: lane = (token t = l/4, chunk q = l%4) -> 32 channels, logits by
-//          fp16 dot2 of q' with (base + code) pairs; 4-lane reduction.
-// V stage: lane = channels 2l, 2l+1 -> their channel-major code words hold all
-//          16 tokens; fp16 dot2 of (p*s) pairs with (base + code) pairs.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ half8 half8_of(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(half8, make_uint4(a, b, c, d));
+}
+__device__ __forceinline__ half8 half8_of(uint4 u) { return __builtin_bit_cast(half8, u); }
+__device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return f32_to_f16_bits(a) | (f32_to_f16_bits(b) << 16);
+}
+// all-reduce max over the four 16-lane rows (lanes with the same lane%16)
+__device__ __forceinline__ float rows_max(float x) { return swap32(swap16(x, true), true); }
+__device__ __forceinline__ float rows_sum(float x) { return swap32(swap16(x, false), false); }
+
+// INT2 history pages [first, end), two pages (32 tokens) per step; wave w
+// takes the pairs starting at first + 2w, + 8, ...
+//
+// Lane l: n = l % 16, r = l / 16.
+// Logits (per page, per 64-channel group g): D[token][head] = sum_c
+//   (base_c + code_c) * (hi + lo)_c, four MFMAs (two k-halves x two limbs),
+//   accumulator started at -sum_c base_c (hi + lo)_c.  A = codes: lane holds
+//   token n's code word r of group g (16 channels) as unpack16 pairs; B =
+//   q' fragments of head n.  D lands as lane (head n, tokens 4r..4r+3).
+// Values: acc[head][channel] += W[head][token] * (base + code)[token][channel],
+//   one MFMA per 16-channel tile and page pair: A = W = fp16(p s_g), held by
+//   the lanes that computed p (head n, tokens 4r+i of both pages); B = the
+//   channel-major code words of channel 16t + n, byte r of each page.  The base
+//   offsets are summed by one more MFMA per group against constant bases.
 template <int G>
 __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int first, int end, int i_hi,
                           SplitSmem& sm) {
-  constexpr int NJ = (G + 3) / 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = lane >> 2, q = lane & 3;
-  const int gv = lane >> 5;                       // group of channels 2l, 2l+1
-  const int tpair = pair_of_k(t & 7), thalf = t >> 3;
-  const float tbase = (float)pair_base(tpair);
+  const int n = lane & 15, r = lane >> 4;
 
-  uint32_t qhi[G][8], qlo[G][8];
-  float alpha_q[G], qsum[G];
-  const QrotRecord* qr = a.qrot + ((size_t)b * a.Hq + h * G);
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const uint4* src = reinterpret_cast<const uint4*>(&qr[hh].limb[16 * q]);
-    const uint4 h0 = src[0], h1 = src[1], l0 = src[2], l1 = src[3];
-    qhi[hh][0] = h0.x; qhi[hh][1] = h0.y; qhi[hh][2] = h0.z; qhi[hh][3] = h0.w;
-    qhi[hh][4] = h1.x; qhi[hh][5] = h1.y; qhi[hh][6] = h1.z; qhi[hh][7] = h1.w;
-    qlo[hh][0] = l0.x; qlo[hh][1] = l0.y; qlo[hh][2] = l0.z; qlo[hh][3] = l0.w;
-    qlo[hh][4] = l1.x; qlo[hh][5] = l1.y; qlo[hh][6] = l1.z; qlo[hh][7] = l1.w;
-    alpha_q[hh] = qr[hh].alpha;
-    qsum[hh] = qr[hh].qsum[q];
-  }
-
-  float m[G], lp[G], acc[G][2];
-  float zacc[NJ][2], oacc[NJ][2];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -INFINITY;
-    lp[hh] = 0.f;
-    acc[hh][0] = acc[hh][1] = 0.f;
-  }
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) zacc[jj][0] = zacc[jj][1] = oacc[jj][0] = oacc[jj][1] = 0.f;
-
-  // physical page ids of this item, once per block
   {
     const int32_t* ptab = a.page_table + (size_t)b * a.max_pages + first;
     for (int i = threadIdx.x; i < end - first; i += 256) sm.pid[i] = ptab[i];
     __syncthreads();
   }
-  uint16_t* wl = reinterpret_cast<uint16_t*>(&sm.w[wave][0][0][0]);
+
+  // q' fragments of head n (zero columns beyond G)
+  half8 qf[2][2][2];
+  f32x4 cinit[2];
+  float qsum[2];
+  {
+    const QrotRecord* rec = a.qrot + ((size_t)b * a.Hq + h * G + (n < G ? n : 0));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int lm = 0; lm < 2; ++lm) {
+          const uint4 u = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][lm][r][0]);
+          qf[g][kh][lm] = half8_of(n < G ? u : make_uint4(0, 0, 0, 0));
+        }
+      const float nc = n < G ? rec->negc[g] : 0.f;
+      cinit[g] = f32x4{nc, nc, nc, nc};
+      qsum[g] = n < G ? rec->qsum[g] : 0.f;
+    }
+  }
+
+  float m_used = -INFINITY, lsum = 0.f, zs[2] = {0.f, 0.f};
+  f32x4 acc[8], accoff[2];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  accoff[0] = accoff[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // fp16 bases of the value-code pairs (4+c, 16+c, 4+c, 16+c), both halves
+  const half8 boff = half8_of(0x44004400u, 0x4C004C00u, 0x44004400u, 0x4C004C00u);
+  const uint32_t perm_sel = (uint32_t)r | (0x0Cu << 8) | ((4u + r) << 16) | (0x0Cu << 24);
+  const PairConsts pk;
+
+  // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
   const size_t head_off = (size_t)h * kBlockBytes;
   const size_t page_stride = (size_t)a.H * kBlockBytes;
-
-  struct PageRegs {
-    uint2 kc, vc, vp;
-    uint32_t kp;
+  // the wave's pages: j -> first + 8 (j / 2) + 2 wave + (j % 2)
+  const int base0 = first + 2 * wave;
+  int n_w = 0;
+  if (base0 < end) n_w = 2 * ((end - base0 + 7) / 8) - ((end - base0 - 1) % 8 == 0 ? 1 : 0);
+  auto page_of = [&](int j) { return base0 + 8 * (j >> 1) + (j & 1); };
+  auto issue = [&](int j) {   // 2 DMA instructions per page
+    const uint8_t* blk = a.pages + (size_t)sm.pid[page_of(j) - first] * page_stride + head_off;
+    uint8_t* dst = &sm.ring[wave][j % kRing][0];
+    __builtin_amdgcn_global_load_lds(blk + 16 * lane, dst, 16, 0, 0);
+    if (lane < 16) __builtin_amdgcn_global_load_lds(blk + 1024 + 16 * lane, dst + 1024, 16, 0, 0);
   };
-  auto load_page = [&](int pg) {
-    const uint8_t* blk = a.pages + (size_t)sm.pid[pg - first] * page_stride + head_off;
-    PageRegs r;
-    r.kc = *reinterpret_cast<const uint2*>(blk + kKCodes + 32 * t + 8 * q);
-    r.kp = *reinterpret_cast<const uint32_t*>(blk + kKParams + 8 * t + 4 * (q >> 1));
-    r.vc = *reinterpret_cast<const uint2*>(blk + kVCodes + 8 * lane);
-    r.vp = *reinterpret_cast<const uint2*>(blk + kVParams + 8 * t);
-    return r;
-  };
+  for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(j);
 
-  int pg = first + wave;
-  PageRegs cur = {}, nxt = {};
-  if (pg < end) cur = load_page(pg);
-  for (; pg < end; pg += 4) {
-    if (pg + 4 < end) nxt = load_page(pg + 4);   // keep the next page in flight
-    const uint2 kc = cur.kc, vc = cur.vc, vp = cur.vp;
-    const uint32_t kp = cur.kp;
-
-    // ---- logits (base-2 units): exact integer dot of Q with the codes ----
-    uint32_t bv[8];   // byte vectors: bv[4w + j] holds channels 16(2q+w) + 4b + j
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bv[j] = (kc.x >> (2 * j)) & 0x03030303u;
-      bv[4 + j] = (kc.y >> (2 * j)) & 0x03030303u;
+  for (int j = 0; j < n_w; j += 2) {
+    const int pp = page_of(j);
+    const bool has1 = j + 1 < n_w;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of the slots being refilled
+    if (j + kRing - 2 < n_w) issue(j + kRing - 2);
+    if (j + kRing - 1 < n_w) issue(j + kRing - 1);
+    if (j + kRing - 1 < n_w) {
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");   // pages j, j+1 landed: 2*(kRing-2) still in flight
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    const float ks = f16_bits_to_f32(kp), kz = f16_bits_to_f32(kp >> 16);
-    const bool tok_ok = pg * 16 + t < i_hi;
-    float lg[G];
+    struct PageRegs {
+      uint32_t kc[2];
+      uint4 kp[2], vp[2];
+      uint32_t vw[8];
+    } cur[2];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      int dh = 0, dl = 0;
+    for (int k = 0; k < 2; ++k) {
+      const uint8_t* blk = &sm.ring[wave][(j + (k == 1 && has1 ? 1 : 0)) % kRing][0];
+      cur[k].kc[0] = *reinterpret_cast<const uint32_t*>(blk + kKCodes + 32 * n + 4 * r);
+      cur[k].kc[1] = *reinterpret_cast<const uint32_t*>(blk + kKCodes + 32 * n + 16 + 4 * r);
+      cur[k].kp[0] = *reinterpret_cast<const uint4*>(blk + kKParams + 32 * r);
+      cur[k].kp[1] = *reinterpret_cast<const uint4*>(blk + kKParams + 32 * r + 16);
+      cur[k].vp[0] = *reinterpret_cast<const uint4*>(blk + kVParams + 32 * r);
+      cur[k].vp[1] = *reinterpret_cast<const uint4*>(blk + kVParams + 32 * r + 16);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        dh = __builtin_amdgcn_sdot4((int)qhi[hh][k], (int)bv[k], dh, false);
-        dl = (int)__builtin_amdgcn_udot4(qlo[hh][k], bv[k], (uint32_t)dl, false);
-      }
-      const float d = (float)(dh * 256 + dl) * alpha_q[hh];
-      const float x = quad_sum(fmaf(ks, d, kz * qsum[hh]));
-      lg[hh] = tok_ok ? x : -INFINITY;
+      for (int t = 0; t < 8; ++t) cur[k].vw[t] = *reinterpret_cast<const uint32_t*>(blk + kVCodes + 4 * (16 * t + n));
     }
 
-    // ---- online softmax (exact running max; the page's first token is valid) ----
-    float alpha[G], pr[G];
+    // ---- logits of both pages: lane (head n, tokens 4r + i) ----
+    float lg[2][4];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float mn = fmaxf(m[hh], tok_max(lg[hh]));
-      alpha[hh] = fast_exp2(m[hh] - mn);
-      pr[hh] = tok_ok ? fast_exp2(lg[hh] - mn) : 0.f;
-      m[hh] = mn;
-      lp[hh] = fmaf(lp[hh], alpha[hh], pr[hh]);
-    }
-
-    // ---- weights p*s (fp16) for the V stage ----
-    const float vs0 = f16_bits_to_f32(vp.x), vz0 = f16_bits_to_f32(vp.x >> 16);
-    const float vs1 = f16_bits_to_f32(vp.y), vz1 = f16_bits_to_f32(vp.y >> 16);
-    wave_lds_sync();
+    for (int k = 0; k < 2; ++k) {
+      const PageRegs& P = cur[k];
+      uint32_t e0[8], e1[8];
+      unpack16(P.kc[0], e0, pk);
+      unpack16(P.kc[1], e1, pk);
+      f32x4 d0 = cinit[0], d1 = cinit[1];
+      const half8 a00 = half8_of(e0[0], e0[1], e0[2], e0[3]), a01 = half8_of(e0[4], e0[5], e0[6], e0[7]);
+      const half8 a10 = half8_of(e1[0], e1[1], e1[2], e1[3]), a11 = half8_of(e1[4], e1[5], e1[6], e1[7]);
+      d0 = mfma16(a00, qf[0][0][0], d0);
+      d0 = mfma16(a01, qf[0][1][0], d0);
+      d0 = mfma16(a00, qf[0][0][1], d0);
+      d0 = mfma16(a01, qf[0][1][1], d0);
+      d1 = mfma16(a10, qf[1][0][0], d1);
+      d1 = mfma16(a11, qf[1][1][0], d1);
+      d1 = mfma16(a10, qf[1][0][1], d1);
+      d1 = mfma16(a11, qf[1][1][1], d1);
+      const uint32_t kw[8] = {P.kp[0].x, P.kp[0].y, P.kp[0].z, P.kp[0].w,
+                              P.kp[1].x, P.kp[1].y, P.kp[1].z, P.kp[1].w};
+      const bool page_ok = k == 0 || has1;
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int hh = q + 4 * jj;
-      if (hh < G) {
-        float prh = 0.f, al = 1.f;
-#pragma unroll
-        for (int x = 0; x < G; ++x)
-          if (x == hh) {
-            prh = pr[x];
-            al = alpha[x];
-          }
-        const uint32_t w0 = f32_to_f16_bits(prh * vs0), w1 = f32_to_f16_bits(prh * vs1);
-        wl[((hh * 2 + 0) * 8 + tpair) * 2 + thalf] = (uint16_t)w0;
-        wl[((hh * 2 + 1) * 8 + tpair) * 2 + thalf] = (uint16_t)w1;
-        zacc[jj][0] = fmaf(zacc[jj][0], al, prh * vz0);
-        zacc[jj][1] = fmaf(zacc[jj][1], al, prh * vz1);
-        oacc[jj][0] = fmaf(oacc[jj][0], al, tbase * f16_bits_to_f32(w0));
-        oacc[jj][1] = fmaf(oacc[jj][1], al, tbase * f16_bits_to_f32(w1));
+      for (int i = 0; i < 4; ++i) {
+        const float s0 = f16_bits_to_f32(kw[2 * i]), z0 = f16_bits_to_f32(kw[2 * i] >> 16);
+        const float s1 = f16_bits_to_f32(kw[2 * i + 1]), z1 = f16_bits_to_f32(kw[2 * i + 1] >> 16);
+        const float x = fmaf(s0, d0[i], fmaf(s1, d1[i], fmaf(z0, qsum[0], z1 * qsum[1])));
+        const bool ok = page_ok && (pp + k) * 16 + 4 * r + i < i_hi;
+        lg[k][i] = ok ? x : -INFINITY;
       }
     }
-    wave_lds_sync();
 
-    // ---- V accumulation on the channel-major code words ----
-    uint32_t e0[8], e1[8];
-    unpack16(vc.x, e0);
-    unpack16(vc.y, e1);
+    // ---- online softmax; rescale only when the max grows by more than 2 (p <= 4) ----
+    float pm = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
+                     fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
+    pm = rows_max(pm);
+    const bool need = pm > m_used + 2.0f;
+    if (__any(need)) {
+      const float m_new = need ? pm : m_used;
+      const float al = fast_exp2(m_used - m_new);
+      lsum *= al;
+      zs[0] *= al;
+      zs[1] *= al;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const uint4* wr = reinterpret_cast<const uint4*>(&sm.w[wave][hh][gv][0]);
-      const uint4 wa = wr[0], wb = wr[1];
-      const uint32_t W[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-      float a0 = acc[hh][0] * alpha[hh], a1 = acc[hh][1] * alpha[hh];
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(al, 4 * r + i);   // rows of acc are heads 4r + i
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        a0 = dot2_f16(W[i], e0[i], a0);
-        a1 = dot2_f16(W[i], e1[i], a1);
+        for (int t = 0; t < 8; ++t) acc[t][i] *= ai;
+        accoff[0][i] *= ai;
+        accoff[1][i] *= ai;
       }
-      acc[hh][0] = a0;
-      acc[hh][1] = a1;
+      m_used = m_new;
     }
-    cur = nxt;
+    float p[2][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[k][i] = fast_exp2(lg[k][i] - m_used);
+        lsum += p[k][i];
+      }
+
+    // ---- weights W = fp16(p s_g) and the zero-point sums ----
+    uint32_t wg[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&cur[0].vp[0]);
+      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&cur[1].vp[0]);
+      const uint32_t a0 = v0[2 * i], b0 = v0[2 * i + 1], a1 = v1[2 * i], b1 = v1[2 * i + 1];
+      wg[0][i] = pack_f16(p[0][i] * f16_bits_to_f32(a0), p[1][i] * f16_bits_to_f32(a1));
+      wg[1][i] = pack_f16(p[0][i] * f16_bits_to_f32(b0), p[1][i] * f16_bits_to_f32(b1));
+      zs[0] = fmaf(p[0][i], f16_bits_to_f32(a0 >> 16), fmaf(p[1][i], f16_bits_to_f32(a1 >> 16), zs[0]));
+      zs[1] = fmaf(p[0][i], f16_bits_to_f32(b0 >> 16), fmaf(p[1][i], f16_bits_to_f32(b1 >> 16), zs[1]));
+    }
+    const half8 W0 = half8_of(wg[0][0], wg[0][1], wg[0][2], wg[0][3]);
+    const half8 W1 = half8_of(wg[1][0], wg[1][1], wg[1][2], wg[1][3]);
+
+    // ---- values ----
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t x = __builtin_amdgcn_perm(cur[1].vw[t], cur[0].vw[t], perm_sel);
+      const uint32_t m16 = pk.m16, b16 = pk.b16, m4 = pk.m4, b4 = pk.b4;
+      const uint32_t l4 = x << 4;
+      const half8 bv = half8_of(((x << 8) & m4) | b4, (l4 & m16) | b16, (l4 & m4) | b4, (x & m16) | b16);
+      acc[t] = mfma16(t < 4 ? W0 : W1, bv, acc[t]);
+    }
+    accoff[0] = mfma16(W0, boff, accoff[0]);
+    accoff[1] = mfma16(W1, boff, accoff[1]);
   }
 
-  // ---- finish the wave: l, and acc += sum(p z) - sum(base * p s) ----
-  float lsum[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) lsum[hh] = tok_sum(lp[hh]);
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-    for (int g = 0; g < 2; ++g) zacc[jj][g] = tok_sum(zacc[jj][g] - oacc[jj][g]);
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float d0 = __shfl(zacc[hh / 4][0], hh % 4);
-    const float d1 = __shfl(zacc[hh / 4][1], hh % 4);
-    const float d = gv ? d1 : d0;
-    acc[hh][0] += d;
-    acc[hh][1] += d;
+  // ---- finish the wave (the result area overlays the page rings: wait for all waves) ----
+  __syncthreads();
+  const float L_h = rows_sum(lsum);
+  const float Z0 = rows_sum(zs[0]), Z1 = rows_sum(zs[1]);
+  if (r == 0 && n < G) {
+    sm.m[wave][n] = m_used;
+    sm.l[wave][n] = L_h;
   }
-  if (lane == 0) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      sm.m[wave][hh] = m[hh];
-      sm.l[wave][hh] = lsum[hh];
+  for (int i = 0; i < 4; ++i) {
+    const int head = 4 * r + i;
+    const float z0 = __shfl(Z0, head & 15), z1 = __shfl(Z1, head & 15);
+    if (head < G) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        sm.acc[wave][head][16 * t + n] = acc[t][i] - (t < 4 ? accoff[0][i] - z0 : accoff[1][i] - z1);
     }
-  }
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    sm.acc[wave][hh][2 * lane] = acc[hh][0];
-    sm.acc[wave][hh][2 * lane + 1] = acc[hh][1];
   }
   merge_waves_and_store<G>(a, b, h, a.n_bsplit + split, sm);
 }
@@ -454,70 +492,93 @@ __global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// reduce: one block per (sequence, KV head); two query heads at a time.
+// reduce: one 128-thread block per (sequence, query head).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
-  __shared__ float y[2][kHeadDim];
-  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const int tid = threadIdx.x, hl = tid >> 7, c = tid & 127;
+constexpr int kReduceThreads = 128;
+
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
+  __shared__ float e_s[1024];         // per-split weight exp2(m_s - M)
+  __shared__ float y[kHeadDim];
+  __shared__ float red[2][2];
+  const int bq = blockIdx.x, b = bq / a.Hq, hq = bq % a.Hq, h = hq / a.G;
+  const int c = threadIdx.x, lane = c & 63, wave = c >> 6;
   const int L = a.seq_lens[b];
+  uint16_t* out = a.out + (size_t)bq * kHeadDim;
+  if (L == 0) {
+    out[c] = 0;
+    return;
+  }
   const int n_b = (bf16_token_count(L, a.sink, a.recent) + kBf16Chunk - 1) / kBf16Chunk;
   const int i_hi = int2_end(L, a.sink, a.recent);
   const int int2_pages = i_hi > a.sink ? (i_hi + kPage - 1) / kPage - a.sink / kPage : 0;
   const int n_i = (int2_pages + a.P - 1) / a.P;
-  const uint16_t* UV = a.u_v + (size_t)h * kHeadDim * kHeadDim;
-  for (int h0 = 0; h0 < a.G; h0 += 2) {
-    const int hh = h0 + hl;
-    const bool act = hh < a.G;
-    const int hq = h * a.G + hh;
-    float plain = 0.f, rot = 0.f, lsum = 0.f;
-    if (act && L > 0) {
-      const float* base = a.part + (size_t)(b * a.Hq + hq) * a.n_total * kPartFloats;
-      float M = -INFINITY;
-      for (int s = 0; s < n_b; ++s) M = fmaxf(M, base[(size_t)s * kPartFloats]);
-      for (int s = 0; s < n_i; ++s) M = fmaxf(M, base[(size_t)(a.n_bsplit + s) * kPartFloats]);
-      for (int s = 0; s < n_b; ++s) {
-        const float* r = base + (size_t)s * kPartFloats;
-        const float e = r[0] == -INFINITY ? 0.f : exp2f(r[0] - M);
-        lsum += e * r[1];
-        plain += e * r[4 + c];
-      }
-      for (int s = 0; s < n_i; ++s) {
-        const float* r = base + (size_t)(a.n_bsplit + s) * kPartFloats;
-        const float e = r[0] == -INFINITY ? 0.f : exp2f(r[0] - M);
-        lsum += e * r[1];
-        rot += e * r[4 + c];
-      }
+  const int n_used = n_b + n_i;   // used items: [0, n_b) BF16, then [n_bsplit, n_bsplit + n_i) INT2
+  auto item = [&](int u) { return u < n_b ? u : a.n_bsplit + (u - n_b); };
+  const float* base = a.part + (size_t)bq * a.n_total * kPartFloats;
+
+  // M = max over the used items' running maxima
+  float mx = -INFINITY;
+  for (int u = c; u < n_used; u += kReduceThreads) mx = fmaxf(mx, base[(size_t)item(u) * kPartFloats]);
+  mx = wave_max_xor(mx, 1, 32);
+  if (lane == 0) red[0][wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(red[0][0], red[0][1]);
+  float ls = 0.f;
+  for (int u = c; u < n_used; u += kReduceThreads) {
+    const float* r = base + (size_t)item(u) * kPartFloats;
+    const float e = r[0] == -INFINITY ? 0.f : exp2f(r[0] - M);
+    e_s[u & 1023] = e;
+    ls += e * r[1];
+  }
+  ls = wave_sum_xor(ls, 1, 32);
+  if (lane == 0) red[1][wave] = ls;
+  __syncthreads();
+  const float lsum = red[1][0] + red[1][1];
+
+  // channel c: plain (BF16 items) and rotated (INT2 items) accumulators
+  float plain = 0.f, rot = 0.f;
+  for (int u = 0; u < n_b; ++u) plain = fmaf(e_s[u], base[(size_t)u * kPartFloats + 4 + c], plain);
+  {
+    const float* pr = base + (size_t)a.n_bsplit * kPartFloats + 4 + c;
+    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+    int u = 0;
+    for (; u + 4 <= n_i; u += 4) {
+      r0 = fmaf(e_s[n_b + u], pr[(size_t)u * kPartFloats], r0);
+      r1 = fmaf(e_s[n_b + u + 1], pr[(size_t)(u + 1) * kPartFloats], r1);
+      r2 = fmaf(e_s[n_b + u + 2], pr[(size_t)(u + 2) * kPartFloats], r2);
+      r3 = fmaf(e_s[n_b + u + 3], pr[(size_t)(u + 3) * kPartFloats], r3);
     }
-    // acc_rot P: z-space channel br(c) takes post-rotation channel c
-    y[hl][bitrev7(c)] = rot;
-    __syncthreads();
-    for (int s = 1; s < kHeadDim; s <<= 1) {
-      if (c < 64) {
-        const int lo = ((c & ~(s - 1)) << 1) | (c & (s - 1)), hi = lo | s;
-        const float x0 = y[hl][lo], x1 = y[hl][hi];
-        y[hl][lo] = x0 + x1;
-        y[hl][hi] = x0 - x1;
-      }
-      __syncthreads();
-    }
-    if (act) {
-      float o = 0.f;
-      const uint16_t* urow = UV + (size_t)c * kHeadDim;   // (y U^T)_c = sum_j y_j U[c][j]
-      for (int jb = 0; jb < kHeadDim; jb += 8) {
-        const uint4 u8 = *reinterpret_cast<const uint4*>(urow + jb);
-        const uint32_t uu[4] = {u8.x, u8.y, u8.z, u8.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          o = fmaf(y[hl][jb + 2 * k], bf16_bits_to_f32(uu[k] & 0xFFFFu), o);
-          o = fmaf(y[hl][jb + 2 * k + 1], bf16_bits_to_f32(uu[k] >> 16), o);
-        }
-      }
-      const float res = L > 0 ? (plain + o * 0.08838834764831845f) / lsum : 0.f;
-      a.out[((size_t)b * a.Hq + hq) * kHeadDim + c] = (uint16_t)f32_to_bf16_bits(res);
+    for (; u < n_i; ++u) r0 = fmaf(e_s[n_b + u], pr[(size_t)u * kPartFloats], r0);
+    rot = (r0 + r1) + (r2 + r3);
+  }
+
+  // acc_rot P: z-space channel br(c) takes post-rotation channel c; then H
+  y[bitrev7(c)] = rot;
+  __syncthreads();
+  for (int s = 1; s < kHeadDim; s <<= 1) {
+    if (c < 64) {
+      const int lo = ((c & ~(s - 1)) << 1) | (c & (s - 1)), hi = lo | s;
+      const float x0 = y[lo], x1 = y[hi];
+      y[lo] = x0 + x1;
+      y[hi] = x0 - x1;
     }
     __syncthreads();
   }
+  // (y U_V^T)_c = sum_j y_j U_V[c][j]
+  const uint16_t* urow = a.u_v + ((size_t)h * kHeadDim + c) * kHeadDim;
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
+  for (int jb = 0; jb < kHeadDim; jb += 8) {
+    const uint4 u8 = *reinterpret_cast<const uint4*>(urow + jb);
+    const uint32_t uu[4] = {u8.x, u8.y, u8.z, u8.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o0 = fmaf(y[jb + 2 * k], bf16_bits_to_f32(uu[k] & 0xFFFFu), o0);
+      o1 = fmaf(y[jb + 2 * k + 1], bf16_bits_to_f32(uu[k] >> 16), o1);
+    }
+  }
+  const float res = (plain + (o0 + o1) * 0.08838834764831845f) / lsum;
+  out[c] = (uint16_t)f32_to_bf16_bits(res);
 }
 
 template <int G>
@@ -533,10 +594,13 @@ DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   const int int2_pages = max(0, max_pages - sink / kPage);
   const long long page_heads = (long long)int2_pages * batch * num_kv_heads;
   long long per = (page_heads + 2047) / 2048;   // aim for ~2048 INT2 items
-  per = per < 32 ? 32 : per > 128 ? 128 : per;
+  p.n_bsplit = (sink + recent + kBf16Chunk - 1) / kBf16Chunk;
+  // keep the items of one sequence within what the reduce merges
+  const long long min_per = (int2_pages + (kMaxItems - p.n_bsplit) - 1) / (kMaxItems - p.n_bsplit);
+  per = per < min_per ? min_per : per;
+  per = per < 32 ? 32 : per > kMaxPagesPerSplit ? kMaxPagesPerSplit : per;
   p.pages_per_split = (int)((per + 3) / 4 * 4);
   p.n_split = int2_pages > 0 ? (int2_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
-  p.n_bsplit = (sink + recent + kBf16Chunk - 1) / kBf16Chunk;
   p.n_total = p.n_split + p.n_bsplit;
   const size_t qrot = (size_t)batch * num_q_heads * kQrotBytes;
   p.qrot_off = 0;
@@ -572,8 +636,7 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.n_split = L.plan.n_split;
   a.n_bsplit = L.plan.n_bsplit;
   a.n_total = L.plan.n_total;
-  const int BH = L.batch * L.num_kv_heads;
-  hipLaunchKernelGGL(rotate_q_kernel, dim3(BH), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(rotate_q_kernel, dim3(L.batch * L.num_q_heads), dim3(128), 0, stream, a);
   switch (a.G) {
     case 1: launch_split<1>(a, L.batch, stream); break;
     case 2: launch_split<2>(a, L.batch, stream); break;
@@ -585,7 +648,7 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     case 8: launch_split<8>(a, L.batch, stream); break;
     default: return 1;
   }
-  hipLaunchKernelGGL(reduce_kernel, dim3(BH), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(reduce_kernel, dim3(L.batch * L.num_q_heads), dim3(kReduceThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

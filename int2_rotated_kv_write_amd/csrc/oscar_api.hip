@@ -96,9 +96,9 @@ int oscar_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer, const
 
 size_t oscar_decode_workspace_bytes(const oscar_shape_t* shape, int32_t batch, int32_t max_pages) {
   if (check_shape(shape) || batch < 0 || max_pages < 1) return 0;
-  return oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink, shape->recent, batch,
-                                 max_pages)
-      .bytes;
+  const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
+                                                         shape->recent, batch, max_pages);
+  return plan.n_total > oscar::kMaxItems ? 0 : plan.bytes;
 }
 
 int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q,
@@ -115,6 +115,7 @@ int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, co
     return fail(OSCAR_EINVAL, "NULL tensor pointer%s");
   const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
                                                          shape->recent, batch, max_pages);
+  if (plan.n_total > oscar::kMaxItems) return fail(OSCAR_EINVAL, "max_pages too large (sequences over ~2M tokens)%s");
   if (!workspace || workspace_bytes < plan.bytes) return fail(OSCAR_ENOWS, "workspace smaller than required%s");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned%s");
   oscar::DecodeLaunch L{};
