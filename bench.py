@@ -36,8 +36,10 @@ WORKLOADS = {
     "qwen3_8b_layer_100k": dict(batch=1, seq_len=100_000, q_heads=32, kv_heads=8, layers=1,
                                 table="contiguous", law="heavy"),
     "ragged_64x4k_128k": dict(batch=64, seq_len=(4096, 131072), q_heads=64, kv_heads=8, layers=1,
-                              table="permuted", law="outlier"),
+                              table="shared_prefix", law="outlier"),
 }
+SHARED_PREFIX_TOKENS = 4096     # ragged workload: 25% of the sequences share their first 4,096 tokens
+PREFILL_TOKENS = 100_000        # write-path workload: one kv_write of 100,000 prefill tokens x 8 KV heads
 
 
 def log(*a):
@@ -67,9 +69,46 @@ def decode_bytes(lens, H, Hq):
 
 
 def write_bytes(n_tokens, H):
-    """kv_write of n tokens (K and V): read 2x256 B per token-head, write 80 B
-    INT2 + 2x256 B ring copy per token-head, U_K and U_V."""
+    """kv_write of n decode tokens (K and V): read 2x256 B per token-head,
+    write 80 B INT2 + 2x256 B ring copy per token-head, U_K and U_V."""
     return n_tokens * H * (512 + 80 + 512) + 2 * H * 128 * 128 * 2
+
+
+def prefill_write_bytes(n_tokens, H, sink=64):
+    """kv_write of positions [0, n) of one sequence (K and V): read 2x256 B
+    per token-head, write 80 B INT2 per token-head at pos >= sink and 2x256 B
+    BF16 per sink or recent token-head, U_K and U_V."""
+    return (H * (n_tokens * 512 + max(0, n_tokens - sink) * 80 + bf16_tokens(n_tokens) * 512)
+            + 2 * H * 128 * 128 * 2)
+
+
+DECODE_SOURCES = ("decode.hip", "common.h", "kernels.h")
+
+
+def decode_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, "int2_rotated_kv_write_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """Measured HBM bytes per decode_attn call from the committed counter
+    summary, valid only for the decode sources it was taken on (else None)."""
+    path = os.path.join(ROOT, "profiles", "decode_attn_counters_concurrent_28x100k_36l.md")
+    if not os.path.exists(path):
+        return None
+    sha = decode_source_sha256()
+    rec = {}
+    for line in open(path):
+        if line.startswith("traffic:"):
+            for kv in line[len("traffic:"):].split():
+                key, val = kv.split("=")
+                rec[key] = val
+    if rec.get("decode_source_sha256") != sha:
+        return None
+    return float(rec["bytes_per_call"])
 
 
 def cpu_baseline(H, layers, seq_len, budget_s=20.0):
@@ -149,8 +188,12 @@ def main():
     u_k_d, u_v_d = bf(u_k), bf(u_v)
 
     # ---- page tables (one per layer, like separate cache pools) ----
+    sharers = []
     if wl["table"] == "permuted":
         table = synth.permuted_page_table(rng, B, max_pages)
+    elif wl["table"] == "shared_prefix":
+        sharers = sorted(int(x) for x in rng.choice(B, B // 4, replace=False))
+        table, _, _ = synth.shared_prefix_page_table(rng, lens, max_pages, SHARED_PREFIX_TOKENS, sharers)
     else:
         table = synth.contiguous_page_table(B, max_pages)
     num_pages = int(table.max()) + 1
@@ -164,12 +207,18 @@ def main():
     for layer in range(NL):
         c = lib.allocate_cache(shape, num_pages, B, dev, u_k=u_k_d.clone(), u_v=u_v_d.clone(),
                                clip_k=float(ck), clip_v=float(cv))
+        prefix_kv = None
         for b in range(B):
             n = int(lens[b]) - 1
             for s0 in range(0, n, 1 << 16):
                 m = min(1 << 16, n - s0)
                 k = sample_kv_device(law, m, gen, dev)
                 v = sample_kv_device(law, m, gen, dev)
+                if s0 == 0 and b in sharers:   # shared prefix: same tokens, same physical pages
+                    if prefix_kv is None:
+                        prefix_kv = (k[:SHARED_PREFIX_TOKENS].clone(), v[:SHARED_PREFIX_TOKENS].clone())
+                    k[:SHARED_PREFIX_TOKENS] = prefix_kv[0]
+                    v[:SHARED_PREFIX_TOKENS] = prefix_kv[1]
                 idx = torch.full((m,), b, dtype=torch.int32, device=dev)
                 pos = torch.arange(s0, s0 + m, dtype=torch.int32, device=dev)
                 after = torch.from_numpy(np.maximum(lens - 1, 0).astype(np.int32)).to(dev)
@@ -188,11 +237,11 @@ def main():
     lens_d = torch.from_numpy(lens.astype(np.int32)).to(dev)
     out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(lib.decode_workspace_bytes(shape, B, max_pages), dtype=torch.uint8, device=dev)
-    # reference kernel of known size for calibrating HBM counters: reads and
-    # writes 256 MiB once (outside the timed region)
-    ref_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    # reference kernel of known size for calibrating HBM counters (a kernel
+    # nothing else launches): reads and writes 256 MiB once, untimed
+    ref_src = torch.ones(32 << 20, dtype=torch.int64, device=dev)
     ref_dst = torch.empty_like(ref_src)
-    torch.mul(ref_src, 1.0, out=ref_dst)
+    torch.bitwise_not(ref_src, out=ref_dst)
     del ref_src, ref_dst
     writes = [lib.prepare_kv_write(shape, caches[l], new_k[l], new_v[l], seq_idx, new_pos, table_d, lens_d)
               for l in range(NL)]
@@ -234,6 +283,38 @@ def main():
     log(f"step {ms_per_step:.3f} ms, decode_attn avg {dec_avg_ms * 1e3:.1f} us/layer, "
         f"{achieved:.0f} GB/s decode, {step_bytes / (elapsed / args.steps) / 1e9:.0f} GB/s step")
 
+    # ---- write path: one kv_write of 100,000 prefill tokens x H KV heads (K and V),
+    # outlier law, its own calibration; HIP events around each call ----
+    del caches, writes, decodes
+    torch.cuda.empty_cache()
+    pw_law = synth.outlier_law(rng, H)
+    pqc, pkc, pvc = synth.calibration_samples(rng, pw_law, Hq // H, 2048)
+    pu_k, pu_v, pck, pcv = lib.calibrate_layer(pqc, pkc, pvc, SIG, 0.999)
+    n_pre = PREFILL_TOKENS
+    pre_pages = math.ceil(n_pre / 16)
+    pre_cache = lib.allocate_cache(shape, pre_pages, 1, dev, u_k=bf(pu_k), u_v=bf(pu_v),
+                                   clip_k=float(pck), clip_v=float(pcv))
+    pre_k = sample_kv_device(pw_law, n_pre, gen, dev)
+    pre_v = sample_kv_device(pw_law, n_pre, gen, dev)
+    pre_table = torch.arange(pre_pages, dtype=torch.int32, device=dev).view(1, pre_pages)
+    pre_write = lib.prepare_kv_write(shape, pre_cache, pre_k, pre_v,
+                                     torch.zeros(n_pre, dtype=torch.int32, device=dev),
+                                     torch.arange(n_pre, dtype=torch.int32, device=dev), pre_table,
+                                     torch.tensor([n_pre], dtype=torch.int32, device=dev))
+    for _ in range(2):
+        pre_write()
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for e0, e1 in pev:
+        e0.record()
+        pre_write()
+        e1.record()
+    torch.cuda.synchronize()
+    pre_us = 1e3 * statistics.mean(e0.elapsed_time(e1) for e0, e1 in pev)
+    pre_bytes = prefill_write_bytes(n_pre, H)
+    pre_gbs = pre_bytes / (pre_us * 1e-6) / 1e9
+    log(f"kv_write prefill of {n_pre} tokens x {H} heads: {pre_us:.1f} us, {pre_gbs:.0f} GB/s")
+    del pre_cache, pre_k, pre_v
+
     cpu = None
     if not args.no_cpu_baseline:
         t_unit, reps, threads = cpu_baseline(H, NL, int(lens.max()))
@@ -244,6 +325,10 @@ def main():
                           f"extrapolated x{units} (batch x KV heads x layers)")}
         log(f"cpu baseline: {t_unit:.3f}s per unit, {threads} threads")
 
+    traffic = None
+    if args.workload == "concurrent_28x100k_36l":
+        traffic = read_traffic()
+
     rec = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -253,9 +338,11 @@ def main():
                    "head_dim": 128, "layers": NL, "page_size": 16, "page_table": wl["table"],
                    "sink": 64, "recent": 256, "step": "per layer: kv_write(1 token/seq) + decode_attn"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "decode_attn (rotate_q + split + reduce), per layer",
                      "bytes_per_launch": dbytes, "avg_launch_us": dec_avg_ms * 1e3},
+        "kv_write_prefill": {"tokens": n_pre, "kv_heads": H, "us": pre_us, "tokens_per_s": n_pre / (pre_us * 1e-6),
+                             "bytes": pre_bytes, "achieved_gbs": pre_gbs, "frac": pre_gbs / PEAK_HBM_GBS},
         "step_hbm_gbs": step_bytes / (elapsed / args.steps) / 1e9,
         "cpu_baseline": cpu,
     }

@@ -1,0 +1,188 @@
+"""GPU parity at the measured sizes, in the launch configurations the
+benchmark times (rules in gpu_harness.py).
+
+* qwen3_8b_layer_100k: one layer, 1 sequence x 100,000 tokens, 32 query /
+  8 KV heads, contiguous pages.  The whole prefill is one kv_write call;
+  every page byte, sink and ring row and every output element is compared
+  with the oracle.
+* concurrent_28x100k: 28 sequences x 100,000 tokens, permuted pages, filled
+  in 65,536-token chunks and decoded in one call, as one layer of the
+  benchmark step.  Sampled (sequence, KV head) pairs are re-derived by the
+  oracle: their page blocks (through the permuted table), BF16 rows and the
+  G = 4 outputs.
+* ragged_64x4k_128k: 64 sequences with lengths uniform in [4096, 131072],
+  64 query / 8 KV heads (G = 8), permuted pages where 16 sequences share the
+  physical pages of a 4,096-token prefix.  Sampled pairs as above, including
+  a sequence that reads the shared prefix through another one's pages.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from gpu_harness import (SIG, compare_kv_write, compare_outputs, device_cache, from_dev_bf16,
+                         host_cache, lib_shape, to_dev_bf16, to_dev_i32)
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(rng, law, G):
+    qc, kc, vc = synth.calibration_samples(rng, law, G, 2048)
+    cal = O.calibrate_layer(qc, kc, vc, SIG)
+    return O.Layer(cal["u_k"], cal["u_v"], cal["clip_k"], cal["clip_v"])
+
+
+def _head_layer(layer: O.Layer, h: int) -> O.Layer:
+    return O.Layer(layer.u_k[h:h + 1], layer.u_v[h:h + 1], layer.clip_k, layer.clip_v)
+
+
+def test_qwen3_8b_layer_100k_full_compare(gpu):
+    import torch
+    import int2_rotated_kv_write_amd as lib
+    rng = np.random.default_rng(0)
+    H, Hq, L = 8, 32, 100_000
+    shape = O.Shape(num_kv_heads=H, num_q_heads=Hq)
+    law = synth.heavy_tail_law(rng, H)
+    layer = _layer(rng, law, Hq // H)
+    P = math.ceil(L / 16)
+    table = synth.contiguous_page_table(1, P)
+    k = law.sample_bf16(rng, L)
+    v = law.sample_bf16(rng, L)
+    print(f"qwen3_8b_layer_100k: oracle kv_write of {L} tokens x {H} heads", flush=True)
+    ref = O.new_cache(shape, P, 1)
+    before = O.new_cache(shape, P, 1)
+    info = O.kv_write(shape, ref, layer, k, v, np.zeros(L, int), np.arange(L), table, [L])
+    dc = device_cache(shape, before, layer, gpu)
+    ls = lib_shape(shape)
+    table_d = to_dev_i32(table, gpu)
+    lens_d = to_dev_i32([L], gpu)
+    lib.kv_write(ls, dc, to_dev_bf16(k, gpu), to_dev_bf16(v, gpu), to_dev_i32(np.zeros(L), gpu),
+                 to_dev_i32(np.arange(L), gpu), table_d, lens_d)
+    torch.cuda.synchronize()
+    stats = compare_kv_write(shape, ref, host_cache(dc), info, before)
+    print("write", stats, flush=True)
+    assert stats["codes"] == 2 * H * (L - 64) * 128
+    del info
+    q = synth.decode_queries(rng, 1, Hq)
+    want = O.decode(shape, ref, layer, q, table, [L], SIG)
+    ws = torch.empty(lib.decode_workspace_bytes(ls, 1, P), dtype=torch.uint8, device=gpu)
+    res = {}
+    for name, cache in (("gpu-written", dc), ("oracle-written", device_cache(shape, ref, layer, gpu))):
+        out = torch.full((1, Hq, 128), float("nan"), dtype=torch.bfloat16, device=gpu)
+        lib.decode_attn(ls, cache, to_dev_bf16(q, gpu), table_d, lens_d, out, ws, SIG)
+        torch.cuda.synchronize()
+        res[name] = compare_outputs(from_dev_bf16(out), want)
+    print("decode", res, flush=True)
+
+
+def _fill_on_device(lib, ls, law, lens, table_d, cache, gen, dev, keep, prefix=None):
+    """Write positions [0, L_b) of every sequence in 65,536-token calls with
+    device-drawn K/V; returns host copies of the sequences in `keep`.
+    prefix = (owner, sharers, n_tok): sharers reuse the owner's first n_tok
+    tokens (their pages are shared; rewriting them stores identical bytes)."""
+    import torch
+    from synth.device import sample_kv_device
+    kept = {}
+    owner_kv = None
+    lens_after = to_dev_i32(lens, dev)
+    for b, L in enumerate(int(x) for x in lens):
+        k = sample_kv_device(law, L, gen, dev)
+        v = sample_kv_device(law, L, gen, dev)
+        if prefix is not None:
+            owner, sharers, n_tok = prefix
+            if b == owner:
+                owner_kv = (k[:n_tok].clone(), v[:n_tok].clone())
+            elif b in sharers:
+                k[:n_tok] = owner_kv[0]
+                v[:n_tok] = owner_kv[1]
+        for s0 in range(0, L, 1 << 16):
+            m = min(1 << 16, L - s0)
+            idx = torch.full((m,), b, dtype=torch.int32, device=dev)
+            pos = torch.arange(s0, s0 + m, dtype=torch.int32, device=dev)
+            lib.kv_write(ls, cache, k[s0:s0 + m], v[s0:s0 + m], idx, pos, table_d, lens_after)
+        if b in keep:
+            kept[b] = (from_dev_bf16(k), from_dev_bf16(v))
+    torch.cuda.synchronize()
+    return kept
+
+
+def _check_pair(shape, layer, dev_cache_host, table, b, h, kv, L, q_bits, out_bits):
+    """Oracle re-derivation of one (sequence, KV head): its page blocks (via
+    the sequence's table row), sink/ring rows and G outputs."""
+    G = shape.num_q_heads // shape.num_kv_heads
+    s1 = O.Shape(num_kv_heads=1, num_q_heads=G)
+    l1 = _head_layer(layer, h)
+    P = math.ceil(L / 16)
+    t1 = synth.contiguous_page_table(1, P)
+    ref = O.new_cache(s1, P, 1)
+    k, v = kv
+    info = O.kv_write(s1, ref, l1, k[:, h:h + 1], v[:, h:h + 1], np.zeros(L, int), np.arange(L), t1, [L])
+    got = O.Cache(pages=np.ascontiguousarray(dev_cache_host.pages[table[b, :P], h][:, None, :]),
+                  k_sink=dev_cache_host.k_sink[b:b + 1, h:h + 1], v_sink=dev_cache_host.v_sink[b:b + 1, h:h + 1],
+                  k_ring=dev_cache_host.k_ring[b:b + 1, h:h + 1], v_ring=dev_cache_host.v_ring[b:b + 1, h:h + 1])
+    before = O.new_cache(s1, P, 1)   # both sides start from zeroed buffers
+    stats = compare_kv_write(s1, ref, got, info, before)
+    want = O.decode(s1, ref, l1, q_bits[b:b + 1, G * h:G * h + G], t1, [L], SIG)
+    res = compare_outputs(out_bits[b:b + 1, G * h:G * h + G], want)
+    return stats, res
+
+
+def _run_sampled(gpu, rng, law, shape, lens, table, num_pages, pairs, seed, prefix=None):
+    import torch
+    import int2_rotated_kv_write_amd as lib
+    B = len(lens)
+    layer = _layer(rng, law, shape.num_q_heads // shape.num_kv_heads)
+    ls = lib_shape(shape)
+    dev_cache = lib.allocate_cache(ls, num_pages, B, gpu, u_k=to_dev_bf16(layer.u_k, gpu),
+                                   u_v=to_dev_bf16(layer.u_v, gpu), clip_k=float(layer.clip_k),
+                                   clip_v=float(layer.clip_v))
+    table_d = to_dev_i32(table, gpu)
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(seed)
+    keep = sorted({b for b, _ in pairs})
+    kept = _fill_on_device(lib, ls, law, lens, table_d, dev_cache, gen, gpu, keep, prefix)
+    q = synth.decode_queries(rng, B, shape.num_q_heads)
+    out = torch.full((B, shape.num_q_heads, 128), float("nan"), dtype=torch.bfloat16, device=gpu)
+    ws = torch.empty(lib.decode_workspace_bytes(ls, B, table.shape[1]), dtype=torch.uint8, device=gpu)
+    lib.decode_attn(ls, dev_cache, to_dev_bf16(q, gpu), table_d, to_dev_i32(lens, gpu), out, ws, SIG)
+    torch.cuda.synchronize()
+    out_bits = from_dev_bf16(out)
+    assert np.isfinite(O.bf16_to_f64(out_bits)).all()
+    host = host_cache(dev_cache)
+    del dev_cache
+    for b, h in pairs:
+        print(f"  pair seq {b} (L={int(lens[b])}) kv head {h}", flush=True)
+        stats, res = _check_pair(shape, layer, host, table, b, h, kept[b], int(lens[b]), q, out_bits)
+        print(f"    write {stats} decode {res}", flush=True)
+
+
+def test_concurrent_28x100k_sampled(gpu):
+    rng = np.random.default_rng(4)
+    B, H, Hq, L = 28, 8, 32, 100_000
+    shape = O.Shape(num_kv_heads=H, num_q_heads=Hq)
+    law = synth.heavy_tail_law(rng, H)
+    lens = np.full(B, L, np.int32)
+    P = math.ceil(L / 16)
+    table = synth.permuted_page_table(rng, B, P)
+    print("concurrent_28x100k: fill, decode, check sampled pairs", flush=True)
+    _run_sampled(gpu, rng, law, shape, lens, table, B * P, [(0, 0), (13, 5), (27, 7)], seed=4)
+
+
+def test_ragged_64x4k_128k_shared_prefix_sampled(gpu):
+    rng = np.random.default_rng(5)
+    B, H, Hq = 64, 8, 64
+    shape = O.Shape(num_kv_heads=H, num_q_heads=Hq)
+    law = synth.outlier_law(rng, H)
+    lens = synth.ragged_lengths(rng, B, 4096, 131072)
+    sharers = sorted(int(x) for x in rng.choice(B, 16, replace=False))
+    max_pages = math.ceil(131072 / 16)
+    table, num_pages, owner = synth.shared_prefix_page_table(rng, lens, max_pages, 4096, sharers)
+    reader = sharers[-1]
+    longest = int(np.argmax(lens))
+    shortest = int(np.argmin(lens))
+    pairs = [(sharers[0], 2), (reader, 6), (longest, 0), (shortest, 7)]
+    print(f"ragged_64x4k_128k: lens sum {int(lens.sum())}, sharers {sharers}", flush=True)
+    _run_sampled(gpu, rng, law, shape, lens, table, num_pages, pairs, seed=5,
+                 prefix=(sharers[0], set(sharers), 4096))
