@@ -143,6 +143,9 @@ size_t oscar_decode_workspace_bytes(const oscar_shape_t* shape, int32_t batch, i
  * where positions < min(sink, L) come from the sink rows, positions >=
  * max(sink, L - recent) from the ring, and the rest from the INT2 pages
  * (dequantized and inverse-rotated).  L == 0 writes zeros.
+ * layer->clip_v must be the threshold the value pages were written with
+ * (checked to be in (0, 16384]): it bounds the value scales, which sets how
+ * far the kernel may defer rescaling its fp16 softmax weights.
  * Returns OSCAR_OK, OSCAR_EINVAL, OSCAR_ENOWS or OSCAR_EHIP. */
 int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer,
                       const uint16_t* q, const int32_t* page_table, int32_t max_pages,

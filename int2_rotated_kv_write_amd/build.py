@@ -21,6 +21,9 @@ SOURCES = ["oscar_api.hip", "kv_write.hip", "decode.hip", "calibrate.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the decode loop rescales them with
+    # VALU ops, which AGPR accumulators would turn into copies every iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -16,6 +16,8 @@
 //             G query heads of a KV head share every code) and acc = (p s) x
 //             codes; online softmax in base 2
 //   reduce    log-sum-exp merge, acc_rot R_V^T = ((acc_rot P) H) U_V^T, bf16 out
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -31,9 +33,9 @@ namespace {
 // the same pairs unpack16 makes of code word c of group g.
 struct QrotRecord {
   uint32_t frag[2][2][2][4][4];
-  float negc[2];   // -sum over the group of (hi + lo)_c * base(c): MFMA accumulator start
-  float qsum[2];   // sum over the group of q'_c (fp32), for the zero-point term
-  float pad[12];
+  float negc[2][2];   // [g][limb]: -sum over group g of limb_c * base(c): MFMA accumulator start
+  float qsum[2];      // sum over the group of q'_c (fp32), for the zero-point term
+  float pad[10];
 };
 static_assert(sizeof(QrotRecord) == kQrotBytes, "record size");
 
@@ -45,6 +47,7 @@ struct DecodeArgs {
   QrotRecord* qrot;
   float* part;
   float sl2e;   // sm_scale * log2(e)
+  float resc_thr;   // lazy rescale threshold tau: INT2 probabilities stay <= 2^tau
   int32_t H, Hq, G, max_pages, sink, recent, P, n_split, n_bsplit, n_total;
 };
 
@@ -99,16 +102,17 @@ __global__ __launch_bounds__(128) void rotate_q_kernel(DecodeArgs a) {
     const uint16_t* src = limb ? ql : qh;
     (&rec->frag[0][0][0][0][0])[j] = (uint32_t)src[ch] | ((uint32_t)src[ch + 8] << 16);
   }
-  if (j < 4) {
-    const int g = j & 1;
+  if (j < 6) {
+    const int g = j & 1, limb = (j >> 1) & 1;
+    const uint16_t* src = limb ? ql : qh;
     float sum = 0.f;
     for (int c = 64 * g; c < 64 * g + 64; ++c) {
-      if (j < 2)
-        sum -= (float)pair_base(pair_of_k(c & 7)) * (f16_bits_to_f32(qh[c]) + f16_bits_to_f32(ql[c]));
+      if (j < 4)
+        sum -= (float)pair_base(pair_of_k(c & 7)) * f16_bits_to_f32(src[c]);
       else
         sum += qs[c];
     }
-    if (j < 2) rec->negc[g] = sum;
+    if (j < 4) rec->negc[g][limb] = sum;
     else rec->qsum[g] = sum;
   }
 }
@@ -117,9 +121,9 @@ __global__ __launch_bounds__(128) void rotate_q_kernel(DecodeArgs a) {
 // split: block (item, KV head, sequence), 4 waves.
 // ---------------------------------------------------------------------------
 constexpr int kMaxPagesPerSplit = 128;
-constexpr int kRing = 8;   // pages in flight per wave (LDS ring, even: pages go in pairs)
+constexpr int kRing = 6;   // pages in flight per wave (LDS ring, even: pages go in pairs)
 // while pages j, j+1 are read, the DMAs of pages j+2 .. j+kRing-1 (two instructions each) may be in flight
-static_assert(2 * (kRing - 2) == 12, "s_waitcnt vmcnt immediate below assumes kRing == 8");
+static_assert(2 * (kRing - 2) == 8, "s_waitcnt vmcnt immediate below assumes kRing == 6");
 
 struct __attribute__((aligned(16))) SplitSmem {
   int32_t pid[kMaxPagesPerSplit];    // physical page ids of the item's page range
@@ -261,24 +265,35 @@ __device__ __forceinline__ float rows_max(float x) { return swap32(swap16(x, tru
 __device__ __forceinline__ float rows_sum(float x) { return swap32(swap16(x, false), false); }
 
 // INT2 history pages [first, end), two pages (32 tokens) per step; wave w
-// takes the pairs starting at first + 2w, + 8, ...
+// takes the pairs starting at first + 2w, + 8, ...  The G query heads are
+// handled in quads (NQ = ceil(G / 4)); lane l: n = l % 16, r = l / 16, and
+// for the logit MFMA column n = 4 hh + a: head 4 quad + hh, a = g' + 2 limb.
 //
-// Lane l: n = l % 16, r = l / 16.
-// Logits (per page, per 64-channel group g): D[token][head] = sum_c
-//   (base_c + code_c) * (hi + lo)_c, four MFMAs (two k-halves x two limbs),
-//   accumulator started at -sum_c base_c (hi + lo)_c.  A = codes: lane holds
-//   token n's code word r of group g (16 channels) as unpack16 pairs; B =
-//   q' fragments of head n.  D lands as lane (head n, tokens 4r..4r+3).
-// Values: acc[head][channel] += W[head][token] * (base + code)[token][channel],
-//   one MFMA per 16-channel tile and page pair: A = W = fp16(p s_g), held by
-//   the lanes that computed p (head n, tokens 4r+i of both pages); B = the
-//   channel-major code words of channel 16t + n, byte r of each page.  The base
-//   offsets are summed by one more MFMA per group against constant bases.
+// Logits, per page and quad: D[token][column] = sum over the channels of
+//   group g' of (base + code) * limb(q')  -- four MFMAs (one per 32-channel
+//   slice; a column's B fragment is zero on the other group's slices), the
+//   accumulator started at -sum base * limb(q').  A = codes: lane holds token
+//   n's code words as unpack16 pairs.  D lands as lane (column n, tokens
+//   4r + i).  Two quad exchanges then finish each logit: limbs (lane ^ 2),
+//   after which the lane keeps tokens 4r + 2 limb (+1) and applies that
+//   group's scale and zero-point term, and groups (lane ^ 1), after which lane
+//   (r, hh, a) holds the logit of token 4r + a of head hh: one value per lane.
+// Values, per page pair and quad: acc[(hh, j)][channel] += A[(hh, j)][k] *
+//   (base + code)[k][channel] with k running over the 32 tokens of the pair;
+//   row (hh, j) only carries the tokens 4r + j (A dword j holds the fp16
+//   weights p s_g of that token in both pages, the other dwords are zero), so
+//   each lane's own (token, head) weights feed the MFMA without any exchange;
+//   the four rows of a head are summed at the end.  B = channel-major code
+//   words of channel 16t + n, byte r of each page.  The base offsets are
+//   summed by one more MFMA per group against constant bases; the zero-point
+//   term sum p z_g is a per-head scalar.
 template <int G>
 __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int first, int end, int i_hi,
                           SplitSmem& sm) {
+  constexpr int NQ = (G + 3) / 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, r = lane >> 4;
+  const int hh = n >> 2, a4 = n & 3, gp = a4 & 1, limb = a4 >> 1;
 
   {
     const int32_t* ptab = a.page_table + (size_t)b * a.max_pages + first;
@@ -286,36 +301,41 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     __syncthreads();
   }
 
-  // q' fragments of head n (zero columns beyond G)
-  half8 qf[2][2][2];
-  f32x4 cinit[2];
-  float qsum[2];
-  {
-    const QrotRecord* rec = a.qrot + ((size_t)b * a.Hq + h * G + (n < G ? n : 0));
+  // q' fragments of column n: head 4 qd + hh, group gp, limb (zero beyond G)
+  half8 qb[NQ][2][2];
+  float cinit[NQ], qs[NQ];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+  for (int qd = 0; qd < NQ; ++qd) {
+    const int head = 4 * qd + hh;
+    const bool ok = head < G;
+    const QrotRecord* rec = a.qrot + ((size_t)b * a.Hq + h * G + (ok ? head : 0));
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int lm = 0; lm < 2; ++lm) {
-          const uint4 u = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][lm][r][0]);
-          qf[g][kh][lm] = half8_of(n < G ? u : make_uint4(0, 0, 0, 0));
-        }
-      const float nc = n < G ? rec->negc[g] : 0.f;
-      cinit[g] = f32x4{nc, nc, nc, nc};
-      qsum[g] = n < G ? rec->qsum[g] : 0.f;
-    }
+      for (int kh = 0; kh < 2; ++kh) {
+        const uint4 u = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][limb][r][0]);
+        qb[qd][g][kh] = half8_of(ok && g == gp ? u : make_uint4(0, 0, 0, 0));
+      }
+    cinit[qd] = ok ? rec->negc[gp][limb] : 0.f;
+    qs[qd] = ok ? rec->qsum[gp] : 0.f;
   }
 
-  float m_used = -INFINITY, lsum = 0.f, zs[2] = {0.f, 0.f};
-  f32x4 acc[8], accoff[2];
+  float m[NQ], lsum[NQ], zs[NQ][2];
+  f32x4 acc[NQ][8], accoff[NQ][2];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  accoff[0] = accoff[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qd = 0; qd < NQ; ++qd) {
+    m[qd] = -INFINITY;
+    lsum[qd] = 0.f;
+    zs[qd][0] = zs[qd][1] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[qd][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accoff[qd][0] = accoff[qd][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   // fp16 bases of the value-code pairs (4+c, 16+c, 4+c, 16+c), both halves
   const half8 boff = half8_of(0x44004400u, 0x4C004C00u, 0x44004400u, 0x4C004C00u);
   const uint32_t perm_sel = (uint32_t)r | (0x0Cu << 8) | ((4u + r) << 16) | (0x0Cu << 24);
   const PairConsts pk;
+  const float tau = a.resc_thr;
 
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
   const size_t head_off = (size_t)h * kBlockBytes;
@@ -340,104 +360,114 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     if (j + kRing - 2 < n_w) issue(j + kRing - 2);
     if (j + kRing - 1 < n_w) issue(j + kRing - 1);
     if (j + kRing - 1 < n_w) {
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");   // pages j, j+1 landed: 2*(kRing-2) still in flight
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // pages j, j+1 landed: 2*(kRing-2) still in flight
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     struct PageRegs {
-      uint32_t kc[2];
-      uint4 kp[2], vp[2];
-      uint32_t vw[8];
+      uint32_t kc[2];   // token n: code words r of group 0 and of group 1
+      uint32_t kp[2];   // (s, z) of group gp for tokens 4r + 2 limb and + 1
+      uint32_t vp[2];   // (s0, z0), (s1, z1) of token 4r + a4
+      uint32_t vw[8];   // value code words of channels 16t + n
     } cur[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const uint8_t* blk = &sm.ring[wave][(j + (k == 1 && has1 ? 1 : 0)) % kRing][0];
-      cur[k].kc[0] = *reinterpret_cast<const uint32_t*>(blk + kKCodes + 32 * n + 4 * r);
-      cur[k].kc[1] = *reinterpret_cast<const uint32_t*>(blk + kKCodes + 32 * n + 16 + 4 * r);
-      cur[k].kp[0] = *reinterpret_cast<const uint4*>(blk + kKParams + 32 * r);
-      cur[k].kp[1] = *reinterpret_cast<const uint4*>(blk + kKParams + 32 * r + 16);
-      cur[k].vp[0] = *reinterpret_cast<const uint4*>(blk + kVParams + 32 * r);
-      cur[k].vp[1] = *reinterpret_cast<const uint4*>(blk + kVParams + 32 * r + 16);
+      const uint32_t* w32 = reinterpret_cast<const uint32_t*>(blk);
+      cur[k].kc[0] = w32[(kKCodes + 32 * n) / 4 + r];
+      cur[k].kc[1] = w32[(kKCodes + 32 * n + 16) / 4 + r];
+      const int t0 = 4 * r + 2 * limb;
+      cur[k].kp[0] = w32[(kKParams + 8 * t0) / 4 + gp];
+      cur[k].kp[1] = w32[(kKParams + 8 * t0 + 8) / 4 + gp];
+      const uint2 v2 = *reinterpret_cast<const uint2*>(blk + kVParams + 8 * (4 * r + a4));
+      cur[k].vp[0] = v2.x;
+      cur[k].vp[1] = v2.y;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) cur[k].vw[t] = *reinterpret_cast<const uint32_t*>(blk + kVCodes + 4 * (16 * t + n));
+      for (int t = 0; t < 8; ++t) cur[k].vw[t] = w32[kVCodes / 4 + 16 * t + n];
     }
 
-    // ---- logits of both pages: lane (head n, tokens 4r + i) ----
-    float lg[2][4];
+    // ---- logits: lane (r, hh, a4) ends with token 4r + a4 of head 4 qd + hh ----
+    float lg[NQ][2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const PageRegs& P = cur[k];
       uint32_t e0[8], e1[8];
       unpack16(P.kc[0], e0, pk);
       unpack16(P.kc[1], e1, pk);
-      f32x4 d0 = cinit[0], d1 = cinit[1];
       const half8 a00 = half8_of(e0[0], e0[1], e0[2], e0[3]), a01 = half8_of(e0[4], e0[5], e0[6], e0[7]);
       const half8 a10 = half8_of(e1[0], e1[1], e1[2], e1[3]), a11 = half8_of(e1[4], e1[5], e1[6], e1[7]);
-      d0 = mfma16(a00, qf[0][0][0], d0);
-      d0 = mfma16(a01, qf[0][1][0], d0);
-      d0 = mfma16(a00, qf[0][0][1], d0);
-      d0 = mfma16(a01, qf[0][1][1], d0);
-      d1 = mfma16(a10, qf[1][0][0], d1);
-      d1 = mfma16(a11, qf[1][1][0], d1);
-      d1 = mfma16(a10, qf[1][0][1], d1);
-      d1 = mfma16(a11, qf[1][1][1], d1);
-      const uint32_t kw[8] = {P.kp[0].x, P.kp[0].y, P.kp[0].z, P.kp[0].w,
-                              P.kp[1].x, P.kp[1].y, P.kp[1].z, P.kp[1].w};
-      const bool page_ok = k == 0 || has1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float s0 = f16_bits_to_f32(kw[2 * i]), z0 = f16_bits_to_f32(kw[2 * i] >> 16);
-        const float s1 = f16_bits_to_f32(kw[2 * i + 1]), z1 = f16_bits_to_f32(kw[2 * i + 1] >> 16);
-        const float x = fmaf(s0, d0[i], fmaf(s1, d1[i], fmaf(z0, qsum[0], z1 * qsum[1])));
-        const bool ok = page_ok && (pp + k) * 16 + 4 * r + i < i_hi;
-        lg[k][i] = ok ? x : -INFINITY;
+      for (int qd = 0; qd < NQ; ++qd) {
+        f32x4 d = f32x4{cinit[qd], cinit[qd], cinit[qd], cinit[qd]};
+        d = mfma16(a00, qb[qd][0][0], d);
+        d = mfma16(a01, qb[qd][0][1], d);
+        d = mfma16(a10, qb[qd][1][0], d);
+        d = mfma16(a11, qb[qd][1][1], d);
+        // limbs: partner lane ^ 2 holds the other limb of the same group
+        const float u0 = d[0] + dpp<kQuadXor2>(d[0]), u1 = d[1] + dpp<kQuadXor2>(d[1]);
+        const float u2 = d[2] + dpp<kQuadXor2>(d[2]), u3 = d[3] + dpp<kQuadXor2>(d[3]);
+        const float y0 = limb ? u2 : u0, y1 = limb ? u3 : u1;
+        // scale and zero-point term of group gp (tokens 4r + 2 limb, + 1)
+        const float x0 = fmaf(f16_bits_to_f32(P.kp[0]), y0, f16_bits_to_f32(P.kp[0] >> 16) * qs[qd]);
+        const float x1 = fmaf(f16_bits_to_f32(P.kp[1]), y1, f16_bits_to_f32(P.kp[1] >> 16) * qs[qd]);
+        // groups: partner lane ^ 1 holds the other group of the same tokens
+        const float v0 = x0 + dpp<kQuadXor1>(x0), v1 = x1 + dpp<kQuadXor1>(x1);
+        lg[qd][k] = gp ? v1 : v0;
+      }
+    }
+    if (!has1 || (pp + 2) * kPage > i_hi) {   // wave-uniform: only the last pair can hold missing tokens
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const bool ok = (k == 0 || has1) && (pp + k) * kPage + 4 * r + a4 < i_hi;
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd) lg[qd][k] = ok ? lg[qd][k] : -INFINITY;
       }
     }
 
-    // ---- online softmax; rescale only when the max grows by more than 2 (p <= 4) ----
-    float pm = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
-                     fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
-    pm = rows_max(pm);
-    const bool need = pm > m_used + 2.0f;
-    if (__any(need)) {
-      const float m_new = need ? pm : m_used;
-      const float al = fast_exp2(m_used - m_new);
-      lsum *= al;
-      zs[0] *= al;
-      zs[1] *= al;
+    // ---- online softmax per head; rescale only when the max grows by more than tau ----
+    float pmax[NQ];
+    bool need_any = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(al, 4 * r + i);   // rows of acc are heads 4r + i
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t][i] *= ai;
-        accoff[0][i] *= ai;
-        accoff[1][i] *= ai;
-      }
-      m_used = m_new;
+    for (int qd = 0; qd < NQ; ++qd) {
+      float pm = fmaxf(lg[qd][0], lg[qd][1]);
+      pm = fmaxf(pm, dpp<kQuadXor1>(pm));
+      pm = fmaxf(pm, dpp<kQuadXor2>(pm));
+      pmax[qd] = rows_max(pm);
+      need_any |= pmax[qd] > m[qd] + tau;
     }
-    float p[2][4];
+    if (__any(need_any)) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+      for (int qd = 0; qd < NQ; ++qd) {
+        const float m_new = pmax[qd] > m[qd] + tau ? pmax[qd] : m[qd];
+        const float al = fast_exp2(m[qd] - m_new);
+        lsum[qd] *= al;
+        zs[qd][0] *= al;
+        zs[qd][1] *= al;
+        const float ai = __shfl(al, 4 * r);   // accumulator rows of this lane belong to head hh' = r
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[k][i] = fast_exp2(lg[k][i] - m_used);
-        lsum += p[k][i];
+        for (int t = 0; t < 8; ++t) acc[qd][t] *= ai;
+        accoff[qd][0] *= ai;
+        accoff[qd][1] *= ai;
+        m[qd] = m_new;
       }
+    }
 
-    // ---- weights W = fp16(p s_g) and the zero-point sums ----
-    uint32_t wg[2][4];
+    // ---- weights W_g = fp16(p) * s_g of this lane's token in both pages ----
+    half8 A[NQ][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&cur[0].vp[0]);
-      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&cur[1].vp[0]);
-      const uint32_t a0 = v0[2 * i], b0 = v0[2 * i + 1], a1 = v1[2 * i], b1 = v1[2 * i + 1];
-      wg[0][i] = pack_f16(p[0][i] * f16_bits_to_f32(a0), p[1][i] * f16_bits_to_f32(a1));
-      wg[1][i] = pack_f16(p[0][i] * f16_bits_to_f32(b0), p[1][i] * f16_bits_to_f32(b1));
-      zs[0] = fmaf(p[0][i], f16_bits_to_f32(a0 >> 16), fmaf(p[1][i], f16_bits_to_f32(a1 >> 16), zs[0]));
-      zs[1] = fmaf(p[0][i], f16_bits_to_f32(b0 >> 16), fmaf(p[1][i], f16_bits_to_f32(b1 >> 16), zs[1]));
+    for (int qd = 0; qd < NQ; ++qd) {
+      const float p0 = fast_exp2(lg[qd][0] - m[qd]), p1 = fast_exp2(lg[qd][1] - m[qd]);
+      lsum[qd] += p0 + p1;
+      const half2v pp2 = half2v{(_Float16)p0, (_Float16)p1};
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t sp = __builtin_amdgcn_perm(cur[1].vp[g], cur[0].vp[g], 0x05040100u);
+        const uint32_t zp = __builtin_amdgcn_perm(cur[1].vp[g], cur[0].vp[g], 0x07060302u);
+        const uint32_t w = __builtin_bit_cast(uint32_t, pp2 * __builtin_bit_cast(half2v, sp));
+        zs[qd][g] = __builtin_amdgcn_fdot2(pp2, __builtin_bit_cast(half2v, zp), zs[qd][g], false);
+        A[qd][g] = half8_of(a4 == 0 ? w : 0u, a4 == 1 ? w : 0u, a4 == 2 ? w : 0u, a4 == 3 ? w : 0u);
+      }
     }
-    const half8 W0 = half8_of(wg[0][0], wg[0][1], wg[0][2], wg[0][3]);
-    const half8 W1 = half8_of(wg[1][0], wg[1][1], wg[1][2], wg[1][3]);
 
     // ---- values ----
 #pragma unroll
@@ -446,28 +476,41 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
       const uint32_t m16 = pk.m16, b16 = pk.b16, m4 = pk.m4, b4 = pk.b4;
       const uint32_t l4 = x << 4;
       const half8 bv = half8_of(((x << 8) & m4) | b4, (l4 & m16) | b16, (l4 & m4) | b4, (x & m16) | b16);
-      acc[t] = mfma16(t < 4 ? W0 : W1, bv, acc[t]);
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) acc[qd][t] = mfma16(A[qd][t >> 2], bv, acc[qd][t]);
     }
-    accoff[0] = mfma16(W0, boff, accoff[0]);
-    accoff[1] = mfma16(W1, boff, accoff[1]);
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      accoff[qd][0] = mfma16(A[qd][0], boff, accoff[qd][0]);
+      accoff[qd][1] = mfma16(A[qd][1], boff, accoff[qd][1]);
+    }
   }
 
   // ---- finish the wave (the result area overlays the page rings: wait for all waves) ----
   __syncthreads();
-  const float L_h = rows_sum(lsum);
-  const float Z0 = rows_sum(zs[0]), Z1 = rows_sum(zs[1]);
-  if (r == 0 && n < G) {
-    sm.m[wave][n] = m_used;
-    sm.l[wave][n] = L_h;
-  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int head = 4 * r + i;
-    const float z0 = __shfl(Z0, head & 15), z1 = __shfl(Z1, head & 15);
-    if (head < G) {
+  for (int qd = 0; qd < NQ; ++qd) {
+    // per-head totals over the 16 lanes of head hh (quad, then rows)
+    float L_h = lsum[qd], Z0 = zs[qd][0], Z1 = zs[qd][1];
+    L_h = rows_sum(quad_sum(L_h));
+    Z0 = rows_sum(quad_sum(Z0));
+    Z1 = rows_sum(quad_sum(Z1));
+    const int head = 4 * qd + hh;
+    if (r == 0 && a4 == 0 && head < G) {
+      sm.m[wave][head] = m[qd];
+      sm.l[wave][head] = L_h;
+    }
+    // accumulator rows of this lane: head 4 qd + r, subsets j = 0..3
+    const float z0 = __shfl(Z0, 4 * r), z1 = __shfl(Z1, 4 * r);
+    const float off0 = (accoff[qd][0][0] + accoff[qd][0][1]) + (accoff[qd][0][2] + accoff[qd][0][3]);
+    const float off1 = (accoff[qd][1][0] + accoff[qd][1][1]) + (accoff[qd][1][2] + accoff[qd][1][3]);
+    const int row_head = 4 * qd + r;
+    if (row_head < G) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        sm.acc[wave][head][16 * t + n] = acc[t][i] - (t < 4 ? accoff[0][i] - z0 : accoff[1][i] - z1);
+      for (int t = 0; t < 8; ++t) {
+        const float s = (acc[qd][t][0] + acc[qd][t][1]) + (acc[qd][t][2] + acc[qd][t][3]);
+        sm.acc[wave][row_head][16 * t + n] = s - (t < 4 ? off0 - z0 : off1 - z1);
+      }
     }
   }
   merge_waves_and_store<G>(a, b, h, a.n_bsplit + split, sm);
@@ -626,6 +669,14 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.qrot = reinterpret_cast<QrotRecord*>(L.workspace + L.plan.qrot_off);
   a.part = reinterpret_cast<float*>(L.workspace + L.plan.part_off);
   a.sl2e = L.sm_scale * 1.4426950408889634f;
+  {
+    // W = fp16(p s) must stay below fp16's maximum: a value scale is at most
+    // fp16((max - min) / 3) <= 2 clip_v / 3 (+ rounding), so p <= 2^tau with
+    // 2^tau * s_max < 65000; tau in [2, 8]
+    const double s_max = 2.0 * L.clip_v / 3.0 * (1.0 + 1.0 / 1024);
+    int tau = (int)std::floor(std::log2(65000.0 / s_max));
+    a.resc_thr = (float)(tau < 2 ? 2 : tau > 8 ? 8 : tau);
+  }
   a.H = L.num_kv_heads;
   a.Hq = L.num_q_heads;
   a.G = L.num_q_heads / L.num_kv_heads;

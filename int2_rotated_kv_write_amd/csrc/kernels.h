@@ -40,7 +40,7 @@ struct DecodeLaunch {
   const int32_t *page_table, *seq_lens;
   uint16_t* out;
   uint8_t* workspace;
-  float sm_scale;
+  float sm_scale, clip_v;
   int32_t num_kv_heads, num_q_heads, max_pages, batch, sink, recent;
   DecodePlan plan;
 };

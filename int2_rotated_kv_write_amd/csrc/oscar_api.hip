@@ -113,6 +113,7 @@ int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, co
   if (!q || !page_table || !seq_lens || !out || !layer->pages || !layer->k_ring || !layer->v_ring || !layer->u_k ||
       !layer->u_v || (shape->sink > 0 && (!layer->k_sink || !layer->v_sink)))
     return fail(OSCAR_EINVAL, "NULL tensor pointer%s");
+  if (!clip_ok(layer->clip_v)) return fail(OSCAR_EINVAL, "clip_v outside (0, 16384]%s");
   const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
                                                          shape->recent, batch, max_pages);
   if (plan.n_total > oscar::kMaxItems) return fail(OSCAR_EINVAL, "max_pages too large (sequences over ~2M tokens)%s");
@@ -132,6 +133,7 @@ int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, co
   L.out = out;
   L.workspace = static_cast<uint8_t*>(workspace);
   L.sm_scale = sm_scale;
+  L.clip_v = layer->clip_v;
   L.num_kv_heads = shape->num_kv_heads;
   L.num_q_heads = shape->num_q_heads;
   L.max_pages = max_pages;

@@ -9,6 +9,16 @@ Parity rules (written out here, used by every GPU test):
     lies within 1e-5 (relative to max(|value|, scale)) of an fp16 rounding
     midpoint; the codes of such a group are then re-derived by the oracle's
     rule with the GPU's scale and zero and held to the rule above;
+  * "relative" is taken relative to the operands the kernel's fp32 arithmetic
+    works on, not only to the result: the rotated values of a token carry an
+    fp32 error that scales with the token's largest rotated magnitude, so
+    each window is at least that allowance, E_w = 8 fp32 ulps of
+    max_j |w_raw_j| (2^-21 max|w_raw|): scale 2/3 E_w, zero E_w, code t
+    4 E_w / s.  This only matters for ill-conditioned groups whose range is
+    tiny next to their values (e.g. 64 values clipped at or just below c:
+    range 3.5e-3 at magnitude 18.7, where fp32 alone moves s by 1e-3
+    relative); elsewhere 1e-5 relative is the wider window.  Such excusals
+    are counted separately (codes_cond, params_cond);
   * bytes outside the slots a call writes must be untouched;
   * decode outputs are bf16; "in bf16 units" is read as: the error of an
     element beyond its own bf16 representation error,
@@ -26,6 +36,7 @@ import oracle as O
 
 SIG = 1 / math.sqrt(128)
 CODE_REL_TOL = 1e-5
+W_ULP_ALLOWANCE = 2.0 ** -21   # 8 fp32 ulps of the token's largest rotated magnitude
 MAX_ABS_TOL = 2e-2
 MEAN_ABS_TOL = 2e-3
 
@@ -69,15 +80,15 @@ def host_cache(dc) -> O.Cache:
                    v_ring=from_dev_bf16(dc.v_ring))
 
 
-def _near_fp16_midpoint(x, scale):
-    d = CODE_REL_TOL * np.maximum(np.abs(x), np.abs(scale))
+def _near_fp16_midpoint(x, scale, slack=0.0):
+    d = np.maximum(CODE_REL_TOL * np.maximum(np.abs(x), np.abs(scale)), slack)
     return O.fp16_rne(x - d).view(np.uint16) != O.fp16_rne(x + d).view(np.uint16)
 
 
-def _near_code_boundary(t):
+def _near_code_boundary(t, slack=0.0):
     near = np.zeros(t.shape, bool)
     for b in (0.5, 1.5, 2.5):
-        near |= np.abs(t - b) <= CODE_REL_TOL * b
+        near |= np.abs(t - b) <= np.maximum(CODE_REL_TOL * b, slack)
     return near
 
 
@@ -102,7 +113,7 @@ def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got
     `got_before` the GPU cache before it (bytes the call must not touch are
     compared against it: earlier calls may differ from the oracle by excused
     near-ties).  Returns counts of excused codes / parameters."""
-    stats = dict(codes=0, codes_excused=0, params=0, params_excused=0)
+    stats = dict(codes=0, codes_excused=0, codes_cond=0, params=0, params_excused=0, params_cond=0)
     H = shape.num_kv_heads
     assert np.array_equal(ref.k_sink, got.k_sink), "k_sink differs"
     assert np.array_equal(ref.v_sink, got.v_sink), "v_sink differs"
@@ -117,10 +128,22 @@ def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got
             z_ref = d["z16"][:, h].view(np.uint16)
             s_got, z_got = par[:, 0::2], par[:, 1::2]
             s_pre, z_pre = d["s_pre"][:, h], d["z_pre"][:, h]
-            bad_s = (s_got != s_ref) & ~_near_fp16_midpoint(s_pre, s_pre)
-            bad_z = (z_got != z_ref) & ~_near_fp16_midpoint(z_pre, s_pre)
-            assert not bad_s.any(), f"{kind} scale mismatch h={h} at {np.argwhere(bad_s)[:4]}"
-            assert not bad_z.any(), f"{kind} zero mismatch h={h} at {np.argwhere(bad_z)[:4]}"
+            e_w = W_ULP_ALLOWANCE * np.abs(d["w_raw"][:, h]).max(axis=1)[:, None]   # [n][1]
+            near_s = _near_fp16_midpoint(s_pre, s_pre, 2.0 / 3.0 * e_w)
+            near_z = _near_fp16_midpoint(z_pre, s_pre, e_w)
+            bad_s = (s_got != s_ref) & ~near_s
+            bad_z = (z_got != z_ref) & ~near_z
+            stats["params_cond"] += int((((s_got != s_ref) & ~_near_fp16_midpoint(s_pre, s_pre))
+                                         | ((z_got != z_ref) & ~_near_fp16_midpoint(z_pre, s_pre))).sum())
+            for bad, what in ((bad_s, "scale"), (bad_z, "zero")):
+                if bad.any():
+                    i, g = np.argwhere(bad)[0]
+                    seg = d["w"][i, h, 64 * g:64 * g + 64]
+                    raise AssertionError(
+                        f"{kind} {what} mismatch h={h} at token {i} group {g} ({int(bad.sum())} total): "
+                        f"s_pre={s_pre[i, g]!r} z_pre={z_pre[i, g]!r} ref s,z=0x{s_ref[i, g]:04x},0x{z_ref[i, g]:04x} "
+                        f"gpu s,z=0x{s_got[i, g]:04x},0x{z_got[i, g]:04x} group max={seg.max()!r} min={seg.min()!r} "
+                        f"max|w_raw|={np.abs(d['w_raw'][i, h]).max()!r}")
             stats["params"] += s_ref.size * 2
             stats["params_excused"] += int((s_got != s_ref).sum() + (z_got != z_ref).sum())
             # reference codes, re-derived with the GPU's parameters where they differ
@@ -133,7 +156,9 @@ def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got
             same = (s_got == s_ref) & (z_got == z_ref)
             assert np.array_equal(code_ref[same[:, g]], d["codes"][:, h][same[:, g]])
             mism = codes != code_ref
-            bad = mism & ~_near_code_boundary(t)
+            slack = np.where(sg == 0, 0.0, 4.0 * e_w / np.where(sg == 0, 1.0, sg))
+            bad = mism & ~_near_code_boundary(t, slack)
+            stats["codes_cond"] += int((mism & ~_near_code_boundary(t)).sum())
             assert not bad.any(), (f"{kind} code mismatch h={h}: {int(bad.sum())} codes, e.g. "
                                    f"t={t[bad][:4]}, gpu={codes[bad][:4]}, ref={code_ref[bad][:4]}")
             stats["codes"] += codes.size
