@@ -291,7 +291,7 @@ template <int G>
 __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int first, int end, int i_hi,
                           SplitSmem& sm) {
   constexpr int NQ = (G + 3) / 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, r = lane >> 4;
   const int hh = n >> 2, a4 = n & 3, gp = a4 & 1, limb = a4 >> 1;
 
@@ -345,13 +345,21 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   int n_w = 0;
   if (base0 < end) n_w = 2 * ((end - base0 + 7) / 8) - ((end - base0 - 1) % 8 == 0 ? 1 : 0);
   auto page_of = [&](int j) { return base0 + 8 * (j >> 1) + (j & 1); };
+  const uint8_t* lane_src = a.pages + head_off + 16 * lane;
   auto issue = [&](int j) {   // 2 DMA instructions per page
-    const uint8_t* blk = a.pages + (size_t)sm.pid[page_of(j) - first] * page_stride + head_off;
+    const int pid = __builtin_amdgcn_readfirstlane(sm.pid[page_of(j) - first]);
+    const uint8_t* blk = lane_src + (size_t)pid * page_stride;
     uint8_t* dst = &sm.ring[wave][j % kRing][0];
-    __builtin_amdgcn_global_load_lds(blk + 16 * lane, dst, 16, 0, 0);
-    if (lane < 16) __builtin_amdgcn_global_load_lds(blk + 1024 + 16 * lane, dst + 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(blk, dst, 16, 0, 0);
+    if (lane < 16) __builtin_amdgcn_global_load_lds(blk + 1024, dst + 1024, 16, 0, 0);
   };
   for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(j);
+  // this lane's byte offsets inside a page block
+  const int t0 = 4 * r + 2 * limb;
+  const int off_kc = kKCodes + 32 * n + 4 * r;            // token n: code word r of group 0 (+16: group 1)
+  const int off_kp = kKParams + 8 * t0 + 4 * gp;          // (s, z) of group gp, tokens t0 and t0 + 1
+  const int off_vp = kVParams + 8 * (4 * r + a4);         // (s0, z0, s1, z1) of token 4r + a4
+  const int off_vw = kVCodes + 4 * n;                     // value code word of channel 16t + n at + 64t
 
   for (int j = 0; j < n_w; j += 2) {
     const int pp = page_of(j);
@@ -370,20 +378,19 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
       uint32_t vp[2];   // (s0, z0), (s1, z1) of token 4r + a4
       uint32_t vw[8];   // value code words of channels 16t + n
     } cur[2];
+    const int slot0 = j % kRing, slot1 = has1 ? slot0 + 1 : slot0;   // wave-uniform
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint8_t* blk = &sm.ring[wave][(j + (k == 1 && has1 ? 1 : 0)) % kRing][0];
-      const uint32_t* w32 = reinterpret_cast<const uint32_t*>(blk);
-      cur[k].kc[0] = w32[(kKCodes + 32 * n) / 4 + r];
-      cur[k].kc[1] = w32[(kKCodes + 32 * n + 16) / 4 + r];
-      const int t0 = 4 * r + 2 * limb;
-      cur[k].kp[0] = w32[(kKParams + 8 * t0) / 4 + gp];
-      cur[k].kp[1] = w32[(kKParams + 8 * t0 + 8) / 4 + gp];
-      const uint2 v2 = *reinterpret_cast<const uint2*>(blk + kVParams + 8 * (4 * r + a4));
+      const uint8_t* blk = &sm.ring[wave][k == 0 ? slot0 : slot1][0];
+      cur[k].kc[0] = *reinterpret_cast<const uint32_t*>(blk + off_kc);
+      cur[k].kc[1] = *reinterpret_cast<const uint32_t*>(blk + off_kc + 16);
+      cur[k].kp[0] = *reinterpret_cast<const uint32_t*>(blk + off_kp);
+      cur[k].kp[1] = *reinterpret_cast<const uint32_t*>(blk + off_kp + 8);
+      const uint2 v2 = *reinterpret_cast<const uint2*>(blk + off_vp);
       cur[k].vp[0] = v2.x;
       cur[k].vp[1] = v2.y;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) cur[k].vw[t] = w32[kVCodes / 4 + 16 * t + n];
+      for (int t = 0; t < 8; ++t) cur[k].vw[t] = *reinterpret_cast<const uint32_t*>(blk + off_vw + 64 * t);
     }
 
     // ---- logits: lane (r, hh, a4) ends with token 4r + a4 of head 4 qd + hh ----
@@ -517,7 +524,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 }
 
 template <int G>
-__global__ __launch_bounds__(256) void split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void split_kernel(DecodeArgs a) {
   __shared__ SplitSmem sm;
   const int item = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int L = a.seq_lens[b];
