@@ -53,41 +53,45 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 //
 // A 32-bit word holds 16 two-bit codes, code k at bits 2k.  unpack16 turns it
 // into 8 fp16 pairs without any integer->float conversion: a code placed in
-// fraction bits 6-7 of an fp16 whose exponent is 2^4 reads as 16 + code; in
-// bits 8-9 under exponent 2^2 it reads as 4 + code.  Pair i holds codes
-// (k_i, k_i + 8) from the low and high halves of the word, with the constant
-// kPairBase[i] added to both.  Consumers subtract sum(base * weight).
+// fraction bits 4-5 of an fp16 whose exponent is 2^6 reads as 64 + code, in
+// bits 6-7 under 2^4 as 16 + code, in bits 8-9 under 2^2 as 4 + code.  The
+// word itself, the word >> 6 and the word << 6 each expose codes at those
+// three positions of both halves, so 8 pairs cost two shifts and eight
+// and-or operations.  Pair i holds codes (k_i, k_i + 8) from the low and
+// high halves of the word, with the constant kPairBase[i] added to both.
+// Consumers subtract sum(base * weight).
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int pair_k(int i) {   // k of pair i
-  return i == 0 ? 3 : i == 1 ? 4 : i == 2 ? 5 : i == 3 ? 6 : i == 4 ? 7 : i == 5 ? 1 : i == 6 ? 2 : 0;
+  return i == 0 ? 2 : i == 1 ? 3 : i == 2 ? 4 : i == 3 ? 5 : i == 4 ? 6 : i == 5 ? 7 : i == 6 ? 0 : 1;
 }
 __host__ __device__ constexpr int pair_base(int i) {
-  return (i == 1 || i == 3 || i == 6) ? 4 : 16;
+  return (i == 0 || i == 3) ? 64 : (i == 2 || i == 5 || i == 7) ? 4 : 16;
 }
 __host__ __device__ constexpr int pair_of_k(int k) {  // inverse of pair_k (k in 0..7)
-  return k == 3 ? 0 : k == 4 ? 1 : k == 5 ? 2 : k == 6 ? 3 : k == 7 ? 4 : k == 1 ? 5 : k == 2 ? 6 : 7;
+  return k == 2 ? 0 : k == 3 ? 1 : k == 4 ? 2 : k == 5 ? 3 : k == 6 ? 4 : k == 7 ? 5 : k == 0 ? 6 : 7;
 }
 
 // Masks and bases live in VGPRs so that (x & m) | b is one v_and_or_b32
 // (a VOP3 instruction cannot take two literal constants on gfx9).
 struct PairConsts {
-  uint32_t m16, b16, m4, b4;
-  __device__ __forceinline__ PairConsts() : m16(0x00C000C0u), b16(0x4C004C00u), m4(0x03000300u), b4(0x44004400u) {
-    asm volatile("" : "+v"(m16), "+v"(b16), "+v"(m4), "+v"(b4));
+  uint32_t m64, b64, m16, b16, m4, b4;
+  __device__ __forceinline__ PairConsts()
+      : m64(0x00300030u), b64(0x54005400u), m16(0x00C000C0u), b16(0x4C004C00u), m4(0x03000300u),
+        b4(0x44004400u) {
+    asm volatile("" : "+v"(m64), "+v"(b64), "+v"(m16), "+v"(b16), "+v"(m4), "+v"(b4));
   }
 };
 
 __device__ __forceinline__ void unpack16(uint32_t x, uint32_t e[8], const PairConsts& k) {
-  const uint32_t m16 = k.m16, b16 = k.b16, m4 = k.m4, b4 = k.b4;   // bits 6-7 -> 16 + c, 8-9 -> 4 + c
-  const uint32_t r4 = x >> 4, r8 = x >> 8, l4 = x << 4, l6 = x << 6;
-  e[0] = (x & m16) | b16;    // k = 3
-  e[1] = (x & m4) | b4;      // k = 4
-  e[2] = (r4 & m16) | b16;   // k = 5
-  e[3] = (r4 & m4) | b4;     // k = 6
-  e[4] = (r8 & m16) | b16;   // k = 7
-  e[5] = (l4 & m16) | b16;   // k = 1
-  e[6] = (l4 & m4) | b4;     // k = 2
-  e[7] = (l6 & m16) | b16;   // k = 0
+  const uint32_t r6 = x >> 6, l6 = x << 6;
+  e[0] = (x & k.m64) | k.b64;    // k = 2
+  e[1] = (x & k.m16) | k.b16;    // k = 3
+  e[2] = (x & k.m4) | k.b4;      // k = 4
+  e[3] = (r6 & k.m64) | k.b64;   // k = 5
+  e[4] = (r6 & k.m16) | k.b16;   // k = 6
+  e[5] = (r6 & k.m4) | k.b4;     // k = 7
+  e[6] = (l6 & k.m16) | k.b16;   // k = 0
+  e[7] = (l6 & k.m4) | k.b4;     // k = 1
 }
 
 // 7-bit / 3-bit index reversal.

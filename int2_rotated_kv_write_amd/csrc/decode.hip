@@ -60,67 +60,122 @@ __device__ __forceinline__ int int2_end(int L, int sink, int recent) {   // INT2
 }
 
 // ---------------------------------------------------------------------------
-// rotate_q: one block per (sequence, KV head); two query heads at a time.
+// rotate_q: one 256-thread block per (sequence, KV head) for its G query
+// heads: U_K staged once in LDS, y = q U_K, FWHT, bit reversal, scale, then
+// the fp16 hi/lo MFMA fragments and offset sums of each head.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void rotate_q_kernel(DecodeArgs a) {
-  __shared__ float y[kHeadDim];
-  __shared__ float qs[kHeadDim];
-  __shared__ uint16_t qh[kHeadDim], ql[kHeadDim];
-  const int bq = blockIdx.x, b = bq / a.Hq, hq = bq % a.Hq, h = hq / a.G;
-  const int j = threadIdx.x;
-  const uint16_t* U = a.u_k + (size_t)h * kHeadDim * kHeadDim;
-  const uint16_t* qv = a.q + (size_t)bq * kHeadDim;
-  float acc0 = 0.f, acc1 = 0.f;
-  for (int i = 0; i < kHeadDim; i += 2) {
-    acc0 = fmaf(bf16_bits_to_f32(qv[i]), bf16_bits_to_f32(U[i * kHeadDim + j]), acc0);
-    acc1 = fmaf(bf16_bits_to_f32(qv[i + 1]), bf16_bits_to_f32(U[(i + 1) * kHeadDim + j]), acc1);
+constexpr int kSideThreads = 256;
+
+__global__ __launch_bounds__(kSideThreads) void rotate_q_kernel(DecodeArgs a) {
+  __shared__ uint4 Us[kHeadDim * kHeadDim / 8];           // U_K[h], row-major bf16
+  __shared__ float qv[kMaxGqa][kHeadDim];
+  __shared__ float y[kMaxGqa][kHeadDim];
+  __shared__ uint16_t qh[kMaxGqa][kHeadDim], ql[kMaxGqa][kHeadDim];
+  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H, G = a.G;
+  const int tid = threadIdx.x, j = tid & (kHeadDim - 1), hs = tid >> 7;
+  const uint4* U = reinterpret_cast<const uint4*>(a.u_k + (size_t)h * kHeadDim * kHeadDim);
+  // issue every global load before the first LDS store (one memory latency, not eight)
+  {
+    constexpr int kPer = kHeadDim * kHeadDim / 8 / kSideThreads;
+    uint4 tmp[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) tmp[k] = U[tid + k * kSideThreads];
+    const uint16_t* qg = a.q + ((size_t)b * a.Hq + h * G) * kHeadDim;
+    uint16_t qb[kMaxGqa * kHeadDim / kSideThreads];
+#pragma unroll
+    for (int k = 0; k < kMaxGqa * kHeadDim / kSideThreads; ++k) {
+      const int e = tid + k * kSideThreads;
+      qb[k] = e < G * kHeadDim ? qg[e] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) Us[tid + k * kSideThreads] = tmp[k];
+#pragma unroll
+    for (int k = 0; k < kMaxGqa * kHeadDim / kSideThreads; ++k) {
+      const int e = tid + k * kSideThreads;
+      if (e < G * kHeadDim) qv[e >> 7][e & 127] = bf16_bits_to_f32(qb[k]);
+    }
   }
-  y[j] = acc0 + acc1;
   __syncthreads();
+  // y[g][j] = sum_i q_g[i] U[i][j]; this thread: column j of heads hs, hs + 2, ... (hs is
+  // wave-uniform); eight independent LDS loads per step, two partial sums per head
+  const uint16_t* Uh = reinterpret_cast<const uint16_t*>(Us);
+  float acc[kMaxGqa / 2][2];
+#pragma unroll
+  for (int k = 0; k < kMaxGqa / 2; ++k) acc[k][0] = acc[k][1] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kHeadDim; i += 8) {
+    float u[8];
+#pragma unroll
+    for (int di = 0; di < 8; ++di) u[di] = bf16_bits_to_f32(Uh[(i + di) * kHeadDim + j]);
+#pragma unroll
+    for (int k = 0; k < kMaxGqa / 2; ++k) {
+      const int g = hs + 2 * k;
+      if (g < G) {
+        const float4 q0 = *reinterpret_cast<const float4*>(&qv[g][i]);
+        const float4 q1 = *reinterpret_cast<const float4*>(&qv[g][i + 4]);
+        acc[k][0] = fmaf(q0.x, u[0], fmaf(q0.y, u[1], fmaf(q0.z, u[2], fmaf(q0.w, u[3], acc[k][0]))));
+        acc[k][1] = fmaf(q1.x, u[4], fmaf(q1.y, u[5], fmaf(q1.z, u[6], fmaf(q1.w, u[7], acc[k][1]))));
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxGqa / 2; ++k)
+    if (hs + 2 * k < G) y[hs + 2 * k][j] = acc[k][0] + acc[k][1];
+  __syncthreads();
+  // FWHT of every head, 64 butterflies per head and stage
   for (int s = 1; s < kHeadDim; s <<= 1) {
-    if (j < 64) {
-      const int lo = ((j & ~(s - 1)) << 1) | (j & (s - 1)), hi = lo | s;
-      const float x0 = y[lo], x1 = y[hi];
-      y[lo] = x0 + x1;
-      y[hi] = x0 - x1;
+    for (int t = tid; t < G * 64; t += kSideThreads) {
+      const int g = t >> 6, c = t & 63;
+      const int lo = ((c & ~(s - 1)) << 1) | (c & (s - 1)), hi = lo | s;
+      const float x0 = y[g][lo], x1 = y[g][hi];
+      y[g][lo] = x0 + x1;
+      y[g][hi] = x0 - x1;
     }
     __syncthreads();
   }
-  {
-    const float w = y[bitrev7(j)] * 0.08838834764831845f * a.sl2e;   // (z P)_j = z_br(j)
+  // w_j = z_br(j) / sqrt(128) * sm_scale * log2(e), split into fp16 hi + lo
+  for (int e = tid; e < G * kHeadDim; e += kSideThreads) {
+    const int g = e >> 7, c = e & 127;
+    const float w = y[g][bitrev7(c)] * 0.08838834764831845f * a.sl2e;
     const uint32_t hb = f32_to_f16_bits(w);
-    qs[j] = w;
-    qh[j] = (uint16_t)hb;
-    ql[j] = (uint16_t)f32_to_f16_bits(w - f16_bits_to_f32(hb));
+    qv[g][c] = w;
+    qh[g][c] = (uint16_t)hb;
+    ql[g][c] = (uint16_t)f32_to_f16_bits(w - f16_bits_to_f32(hb));
   }
   __syncthreads();
-  QrotRecord* rec = a.qrot + bq;
-  {
-    // j = (((g*2 + kh)*2 + limb)*4 + c)*4 + v
-    const int v = j & 3, c = (j >> 2) & 3, limb = (j >> 4) & 1, kh = (j >> 5) & 1, g = (j >> 6) & 1;
-    const int ch = 64 * g + 16 * c + pair_k(4 * kh + v);
-    const uint16_t* src = limb ? ql : qh;
-    (&rec->frag[0][0][0][0][0])[j] = (uint32_t)src[ch] | ((uint32_t)src[ch + 8] << 16);
+  for (int e = tid; e < G * kHeadDim; e += kSideThreads) {
+    // dword e of head g: frag index (((gr*2 + kh)*2 + limb)*4 + c)*4 + v
+    const int g = e >> 7, jj = e & 127;
+    const int v = jj & 3, c = (jj >> 2) & 3, limb = (jj >> 4) & 1, kh = (jj >> 5) & 1, gr = (jj >> 6) & 1;
+    const int ch = 64 * gr + 16 * c + pair_k(4 * kh + v);
+    const uint16_t* src = limb ? ql[g] : qh[g];
+    QrotRecord* rec = a.qrot + (size_t)b * a.Hq + h * G + g;
+    (&rec->frag[0][0][0][0][0])[jj] = (uint32_t)src[ch] | ((uint32_t)src[ch + 8] << 16);
   }
-  if (j < 6) {
-    const int g = j & 1, limb = (j >> 1) & 1;
-    const uint16_t* src = limb ? ql : qh;
-    float sum = 0.f;
-    for (int c = 64 * g; c < 64 * g + 64; ++c) {
-      if (j < 4)
-        sum -= (float)pair_base(pair_of_k(c & 7)) * f16_bits_to_f32(src[c]);
-      else
-        sum += qs[c];
+  // offset sums, one wave per head: lane l takes channel 64 gr + l
+  const int lane = tid & 63;
+  for (int g = tid >> 6; g < G; g += kSideThreads / 64) {
+    QrotRecord* rec = a.qrot + (size_t)b * a.Hq + h * G + g;
+    const float base = (float)pair_base(pair_of_k(lane & 7));
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {
+      const int c = 64 * gr + lane;
+      const float nh = wave_sum_xor(-base * f16_bits_to_f32(qh[g][c]), 1, 32);
+      const float nl = wave_sum_xor(-base * f16_bits_to_f32(ql[g][c]), 1, 32);
+      const float qs = wave_sum_xor(qv[g][c], 1, 32);
+      if (lane == 0) {
+        rec->negc[gr][0] = nh;
+        rec->negc[gr][1] = nl;
+        rec->qsum[gr] = qs;
+      }
     }
-    if (j < 4) rec->negc[g][limb] = sum;
-    else rec->qsum[g] = sum;
   }
 }
 
 // ---------------------------------------------------------------------------
 // split: block (item, KV head, sequence), 4 waves.
 // ---------------------------------------------------------------------------
-constexpr int kMaxPagesPerSplit = 128;
+constexpr int kMaxPagesPerSplit = 1024;
 constexpr int kRing = 6;   // pages in flight per wave (LDS ring, even: pages go in pairs)
 // while pages j, j+1 are read, the DMAs of pages j+2 .. j+kRing-1 (two instructions each) may be in flight
 static_assert(2 * (kRing - 2) == 8, "s_waitcnt vmcnt immediate below assumes kRing == 6");
@@ -297,7 +352,17 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 
   {
     const int32_t* ptab = a.page_table + (size_t)b * a.max_pages + first;
-    for (int i = threadIdx.x; i < end - first; i += 256) sm.pid[i] = ptab[i];
+    int32_t ids[kMaxPagesPerSplit / 256];   // all loads in flight before the LDS stores
+#pragma unroll
+    for (int k = 0; k < kMaxPagesPerSplit / 256; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      ids[k] = i < end - first ? ptab[i] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxPagesPerSplit / 256; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      if (i < end - first) sm.pid[i] = ids[k];
+    }
     __syncthreads();
   }
 
@@ -331,8 +396,8 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     for (int t = 0; t < 8; ++t) acc[qd][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     accoff[qd][0] = accoff[qd][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // fp16 bases of the value-code pairs (4+c, 16+c, 4+c, 16+c), both halves
-  const half8 boff = half8_of(0x44004400u, 0x4C004C00u, 0x44004400u, 0x4C004C00u);
+  // fp16 bases of the value-code pairs (64+c, 16+c, 64+c, 16+c), both halves
+  const half8 boff = half8_of(0x54005400u, 0x4C004C00u, 0x54005400u, 0x4C004C00u);
   const uint32_t perm_sel = (uint32_t)r | (0x0Cu << 8) | ((4u + r) << 16) | (0x0Cu << 24);
   const PairConsts pk;
   const float tau = a.resc_thr;
@@ -479,10 +544,11 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     // ---- values ----
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
+      // slots 4r + d of both pages: d = 0, 1 from x << 4 (bits 4-5, 6-7), d = 2, 3 from x
       const uint32_t x = __builtin_amdgcn_perm(cur[1].vw[t], cur[0].vw[t], perm_sel);
-      const uint32_t m16 = pk.m16, b16 = pk.b16, m4 = pk.m4, b4 = pk.b4;
       const uint32_t l4 = x << 4;
-      const half8 bv = half8_of(((x << 8) & m4) | b4, (l4 & m16) | b16, (l4 & m4) | b4, (x & m16) | b16);
+      const half8 bv = half8_of((l4 & pk.m64) | pk.b64, (l4 & pk.m16) | pk.b16, (x & pk.m64) | pk.b64,
+                                (x & pk.m16) | pk.b16);
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) acc[qd][t] = mfma16(A[qd][t >> 2], bv, acc[qd][t]);
     }
@@ -542,21 +608,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
 }
 
 // ---------------------------------------------------------------------------
-// reduce: one 128-thread block per (sequence, query head).
+// reduce: one 256-thread block per (sequence, KV head) for its G query heads:
+// log-sum-exp merge of the partial records, then acc_rot R_V^T =
+// ((acc_rot P) H) U_V^T with U_V staged once in LDS, bf16 out.
 // ---------------------------------------------------------------------------
-constexpr int kReduceThreads = 128;
-
-__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
-  __shared__ float e_s[1024];         // per-split weight exp2(m_s - M)
-  __shared__ float y[kHeadDim];
-  __shared__ float red[2][2];
-  const int bq = blockIdx.x, b = bq / a.Hq, hq = bq % a.Hq, h = hq / a.G;
-  const int c = threadIdx.x, lane = c & 63, wave = c >> 6;
+__global__ __launch_bounds__(kSideThreads) void reduce_kernel(DecodeArgs a) {
+  constexpr int kURow = kHeadDim / 8 + 1;                 // uint4 per padded U row (272 B)
+  __shared__ uint4 Us[kHeadDim * kURow];                  // U_V[h] rows, padded against bank conflicts
+  __shared__ float e_s[kMaxGqa][kMaxItems];               // per-item weight exp2(m_u - M)
+  __shared__ float y[kMaxGqa][kHeadDim];
+  __shared__ float lsum_s[kMaxGqa];
+  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H, G = a.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = tid & 127, hs = tid >> 7;
   const int L = a.seq_lens[b];
-  uint16_t* out = a.out + (size_t)bq * kHeadDim;
+  uint16_t* out = a.out + ((size_t)b * a.Hq + h * G) * kHeadDim;
   if (L == 0) {
-    out[c] = 0;
+    for (int e = tid; e < G * kHeadDim; e += kSideThreads) out[e] = 0;
     return;
+  }
+  {
+    const uint4* U = reinterpret_cast<const uint4*>(a.u_v + (size_t)h * kHeadDim * kHeadDim);
+    constexpr int kPer = kHeadDim * kHeadDim / 8 / kSideThreads;
+    uint4 tmp[kPer];   // all loads in flight before the LDS stores
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) tmp[k] = U[tid + k * kSideThreads];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kSideThreads;
+      Us[(i >> 4) * kURow + (i & 15)] = tmp[k];
+    }
   }
   const int n_b = (bf16_token_count(L, a.sink, a.recent) + kBf16Chunk - 1) / kBf16Chunk;
   const int i_hi = int2_end(L, a.sink, a.recent);
@@ -564,71 +644,113 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
   const int n_i = (int2_pages + a.P - 1) / a.P;
   const int n_used = n_b + n_i;   // used items: [0, n_b) BF16, then [n_bsplit, n_bsplit + n_i) INT2
   auto item = [&](int u) { return u < n_b ? u : a.n_bsplit + (u - n_b); };
-  const float* base = a.part + (size_t)bq * a.n_total * kPartFloats;
+  auto part = [&](int g) { return a.part + ((size_t)b * a.Hq + h * G + g) * a.n_total * kPartFloats; };
 
-  // M = max over the used items' running maxima
-  float mx = -INFINITY;
-  for (int u = c; u < n_used; u += kReduceThreads) mx = fmaxf(mx, base[(size_t)item(u) * kPartFloats]);
-  mx = wave_max_xor(mx, 1, 32);
-  if (lane == 0) red[0][wave] = mx;
-  __syncthreads();
-  const float M = fmaxf(red[0][0], red[0][1]);
-  float ls = 0.f;
-  for (int u = c; u < n_used; u += kReduceThreads) {
-    const float* r = base + (size_t)item(u) * kPartFloats;
-    const float e = r[0] == -INFINITY ? 0.f : exp2f(r[0] - M);
-    e_s[u & 1023] = e;
-    ls += e * r[1];
-  }
-  ls = wave_sum_xor(ls, 1, 32);
-  if (lane == 0) red[1][wave] = ls;
-  __syncthreads();
-  const float lsum = red[1][0] + red[1][1];
-
-  // channel c: plain (BF16 items) and rotated (INT2 items) accumulators
-  float plain = 0.f, rot = 0.f;
-  for (int u = 0; u < n_b; ++u) plain = fmaf(e_s[u], base[(size_t)u * kPartFloats + 4 + c], plain);
-  {
-    const float* pr = base + (size_t)a.n_bsplit * kPartFloats + 4 + c;
-    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-    int u = 0;
-    for (; u + 4 <= n_i; u += 4) {
-      r0 = fmaf(e_s[n_b + u], pr[(size_t)u * kPartFloats], r0);
-      r1 = fmaf(e_s[n_b + u + 1], pr[(size_t)(u + 1) * kPartFloats], r1);
-      r2 = fmaf(e_s[n_b + u + 2], pr[(size_t)(u + 2) * kPartFloats], r2);
-      r3 = fmaf(e_s[n_b + u + 3], pr[(size_t)(u + 3) * kPartFloats], r3);
+  // per head: M = max of the items' running maxima, item weights, l total (one wave per head)
+  for (int g = wave; g < G; g += 4) {
+    const float* base = part(g);
+    float mx = -INFINITY;
+    for (int u0 = 0; u0 < n_used; u0 += 256) {   // (m, l) of up to 4 items per lane in flight at once
+      float2 ml[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int u = u0 + lane + 64 * k;
+        ml[k] = u < n_used ? *reinterpret_cast<const float2*>(base + (size_t)item(u) * kPartFloats)
+                           : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        mx = fmaxf(mx, ml[k].x);
+        const int u = u0 + lane + 64 * k;
+        if (u < n_used) e_s[g][u] = ml[k].x;   // the item's max for now
+      }
     }
-    for (; u < n_i; ++u) r0 = fmaf(e_s[n_b + u], pr[(size_t)u * kPartFloats], r0);
-    rot = (r0 + r1) + (r2 + r3);
+    mx = wave_max_xor(mx, 1, 32);
+    float ls = 0.f;
+    for (int u = lane; u < n_used; u += 64) {
+      const float m_u = e_s[g][u];
+      const float e = m_u == -INFINITY ? 0.f : exp2f(m_u - mx);
+      e_s[g][u] = e;
+      ls += e * base[(size_t)item(u) * kPartFloats + 1];
+    }
+    ls = wave_sum_xor(ls, 1, 32);
+    if (lane == 0) lsum_s[g] = ls;
   }
+  __syncthreads();
 
-  // acc_rot P: z-space channel br(c) takes post-rotation channel c; then H
-  y[bitrev7(c)] = rot;
+  // channel c of heads hs, hs + 2, ... (hs is wave-uniform): plain (BF16 items) and rotated
+  // (INT2 items) sums; the loads of 16 items of every head are in flight together
+  float plain[kMaxGqa / 2], rot[kMaxGqa / 2];
+#pragma unroll
+  for (int k = 0; k < kMaxGqa / 2; ++k) plain[k] = rot[k] = 0.f;
+  for (int u0 = 0; u0 < n_used; u0 += 16) {
+    float v[kMaxGqa / 2][16];
+#pragma unroll
+    for (int k = 0; k < kMaxGqa / 2; ++k) {
+      const int g = hs + 2 * k;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        const int u = u0 + d;
+        v[k][d] = (g < G && u < n_used) ? part(g)[(size_t)item(u) * kPartFloats + 4 + c] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxGqa / 2; ++k) {
+      const int g = hs + 2 * k;
+      if (g >= G) continue;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        const int u = u0 + d;
+        if (u < n_used) {
+          const float w = e_s[g][u] * v[k][d];
+          if (u < n_b) plain[k] += w;
+          else rot[k] += w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxGqa / 2; ++k)   // acc_rot P: z-space channel br(c) takes post-rotation channel c
+    if (hs + 2 * k < G) y[hs + 2 * k][bitrev7(c)] = rot[k];
   __syncthreads();
   for (int s = 1; s < kHeadDim; s <<= 1) {
-    if (c < 64) {
-      const int lo = ((c & ~(s - 1)) << 1) | (c & (s - 1)), hi = lo | s;
-      const float x0 = y[lo], x1 = y[hi];
-      y[lo] = x0 + x1;
-      y[hi] = x0 - x1;
+    for (int t = tid; t < G * 64; t += kSideThreads) {
+      const int g = t >> 6, cc = t & 63;
+      const int lo = ((cc & ~(s - 1)) << 1) | (cc & (s - 1)), hi = lo | s;
+      const float x0 = y[g][lo], x1 = y[g][hi];
+      y[g][lo] = x0 + x1;
+      y[g][hi] = x0 - x1;
     }
     __syncthreads();
   }
-  // (y U_V^T)_c = sum_j y_j U_V[c][j]
-  const uint16_t* urow = a.u_v + ((size_t)h * kHeadDim + c) * kHeadDim;
-  float o0 = 0.f, o1 = 0.f;
-#pragma unroll 4
-  for (int jb = 0; jb < kHeadDim; jb += 8) {
-    const uint4 u8 = *reinterpret_cast<const uint4*>(urow + jb);
+  // (y U_V^T)_c = sum_k y_k U_V[c][k], row c of U_V shared by this thread's heads
+  float o[kMaxGqa / 2];
+#pragma unroll
+  for (int k = 0; k < kMaxGqa / 2; ++k) o[k] = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < kHeadDim / 8; ++kb) {
+    const uint4 u8 = Us[c * kURow + kb];
     const uint32_t uu[4] = {u8.x, u8.y, u8.z, u8.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      o0 = fmaf(y[jb + 2 * k], bf16_bits_to_f32(uu[k] & 0xFFFFu), o0);
-      o1 = fmaf(y[jb + 2 * k + 1], bf16_bits_to_f32(uu[k] >> 16), o1);
+    for (int k = 0; k < kMaxGqa / 2; ++k) {
+      const int g = hs + 2 * k;
+      if (g < G) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          o[k] = fmaf(y[g][8 * kb + 2 * q], bf16_bits_to_f32(uu[q] & 0xFFFFu), o[k]);
+          o[k] = fmaf(y[g][8 * kb + 2 * q + 1], bf16_bits_to_f32(uu[q] >> 16), o[k]);
+        }
+      }
     }
   }
-  const float res = (plain + (o0 + o1) * 0.08838834764831845f) / lsum;
-  out[c] = (uint16_t)f32_to_bf16_bits(res);
+#pragma unroll
+  for (int k = 0; k < kMaxGqa / 2; ++k) {
+    const int g = hs + 2 * k;
+    if (g < G) {
+      const float res = (plain[k] + o[k] * 0.08838834764831845f) / lsum_s[g];
+      out[(size_t)g * kHeadDim + c] = (uint16_t)f32_to_bf16_bits(res);
+    }
+  }
 }
 
 template <int G>
@@ -641,16 +763,26 @@ void launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
 DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t recent,
                             int32_t batch, int32_t max_pages) {
   DecodePlan p{};
-  const int int2_pages = max(0, max_pages - sink / kPage);
-  const long long page_heads = (long long)int2_pages * batch * num_kv_heads;
-  long long per = (page_heads + 2047) / 2048;   // aim for ~2048 INT2 items
+  const long long int2_pages = max(0, max_pages - sink / kPage);
+  const long long bh = (long long)batch * num_kv_heads;
   p.n_bsplit = (sink + recent + kBf16Chunk - 1) / kBf16Chunk;
-  // keep the items of one sequence within what the reduce merges
-  const long long min_per = (int2_pages + (kMaxItems - p.n_bsplit) - 1) / (kMaxItems - p.n_bsplit);
-  per = per < min_per ? min_per : per;
-  per = per < 32 ? 32 : per > kMaxPagesPerSplit ? kMaxPagesPerSplit : per;
-  p.pages_per_split = (int)((per + 3) / 4 * 4);
-  p.n_split = int2_pages > 0 ? (int2_pages + p.pages_per_split - 1) / p.pages_per_split : 0;
+  // Items per (sequence, KV head): m ranges of ~320 pages (measured on MI355X at
+  // 28 x 100K tokens: 192-512 pages per item are within 2% of each other;
+  // 128 is 4% and 692 6% slower), but at least enough items to give every
+  // resident block slot work (4 per CU for G <= 4, 2 above, 256 CUs).
+  const long long slots = (num_q_heads / num_kv_heads <= 4 ? 4 : 2) * 256;
+  const long long max_m = kMaxItems - p.n_bsplit;
+  long long best_m = 0;
+  if (int2_pages > 0 && bh > 0) {
+    best_m = max((int2_pages + 319) / 320, (slots + bh - 1) / bh);
+    best_m = min(best_m, min(max_m, (int2_pages + 15) / 16));   // at least 16 pages per item
+    best_m = max(best_m, (int2_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit);
+  }
+  long long per = best_m > 0 ? (int2_pages + best_m - 1) / best_m : kPage;
+  per = (per + 3) / 4 * 4;   // whole rounds of the 4 waves' page pairs
+  if (per > kMaxPagesPerSplit) per = kMaxPagesPerSplit;
+  p.pages_per_split = (int)per;
+  p.n_split = int2_pages > 0 ? (int)((int2_pages + per - 1) / per) : 0;
   p.n_total = p.n_split + p.n_bsplit;
   const size_t qrot = (size_t)batch * num_q_heads * kQrotBytes;
   p.qrot_off = 0;
@@ -694,7 +826,7 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.n_split = L.plan.n_split;
   a.n_bsplit = L.plan.n_bsplit;
   a.n_total = L.plan.n_total;
-  hipLaunchKernelGGL(rotate_q_kernel, dim3(L.batch * L.num_q_heads), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(rotate_q_kernel, dim3(L.batch * L.num_kv_heads), dim3(kSideThreads), 0, stream, a);
   switch (a.G) {
     case 1: launch_split<1>(a, L.batch, stream); break;
     case 2: launch_split<2>(a, L.batch, stream); break;
@@ -706,7 +838,7 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     case 8: launch_split<8>(a, L.batch, stream); break;
     default: return 1;
   }
-  hipLaunchKernelGGL(reduce_kernel, dim3(L.batch * L.num_q_heads), dim3(kReduceThreads), 0, stream, a);
+  hipLaunchKernelGGL(reduce_kernel, dim3(L.batch * L.num_kv_heads), dim3(kSideThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
