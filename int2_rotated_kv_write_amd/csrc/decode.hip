@@ -309,6 +309,15 @@ __device__ __forceinline__ half8 half8_of(uint32_t a, uint32_t b, uint32_t c, ui
   return __builtin_bit_cast(half8, make_uint4(a, b, c, d));
 }
 __device__ __forceinline__ half8 half8_of(uint4 u) { return __builtin_bit_cast(half8, u); }
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4, LDS base in M0).  Issued as inline assembly so the
+// compiler does not see an LDS write it cannot disambiguate from the ring
+// slots being read (it would wait for every outstanding load before each LDS
+// read, defeating the prefetch); the loop's own s_waitcnt vmcnt orders it.
+__device__ __forceinline__ void dma_to_lds16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+}
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -378,11 +387,16 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        const uint4 u = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][limb][r][0]);
-        qb[qd][g][kh] = half8_of(ok && g == gp ? u : make_uint4(0, 0, 0, 0));
+        uint4 u = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][limb][r][0]);
+        u = ok && g == gp ? u : make_uint4(0, 0, 0, 0);
+        // consume the load here: its wait must not land inside the page loop, where it
+        // would also wait for every page DMA in flight
+        asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+        qb[qd][g][kh] = half8_of(u);
       }
     cinit[qd] = ok ? rec->negc[gp][limb] : 0.f;
     qs[qd] = ok ? rec->qsum[gp] : 0.f;
+    asm volatile("" : "+v"(cinit[qd]), "+v"(qs[qd]));
   }
 
   float m[NQ], lsum[NQ], zs[NQ][2];
@@ -414,9 +428,9 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   auto issue = [&](int j) {   // 2 DMA instructions per page
     const int pid = __builtin_amdgcn_readfirstlane(sm.pid[page_of(j) - first]);
     const uint8_t* blk = lane_src + (size_t)pid * page_stride;
-    uint8_t* dst = &sm.ring[wave][j % kRing][0];
-    __builtin_amdgcn_global_load_lds(blk, dst, 16, 0, 0);
-    if (lane < 16) __builtin_amdgcn_global_load_lds(blk + 1024, dst + 1024, 16, 0, 0);
+    const uint32_t dst = (uint32_t)(uintptr_t)&sm.ring[wave][j % kRing][0];
+    dma_to_lds16(blk, dst);
+    if (lane < 16) dma_to_lds16(blk + 1024, dst + 1024);
   };
   for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(j);
   // this lane's byte offsets inside a page block
@@ -459,13 +473,13 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     }
 
     // ---- logits: lane (r, hh, a4) ends with token 4r + a4 of head 4 qd + hh ----
-    float lg[NQ][2];
+    // all MFMA chains of both pages first, so they overlap each other's latency
+    f32x4 dq[2][NQ];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const PageRegs& P = cur[k];
       uint32_t e0[8], e1[8];
-      unpack16(P.kc[0], e0, pk);
-      unpack16(P.kc[1], e1, pk);
+      unpack16(cur[k].kc[0], e0, pk);
+      unpack16(cur[k].kc[1], e1, pk);
       const half8 a00 = half8_of(e0[0], e0[1], e0[2], e0[3]), a01 = half8_of(e0[4], e0[5], e0[6], e0[7]);
       const half8 a10 = half8_of(e1[0], e1[1], e1[2], e1[3]), a11 = half8_of(e1[4], e1[5], e1[6], e1[7]);
 #pragma unroll
@@ -475,6 +489,16 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
         d = mfma16(a01, qb[qd][0][1], d);
         d = mfma16(a10, qb[qd][1][0], d);
         d = mfma16(a11, qb[qd][1][1], d);
+        dq[k][qd] = d;
+      }
+    }
+    float lg[NQ][2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const PageRegs& P = cur[k];
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        const f32x4 d = dq[k][qd];
         // limbs: partner lane ^ 2 holds the other limb of the same group
         const float u0 = d[0] + dpp<kQuadXor2>(d[0]), u1 = d[1] + dpp<kQuadXor2>(d[1]);
         const float u2 = d[2] + dpp<kQuadXor2>(d[2]), u3 = d[3] + dpp<kQuadXor2>(d[3]);
