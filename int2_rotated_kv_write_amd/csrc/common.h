@@ -71,14 +71,15 @@ __host__ __device__ constexpr int pair_of_k(int k) {  // inverse of pair_k (k in
   return k == 2 ? 0 : k == 3 ? 1 : k == 4 ? 2 : k == 5 ? 3 : k == 6 ? 4 : k == 7 ? 5 : k == 0 ? 6 : 7;
 }
 
-// Masks and bases live in VGPRs so that (x & m) | b is one v_and_or_b32
-// (a VOP3 instruction cannot take two literal constants on gfx9).
+// Masks in SGPRs, bases in VGPRs, so that (x & m) | b is one v_and_or_b32
+// (on gfx9 a VOP3 instruction takes no literal and at most one SGPR).
 struct PairConsts {
   uint32_t m64, b64, m16, b16, m4, b4;
   __device__ __forceinline__ PairConsts()
       : m64(0x00300030u), b64(0x54005400u), m16(0x00C000C0u), b16(0x4C004C00u), m4(0x03000300u),
         b4(0x44004400u) {
-    asm volatile("" : "+v"(m64), "+v"(b64), "+v"(m16), "+v"(b16), "+v"(m4), "+v"(b4));
+    asm volatile("" : "+s"(m64), "+s"(m16), "+s"(m4));
+    asm volatile("" : "+v"(b64), "+v"(b16), "+v"(b4));
   }
 };
 

@@ -175,13 +175,12 @@ __global__ __launch_bounds__(kSideThreads) void rotate_q_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // split: block (item, KV head, sequence), 4 waves.
 // ---------------------------------------------------------------------------
-constexpr int kMaxPagesPerSplit = 1024;
-constexpr int kRing = 6;   // pages in flight per wave (LDS ring, even: pages go in pairs)
+constexpr int kMaxPagesPerSplit = 512;
+constexpr int kRing = 8;   // pages in flight per wave (LDS ring, even: pages go in pairs)
 // while pages j, j+1 are read, the DMAs of pages j+2 .. j+kRing-1 (two instructions each) may be in flight
-static_assert(2 * (kRing - 2) == 8, "s_waitcnt vmcnt immediate below assumes kRing == 6");
+static_assert(2 * (kRing - 2) == 12, "s_waitcnt vmcnt immediate below assumes kRing == 8");
 
 struct __attribute__((aligned(16))) SplitSmem {
-  int32_t pid[kMaxPagesPerSplit];    // physical page ids of the item's page range
   union {
     uint8_t ring[4][kRing][kBlockBytes];   // INT2 items: per-wave ring of page blocks
     struct {
@@ -310,13 +309,14 @@ __device__ __forceinline__ half8 half8_of(uint32_t a, uint32_t b, uint32_t c, ui
 }
 __device__ __forceinline__ half8 half8_of(uint4 u) { return __builtin_bit_cast(half8, u); }
 
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
-// (global_load_lds_dwordx4, LDS base in M0).  Issued as inline assembly so the
+// 16 bytes per lane from global memory (wave-uniform base + per-lane offset)
+// straight into LDS at lds_base + 16 * lane (global_load_lds_dwordx4, LDS base in M0).  Issued as inline assembly so the
 // compiler does not see an LDS write it cannot disambiguate from the ring
 // slots being read (it would wait for every outstanding load before each LDS
 // read, defeating the prefetch); the loop's own s_waitcnt vmcnt orders it.
-__device__ __forceinline__ void dma_to_lds16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base) : "memory", "m0");
+__device__ __forceinline__ void dma_to_lds16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
 }
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -359,22 +359,6 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   const int n = lane & 15, r = lane >> 4;
   const int hh = n >> 2, a4 = n & 3, gp = a4 & 1, limb = a4 >> 1;
 
-  {
-    const int32_t* ptab = a.page_table + (size_t)b * a.max_pages + first;
-    int32_t ids[kMaxPagesPerSplit / 256];   // all loads in flight before the LDS stores
-#pragma unroll
-    for (int k = 0; k < kMaxPagesPerSplit / 256; ++k) {
-      const int i = threadIdx.x + 256 * k;
-      ids[k] = i < end - first ? ptab[i] : 0;
-    }
-#pragma unroll
-    for (int k = 0; k < kMaxPagesPerSplit / 256; ++k) {
-      const int i = threadIdx.x + 256 * k;
-      if (i < end - first) sm.pid[i] = ids[k];
-    }
-    __syncthreads();
-  }
-
   // q' fragments of column n: head 4 qd + hh, group gp, limb (zero beyond G)
   half8 qb[NQ][2][2];
   float cinit[NQ], qs[NQ];
@@ -411,9 +395,9 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     accoff[qd][0] = accoff[qd][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // fp16 bases of the value-code pairs (64+c, 16+c, 64+c, 16+c), both halves
-  const half8 boff = half8_of(0x54005400u, 0x4C004C00u, 0x54005400u, 0x4C004C00u);
   const uint32_t perm_sel = (uint32_t)r | (0x0Cu << 8) | ((4u + r) << 16) | (0x0Cu << 24);
   const PairConsts pk;
+  const half8 boff = half8_of(pk.b64, pk.b16, pk.b64, pk.b16);
   const float tau = a.resc_thr;
 
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
@@ -424,13 +408,32 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   int n_w = 0;
   if (base0 < end) n_w = 2 * ((end - base0 + 7) / 8) - ((end - base0 - 1) % 8 == 0 ? 1 : 0);
   auto page_of = [&](int j) { return base0 + 8 * (j >> 1) + (j & 1); };
-  const uint8_t* lane_src = a.pages + head_off + 16 * lane;
+  const uint32_t lane_off = (uint32_t)(head_off + 16 * lane);   // byte offset of this lane in a page row
+  // physical page ids of the wave's pages, held in VGPRs: lane l keeps page j = l + 64 k
+  // (loaded and consumed here, so no load is pending inside the page loop)
+  constexpr int kIdRegs = kMaxPagesPerSplit / 4 / 64;
+  int32_t pid_reg[kIdRegs];
+  {
+    const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) {
+      const int j = lane + 64 * k;
+      pid_reg[k] = j < n_w ? ptab[page_of(j)] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(pid_reg[k]));
+  }
+  auto pid_of = [&](int j) {   // wave-uniform j
+    int v = pid_reg[0];
+#pragma unroll
+    for (int q = 1; q < kIdRegs; ++q) v = (j >> 6) == q ? pid_reg[q] : v;
+    return __builtin_amdgcn_readlane(v, j & 63);
+  };
   auto issue = [&](int j) {   // 2 DMA instructions per page
-    const int pid = __builtin_amdgcn_readfirstlane(sm.pid[page_of(j) - first]);
-    const uint8_t* blk = lane_src + (size_t)pid * page_stride;
+    const uint8_t* row = a.pages + (size_t)pid_of(j) * page_stride;   // wave-uniform
     const uint32_t dst = (uint32_t)(uintptr_t)&sm.ring[wave][j % kRing][0];
-    dma_to_lds16(blk, dst);
-    if (lane < 16) dma_to_lds16(blk + 1024, dst + 1024);
+    dma_to_lds16(row, lane_off, dst);
+    if (lane < 16) dma_to_lds16(row, lane_off + 1024, dst + 1024);
   };
   for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(j);
   // this lane's byte offsets inside a page block
@@ -447,7 +450,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     if (j + kRing - 2 < n_w) issue(j + kRing - 2);
     if (j + kRing - 1 < n_w) issue(j + kRing - 1);
     if (j + kRing - 1 < n_w) {
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // pages j, j+1 landed: 2*(kRing-2) still in flight
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");   // pages j, j+1 landed: 2*(kRing-2) still in flight
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
