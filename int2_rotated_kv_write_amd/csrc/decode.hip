@@ -217,35 +217,53 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, int b
   }
 }
 
-// BF16 sink + recent tokens, 64 per item, 16 per wave; plain (unrotated) q.
+// BF16 sink + recent tokens, kBf16Chunk per item; the block's waves take 16-token
+// groups round-robin and keep an online softmax across their groups; plain
+// (unrotated) q.
 template <int G>
 __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, SplitSmem& sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = lane >> 2, q = lane & 3;
   const int nsink = min(a.sink, L);
   const int r_lo = L > a.sink ? max(a.sink, L - a.recent) : L;
   const int nb = bf16_token_count(L, a.sink, a.recent);
-  const int jbase = chunk * kBf16Chunk + 16 * wave;
   const size_t head_row = (size_t)b * a.H + h;
 
+  const int ring0 = r_lo % a.recent;   // ring row of the oldest recent token; rows wrap at most once
   auto row_offset = [&](int jj) -> size_t {   // element offset of BF16 token jj's row
     if (jj < nsink) return (head_row * a.sink + jj) * kHeadDim;
-    const int p = r_lo + (jj - nsink);
-    return (head_row * a.recent + (p % a.recent)) * kHeadDim;
+    int row = ring0 + (jj - nsink);
+    row = row >= a.recent ? row - a.recent : row;
+    return (head_row * a.recent + row) * kHeadDim;
   };
   auto kbuf = [&](int jj) { return jj < nsink ? a.k_sink : a.k_ring; };
   auto vbuf = [&](int jj) { return jj < nsink ? a.v_sink : a.v_ring; };
 
-  const int j = jbase + t;
-  const bool valid = j < nb;
-  float lg[G];
-  {
+  float m[G], lsum[G], acc[G][2];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    lsum[hh] = 0.f;
+    acc[hh][0] = acc[hh][1] = 0.f;
+  }
+  for (int round = 0; round < kBf16Chunk / 64; ++round) {
+    const int jbase = chunk * kBf16Chunk + 16 * (4 * round + wave);
+    if (jbase >= nb) break;   // wave-uniform
+    const int j = jbase + t;
+    const bool valid = j < nb;
     uint4 kd[4] = {};
     if (valid) {
       const uint16_t* krow = kbuf(j) + row_offset(j) + 32 * q;
 #pragma unroll
       for (int x = 0; x < 4; ++x) kd[x] = reinterpret_cast<const uint4*>(krow)[x];
     }
+    uint32_t vv[16];   // all 16 value rows of the group in flight together
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+      const int jj = jbase + tt;
+      vv[tt] = jj < nb ? *reinterpret_cast<const uint32_t*>(vbuf(jj) + row_offset(jj) + 2 * lane) : 0u;
+    }
+    float lg[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const uint16_t* qv = a.q + ((size_t)b * a.Hq + h * G + hh) * kHeadDim + 32 * q;
@@ -262,29 +280,28 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
       d += __shfl_xor(d, 2);
       lg[hh] = valid ? d * a.sl2e : -INFINITY;
     }
-  }
-  float m[G], lsum[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m[hh] = wave_max_xor(lg[hh], 4, 32);
-    const float p = (valid && m[hh] != -INFINITY) ? exp2f(lg[hh] - m[hh]) : 0.f;
-    lsum[hh] = wave_sum_xor(p, 4, 32);
-    if (q == 0) sm.p[wave][hh][t] = p;
-  }
-  wave_lds_sync();
-  float acc[G][2];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) acc[hh][0] = acc[hh][1] = 0.f;
-  for (int tt = 0; tt < 16; ++tt) {
-    const int jj = jbase + tt;
-    if (jj >= nb) break;   // wave-uniform
-    const uint32_t vv = *reinterpret_cast<const uint32_t*>(vbuf(jj) + row_offset(jj) + 2 * lane);
-    const float v0 = bf16_bits_to_f32(vv & 0xFFFFu), v1 = bf16_bits_to_f32(vv >> 16);
+    wave_lds_sync();   // the previous group's weights have been read
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float p = sm.p[wave][hh][tt];
-      acc[hh][0] = fmaf(p, v0, acc[hh][0]);
-      acc[hh][1] = fmaf(p, v1, acc[hh][1]);
+      const float m_new = fmaxf(m[hh], wave_max_xor(lg[hh], 4, 32));   // finite: the group has a token
+      const float al = exp2f(m[hh] - m_new);
+      const float p = valid ? exp2f(lg[hh] - m_new) : 0.f;
+      lsum[hh] = lsum[hh] * al + wave_sum_xor(p, 4, 32);
+      acc[hh][0] *= al;
+      acc[hh][1] *= al;
+      m[hh] = m_new;
+      if (q == 0) sm.p[wave][hh][t] = p;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+      const float v0 = bf16_bits_to_f32(vv[tt] & 0xFFFFu), v1 = bf16_bits_to_f32(vv[tt] >> 16);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float p = sm.p[wave][hh][tt];   // 0 beyond the last token
+        acc[hh][0] = fmaf(p, v0, acc[hh][0]);
+        acc[hh][1] = fmaf(p, v1, acc[hh][1]);
+      }
     }
   }
   if (lane == 0) {

@@ -27,7 +27,7 @@ struct DecodePlan {
 
 constexpr int kQrotBytes = 576;      // rotated-query record per (sequence, query head)
 constexpr int kPartFloats = 132;     // m, l, 2 pad, acc[128]
-constexpr int kBf16Chunk = 64;       // BF16 tokens per split item
+constexpr int kBf16Chunk = 320;      // BF16 tokens per split item (multiple of 64)
 constexpr int kMaxItems = 1024;      // partial records per (sequence, query head) the reduce can merge
 
 DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t recent,

@@ -21,6 +21,7 @@ namespace oscar {
 namespace {
 
 constexpr int kTilesPerWave = 8;    // 4 waves x 8 tiles = 512 tokens per block
+constexpr int kUtRow = kHeadDim + 8;   // U^T row stride in LDS (272 B): conflict-free fragment reads
 
 struct KvWriteArgs {
   const uint16_t* x[2];
@@ -38,7 +39,7 @@ struct KvWriteArgs {
 };
 
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ut[kHeadDim * kHeadDim];   // U^T, 32 KB
+  __shared__ __attribute__((aligned(16))) uint16_t ut[kHeadDim * kUtRow];      // U^T, rows padded
   __shared__ __attribute__((aligned(16))) uint8_t vbytes[4][kHeadDim][16];    // V transposition
 
   const int kind = a.kind_of_z[blockIdx.z];
@@ -48,16 +49,26 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   const int n = lane & 15;   // token within the tile (MFMA N index)
   const int q = lane >> 4;   // channel quarter: channels 16mt + 4q + r
 
-  // ---- stage U^T: ut[j][i] = U[i][j] ----
+  // ---- stage U^T: ut[j][i] = U[i][j]; consecutive threads take consecutive rows i,
+  // so each LDS store instruction writes consecutive halfwords ----
   const uint16_t* U = a.u[kind] + (size_t)h * kHeadDim * kHeadDim;
-  for (int e = tid; e < kHeadDim * kHeadDim / 8; e += 256) {
-    const uint4 v = reinterpret_cast<const uint4*>(U)[e];
-    const int i = e >> 4, j0 = (e & 15) * 8;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  {
+    constexpr int kPer = kHeadDim * kHeadDim / 8 / 256;
+    uint4 v[kPer];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ut[(j0 + 2 * k) * kHeadDim + i] = (uint16_t)(w[k] & 0xFFFFu);
-      ut[(j0 + 2 * k + 1) * kHeadDim + i] = (uint16_t)(w[k] >> 16);
+    for (int k = 0; k < kPer; ++k) {
+      const int e = tid + 256 * k, i = e & (kHeadDim - 1), jb = e >> 7;
+      v[k] = reinterpret_cast<const uint4*>(U + i * kHeadDim)[jb];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = tid + 256 * k, i = e & (kHeadDim - 1), j0 = (e >> 7) * 8;
+      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        ut[(j0 + 2 * q2) * kUtRow + i] = (uint16_t)(w[q2] & 0xFFFFu);
+        ut[(j0 + 2 * q2 + 1) * kUtRow + i] = (uint16_t)(w[q2] >> 16);
+      }
     }
   }
   __syncthreads();
@@ -69,7 +80,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      afrag[mt][ks] = *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kHeadDim + 32 * ks + 8 * q]);
+      afrag[mt][ks] = *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kUtRow + 32 * ks + 8 * q]);
 
   const float clip = a.clip[kind];
   const uint16_t* X = a.x[kind];
@@ -134,15 +145,28 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
         v[i | s] = x0 - x1;
       }
     }
-    // cross-lane bits: channel bit 2 = lane bit 4, channel bit 3 = lane bit 5
+    // cross-lane bits: channel bit 2 = lane bit 4, channel bit 3 = lane bit 5.  Registers
+    // x = v[i], y = v[i ^ 8] go through a permlane swap, which leaves in each lane the
+    // (bit-clear, bit-set) partner values of one of them; sum and difference are the
+    // butterfly outputs, and a second swap of (sum, difference) puts every result back
+    // in the lane and register it came from.
 #pragma unroll
-    for (int m = 16; m <= 32; m <<= 1) {
-      const bool upper = (lane & m) != 0;
+    for (int i = 0; i < 32; ++i) {
+      if (i & 8) continue;
+      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
+      const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
+      r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
+      v[i] = __uint_as_float(r[0]);
+      v[i | 8] = __uint_as_float(r[1]);
+    }
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float o = __shfl_xor(v[i], m);
-        v[i] = upper ? (o - v[i]) : (v[i] + o);
-      }
+    for (int i = 0; i < 32; ++i) {
+      if (i & 8) continue;
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
+      const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
+      r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
+      v[i] = __uint_as_float(r[0]);
+      v[i | 8] = __uint_as_float(r[1]);
     }
 
     // ---- scale, clip, group min/max ----
@@ -166,18 +190,18 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     float sf[2], zf[2], inv[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      sbits[g] = f32_to_f16_bits((mx[g] - mn[g]) / 3.0f);
+      sbits[g] = f32_to_f16_bits((mx[g] - mn[g]) * (1.0f / 3.0f));
       zbits[g] = f32_to_f16_bits(mn[g]);
       sf[g] = f16_bits_to_f32(sbits[g]);
       zf[g] = f16_bits_to_f32(zbits[g]);
-      inv[g] = sf[g] > 0.f ? 1.0f / sf[g] : 0.f;
+      inv[g] = sf[g] > 0.f ? __builtin_amdgcn_rcpf(sf[g]) : 0.f;
+      zf[g] = -zf[g] * inv[g];   // t = w * inv - z * inv
     }
     uint32_t code[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      float tq = (v[i] - zf[i & 1]) * inv[i & 1];
-      tq = fminf(fmaxf(__builtin_rintf(tq), 0.f), 3.f);
-      code[i] = (uint32_t)tq;
+      const float tq = __builtin_amdgcn_fmed3f(fmaf(v[i], inv[i & 1], zf[i & 1]), 0.f, 3.f);
+      code[i] = (uint32_t)__builtin_rintf(tq);
     }
 
     // ---- store INT2 ----
