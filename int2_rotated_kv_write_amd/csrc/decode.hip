@@ -400,8 +400,10 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     asm volatile("" : "+v"(cinit[qd]), "+v"(qs[qd]));
   }
 
+  // zs[g]: per-head correction of group g's channels, sum over tokens of p z_g minus the
+  // fp16 bases the value MFMA adds (base * W_g), accumulated by v_dot2
   float m[NQ], lsum[NQ], zs[NQ][2];
-  f32x4 acc[NQ][8], accoff[NQ][2];
+  f32x4 acc[NQ][8];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
     m[qd] = -INFINITY;
@@ -409,12 +411,12 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     zs[qd][0] = zs[qd][1] = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[qd][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accoff[qd][0] = accoff[qd][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // fp16 bases of the value-code pairs (64+c, 16+c, 64+c, 16+c), both halves
   const uint32_t perm_sel = (uint32_t)r | (0x0Cu << 8) | ((4u + r) << 16) | (0x0Cu << 24);
   const PairConsts pk;
-  const half8 boff = half8_of(pk.b64, pk.b16, pk.b64, pk.b16);
+  // the value B operand's dword a4 carries fp16 base 64 (a4 even) or 16 (odd) on both
+  // halves: this lane's weights (dword a4 of A) pick up -base each
+  const half2v nbase = a4 & 1 ? half2v{(_Float16)-16.f, (_Float16)-16.f} : half2v{(_Float16)-64.f, (_Float16)-64.f};
   const float tau = a.resc_thr;
 
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
@@ -562,8 +564,6 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
         const float ai = __shfl(al, 4 * r);   // accumulator rows of this lane belong to head hh' = r
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[qd][t] *= ai;
-        accoff[qd][0] *= ai;
-        accoff[qd][1] *= ai;
         m[qd] = m_new;
       }
     }
@@ -581,6 +581,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
         const uint32_t zp = __builtin_amdgcn_perm(cur[1].vp[g], cur[0].vp[g], 0x07060302u);
         const uint32_t w = __builtin_bit_cast(uint32_t, pp2 * __builtin_bit_cast(half2v, sp));
         zs[qd][g] = __builtin_amdgcn_fdot2(pp2, __builtin_bit_cast(half2v, zp), zs[qd][g], false);
+        zs[qd][g] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w), nbase, zs[qd][g], false);
         A[qd][g] = half8_of(a4 == 0 ? w : 0u, a4 == 1 ? w : 0u, a4 == 2 ? w : 0u, a4 == 3 ? w : 0u);
       }
     }
@@ -595,11 +596,6 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
                                 (x & pk.m16) | pk.b16);
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) acc[qd][t] = mfma16(A[qd][t >> 2], bv, acc[qd][t]);
-    }
-#pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) {
-      accoff[qd][0] = mfma16(A[qd][0], boff, accoff[qd][0]);
-      accoff[qd][1] = mfma16(A[qd][1], boff, accoff[qd][1]);
     }
   }
 
@@ -619,14 +615,12 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     }
     // accumulator rows of this lane: head 4 qd + r, subsets j = 0..3
     const float z0 = __shfl(Z0, 4 * r), z1 = __shfl(Z1, 4 * r);
-    const float off0 = (accoff[qd][0][0] + accoff[qd][0][1]) + (accoff[qd][0][2] + accoff[qd][0][3]);
-    const float off1 = (accoff[qd][1][0] + accoff[qd][1][1]) + (accoff[qd][1][2] + accoff[qd][1][3]);
     const int row_head = 4 * qd + r;
     if (row_head < G) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const float s = (acc[qd][t][0] + acc[qd][t][1]) + (acc[qd][t][2] + acc[qd][t][3]);
-        sm.acc[wave][row_head][16 * t + n] = s - (t < 4 ? off0 - z0 : off1 - z1);
+        sm.acc[wave][row_head][16 * t + n] = s + (t < 4 ? z0 : z1);
       }
     }
   }
