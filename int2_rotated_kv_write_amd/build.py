@@ -24,6 +24,10 @@ FLAGS = [
     # MFMA accumulators in ordinary VGPRs: the decode loop rescales them with
     # VALU ops, which AGPR accumulators would turn into copies every iteration
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # device code only: no NaN operands, so max/min need no canonicalising moves
+    # (the softmax max reductions become single DPP max instructions); host
+    # code keeps its NaN checks on user arguments
+    "-Xarch_device", "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
 ]
 

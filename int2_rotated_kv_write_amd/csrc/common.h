@@ -125,6 +125,7 @@ __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+constexpr int kQuadRot1 = 0x39;   // quad_perm [1, 2, 3, 0]: lane i of a quad reads lane (i + 1) % 4
 
 __device__ __forceinline__ float swap16(float x, bool is_max) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -372,6 +372,7 @@ template <int G>
 __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int first, int end, int i_hi,
                           SplitSmem& sm) {
   constexpr int NQ = (G + 3) / 4;
+  i_hi = __builtin_amdgcn_readfirstlane(i_hi);   // block-uniform: keeps the tail test a scalar branch
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, r = lane >> 4;
   const int hh = n >> 2, a4 = n & 3, gp = a4 & 1, limb = a4 >> 1;
@@ -418,6 +419,11 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   // halves: this lane's weights (dword a4 of A) pick up -base each
   const half2v nbase = a4 & 1 ? half2v{(_Float16)-16.f, (_Float16)-16.f} : half2v{(_Float16)-64.f, (_Float16)-64.f};
   const float tau = a.resc_thr;
+  // byte selectors placing the weight limbs in the A operand (v_perm: bytes 4-7 = hi, 0-3 = lo,
+  // 0x0C = zero): dword a4 takes the hi limb, dword (a4 + 1) % 4 the lo limb from lane a4 + 1
+  uint32_t wsel[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) wsel[d] = a4 == d ? 0x07060504u : ((a4 + 1) & 3) == d ? 0x03020100u : 0x0C0C0C0Cu;
 
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
   const size_t head_off = (size_t)h * kBlockBytes;
@@ -568,21 +574,34 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
       }
     }
 
-    // ---- weights W_g = fp16(p) * s_g of this lane's token in both pages ----
+    // ---- weights W_g = p s_g of this lane's token in both pages as fp16 hi + lo ----
+    // A single fp16 rounding of p s_g would leave a relative error on the code part of the
+    // token's value but not on its zero-point part p z_g; the codes' common level (about 1.5)
+    // turns that into an error shared by all 64 channels of the group, which the inverse
+    // rotation concentrates in one or two output channels.  With hi + lo the products are
+    // exact to about 2^-22.  Row (hh, a4) of the value MFMA carries the hi limb of token a4
+    // at k-slot a4 and the lo limb of token (a4 + 1) % 4 (from the next lane of the quad)
+    // at that token's k-slot; the four rows of a head are summed at the end.
     half8 A[NQ][2];
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
       const float p0 = fast_exp2(lg[qd][0] - m[qd]), p1 = fast_exp2(lg[qd][1] - m[qd]);
       lsum[qd] += p0 + p1;
-      const half2v pp2 = half2v{(_Float16)p0, (_Float16)p1};
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const uint32_t sp = __builtin_amdgcn_perm(cur[1].vp[g], cur[0].vp[g], 0x05040100u);
-        const uint32_t zp = __builtin_amdgcn_perm(cur[1].vp[g], cur[0].vp[g], 0x07060302u);
-        const uint32_t w = __builtin_bit_cast(uint32_t, pp2 * __builtin_bit_cast(half2v, sp));
-        zs[qd][g] = __builtin_amdgcn_fdot2(pp2, __builtin_bit_cast(half2v, zp), zs[qd][g], false);
-        zs[qd][g] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w), nbase, zs[qd][g], false);
-        A[qd][g] = half8_of(a4 == 0 ? w : 0u, a4 == 1 ? w : 0u, a4 == 2 ? w : 0u, a4 == 3 ? w : 0u);
+        const uint32_t v0 = cur[0].vp[g], v1 = cur[1].vp[g];   // (s_g | z_g << 16) of the token in each page
+        zs[qd][g] = fmaf(p0, f16_bits_to_f32(v0 >> 16), fmaf(p1, f16_bits_to_f32(v1 >> 16), zs[qd][g]));
+        const float ps0 = p0 * f16_bits_to_f32(v0), ps1 = p1 * f16_bits_to_f32(v1);
+        const half2v hi2 = half2v{(_Float16)ps0, (_Float16)ps1};
+        const half2v lo2 = half2v{(_Float16)(ps0 - (float)hi2[0]), (_Float16)(ps1 - (float)hi2[1])};
+        // the fp16 bases the value MFMA adds at this token's k-slot, times both limbs
+        zs[qd][g] = __builtin_amdgcn_fdot2(hi2, nbase, zs[qd][g], false);
+        zs[qd][g] = __builtin_amdgcn_fdot2(lo2, nbase, zs[qd][g], false);
+        const uint32_t wh = __builtin_bit_cast(uint32_t, hi2);
+        const int lo_bits = __builtin_bit_cast(int, lo2);   // every quad lane has a source: old is unused
+        const uint32_t wl = (uint32_t)__builtin_amdgcn_update_dpp(lo_bits, lo_bits, kQuadRot1, 0xF, 0xF, false);
+        A[qd][g] = half8_of(__builtin_amdgcn_perm(wh, wl, wsel[0]), __builtin_amdgcn_perm(wh, wl, wsel[1]),
+                            __builtin_amdgcn_perm(wh, wl, wsel[2]), __builtin_amdgcn_perm(wh, wl, wsel[3]));
       }
     }
 
