@@ -403,11 +403,14 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 
   // zs[g]: per-head correction of group g's channels, sum over tokens of p z_g minus the
   // fp16 bases the value MFMA adds (base * W_g), accumulated by v_dot2
-  float m[NQ], lsum[NQ], zs[NQ][2];
+  // m: running reference maximum of the head's logits; logits are formed relative to it
+  // (each of the two group terms carries hm = -m / 2)
+  float m[NQ], hm[NQ], lsum[NQ], zs[NQ][2];
   f32x4 acc[NQ][8];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
-    m[qd] = -INFINITY;
+    m[qd] = 0.f;     // set by the first pair, which always takes the rescale branch
+    hm[qd] = 0.f;
     lsum[qd] = 0.f;
     zs[qd][0] = zs[qd][1] = 0.f;
 #pragma unroll
@@ -454,13 +457,13 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     for (int q = 1; q < kIdRegs; ++q) v = (j >> 6) == q ? pid_reg[q] : v;
     return __builtin_amdgcn_readlane(v, j & 63);
   };
-  auto issue = [&](int j) {   // 2 DMA instructions per page
+  auto issue = [&](int j, int slot) {   // 2 DMA instructions per page; slot = j % kRing
     const uint8_t* row = a.pages + (size_t)pid_of(j) * page_stride;   // wave-uniform
-    const uint32_t dst = (uint32_t)(uintptr_t)&sm.ring[wave][j % kRing][0];
+    const uint32_t dst = (uint32_t)(uintptr_t)&sm.ring[wave][slot][0];
     dma_to_lds16(row, lane_off, dst);
     if (lane < 16) dma_to_lds16(row, lane_off + 1024, dst + 1024);
   };
-  for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(j);
+  for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(j, j);
   // this lane's byte offsets inside a page block
   const int t0 = 4 * r + 2 * limb;
   const int off_kc = kKCodes + 32 * n + 4 * r;            // token n: code word r of group 0 (+16: group 1)
@@ -468,12 +471,17 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   const int off_vp = kVParams + 8 * (4 * r + a4);         // (s0, z0, s1, z1) of token 4r + a4
   const int off_vw = kVCodes + 4 * n;                     // value code word of channel 16t + n at + 64t
 
-  for (int j = 0; j < n_w; j += 2) {
+  // unrolled over one turn of the ring, so every slot offset is an immediate
+  for (int j0 = 0; j0 < n_w; j0 += kRing)
+#pragma unroll
+  for (int u = 0; u < kRing / 2; ++u) {
+    const int j = j0 + 2 * u;
+    if (j >= n_w) break;   // wave-uniform
     const int pp = page_of(j);
     const bool has1 = j + 1 < n_w;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of the slots being refilled
-    if (j + kRing - 2 < n_w) issue(j + kRing - 2);
-    if (j + kRing - 1 < n_w) issue(j + kRing - 1);
+    if (j + kRing - 2 < n_w) issue(j + kRing - 2, (2 * u + kRing - 2) % kRing);
+    if (j + kRing - 1 < n_w) issue(j + kRing - 1, (2 * u + kRing - 1) % kRing);
     if (j + kRing - 1 < n_w) {
       asm volatile("s_waitcnt vmcnt(12)" ::: "memory");   // pages j, j+1 landed: 2*(kRing-2) still in flight
     } else {
@@ -485,10 +493,9 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
       uint32_t vp[2];   // (s0, z0), (s1, z1) of token 4r + a4
       uint32_t vw[8];   // value code words of channels 16t + n
     } cur[2];
-    const int slot0 = j % kRing, slot1 = has1 ? slot0 + 1 : slot0;   // wave-uniform
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint8_t* blk = &sm.ring[wave][k == 0 ? slot0 : slot1][0];
+      const uint8_t* blk = &sm.ring[wave][2 * u + k][0];   // without page j + 1 its slot holds stale bytes
       cur[k].kc[0] = *reinterpret_cast<const uint32_t*>(blk + off_kc);
       cur[k].kc[1] = *reinterpret_cast<const uint32_t*>(blk + off_kc + 16);
       cur[k].kp[0] = *reinterpret_cast<const uint32_t*>(blk + off_kp);
@@ -499,6 +506,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 #pragma unroll
       for (int t = 0; t < 8; ++t) cur[k].vw[t] = *reinterpret_cast<const uint32_t*>(blk + off_vw + 64 * t);
     }
+    if (!has1) cur[1].vp[0] = cur[1].vp[1] = 0u;   // its weights are 0 * (s, z): keep them finite
 
     // ---- logits: lane (r, hh, a4) ends with token 4r + a4 of head 4 qd + hh ----
     // all MFMA chains of both pages first, so they overlap each other's latency
@@ -532,8 +540,8 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
         const float u2 = d[2] + dpp<kQuadXor2>(d[2]), u3 = d[3] + dpp<kQuadXor2>(d[3]);
         const float y0 = limb ? u2 : u0, y1 = limb ? u3 : u1;
         // scale and zero-point term of group gp (tokens 4r + 2 limb, + 1)
-        const float x0 = fmaf(f16_bits_to_f32(P.kp[0]), y0, f16_bits_to_f32(P.kp[0] >> 16) * qs[qd]);
-        const float x1 = fmaf(f16_bits_to_f32(P.kp[1]), y1, f16_bits_to_f32(P.kp[1] >> 16) * qs[qd]);
+        const float x0 = fmaf(f16_bits_to_f32(P.kp[0]), y0, fmaf(f16_bits_to_f32(P.kp[0] >> 16), qs[qd], hm[qd]));
+        const float x1 = fmaf(f16_bits_to_f32(P.kp[1]), y1, fmaf(f16_bits_to_f32(P.kp[1] >> 16), qs[qd], hm[qd]));
         // groups: partner lane ^ 1 holds the other group of the same tokens
         const float v0 = x0 + dpp<kQuadXor1>(x0), v1 = x1 + dpp<kQuadXor1>(x1);
         lg[qd][k] = gp ? v1 : v0;
@@ -548,29 +556,31 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
       }
     }
 
-    // ---- online softmax per head; rescale only when the max grows by more than tau ----
-    float pmax[NQ];
-    bool need_any = false;
+    // ---- online softmax per head (logits are relative to m); rescale only when the max
+    // grows by more than tau.  A lane test first: the head maxima are reduced only on the
+    // rare pairs that rescale.
+    bool need_any = j == 0;
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) {
-      float pm = fmaxf(lg[qd][0], lg[qd][1]);
-      pm = fmaxf(pm, dpp<kQuadXor1>(pm));
-      pm = fmaxf(pm, dpp<kQuadXor2>(pm));
-      pmax[qd] = rows_max(pm);
-      need_any |= pmax[qd] > m[qd] + tau;
-    }
+    for (int qd = 0; qd < NQ; ++qd) need_any |= fmaxf(lg[qd][0], lg[qd][1]) > tau;
     if (__any(need_any)) {
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        const float m_new = pmax[qd] > m[qd] + tau ? pmax[qd] : m[qd];
-        const float al = fast_exp2(m[qd] - m_new);
+        float pm = fmaxf(lg[qd][0], lg[qd][1]);
+        pm = fmaxf(pm, dpp<kQuadXor1>(pm));
+        pm = fmaxf(pm, dpp<kQuadXor2>(pm));
+        pm = rows_max(pm);   // finite: every pair has a valid token
+        const float dm = j == 0 || pm > tau ? pm : 0.f;
+        const float al = fast_exp2(-dm);
+        m[qd] += dm;
+        hm[qd] = -0.5f * m[qd];
+        lg[qd][0] -= dm;
+        lg[qd][1] -= dm;
         lsum[qd] *= al;
         zs[qd][0] *= al;
         zs[qd][1] *= al;
         const float ai = __shfl(al, 4 * r);   // accumulator rows of this lane belong to head hh' = r
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[qd][t] *= ai;
-        m[qd] = m_new;
       }
     }
 
@@ -585,7 +595,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     half8 A[NQ][2];
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      const float p0 = fast_exp2(lg[qd][0] - m[qd]), p1 = fast_exp2(lg[qd][1] - m[qd]);
+      const float p0 = fast_exp2(lg[qd][0]), p1 = fast_exp2(lg[qd][1]);
       lsum[qd] += p0 + p1;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
