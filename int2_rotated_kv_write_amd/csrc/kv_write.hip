@@ -49,6 +49,27 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   const int n = lane & 15;   // token within the tile (MFMA N index)
   const int q = lane >> 4;   // channel quarter: channels 16mt + 4q + r
 
+  const uint16_t* X = a.x[kind];
+  // per-tile inputs, loaded one tile ahead so their latency overlaps the previous tile's math
+  // (the first tile's before U^T is staged)
+  struct TileIn {
+    uint4 x[4];   // x[t][h][32ks + 8q .. +7]
+    int b, p;
+    bool valid;
+  };
+  auto load_tile = [&](int it, TileIn& in) {
+    const int t = ((blockIdx.x * kTilesPerWave + it) * 4 + wave) * 16 + n;
+    in.valid = t < a.num_tokens;
+    in.b = in.valid ? a.seq_idx[t] : 0;
+    in.p = in.valid ? a.pos[t] : 0;
+    const uint16_t* xrow = X + ((size_t)(in.valid ? t : 0) * a.num_heads + h) * kHeadDim;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      in.x[ks] = in.valid ? *reinterpret_cast<const uint4*>(xrow + 32 * ks + 8 * q) : make_uint4(0, 0, 0, 0);
+  };
+  TileIn nxt;
+  load_tile(0, nxt);
+
   // ---- stage U^T: ut[j][i] = U[i][j]; consecutive threads take consecutive rows i,
   // so each LDS store instruction writes consecutive halfwords ----
   const uint16_t* U = a.u[kind] + (size_t)h * kHeadDim * kHeadDim;
@@ -83,26 +104,27 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
       afrag[mt][ks] = *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kUtRow + 32 * ks + 8 * q]);
 
   const float clip = a.clip[kind];
-  const uint16_t* X = a.x[kind];
   uint16_t* sink_buf = a.sink[kind];
   uint16_t* ring_buf = a.ring[kind];
   const int params_off = kind == 0 ? kKParams : kVParams;
 
+
   for (int it = 0; it < kTilesPerWave; ++it) {
     const int tile = (blockIdx.x * kTilesPerWave + it) * 4 + wave;
     if (tile >= a.num_tiles) break;   // wave-uniform
-    const int t = tile * 16 + n;
-    const bool valid = t < a.num_tokens;
-    const int b = valid ? a.seq_idx[t] : 0;
-    const int p = valid ? a.pos[t] : 0;
+    const TileIn cur = nxt;
+    if (it + 1 < kTilesPerWave && tile + 4 < a.num_tiles) load_tile(it + 1, nxt);
+    const bool valid = cur.valid;
+    const int b = cur.b, p = cur.p;
+    const bool is_int2 = valid && p >= a.sink_len;
+    // this token's page block (its id is loaded before the math that hides the latency)
+    const int32_t pid = is_int2 ? a.page_table[(size_t)b * a.max_pages + (p >> 4)] : 0;
 
-    // ---- B fragments: x[t][h][32ks + 8q .. +7] ----
     bf16x8 bfrag[4];
     uint4 xraw[4];
-    const uint16_t* xrow = X + ((size_t)(valid ? t : 0) * a.num_heads + h) * kHeadDim;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      xraw[ks] = valid ? *reinterpret_cast<const uint4*>(xrow + 32 * ks + 8 * q) : make_uint4(0, 0, 0, 0);
+      xraw[ks] = cur.x[ks];
       bfrag[ks] = __builtin_bit_cast(bf16x8, xraw[ks]);
     }
 
@@ -205,16 +227,11 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     }
 
     // ---- store INT2 ----
-    const bool is_int2 = valid && p >= a.sink_len;
     // whole aligned page written by this tile?
     const int b0 = __shfl(b, 0), p0 = __shfl(p, 0);
     const bool full_page = __all(is_int2 && b == b0 && p == p0 + n && (p0 & 15) == 0);
-    uint8_t* blk = nullptr;
+    uint8_t* blk = a.pages + ((size_t)pid * a.num_heads + h) * kBlockBytes;   // used only if is_int2
     const int slot = p & 15;
-    if (is_int2) {
-      const int32_t pid = a.page_table[(size_t)b * a.max_pages + (p >> 4)];
-      blk = a.pages + ((size_t)pid * a.num_heads + h) * kBlockBytes;
-    }
     if (kind == 0) {
       // K, token-major: post-rotation channel j = 64 r0 + 32 r1 + 16 q0 + 8 q1 + bitrev3(mt)
       // -> halfword (j / 8) = 8 r0 + 4 r1 + 2 q0 + q1, bit 2 * bitrev3(mt).
@@ -237,11 +254,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
         vbytes[wave][j][n] = (uint8_t)code[i];
       }
       wave_lds_sync();
-      const uint8_t* page_blk = nullptr;
-      {
-        const int32_t pid = a.page_table[(size_t)b0 * a.max_pages + (p0 >> 4)];
-        page_blk = a.pages + ((size_t)pid * a.num_heads + h) * kBlockBytes;
-      }
+      // every lane of the tile holds the same page: lane 0's id
+      const uint8_t* page_blk = a.pages + ((size_t)__shfl(pid, 0) * a.num_heads + h) * kBlockBytes;
       uint32_t words[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
