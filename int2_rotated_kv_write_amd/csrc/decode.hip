@@ -675,154 +675,110 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
 }
 
 // ---------------------------------------------------------------------------
-// reduce: one 256-thread block per (sequence, KV head) for its G query heads:
-// log-sum-exp merge of the partial records, then acc_rot R_V^T =
-// ((acc_rot P) H) U_V^T with U_V staged once in LDS, bf16 out.
+// reduce: one block of G x 128 threads per (sequence, KV head); thread (g, c)
+// owns output channel c of query head g.  Every partial record of a batch of
+// up to 32 items is requested at once (one memory latency per batch), merged
+// with a running log-sum-exp in registers; then acc_rot R_V^T =
+// ((acc_rot P) H) U_V^T with U_V staged in LDS, bf16 out.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSideThreads) void reduce_kernel(DecodeArgs a) {
+constexpr int kReduceBatch = 32;
+
+template <int G>
+__global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
   constexpr int kURow = kHeadDim / 8 + 1;                 // uint4 per padded U row (272 B)
   __shared__ uint4 Us[kHeadDim * kURow];                  // U_V[h] rows, padded against bank conflicts
-  __shared__ float e_s[kMaxGqa][kMaxItems];               // per-item weight exp2(m_u - M)
   __shared__ float y[kMaxGqa][kHeadDim];
-  __shared__ float lsum_s[kMaxGqa];
-  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H, G = a.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = tid & 127, hs = tid >> 7;
+  constexpr int nthr = G * kHeadDim;
+  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x, g = tid >> 7, c = tid & (kHeadDim - 1);
   const int L = a.seq_lens[b];
-  uint16_t* out = a.out + ((size_t)b * a.Hq + h * G) * kHeadDim;
+  uint16_t* out = a.out + ((size_t)b * a.Hq + h * G + g) * kHeadDim;
   if (L == 0) {
-    for (int e = tid; e < G * kHeadDim; e += kSideThreads) out[e] = 0;
+    out[c] = 0;
     return;
   }
-  {
-    const uint4* U = reinterpret_cast<const uint4*>(a.u_v + (size_t)h * kHeadDim * kHeadDim);
-    constexpr int kPer = kHeadDim * kHeadDim / 8 / kSideThreads;
-    uint4 tmp[kPer];   // all loads in flight before the LDS stores
+  // U_V loads first (stored to LDS after the record loads are also in flight)
+  constexpr int kUChunks = kHeadDim * kHeadDim / 8;       // uint4 per U
+  const uint4* U = reinterpret_cast<const uint4*>(a.u_v + (size_t)h * kHeadDim * kHeadDim);
+  constexpr int kUPer = (kUChunks + nthr - 1) / nthr;
+  uint4 utmp[kUPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) tmp[k] = U[tid + k * kSideThreads];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kSideThreads;
-      Us[(i >> 4) * kURow + (i & 15)] = tmp[k];
-    }
+  for (int k = 0; k < kUPer; ++k) {
+    const int i = tid + k * nthr;
+    utmp[k] = i < kUChunks ? U[i] : make_uint4(0, 0, 0, 0);
   }
+
   const int n_b = (bf16_token_count(L, a.sink, a.recent) + kBf16Chunk - 1) / kBf16Chunk;
   const int i_hi = int2_end(L, a.sink, a.recent);
   const int int2_pages = i_hi > a.sink ? (i_hi + kPage - 1) / kPage - a.sink / kPage : 0;
   const int n_i = (int2_pages + a.P - 1) / a.P;
   const int n_used = n_b + n_i;   // used items: [0, n_b) BF16, then [n_bsplit, n_bsplit + n_i) INT2
-  auto item = [&](int u) { return u < n_b ? u : a.n_bsplit + (u - n_b); };
-  auto part = [&](int g) { return a.part + ((size_t)b * a.Hq + h * G + g) * a.n_total * kPartFloats; };
-
-  // per head: M = max of the items' running maxima, item weights, l total (one wave per head)
-  for (int g = wave; g < G; g += 4) {
-    const float* base = part(g);
-    float mx = -INFINITY;
-    for (int u0 = 0; u0 < n_used; u0 += 256) {   // (m, l) of up to 4 items per lane in flight at once
-      float2 ml[4];
+  const float* base = a.part + ((size_t)b * a.Hq + h * G + g) * a.n_total * kPartFloats;
+  float M = -INFINITY, lsum = 0.f, plain = 0.f, rot = 0.f;
+  for (int u0 = 0; u0 < n_used; u0 += kReduceBatch) {
+    float mu[kReduceBatch], lu[kReduceBatch], vu[kReduceBatch];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int u = u0 + lane + 64 * k;
-        ml[k] = u < n_used ? *reinterpret_cast<const float2*>(base + (size_t)item(u) * kPartFloats)
-                           : make_float2(-INFINITY, 0.f);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        mx = fmaxf(mx, ml[k].x);
-        const int u = u0 + lane + 64 * k;
-        if (u < n_used) e_s[g][u] = ml[k].x;   // the item's max for now
-      }
+    for (int d = 0; d < kReduceBatch; ++d) {
+      const int u = u0 + d;
+      const bool ok = u < n_used;
+      const float* r = base + (size_t)(!ok ? 0 : u < n_b ? u : a.n_bsplit + (u - n_b)) * kPartFloats;
+      mu[d] = ok ? r[0] : -INFINITY;   // the same address across the 128 threads of a head
+      lu[d] = ok ? r[1] : 0.f;
+      vu[d] = ok ? r[4 + c] : 0.f;
     }
-    mx = wave_max_xor(mx, 1, 32);
-    float ls = 0.f;
-    for (int u = lane; u < n_used; u += 64) {
-      const float m_u = e_s[g][u];
-      const float e = m_u == -INFINITY ? 0.f : exp2f(m_u - mx);
-      e_s[g][u] = e;
-      ls += e * base[(size_t)item(u) * kPartFloats + 1];
-    }
-    ls = wave_sum_xor(ls, 1, 32);
-    if (lane == 0) lsum_s[g] = ls;
-  }
-  __syncthreads();
-
-  // channel c of heads hs, hs + 2, ... (hs is wave-uniform): plain (BF16 items) and rotated
-  // (INT2 items) sums; the loads of 16 items of every head are in flight together
-  float plain[kMaxGqa / 2], rot[kMaxGqa / 2];
+    float bm = M;
 #pragma unroll
-  for (int k = 0; k < kMaxGqa / 2; ++k) plain[k] = rot[k] = 0.f;
-  for (int u0 = 0; u0 < n_used; u0 += 16) {
-    float v[kMaxGqa / 2][16];
+    for (int d = 0; d < kReduceBatch; ++d) bm = fmaxf(bm, mu[d]);
+    const float sc = M == -INFINITY ? 0.f : exp2f(M - bm);
+    lsum *= sc;
+    plain *= sc;
+    rot *= sc;
+    M = bm;
 #pragma unroll
-    for (int k = 0; k < kMaxGqa / 2; ++k) {
-      const int g = hs + 2 * k;
-#pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const int u = u0 + d;
-        v[k][d] = (g < G && u < n_used) ? part(g)[(size_t)item(u) * kPartFloats + 4 + c] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kMaxGqa / 2; ++k) {
-      const int g = hs + 2 * k;
-      if (g >= G) continue;
-#pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const int u = u0 + d;
-        if (u < n_used) {
-          const float w = e_s[g][u] * v[k][d];
-          if (u < n_b) plain[k] += w;
-          else rot[k] += w;
-        }
-      }
+    for (int d = 0; d < kReduceBatch; ++d) {
+      const float e = mu[d] == -INFINITY ? 0.f : exp2f(mu[d] - M);
+      lsum = fmaf(e, lu[d], lsum);
+      if (u0 + d < n_b) plain = fmaf(e, vu[d], plain);
+      else rot = fmaf(e, vu[d], rot);
     }
   }
 #pragma unroll
-  for (int k = 0; k < kMaxGqa / 2; ++k)   // acc_rot P: z-space channel br(c) takes post-rotation channel c
-    if (hs + 2 * k < G) y[hs + 2 * k][bitrev7(c)] = rot[k];
+  for (int k = 0; k < kUPer; ++k) {
+    const int i = tid + k * nthr;
+    if (i < kUChunks) Us[(i >> 4) * kURow + (i & 15)] = utmp[k];
+  }
+  y[g][bitrev7(c)] = rot;   // acc_rot P: z-space channel br(c) takes post-rotation channel c
   __syncthreads();
   for (int s = 1; s < kHeadDim; s <<= 1) {
-    for (int t = tid; t < G * 64; t += kSideThreads) {
-      const int g = t >> 6, cc = t & 63;
+    for (int t = tid; t < G * 64; t += nthr) {
+      const int gg = t >> 6, cc = t & 63;
       const int lo = ((cc & ~(s - 1)) << 1) | (cc & (s - 1)), hi = lo | s;
-      const float x0 = y[g][lo], x1 = y[g][hi];
-      y[g][lo] = x0 + x1;
-      y[g][hi] = x0 - x1;
+      const float x0 = y[gg][lo], x1 = y[gg][hi];
+      y[gg][lo] = x0 + x1;
+      y[gg][hi] = x0 - x1;
     }
     __syncthreads();
   }
-  // (y U_V^T)_c = sum_k y_k U_V[c][k], row c of U_V shared by this thread's heads
-  float o[kMaxGqa / 2];
-#pragma unroll
-  for (int k = 0; k < kMaxGqa / 2; ++k) o[k] = 0.f;
+  // (y U_V^T)_c = sum_k y_k U_V[c][k]
+  float o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < kHeadDim / 8; ++kb) {
     const uint4 u8 = Us[c * kURow + kb];
     const uint32_t uu[4] = {u8.x, u8.y, u8.z, u8.w};
 #pragma unroll
-    for (int k = 0; k < kMaxGqa / 2; ++k) {
-      const int g = hs + 2 * k;
-      if (g < G) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o[k] = fmaf(y[g][8 * kb + 2 * q], bf16_bits_to_f32(uu[q] & 0xFFFFu), o[k]);
-          o[k] = fmaf(y[g][8 * kb + 2 * q + 1], bf16_bits_to_f32(uu[q] >> 16), o[k]);
-        }
-      }
+    for (int q = 0; q < 4; ++q) {
+      o0 = fmaf(y[g][8 * kb + 2 * q], bf16_bits_to_f32(uu[q] & 0xFFFFu), o0);
+      o1 = fmaf(y[g][8 * kb + 2 * q + 1], bf16_bits_to_f32(uu[q] >> 16), o1);
     }
   }
-#pragma unroll
-  for (int k = 0; k < kMaxGqa / 2; ++k) {
-    const int g = hs + 2 * k;
-    if (g < G) {
-      const float res = (plain[k] + o[k] * 0.08838834764831845f) / lsum_s[g];
-      out[(size_t)g * kHeadDim + c] = (uint16_t)f32_to_bf16_bits(res);
-    }
-  }
+  const float res = (plain + (o0 + o1) * 0.08838834764831845f) / lsum;
+  out[c] = (uint16_t)f32_to_bf16_bits(res);
 }
 
 template <int G>
 void launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
   hipLaunchKernelGGL(split_kernel<G>, dim3(a.n_total, a.H, B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(reduce_kernel<G>, dim3(B * a.H), dim3(G * kHeadDim), 0, stream, a);
 }
 
 }  // namespace
@@ -905,7 +861,6 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     case 8: launch_split<8>(a, L.batch, stream); break;
     default: return 1;
   }
-  hipLaunchKernelGGL(reduce_kernel, dim3(L.batch * L.num_kv_heads), dim3(kSideThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
