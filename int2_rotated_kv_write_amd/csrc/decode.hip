@@ -183,14 +183,22 @@ static_assert(2 * (kRing - 2) == 12, "s_waitcnt vmcnt immediate below assumes kR
 struct __attribute__((aligned(16))) SplitSmem {
   union {
     uint8_t ring[4][kRing][kBlockBytes];   // INT2 items: per-wave ring of page blocks
-    struct {
-      float p[4][kMaxGqa][16];             // BF16 items: probabilities per token
-      float m[4][kMaxGqa];
-      float l[4][kMaxGqa];
-      float acc[4][kMaxGqa][kHeadDim];
-    };
+    float p[4][kMaxGqa][16];               // BF16 items: probabilities per token (inside wave 0's ring)
   };
 };
+
+// A wave's (m, l, acc) for the block merge, in the upper half of its own page ring (slots
+// 4..7): written as soon as the wave is done, without waiting for the other waves; clear of
+// the BF16 probability scratch, which lies in wave 0's lower slots.
+struct WaveResult {
+  float acc[kMaxGqa][kHeadDim];
+  float m[kMaxGqa], l[kMaxGqa];
+};
+static_assert(sizeof(WaveResult) <= (kRing - kRing / 2) * kBlockBytes, "wave result fits its ring's upper half");
+static_assert(sizeof(float) * 4 * kMaxGqa * 16 <= (kRing / 2) * kBlockBytes, "BF16 scratch below wave 0's results");
+__device__ __forceinline__ WaveResult& wave_result(SplitSmem& sm, int w) {
+  return *reinterpret_cast<WaveResult*>(&sm.ring[w][kRing / 2][0]);
+}
 
 template <int G>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, int b, int h, int item,
@@ -200,13 +208,14 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, int b
     const int hh = o >> 7, c = o & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.m[w][hh]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wave_result(sm, w).m[hh]);
     float val = 0.f, lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float e = sm.m[w][hh] == -INFINITY ? 0.f : exp2f(sm.m[w][hh] - M);
-      val += e * sm.acc[w][hh][c];
-      lsum += e * sm.l[w][hh];
+      const WaveResult& r = wave_result(sm, w);
+      const float e = r.m[hh] == -INFINITY ? 0.f : exp2f(r.m[hh] - M);
+      val += e * r.acc[hh][c];
+      lsum += e * r.l[hh];
     }
     float* rec = a.part + ((size_t)(b * a.Hq + h * G + hh) * a.n_total + item) * kPartFloats;
     rec[4 + c] = val;
@@ -246,23 +255,39 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
     lsum[hh] = 0.f;
     acc[hh][0] = acc[hh][1] = 0.f;
   }
+  // one 16-token group per wave and round; the next round's rows are requested before this
+  // round's math, so the loads of consecutive rounds overlap
+  struct RoundIn {
+    uint4 kd[4];       // K row of token t: channels 32q .. 32q + 31
+    uint32_t vv[16];   // V rows of the group's 16 tokens: channels 2 lane, + 1
+  };
+  auto load_round = [&](int round, RoundIn& in) {
+    const int jbase = chunk * kBf16Chunk + 16 * (4 * round + wave);
+    const int j = jbase + t;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) in.kd[x] = make_uint4(0, 0, 0, 0);
+    if (j < nb) {
+      const uint16_t* krow = kbuf(j) + row_offset(j) + 32 * q;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) in.kd[x] = reinterpret_cast<const uint4*>(krow)[x];
+    }
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+      const int jj = jbase + tt;
+      in.vv[tt] = jj < nb ? *reinterpret_cast<const uint32_t*>(vbuf(jj) + row_offset(jj) + 2 * lane) : 0u;
+    }
+  };
+  RoundIn nxt;
+  load_round(0, nxt);
   for (int round = 0; round < kBf16Chunk / 64; ++round) {
     const int jbase = chunk * kBf16Chunk + 16 * (4 * round + wave);
     if (jbase >= nb) break;   // wave-uniform
     const int j = jbase + t;
     const bool valid = j < nb;
-    uint4 kd[4] = {};
-    if (valid) {
-      const uint16_t* krow = kbuf(j) + row_offset(j) + 32 * q;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) kd[x] = reinterpret_cast<const uint4*>(krow)[x];
-    }
-    uint32_t vv[16];   // all 16 value rows of the group in flight together
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-      const int jj = jbase + tt;
-      vv[tt] = jj < nb ? *reinterpret_cast<const uint32_t*>(vbuf(jj) + row_offset(jj) + 2 * lane) : 0u;
-    }
+    const RoundIn cur = nxt;
+    if (round + 1 < kBf16Chunk / 64 && jbase + 64 < nb) load_round(round + 1, nxt);
+    const uint4* kd = cur.kd;
+    const uint32_t* vv = cur.vv;
     float lg[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -307,14 +332,14 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
   if (lane == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      sm.m[wave][hh] = m[hh];
-      sm.l[wave][hh] = lsum[hh];
+      wave_result(sm, wave).m[hh] = m[hh];
+      wave_result(sm, wave).l[hh] = lsum[hh];
     }
   }
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    sm.acc[wave][hh][2 * lane] = acc[hh][0];
-    sm.acc[wave][hh][2 * lane + 1] = acc[hh][1];
+    wave_result(sm, wave).acc[hh][2 * lane] = acc[hh][0];
+    wave_result(sm, wave).acc[hh][2 * lane + 1] = acc[hh][1];
   }
   merge_waves_and_store<G>(a, b, h, chunk, sm);
 }
@@ -628,8 +653,8 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     }
   }
 
-  // ---- finish the wave (the result area overlays the page rings: wait for all waves) ----
-  __syncthreads();
+  // ---- finish the wave: its result goes to its own ring (all of its page loads have landed) ----
+  WaveResult& res = wave_result(sm, wave);
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
     // per-head totals over the 16 lanes of head hh (quad, then rows)
@@ -639,8 +664,8 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     Z1 = rows_sum(quad_sum(Z1));
     const int head = 4 * qd + hh;
     if (r == 0 && a4 == 0 && head < G) {
-      sm.m[wave][head] = m[qd];
-      sm.l[wave][head] = L_h;
+      res.m[head] = n_w > 0 ? m[qd] : -INFINITY;   // a wave without pages contributes nothing
+      res.l[head] = L_h;
     }
     // accumulator rows of this lane: head 4 qd + r, subsets j = 0..3
     const float z0 = __shfl(Z0, 4 * r), z1 = __shfl(Z1, 4 * r);
@@ -649,7 +674,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const float s = (acc[qd][t][0] + acc[qd][t][1]) + (acc[qd][t][2] + acc[qd][t][3]);
-        sm.acc[wave][row_head][16 * t + n] = s + (t < 4 ? z0 : z1);
+        res.acc[row_head][16 * t + n] = s + (t < 4 ? z0 : z1);
       }
     }
   }
