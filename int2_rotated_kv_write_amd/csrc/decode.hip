@@ -45,7 +45,8 @@ struct DecodeArgs {
   const int32_t *page_table, *seq_lens;
   uint16_t* out;
   QrotRecord* qrot;
-  float* part;
+  float* part;     // partial accumulators acc[128] per (sequence, query head, item)
+  float2* part_ml; // their (m, l)
   float sl2e;   // sm_scale * log2(e)
   float resc_thr;   // lazy rescale threshold tau: INT2 probabilities stay <= 2^tau
   int32_t H, Hq, G, max_pages, sink, recent, P, n_split, n_bsplit, n_total;
@@ -217,12 +218,9 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, int b
       val += e * r.acc[hh][c];
       lsum += e * r.l[hh];
     }
-    float* rec = a.part + ((size_t)(b * a.Hq + h * G + hh) * a.n_total + item) * kPartFloats;
-    rec[4 + c] = val;
-    if (c == 0) {
-      rec[0] = M;
-      rec[1] = lsum;
-    }
+    const size_t rec = (size_t)(b * a.Hq + h * G + hh) * a.n_total + item;
+    a.part[rec * kHeadDim + c] = val;   // whole 512-byte record, line-aligned
+    if (c == 0) a.part_ml[rec] = make_float2(M, lsum);
   }
 }
 
@@ -738,7 +736,7 @@ __global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
   const int int2_pages = i_hi > a.sink ? (i_hi + kPage - 1) / kPage - a.sink / kPage : 0;
   const int n_i = (int2_pages + a.P - 1) / a.P;
   const int n_used = n_b + n_i;   // used items: [0, n_b) BF16, then [n_bsplit, n_bsplit + n_i) INT2
-  const float* base = a.part + ((size_t)b * a.Hq + h * G + g) * a.n_total * kPartFloats;
+  const size_t rec0 = ((size_t)b * a.Hq + h * G + g) * a.n_total;
   float M = -INFINITY, lsum = 0.f, plain = 0.f, rot = 0.f;
   for (int u0 = 0; u0 < n_used; u0 += kReduceBatch) {
     float mu[kReduceBatch], lu[kReduceBatch], vu[kReduceBatch];
@@ -746,10 +744,11 @@ __global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
     for (int d = 0; d < kReduceBatch; ++d) {
       const int u = u0 + d;
       const bool ok = u < n_used;
-      const float* r = base + (size_t)(!ok ? 0 : u < n_b ? u : a.n_bsplit + (u - n_b)) * kPartFloats;
-      mu[d] = ok ? r[0] : -INFINITY;   // the same address across the 128 threads of a head
-      lu[d] = ok ? r[1] : 0.f;
-      vu[d] = ok ? r[4 + c] : 0.f;
+      const size_t rec = rec0 + (!ok ? 0 : u < n_b ? u : a.n_bsplit + (u - n_b));
+      const float2 ml = ok ? a.part_ml[rec] : make_float2(-INFINITY, 0.f);   // same address across a head
+      mu[d] = ml.x;
+      lu[d] = ml.y;
+      vu[d] = ok ? a.part[rec * kHeadDim + c] : 0.f;
     }
     float bm = M;
 #pragma unroll
@@ -814,15 +813,16 @@ DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   const long long int2_pages = max(0, max_pages - sink / kPage);
   const long long bh = (long long)batch * num_kv_heads;
   p.n_bsplit = (sink + recent + kBf16Chunk - 1) / kBf16Chunk;
-  // Items per (sequence, KV head): m ranges of ~320 pages (measured on MI355X at
-  // 28 x 100K tokens: 192-512 pages per item are within 2% of each other;
-  // 128 is 4% and 692 6% slower), but at least enough items to give every
-  // resident block slot work (4 per CU for G <= 4, 2 above, 256 CUs).
+  // Items per (sequence, KV head): m ranges of ~400 pages (measured on MI355X at
+  // 28 x 100K tokens: 16 to 20 items per (sequence, KV head) are within 0.7% of
+  // each other, 13 items -- three rounds of block slots -- is 2.5% and 41 items 5%
+  // slower), but at least enough items to give every resident block slot work
+  // (4 per CU for G <= 4, 2 above, 256 CUs).
   const long long slots = (num_q_heads / num_kv_heads <= 4 ? 4 : 2) * 256;
   const long long max_m = kMaxItems - p.n_bsplit;
   long long best_m = 0;
   if (int2_pages > 0 && bh > 0) {
-    best_m = max((int2_pages + 319) / 320, (slots + bh - 1) / bh);
+    best_m = max((int2_pages + 399) / 400, (slots + bh - 1) / bh);
     best_m = min(best_m, min(max_m, (int2_pages + 15) / 16));   // at least 16 pages per item
     best_m = max(best_m, (int2_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit);
   }
@@ -834,8 +834,10 @@ DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   p.n_total = p.n_split + p.n_bsplit;
   const size_t qrot = (size_t)batch * num_q_heads * kQrotBytes;
   p.qrot_off = 0;
-  p.part_off = (qrot + 255) / 256 * 256;
-  p.bytes = p.part_off + (size_t)batch * num_q_heads * p.n_total * kPartFloats * sizeof(float);
+  p.part_off = (qrot + 511) / 512 * 512;   // records on 128-byte line boundaries
+  const size_t n_rec = (size_t)batch * num_q_heads * p.n_total;
+  p.ml_off = p.part_off + n_rec * kHeadDim * sizeof(float);
+  p.bytes = p.ml_off + n_rec * sizeof(float2);
   return p;
 }
 
@@ -855,6 +857,7 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.out = L.out;
   a.qrot = reinterpret_cast<QrotRecord*>(L.workspace + L.plan.qrot_off);
   a.part = reinterpret_cast<float*>(L.workspace + L.plan.part_off);
+  a.part_ml = reinterpret_cast<float2*>(L.workspace + L.plan.ml_off);
   a.sl2e = L.sm_scale * 1.4426950408889634f;
   {
     // W = fp16(p s) must stay below fp16's maximum: a value scale is at most

@@ -22,11 +22,10 @@ struct KvWriteLaunch {
 // (sequence, query head) owns n_bsplit + n_split partial records.
 struct DecodePlan {
   int32_t pages_per_split, n_split, n_bsplit, n_total;
-  size_t qrot_off, part_off, bytes;
+  size_t qrot_off, part_off, ml_off, bytes;
 };
 
 constexpr int kQrotBytes = 576;      // rotated-query record per (sequence, query head)
-constexpr int kPartFloats = 132;     // m, l, 2 pad, acc[128]
 constexpr int kBf16Chunk = 320;      // BF16 tokens per split item (multiple of 64)
 constexpr int kMaxItems = 1024;      // partial records per (sequence, query head) the reduce can merge
 
