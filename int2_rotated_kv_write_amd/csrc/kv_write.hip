@@ -7,12 +7,15 @@
 // rotated, clipped and quantized at write time; sink and recent tokens stay
 // BF16); the Spanish summary "Resumen Tecnico: OSCAR ...", section 2.2 B.
 //
-// Work decomposition: one 256-thread block per (chunk of 16-token tiles,
-// KV head, K-or-V).  The block stages U^T in LDS once; each wave keeps all 32
-// MFMA A-fragments of U^T in registers and walks its tiles.  Per tile of 16
+// Work decomposition: 256-thread blocks per (KV head, K-or-V), about two per
+// CU over the whole grid; each walks groups of four 16-token tiles (one per
+// wave) strided by the grid.  The block stages U^T in LDS once; each wave keeps
+// all 32 MFMA A-fragments of U^T in registers and walks its tiles.  Per tile of 16
 // tokens the wave computes y^T = U^T x^T with 32 v_mfma_f32_16x16x32_bf16;
 // lane l then owns token l%16 and channels 16*mt + 4*(l/16) + r (mt<8, r<4),
 // so five of the seven butterfly stages are in registers and two cross lanes.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -20,7 +23,6 @@ namespace oscar {
 
 namespace {
 
-constexpr int kTilesPerWave = 8;    // 4 waves x 8 tiles = 512 tokens per block
 constexpr int kUtRow = kHeadDim + 8;   // U^T row stride in LDS (272 B): conflict-free fragment reads
 
 struct KvWriteArgs {
@@ -57,8 +59,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     int b, p;
     bool valid;
   };
-  auto load_tile = [&](int it, TileIn& in) {
-    const int t = ((blockIdx.x * kTilesPerWave + it) * 4 + wave) * 16 + n;
+  auto load_tile = [&](int tg, TileIn& in) {   // tile 4 tg + wave
+    const int t = (tg * 4 + wave) * 16 + n;
     in.valid = t < a.num_tokens;
     in.b = in.valid ? a.seq_idx[t] : 0;
     in.p = in.valid ? a.pos[t] : 0;
@@ -67,8 +69,9 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     for (int ks = 0; ks < 4; ++ks)
       in.x[ks] = in.valid ? *reinterpret_cast<const uint4*>(xrow + 32 * ks + 8 * q) : make_uint4(0, 0, 0, 0);
   };
+  const int n_groups = (a.num_tiles + 3) / 4;   // groups of four 16-token tiles, one per wave
   TileIn nxt;
-  load_tile(0, nxt);
+  load_tile(blockIdx.x, nxt);
 
   // ---- stage U^T: ut[j][i] = U[i][j]; consecutive threads take consecutive rows i,
   // so each LDS store instruction writes consecutive halfwords ----
@@ -109,11 +112,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   const int params_off = kind == 0 ? kKParams : kVParams;
 
 
-  for (int it = 0; it < kTilesPerWave; ++it) {
-    const int tile = (blockIdx.x * kTilesPerWave + it) * 4 + wave;
-    if (tile >= a.num_tiles) break;   // wave-uniform
+  // the block walks tile groups blockIdx.x, + gridDim.x, ...: U^T is staged once per block
+  for (int tg = blockIdx.x; tg < n_groups; tg += gridDim.x) {
+    const int tile = tg * 4 + wave;
+    if (tile >= a.num_tiles) break;   // wave-uniform (only in the last group)
     const TileIn cur = nxt;
-    if (it + 1 < kTilesPerWave && tile + 4 < a.num_tiles) load_tile(it + 1, nxt);
+    if (tg + (int)gridDim.x < n_groups) load_tile(tg + gridDim.x, nxt);
     const bool valid = cur.valid;
     const int b = cur.b, p = cur.p;
     const bool is_int2 = valid && p >= a.sink_len;
@@ -293,6 +297,18 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
 
 }  // namespace
 
+int device_cus() {   // compute units of the current device (cached per device)
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream) {
   KvWriteArgs a{};
   int nz = 0;
@@ -321,8 +337,11 @@ int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream) {
   a.sink_len = L.sink;
   a.recent = L.recent;
   a.num_tiles = (L.num_tokens + 15) / 16;
-  const int tiles_per_block = 4 * kTilesPerWave;
-  dim3 grid((a.num_tiles + tiles_per_block - 1) / tiles_per_block, L.num_kv_heads, nz);
+  // blocks per (KV head, K/V): enough for two resident blocks per CU over the whole grid
+  // (the register budget allows two), never more than there are tile groups
+  const int n_groups = (a.num_tiles + 3) / 4;
+  const int per_slice = std::max(1, (2 * device_cus() + L.num_kv_heads * nz - 1) / (L.num_kv_heads * nz));
+  dim3 grid(std::min(n_groups, per_slice), L.num_kv_heads, nz);
   hipLaunchKernelGGL(kv_write_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
