@@ -7,10 +7,10 @@
 // rotated, clipped and quantized at write time; sink and recent tokens stay
 // BF16); the Spanish summary "Resumen Tecnico: OSCAR ...", section 2.2 B.
 //
-// Work decomposition: 256-thread blocks per (KV head, K-or-V), about two per
-// CU over the whole grid; each walks groups of four 16-token tiles (one per
-// wave) strided by the grid.  The block stages U^T in LDS once; each wave keeps
-// all 32 MFMA A-fragments of U^T in registers and walks its tiles.  Per tile of 16
+// Work decomposition: 256-thread blocks per (KV head, K-or-V), about three per
+// CU over the whole grid (43 KB of LDS and 3 waves per SIMD each); each walks
+// groups of four 16-token tiles (one per wave) strided by the grid.  The block
+// stages U^T in LDS once; each wave reads its MFMA A-fragments from there.  Per tile of 16
 // tokens the wave computes y^T = U^T x^T with 32 v_mfma_f32_16x16x32_bf16;
 // lane l then owns token l%16 and channels 16*mt + 4*(l/16) + r (mt<8, r<4),
 // so five of the seven butterfly stages are in registers and two cross lanes.
@@ -40,7 +40,7 @@ struct KvWriteArgs {
   int32_t kind_of_z[2];
 };
 
-__global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void kv_write_kernel(KvWriteArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ut[kHeadDim * kUtRow];      // U^T, rows padded
   __shared__ __attribute__((aligned(16))) uint8_t vbytes[4][kHeadDim][16];    // V transposition
 
@@ -98,13 +98,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   __syncthreads();
 
   // A fragment (mt, ks): rows = output channel 16mt + n', cols = input channels
-  // 32ks + 8q' .. +7 (the same k mapping as the B fragment below).
-  bf16x8 afrag[8][4];
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      afrag[mt][ks] = *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kUtRow + 32 * ks + 8 * q]);
+  // 32ks + 8q' .. +7 (the same k mapping as the B fragment below), read from LDS for
+  // every tile: holding all 32 in registers would cost 128 VGPRs and a third of the
+  // waves per SIMD.
+  auto afrag = [&](int mt, int ks) {
+    return *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kUtRow + 32 * ks + 8 * q]);
+  };
 
   const float clip = a.clip[kind];
   uint16_t* sink_buf = a.sink[kind];
@@ -154,7 +153,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[mt][ks], bfrag[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag(mt, ks), bfrag[ks], acc, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[4 * mt + r] = acc[r];
     }
@@ -337,10 +336,10 @@ int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream) {
   a.sink_len = L.sink;
   a.recent = L.recent;
   a.num_tiles = (L.num_tokens + 15) / 16;
-  // blocks per (KV head, K/V): enough for two resident blocks per CU over the whole grid
-  // (the register budget allows two), never more than there are tile groups
+  // blocks per (KV head, K/V): enough for three resident blocks per CU over the whole
+  // grid (LDS and registers allow three), never more than there are tile groups
   const int n_groups = (a.num_tiles + 3) / 4;
-  const int per_slice = std::max(1, (2 * device_cus() + L.num_kv_heads * nz - 1) / (L.num_kv_heads * nz));
+  const int per_slice = std::max(1, (3 * device_cus() + L.num_kv_heads * nz - 1) / (L.num_kv_heads * nz));
   dim3 grid(std::min(n_groups, per_slice), L.num_kv_heads, nz);
   hipLaunchKernelGGL(kv_write_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
