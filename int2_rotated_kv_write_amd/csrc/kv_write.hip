@@ -24,6 +24,15 @@ namespace oscar {
 namespace {
 
 constexpr int kUtRow = kHeadDim + 8;   // U^T row stride in LDS (272 B): conflict-free fragment reads
+constexpr float kInvSqrt128 = 0.08838834764831845f;
+
+// LDS row of channel j in the V transposition buffer: channel bits 3, 4 (the lane's
+// quarter when the codes are written) go to row bits 0, 1 and bits 1, 2 to row bits 2, 3,
+// so both the byte writes (4 quarters x 16 tokens) and the 16-byte row reads (16
+// consecutive channels) fall in distinct LDS banks.
+__device__ __forceinline__ int vrow(int j) {
+  return ((j >> 3) & 3) | (((j >> 1) & 3) << 2) | ((j & 1) << 4) | (j & 0x60);
+}
 
 struct KvWriteArgs {
   const uint16_t* x[2];
@@ -105,7 +114,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     return *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kUtRow + 32 * ks + 8 * q]);
   };
 
-  const float clip = a.clip[kind];
+  const float clip_s = a.clip[kind] * 11.313708498984761f;   // clip threshold before the 1/sqrt(128)
   uint16_t* sink_buf = a.sink[kind];
   uint16_t* ring_buf = a.ring[kind];
   const int params_off = kind == 0 ? kKParams : kVParams;
@@ -194,17 +203,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       v[i | 8] = __uint_as_float(r[1]);
     }
 
-    // ---- scale, clip, group min/max ----
+    // ---- clip, group min/max (v holds the rotation times sqrt(128): the 1/sqrt(128)
+    // goes into the clip threshold, the group parameters and the code scale below) ----
     // channel c = 16mt + 4q + r goes to post-rotation index j = bitrev7(c),
     // whose group j/64 is bit 0 of c, i.e. r & 1.
     float mn[2] = {INFINITY, INFINITY}, mx[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      float w = v[i] * 0.08838834764831845f;
-      w = fminf(fmaxf(w, -clip), clip);
-      v[i] = w;
-      mn[i & 1] = fminf(mn[i & 1], w);
-      mx[i & 1] = fmaxf(mx[i & 1], w);
+      v[i] = __builtin_amdgcn_fmed3f(v[i], -clip_s, clip_s);
+      mn[i & 1] = fminf(mn[i & 1], v[i]);
+      mx[i & 1] = fmaxf(mx[i & 1], v[i]);
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -215,19 +223,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     float sf[2], zf[2], inv[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      sbits[g] = f32_to_f16_bits((mx[g] - mn[g]) * (1.0f / 3.0f));
-      zbits[g] = f32_to_f16_bits(mn[g]);
+      sbits[g] = f32_to_f16_bits((mx[g] - mn[g]) * (kInvSqrt128 / 3.0f));
+      zbits[g] = f32_to_f16_bits(mn[g] * kInvSqrt128);   // = the smallest scaled value, rounded once
       sf[g] = f16_bits_to_f32(sbits[g]);
       zf[g] = f16_bits_to_f32(zbits[g]);
       inv[g] = sf[g] > 0.f ? __builtin_amdgcn_rcpf(sf[g]) : 0.f;
-      zf[g] = -zf[g] * inv[g];   // t = w * inv - z * inv
+      zf[g] = -zf[g] * inv[g];          // t = w * inv - z * inv with w = v / sqrt(128)
+      inv[g] = inv[g] * kInvSqrt128;
     }
-    uint32_t code[32];
+    float tq[32];   // (w - z) / s clamped to [0, 3]; rounded to the code where it is stored
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float tq = __builtin_amdgcn_fmed3f(fmaf(v[i], inv[i & 1], zf[i & 1]), 0.f, 3.f);
-      code[i] = (uint32_t)__builtin_rintf(tq);
-    }
+    for (int i = 0; i < 32; ++i) tq[i] = __builtin_amdgcn_fmed3f(fmaf(v[i], inv[i & 1], zf[i & 1]), 0.f, 3.f);
 
     // ---- store INT2 ----
     // whole aligned page written by this tile?
@@ -241,20 +247,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       if (is_int2) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          uint32_t hw = 0;
+          float hf = 0.f;   // sum of code * 4^k: exact in fp32 (16 bits)
 #pragma unroll
-          for (int mt = 0; mt < 8; ++mt) hw |= code[4 * mt + r] << (2 * bitrev3(mt));
+          for (int mt = 0; mt < 8; ++mt) hf = fmaf(__builtin_rintf(tq[4 * mt + r]), (float)(1 << (2 * bitrev3(mt))), hf);
+          const uint32_t hw = (uint32_t)hf;
           const int hidx = 8 * (r & 1) + 4 * (r >> 1) + 2 * (q & 1) + (q >> 1);
           *reinterpret_cast<uint16_t*>(blk + kKCodes + 32 * slot + 2 * hidx) = (uint16_t)hw;
         }
       }
     } else if (full_page) {
-      // V, channel-major, whole page: transpose through LDS, write whole words.
+      // V, channel-major, whole page: transpose through LDS, write whole words.  The code
+      // byte is the low byte of tq + 2^23 (adding 2^23 rounds to the nearest integer, ties
+      // to even, exactly like rint).
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int mt = i >> 2, r = i & 3;
         const int j = 64 * (r & 1) + 32 * (r >> 1) + 16 * (q & 1) + 8 * (q >> 1) + bitrev3(mt);
-        vbytes[wave][j][n] = (uint8_t)code[i];
+        vbytes[wave][vrow(j)][n] = (uint8_t)__float_as_uint(tq[i] + 8388608.0f);
       }
       wave_lds_sync();
       // every lane of the tile holds the same page: lane 0's id
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       uint32_t words[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint4 by = *reinterpret_cast<const uint4*>(&vbytes[wave][2 * lane + c][0]);
+        const uint4 by = *reinterpret_cast<const uint4*>(&vbytes[wave][vrow(2 * lane + c)][0]);
         const uint32_t parts[4] = {by.x, by.y, by.z, by.w};
         uint32_t wv = 0;
 #pragma unroll
@@ -283,8 +292,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       for (int i = 0; i < 32; ++i) {
         const int mt = i >> 2, r = i & 3;
         const int j = 64 * (r & 1) + 32 * (r >> 1) + 16 * (q & 1) + 8 * (q >> 1) + bitrev3(mt);
+        const uint32_t code = (uint32_t)__builtin_rintf(tq[i]);
         atomicAnd(&words[j], clear);
-        if (code[i]) atomicOr(&words[j], code[i] << (2 * slot));
+        if (code) atomicOr(&words[j], code << (2 * slot));
       }
     }
     if (is_int2 && q == 0) {
