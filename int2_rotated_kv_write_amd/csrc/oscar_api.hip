@@ -116,7 +116,7 @@ int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, co
   if (!clip_ok(layer->clip_v)) return fail(OSCAR_EINVAL, "clip_v outside (0, 16384]%s");
   const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
                                                          shape->recent, batch, max_pages);
-  if (plan.n_total > oscar::kMaxItems) return fail(OSCAR_EINVAL, "max_pages too large (sequences over ~2M tokens)%s");
+  if (plan.n_total > oscar::kMaxItems) return fail(OSCAR_EINVAL, "max_pages too large (sequences over ~8M tokens)%s");
   if (!workspace || workspace_bytes < plan.bytes) return fail(OSCAR_ENOWS, "workspace smaller than required%s");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned%s");
   oscar::DecodeLaunch L{};
