@@ -355,7 +355,9 @@ __device__ __forceinline__ half8 half8_of(uint4 u) { return __builtin_bit_cast(h
 // slots being read (it would wait for every outstanding load before each LDS
 // read, defeating the prefetch); the loop's own s_waitcnt vmcnt orders it.
 __device__ __forceinline__ void dma_to_lds16(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+  // one wait state between the M0 write and the load that reads it (the compiler puts the same
+  // s_nop in front of its own LDS-DMA loads; inline assembly is not checked for it)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
