@@ -49,7 +49,7 @@ struct DecodeArgs {
   float2* part_ml; // their (m, l)
   float sl2e;   // sm_scale * log2(e)
   float resc_thr;   // lazy rescale threshold tau: INT2 probabilities stay <= 2^tau
-  int32_t H, Hq, G, max_pages, sink, recent, P, n_split, n_bsplit, n_total;
+  int32_t H, Hq, G, B, max_pages, sink, recent, P, n_split, n_bsplit, n_total;
 };
 
 __device__ __forceinline__ int bf16_token_count(int L, int sink, int recent) {
@@ -684,7 +684,13 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void split_kernel(DecodeArgs a) {
   __shared__ SplitSmem sm;
-  const int item = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // 1D grid: every (sequence, KV head)'s INT2 ranges first, then all BF16 chunks, which are
+  // short and fill the block slots the last INT2 ranges leave idle (measured 1.7% faster
+  // than a (sequence, KV head)-major order at 28 x 100K)
+  const int nbh = a.B * a.H, w = blockIdx.x, n_int2 = nbh * a.n_split;
+  const int bh = w < n_int2 ? w / a.n_split : (w - n_int2) / a.n_bsplit;
+  const int item = w < n_int2 ? a.n_bsplit + (w - bh * a.n_split) : (w - n_int2) - bh * a.n_bsplit;
+  const int b = bh / a.H, h = bh - b * a.H;
   const int L = a.seq_lens[b];
   if (item < a.n_bsplit) {
     if (item * kBf16Chunk >= bf16_token_count(L, a.sink, a.recent)) return;
@@ -803,7 +809,7 @@ __global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
 
 template <int G>
 void launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(split_kernel<G>, dim3(a.n_total, a.H, B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(split_kernel<G>, dim3(a.n_total * a.H * B), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(reduce_kernel<G>, dim3(B * a.H), dim3(G * kHeadDim), 0, stream, a);
 }
 
@@ -872,6 +878,7 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.H = L.num_kv_heads;
   a.Hq = L.num_q_heads;
   a.G = L.num_q_heads / L.num_kv_heads;
+  a.B = L.batch;
   a.max_pages = L.max_pages;
   a.sink = L.sink;
   a.recent = L.recent;
