@@ -488,6 +488,14 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     dma_to_lds16(row, lane_off, dst);
     if (lane < 16) dma_to_lds16(row, lane_off + 1024, dst + 1024);
   };
+  // A pair without its second page reads that page's slot anyway and weights it with p = 0;
+  // the slot then holds an earlier page of this wave or, before the ring's first turn, the
+  // zeros written here, so the value scales it multiplies stay finite.
+  {
+    static_assert(kRing * 16 == 128, "one 16-byte store per lane covers the V parameters of every slot");
+    *reinterpret_cast<uint4*>(&sm.ring[wave][lane >> 3][kVParams + 16 * (lane & 7)]) = make_uint4(0, 0, 0, 0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // before any page lands in these slots
+  }
   for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(j, j);
   // this lane's byte offsets inside a page block
   const int t0 = 4 * r + 2 * limb;
@@ -531,7 +539,6 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 #pragma unroll
       for (int t = 0; t < 8; ++t) cur[k].vw[t] = *reinterpret_cast<const uint32_t*>(blk + off_vw + 64 * t);
     }
-    if (!has1) cur[1].vp[0] = cur[1].vp[1] = 0u;   // its weights are 0 * (s, z): keep them finite
 
     // ---- logits: lane (r, hh, a4) ends with token 4r + a4 of head 4 qd + hh ----
     // all MFMA chains of both pages first, so they overlap each other's latency
