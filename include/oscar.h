@@ -122,7 +122,11 @@ int oscar_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer,
                    int32_t max_pages, const int32_t* seq_lens_after, hipStream_t stream);
 
 /* Bytes of device workspace oscar_decode_attn needs for `batch` sequences
- * whose page_table rows hold `max_pages` entries.  0 on invalid arguments. */
+ * whose page_table rows hold `max_pages` entries.  0 on invalid arguments,
+ * including max_pages beyond what one call can split: the INT2 pages after the
+ * sink pages go to at most 1,023 ranges of at most 512 pages (max_pages <=
+ * sink/16 + 523,776, about 8.4M tokens).  Calls that share a workspace must
+ * not overlap in time. */
 size_t oscar_decode_workspace_bytes(const oscar_shape_t* shape, int32_t batch, int32_t max_pages);
 
 /* decode_attn -- one decode step of attention over the mixed-precision paged
