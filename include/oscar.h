@@ -124,9 +124,9 @@ int oscar_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer,
 /* Bytes of device workspace oscar_decode_attn needs for `batch` sequences
  * whose page_table rows hold `max_pages` entries.  0 on invalid arguments,
  * including max_pages beyond what one call can split: the INT2 pages after the
- * sink pages go to at most 1,023 ranges of at most 512 pages (max_pages <=
- * sink/16 + 523,776, about 8.4M tokens).  Calls that share a workspace must
- * not overlap in time. */
+ * sink pages go to at most 1,024 - ceil((sink + recent) / 320) ranges of at most
+ * 512 pages (sink 64, recent 256: max_pages <= 4 + 523,776, about 8.4M tokens).
+ * Calls that share a workspace must not overlap in time. */
 size_t oscar_decode_workspace_bytes(const oscar_shape_t* shape, int32_t batch, int32_t max_pages);
 
 /* decode_attn -- one decode step of attention over the mixed-precision paged

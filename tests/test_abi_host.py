@@ -103,3 +103,14 @@ def test_workspace_grows_with_batch_and_pages():
     b = L.oscar_decode_workspace_bytes(ctypes.byref(s), 2, 100)
     c = L.oscar_decode_workspace_bytes(ctypes.byref(s), 2, 10000)
     assert 0 < a < b < c
+
+
+def test_workspace_max_pages_limit():
+    """One call splits the INT2 pages after the sink pages into at most 1,023
+    ranges of at most 512 pages: max_pages = sink/16 + 523,776 is the largest
+    accepted (about 8.4M tokens), one more page is rejected with size 0."""
+    L = lib.load()
+    s = good_shape()
+    top = s.sink // 16 + 1023 * 512
+    assert L.oscar_decode_workspace_bytes(ctypes.byref(s), 1, top) > 0
+    assert L.oscar_decode_workspace_bytes(ctypes.byref(s), 1, top + 1) == 0
