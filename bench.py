@@ -68,6 +68,15 @@ def decode_bytes(lens, H, Hq):
     return tot
 
 
+def bf16_decode_bytes(lens, H, Hq):
+    """Algorithmic HBM bytes of one bf16_decode_attn call: 512 B per token-head
+    (K and V), q and out, one page-table entry per page."""
+    tot = 0
+    for L in lens:
+        tot += H * int(L) * 512 + 4 * math.ceil(int(L) / 16)
+    return tot + len(lens) * Hq * 128 * 2 * 2
+
+
 def write_bytes(n_tokens, H):
     """kv_write of n decode tokens (K and V): read 2x256 B per token-head,
     write 80 B INT2 + 2x256 B ring copy per token-head, U_K and U_V."""
@@ -315,6 +324,33 @@ def main():
     log(f"kv_write prefill of {n_pre} tokens x {H} heads: {pre_us:.1f} us, {pre_gbs:.0f} GB/s")
     del pre_cache, pre_k, pre_v
 
+    # ---- the BF16 baseline: the same sequences, heads and page table in an
+    # all-BF16 paged cache, one bf16_decode_attn per layer; HIP events ----
+    from synth.device import fill_bf16_pages_device
+    torch.cuda.empty_cache()
+    b16_pages = torch.zeros((num_pages, H, 4096), dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        L = int(lens[b])
+        if L:
+            fill_bf16_pages_device(b16_pages, sample_kv_device(law, L, gen, dev), sample_kv_device(law, L, gen, dev),
+                                   table_d[b])
+    b16_ws = torch.empty(lib.bf16_decode_workspace_bytes(H, Hq, B, max_pages), dtype=torch.uint8, device=dev)
+    b16_call = lib.prepare_bf16_decode_attn(H, Hq, b16_pages, qs[0], table_d, lens_d, out, b16_ws, SIG)
+    for _ in range(2):
+        b16_call()
+    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for e0, e1 in bev:
+        e0.record()
+        b16_call()
+        e1.record()
+    torch.cuda.synchronize()
+    b16_us = 1e3 * statistics.mean(e0.elapsed_time(e1) for e0, e1 in bev)
+    b16_bytes = bf16_decode_bytes(lens, H, Hq)
+    b16_gbs = b16_bytes / (b16_us * 1e-6) / 1e9
+    log(f"bf16 baseline decode: {b16_us:.1f} us/layer, {b16_gbs:.0f} GB/s; "
+        f"INT2 decode_attn is {b16_us / (dec_avg_ms * 1e3):.2f}x faster")
+    del b16_pages, b16_ws, b16_call
+
     cpu = None
     if not args.no_cpu_baseline:
         t_unit, reps, threads = cpu_baseline(H, NL, int(lens.max()))
@@ -343,6 +379,10 @@ def main():
                      "bytes_per_launch": dbytes, "avg_launch_us": dec_avg_ms * 1e3},
         "kv_write_prefill": {"tokens": n_pre, "kv_heads": H, "us": pre_us, "tokens_per_s": n_pre / (pre_us * 1e-6),
                              "bytes": pre_bytes, "achieved_gbs": pre_gbs, "frac": pre_gbs / PEAK_HBM_GBS},
+        "bf16_baseline": {"kernel": "bf16_decode_attn (split + reduce) over an all-BF16 paged cache, per layer",
+                          "us": b16_us, "bytes": b16_bytes, "achieved_gbs": b16_gbs,
+                          "frac": b16_gbs / PEAK_HBM_GBS, "int2_speedup": b16_us / (dec_avg_ms * 1e3),
+                          "cache_bytes_ratio": b16_bytes / dbytes},
         "step_hbm_gbs": step_bytes / (elapsed / args.steps) / 1e9,
         "cpu_baseline": cpu,
     }

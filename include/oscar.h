@@ -156,6 +156,42 @@ int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer,
                       const int32_t* seq_lens, int32_t batch, float sm_scale, uint16_t* out,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* BF16 paged decode -- the baseline the pages measure OSCAR against: their
+ * 100K-context decode speedups are relative to a BF16 KV cache ([it]
+ * "Velocita di decodifica"; [es] section 4, which also gives the ~8x memory
+ * reduction).  Plain attention over an all-BF16 paged cache at the same
+ * shapes, so the INT2 path's gain can be measured per layer on one GPU.
+ *
+ * BF16 page block (one 8192-byte block per physical page id and KV head;
+ * `pages` is [num_pages][num_kv_heads][4096] bf16):
+ *   elements [   0, 2048) K, token-major: slot t, channel c at 128*t + c
+ *   elements [2048, 4096) V, channel-major: channel c, slot t at 2048 + 16*c + t
+ *
+ * Workspace bytes for `batch` sequences whose page_table rows hold
+ * `max_pages` entries; 0 on invalid arguments (1 <= num_kv_heads,
+ * num_q_heads a multiple of it with ratio <= 8, batch >= 0, max_pages >= 1).
+ * Calls that share a workspace must not overlap in time. */
+size_t oscar_bf16_decode_workspace_bytes(int32_t num_kv_heads, int32_t num_q_heads, int32_t batch,
+                                         int32_t max_pages);
+
+/* bf16_decode_attn -- out = softmax(sm_scale * q . K^T) V over positions
+ * [0, L) of each sequence, position p at slot p % 16 of page
+ * page_table[b][p / 16], KV head h = query head / (num_q_heads/num_kv_heads).
+ *   pages      bf16 [num_pages][num_kv_heads][4096] (format above)
+ *   q          bf16 [batch][num_q_heads][128]
+ *   page_table int32 [batch][max_pages]
+ *   seq_lens   int32 [batch], 0 <= L <= 16 * max_pages (not checked on device)
+ *   out        bf16 [batch][num_q_heads][128] (round to nearest even); L == 0
+ *              writes zeros
+ *   workspace  >= oscar_bf16_decode_workspace_bytes(...) bytes, 256-byte
+ *              aligned; clobbered
+ * Slots past L in a sequence's last page may hold anything (they are
+ * masked).  Returns OSCAR_OK, OSCAR_EINVAL, OSCAR_ENOWS or OSCAR_EHIP. */
+int oscar_bf16_decode_attn(int32_t num_kv_heads, int32_t num_q_heads, const uint16_t* pages,
+                           const uint16_t* q, const int32_t* page_table, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t batch, float sm_scale, uint16_t* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* calibrate_layer -- HOST, offline: the calibration of [es] 2.2 A (steps 1-4)
  * and [ru] paragraph 2 for one layer, in fp64 on host memory.
  *   q_cal  host double [H_kv][gqa][num_samples][128] calibration queries

@@ -9,13 +9,14 @@ the first call does, and raises if the library is missing.
 """
 from ._native import load, library_path
 from .api import (
-    CacheBuffers, CacheShape, OscarError, allocate_cache, calibrate_layer,
-    decode_attn, decode_workspace_bytes, kv_write, prepare_decode_attn, prepare_kv_write,
-    status_string,
+    CacheBuffers, CacheShape, OscarError, allocate_cache, bf16_decode_attn,
+    bf16_decode_workspace_bytes, calibrate_layer, decode_attn, decode_workspace_bytes, kv_write,
+    prepare_bf16_decode_attn, prepare_decode_attn, prepare_kv_write, status_string,
 )
 
 __all__ = [
     "load", "library_path", "CacheShape", "CacheBuffers", "OscarError",
     "allocate_cache", "kv_write", "decode_attn", "decode_workspace_bytes",
     "calibrate_layer", "status_string", "prepare_kv_write", "prepare_decode_attn",
+    "bf16_decode_attn", "bf16_decode_workspace_bytes", "prepare_bf16_decode_attn",
 ]

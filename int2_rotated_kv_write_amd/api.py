@@ -16,6 +16,7 @@ from ._native import OscarLayer, OscarShape, load
 
 HEAD_DIM = 128
 PAGE_BLOCK = 1280
+BF16_PAGE_ELEMS = 4096     # bf16 elements per (page, KV head) of the BF16 baseline cache
 
 
 class OscarError(RuntimeError):
@@ -169,6 +170,39 @@ def decode_attn(shape: CacheShape, cache: CacheBuffers, q, page_table, seq_lens,
     _check(rc)
 
 
+def bf16_decode_workspace_bytes(num_kv_heads: int, num_q_heads: int, batch: int, max_pages: int) -> int:
+    return int(load().oscar_bf16_decode_workspace_bytes(num_kv_heads, num_q_heads, batch, max_pages))
+
+
+def _bf16_decode_args(num_kv_heads, num_q_heads, pages, q, page_table, seq_lens, out, workspace,
+                      sm_scale, stream):
+    import torch
+    B = int(seq_lens.numel())
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if pages.dim() != 3 or tuple(pages.shape[1:]) != (num_kv_heads, BF16_PAGE_ELEMS):
+        raise OscarError("pages must be bfloat16 [num_pages][H_kv][4096]")
+    if page_table.dim() != 2 or page_table.shape[0] < B:
+        raise OscarError("page_table must be [>= batch][max_pages]")
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise OscarError("workspace must be a uint8 device tensor")
+    return (num_kv_heads, num_q_heads, _dev(pages, torch.bfloat16, "pages"),
+            _dev(q, torch.bfloat16, "q", (B, num_q_heads, HEAD_DIM)),
+            _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
+            _dev(seq_lens, torch.int32, "seq_lens", (B,)), B, float(sm_scale),
+            _dev(out, torch.bfloat16, "out", (B, num_q_heads, HEAD_DIM)),
+            workspace.data_ptr(), workspace.numel(), _stream(stream))
+
+
+def bf16_decode_attn(num_kv_heads: int, num_q_heads: int, pages, q, page_table, seq_lens, out, workspace,
+                     sm_scale: float | None = None, stream=None) -> None:
+    """oscar_bf16_decode_attn: the BF16 paged-cache baseline.  pages bfloat16
+    [num_pages][H_kv][4096] (K token-major, then V channel-major per block),
+    q / out bfloat16 [B][Hq][128], seq_lens int32 [B]."""
+    _check(load().oscar_bf16_decode_attn(*_bf16_decode_args(num_kv_heads, num_q_heads, pages, q, page_table,
+                                                            seq_lens, out, workspace, sm_scale, stream)))
+
+
 def calibrate_layer(q_cal: np.ndarray, k_cal: np.ndarray, v_cal: np.ndarray, sm_scale: float,
                     quantile: float = 0.999, num_threads: int = 0):
     """oscar_calibrate_layer (host, offline).  q_cal float64 [H][G][N][128],
@@ -232,3 +266,10 @@ def prepare_decode_attn(shape: CacheShape, cache: CacheBuffers, q, page_table, s
             _dev(out, torch.bfloat16, "out", (B, shape.num_q_heads, HEAD_DIM)),
             workspace.data_ptr(), workspace.numel(), _stream(stream))
     return PreparedCall(load().oscar_decode_attn, args, (cs, cl, q, page_table, seq_lens, out, workspace))
+
+
+def prepare_bf16_decode_attn(num_kv_heads: int, num_q_heads: int, pages, q, page_table, seq_lens, out,
+                             workspace, sm_scale: float | None = None, stream=None) -> PreparedCall:
+    args = _bf16_decode_args(num_kv_heads, num_q_heads, pages, q, page_table, seq_lens, out, workspace,
+                             sm_scale, stream)
+    return PreparedCall(load().oscar_bf16_decode_attn, args, (pages, q, page_table, seq_lens, out, workspace))

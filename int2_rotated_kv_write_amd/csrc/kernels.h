@@ -44,7 +44,28 @@ struct DecodeLaunch {
   DecodePlan plan;
 };
 
+// BF16 paged decode (the comparison kernel): `n_split` ranges of
+// `pages_per_split` pages per (sequence, KV head), one partial record each.
+struct B16Plan {
+  int32_t pages_per_split, n_split;
+  size_t part_off, ml_off, bytes;
+};
+
+B16Plan make_bf16_decode_plan(int32_t num_kv_heads, int32_t batch, int32_t max_pages, int32_t num_q_heads);
+
+struct B16Launch {
+  const uint8_t* pages;
+  const uint16_t* q;
+  const int32_t *page_table, *seq_lens;
+  uint16_t* out;
+  uint8_t* workspace;
+  float sm_scale;
+  int32_t num_kv_heads, num_q_heads, max_pages, batch;
+  B16Plan plan;
+};
+
 int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream);
 int launch_decode(const DecodeLaunch& L, hipStream_t stream);
+int launch_bf16_decode(const B16Launch& L, hipStream_t stream);
 
 }  // namespace oscar

@@ -145,4 +145,52 @@ int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, co
   return OSCAR_OK;
 }
 
+namespace {
+int check_bf16_heads(int32_t num_kv_heads, int32_t num_q_heads) {
+  if (num_kv_heads < 1) return fail(OSCAR_EINVAL, "num_kv_heads must be >= 1%s");
+  if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return fail(OSCAR_EINVAL, "num_q_heads must be a positive multiple of num_kv_heads%s");
+  if (num_q_heads / num_kv_heads > 8) return fail(OSCAR_EINVAL, "num_q_heads / num_kv_heads must be <= 8%s");
+  return OSCAR_OK;
+}
+}  // namespace
+
+size_t oscar_bf16_decode_workspace_bytes(int32_t num_kv_heads, int32_t num_q_heads, int32_t batch,
+                                         int32_t max_pages) {
+  if (check_bf16_heads(num_kv_heads, num_q_heads) || batch < 0 || max_pages < 1) return 0;
+  return oscar::make_bf16_decode_plan(num_kv_heads, batch, max_pages, num_q_heads).bytes;
+}
+
+int oscar_bf16_decode_attn(int32_t num_kv_heads, int32_t num_q_heads, const uint16_t* pages, const uint16_t* q,
+                           const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                           float sm_scale, uint16_t* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (int rc = check_bf16_heads(num_kv_heads, num_q_heads)) return rc;
+  if (batch < 0) return fail(OSCAR_EINVAL, "batch < 0%s");
+  if (max_pages < 1) return fail(OSCAR_EINVAL, "max_pages must be >= 1%s");
+  if (!std::isfinite(sm_scale)) return fail(OSCAR_EINVAL, "sm_scale is not finite%s");
+  if (batch == 0) return OSCAR_OK;
+  if (!pages || !q || !page_table || !seq_lens || !out) return fail(OSCAR_EINVAL, "NULL tensor pointer%s");
+  const oscar::B16Plan plan = oscar::make_bf16_decode_plan(num_kv_heads, batch, max_pages, num_q_heads);
+  if ((long long)batch * num_kv_heads * plan.n_split > 0x7FFFFFFFLL)
+    return fail(OSCAR_EINVAL, "batch x num_kv_heads x ranges exceeds the grid limit%s");
+  if (!workspace || workspace_bytes < plan.bytes) return fail(OSCAR_ENOWS, "workspace smaller than required%s");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned%s");
+  oscar::B16Launch L{};
+  L.pages = reinterpret_cast<const uint8_t*>(pages);
+  L.q = q;
+  L.page_table = page_table;
+  L.seq_lens = seq_lens;
+  L.out = out;
+  L.workspace = static_cast<uint8_t*>(workspace);
+  L.sm_scale = sm_scale;
+  L.num_kv_heads = num_kv_heads;
+  L.num_q_heads = num_q_heads;
+  L.max_pages = max_pages;
+  L.batch = batch;
+  L.plan = plan;
+  if (oscar::launch_bf16_decode(L, stream)) return hip_fail("bf16 decode launch");
+  return OSCAR_OK;
+}
+
 }  // extern "C"

@@ -36,7 +36,8 @@ __all__ = [
     "hadamard", "bitrev7", "bitrev_permutation", "rotate", "rotation", "quantize",
     "pack_k_codes", "unpack_k_codes", "regions", "kv_write", "gather_sequence",
     "decode", "decode_folded", "query_covariance", "score_weighted_covariance",
-    "eigenbasis", "calibrate_layer", "new_cache",
+    "eigenbasis", "calibrate_layer", "new_cache", "BF16_BLOCK", "new_bf16_pages",
+    "bf16_pages_write", "bf16_pages_gather", "decode_bf16_paged",
 ]
 
 D = 128                      # head_dim
@@ -433,6 +434,74 @@ def decode_folded(shape: Shape, cache: Cache, layer: Layer, q_bits, page_table,
                 npl = len(plainK)
                 acc = p[:npl] @ plainV + (p[npl:] @ Vr) @ Rv.T
                 out[b, hq] = acc / p.sum()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# all-BF16 paged cache: the baseline OSCAR is measured against ([it] "Velocita
+# di decodifica" and [es] section 4 state the 100K-context decode speedups
+# relative to a BF16 KV cache).  Block per (physical page, KV head): 4096 bf16
+# elements, K token-major (slot t, channel c at 128 t + c), then V
+# channel-major (channel c, slot t at 2048 + 16 c + t).  The layout is this
+# library's own; the pages only say the cache is paged.
+# ----------------------------------------------------------------------------
+BF16_BLOCK = 4096
+
+
+def new_bf16_pages(num_pages: int, num_kv_heads: int) -> np.ndarray:
+    return np.zeros((num_pages, num_kv_heads, BF16_BLOCK), np.uint16)
+
+
+def bf16_pages_write(pages: np.ndarray, k_bits, v_bits, seq_idx, pos, page_table,
+                     page_size: int = 16) -> None:
+    """Store tokens (bf16 bits [T][H][128]) unchanged: token (seq, pos) goes to
+    slot pos % 16 of physical page page_table[seq][pos // 16]."""
+    k_bits = np.asarray(k_bits, np.uint16)
+    v_bits = np.asarray(v_bits, np.uint16)
+    table = np.asarray(page_table)
+    ch = np.arange(D)
+    for t in range(len(seq_idx)):
+        pid = int(table[int(seq_idx[t]), int(pos[t]) // page_size])
+        slot = int(pos[t]) % page_size
+        blk = pages[pid]                        # [H][4096] view
+        blk[:, D * slot + ch] = k_bits[t]
+        blk[:, 2048 + 16 * ch + slot] = v_bits[t]
+
+
+def bf16_pages_gather(pages: np.ndarray, page_table, b: int, h: int, L: int, page_size: int = 16):
+    """K and V [L][128] (fp64, exact) of sequence b, KV head h from the BF16 pages."""
+    p = np.arange(L)
+    pid = np.asarray(page_table)[b, p // page_size].astype(np.int64)
+    slot = (p % page_size)[:, None]
+    ch = np.arange(D)[None, :]
+    blocks = pages[pid, h]                      # [L][4096]
+    K = np.take_along_axis(blocks, D * slot + ch, axis=1)
+    V = np.take_along_axis(blocks, 2048 + 16 * ch + slot, axis=1)
+    return bf16_to_f64(K), bf16_to_f64(V)
+
+
+def decode_bf16_paged(pages: np.ndarray, q_bits, page_table, seq_lens, num_kv_heads: int,
+                      sm_scale: float, batches=None, heads=None):
+    """Plain decode attention over the all-BF16 paged cache, fp64:
+    out[b, hq] = softmax(sm_scale * q . K^T) V over the L = seq_lens[b] tokens
+    of KV head hq // G.  L == 0 gives zeros.  ``batches``/``heads`` restrict the
+    computation to a sample (others are left at zero)."""
+    q = bf16_to_f64(q_bits)
+    B, Hq, _ = q.shape
+    G = Hq // num_kv_heads
+    out = np.zeros((B, Hq, D))
+    batches = range(B) if batches is None else batches
+    kv_heads = range(num_kv_heads) if heads is None else heads
+    for b in batches:
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        for h in kv_heads:
+            K, V = bf16_pages_gather(pages, page_table, b, h, L)
+            for hq in range(h * G, (h + 1) * G):
+                logits = sm_scale * (K @ q[b, hq])
+                p = np.exp(logits - logits.max())
+                out[b, hq] = (p @ V) / p.sum()
     return out
 
 

@@ -114,3 +114,32 @@ def test_workspace_max_pages_limit():
     top = s.sink // 16 + 1023 * 512
     assert L.oscar_decode_workspace_bytes(ctypes.byref(s), 1, top) > 0
     assert L.oscar_decode_workspace_bytes(ctypes.byref(s), 1, top + 1) == 0
+
+
+def test_bf16_decode_argument_checks():
+    """The BF16 baseline decode: bad head counts, NaN scale, NULL pointers and
+    small or misaligned workspaces are rejected on the host; batch 0 is a no-op."""
+    L = lib.load()
+    need = L.oscar_bf16_decode_workspace_bytes(8, 32, 28, 6250)
+    assert need >= 28 * 32 * 16 * (128 * 4 + 8)   # at least 16 ranges per (sequence, KV head) at 100K
+    for h, hq in ((0, 8), (8, 30), (1, 9)):
+        assert L.oscar_bf16_decode_workspace_bytes(h, hq, 2, 10) == 0
+        assert L.oscar_bf16_decode_attn(h, hq, 1, 1, 1, 10, 1, 2, 0.088, 1, 256, 1 << 30, None) == 1
+    assert L.oscar_bf16_decode_workspace_bytes(8, 32, 2, 0) == 0
+    args = lambda **kw: dict(dict(pages=1, q=1, table=1, mp=6250, lens=1, B=28, sc=0.088, out=1, ws=256, n=need), **kw)
+    call = lambda a: L.oscar_bf16_decode_attn(8, 32, a["pages"], a["q"], a["table"], a["mp"], a["lens"], a["B"],
+                                              a["sc"], a["out"], a["ws"], a["n"], None)
+    assert call(args(n=need - 1)) == 2
+    assert call(args(ws=257)) == 1
+    assert call(args(pages=None)) == 1
+    assert call(args(sc=float("inf"))) == 1
+    assert call(args(mp=0)) == 1
+    assert call(args(B=0, ws=None, n=0)) == 0
+    assert a_grows(L)
+
+
+def a_grows(L):
+    a = L.oscar_bf16_decode_workspace_bytes(8, 32, 1, 100)
+    b = L.oscar_bf16_decode_workspace_bytes(8, 32, 2, 100)
+    c = L.oscar_bf16_decode_workspace_bytes(8, 32, 2, 10000)
+    return 0 < a < b < c
