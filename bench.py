@@ -351,6 +351,22 @@ def main():
         f"INT2 decode_attn is {b16_us / (dec_avg_ms * 1e3):.2f}x faster")
     del b16_pages, b16_ws, b16_call
 
+    # ---- practical read ceiling: one plain stream over 8 GiB (library probe) ----
+    torch.cuda.empty_cache()
+    probe_buf = torch.ones(8 << 30, dtype=torch.uint8, device=dev)
+    probe_sink = torch.empty(lib.read_probe_sink_bytes(), dtype=torch.uint8, device=dev)
+    probe = lib.prepare_read_probe(probe_buf, probe_sink)
+    probe()
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for e0, e1 in rev:
+        e0.record()
+        probe()
+        e1.record()
+    torch.cuda.synchronize()
+    read_gbs = (8 << 30) / (1e-3 * statistics.median(e0.elapsed_time(e1) for e0, e1 in rev)) / 1e9
+    log(f"read probe: {read_gbs:.0f} GB/s (decode_attn at {achieved / read_gbs:.1%} of it)")
+    del probe_buf, probe_sink, probe
+
     cpu = None
     if not args.no_cpu_baseline:
         t_unit, reps, threads = cpu_baseline(H, NL, int(lens.max()))
@@ -376,7 +392,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "decode_attn (rotate_q + split + reduce), per layer",
-                     "bytes_per_launch": dbytes, "avg_launch_us": dec_avg_ms * 1e3},
+                     "bytes_per_launch": dbytes, "avg_launch_us": dec_avg_ms * 1e3,
+                     "practical_read_gbs": read_gbs, "frac_of_practical": achieved / read_gbs},
         "kv_write_prefill": {"tokens": n_pre, "kv_heads": H, "us": pre_us, "tokens_per_s": n_pre / (pre_us * 1e-6),
                              "bytes": pre_bytes, "achieved_gbs": pre_gbs, "frac": pre_gbs / PEAK_HBM_GBS},
         "bf16_baseline": {"kernel": "bf16_decode_attn (split + reduce) over an all-BF16 paged cache, per layer",

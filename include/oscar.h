@@ -192,6 +192,16 @@ int oscar_bf16_decode_attn(int32_t num_kv_heads, int32_t num_q_heads, const uint
                            const int32_t* seq_lens, int32_t batch, float sm_scale, uint16_t* out,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Measurement aid, not part of the method: streams `bytes` (a positive
+ * multiple of 16, 16-byte aligned device buffer) once with plain 16-byte
+ * loads and writes one word per thread to `sink` (device, at least
+ * oscar_read_probe_sink_bytes() bytes).  Timing it gives the HBM read rate
+ * a plain stream reaches on the device: the practical ceiling reported next
+ * to the 8 TB/s specification for the bandwidth-bound decode.  Returns
+ * OSCAR_OK, OSCAR_EINVAL, OSCAR_ENOWS or OSCAR_EHIP. */
+size_t oscar_read_probe_sink_bytes(void);
+int oscar_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_bytes, hipStream_t stream);
+
 /* calibrate_layer -- HOST, offline: the calibration of [es] 2.2 A (steps 1-4)
  * and [ru] paragraph 2 for one layer, in fp64 on host memory.
  *   q_cal  host double [H_kv][gqa][num_samples][128] calibration queries

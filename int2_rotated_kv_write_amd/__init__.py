@@ -11,7 +11,8 @@ from ._native import load, library_path
 from .api import (
     CacheBuffers, CacheShape, OscarError, allocate_cache, bf16_decode_attn,
     bf16_decode_workspace_bytes, calibrate_layer, decode_attn, decode_workspace_bytes, kv_write,
-    prepare_bf16_decode_attn, prepare_decode_attn, prepare_kv_write, status_string,
+    prepare_bf16_decode_attn, prepare_decode_attn, prepare_kv_write, prepare_read_probe,
+    read_probe_sink_bytes, status_string,
 )
 
 __all__ = [
@@ -19,4 +20,5 @@ __all__ = [
     "allocate_cache", "kv_write", "decode_attn", "decode_workspace_bytes",
     "calibrate_layer", "status_string", "prepare_kv_write", "prepare_decode_attn",
     "bf16_decode_attn", "bf16_decode_workspace_bytes", "prepare_bf16_decode_attn",
+    "prepare_read_probe", "read_probe_sink_bytes",
 ]

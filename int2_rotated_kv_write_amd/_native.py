@@ -25,6 +25,7 @@ class OscarLayer(ctypes.Structure):
 
 EXPORTS = ("oscar_kv_write", "oscar_decode_workspace_bytes", "oscar_decode_attn",
            "oscar_bf16_decode_workspace_bytes", "oscar_bf16_decode_attn",
+           "oscar_read_probe_sink_bytes", "oscar_read_probe",
            "oscar_calibrate_layer", "oscar_status_string", "oscar_last_error")
 
 
@@ -54,6 +55,10 @@ def load() -> ctypes.CDLL:
     lib.oscar_bf16_decode_attn.argtypes = [c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_i32, c_ptr, c_i32,
                                            ctypes.c_float, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]
     lib.oscar_bf16_decode_attn.restype = ctypes.c_int
+    lib.oscar_read_probe_sink_bytes.argtypes = []
+    lib.oscar_read_probe_sink_bytes.restype = ctypes.c_size_t
+    lib.oscar_read_probe.argtypes = [c_ptr, ctypes.c_size_t, c_ptr, ctypes.c_size_t, c_ptr]
+    lib.oscar_read_probe.restype = ctypes.c_int
     dp = ctypes.POINTER(ctypes.c_double)
     lib.oscar_calibrate_layer.argtypes = [c_i32, c_i32, c_i32, dp, dp, dp, ctypes.c_double,
                                           ctypes.c_double, c_ptr, c_ptr,

@@ -273,3 +273,17 @@ def prepare_bf16_decode_attn(num_kv_heads: int, num_q_heads: int, pages, q, page
     args = _bf16_decode_args(num_kv_heads, num_q_heads, pages, q, page_table, seq_lens, out, workspace,
                              sm_scale, stream)
     return PreparedCall(load().oscar_bf16_decode_attn, args, (pages, q, page_table, seq_lens, out, workspace))
+
+
+def read_probe_sink_bytes() -> int:
+    return int(load().oscar_read_probe_sink_bytes())
+
+
+def prepare_read_probe(buf, sink, stream=None) -> PreparedCall:
+    """oscar_read_probe (measurement aid): one plain read of the whole device
+    tensor `buf`; `sink` is a uint8 device tensor of read_probe_sink_bytes()."""
+    if not buf.is_cuda or not sink.is_cuda or not buf.is_contiguous():
+        raise OscarError("read probe buffers must be contiguous device tensors")
+    nbytes = buf.numel() * buf.element_size()
+    args = (buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * sink.element_size(), _stream(stream))
+    return PreparedCall(load().oscar_read_probe, args, (buf, sink))

@@ -34,6 +34,7 @@ constexpr int kB16Block = 8192;
 constexpr int kB16VOff = 4096;
 constexpr int kB16MaxPages = 512;   // pages per range (a wave keeps its page ids in 2 VGPRs)
 constexpr int kB16Reduce = 32;
+constexpr int kB16Ahead = 3;     // pages in flight per wave while one is processed
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 
@@ -187,22 +188,23 @@ __global__ __launch_bounds__(256) void b16_split_kernel(B16Args a) {
     }
   };
 
-  // two pages in flight while one is processed; unrolled over the 3 buffers so
-  // each buffer stays in fixed registers.  The prefetch is unconditional (past
-  // the wave's last page it reloads that page, which is still in L2): with a
-  // conditional one the compiler's wait before each page became vmcnt(0),
-  // which also waited for the pages behind it.
-  B16Page buf[3];
+  // kB16Ahead pages in flight while one is processed; unrolled over the
+  // buffers so each stays in fixed registers.  The prefetch is unconditional
+  // (past the wave's last page it reloads that page, which is still in L2):
+  // with a conditional one the compiler's wait before each page became
+  // vmcnt(0), which also waited for the pages behind it.
+  constexpr int NB = kB16Ahead + 1;
+  B16Page buf[NB];
   if (n_w > 0) {
-    load_b16_page(buf[0], blk_of(0), koff, voff);
-    load_b16_page(buf[1], blk_of(min(1, n_w - 1)), koff, voff);
-  }
-  for (int j0 = 0; j0 < n_w; j0 += 3) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+    for (int u = 0; u < kB16Ahead; ++u) load_b16_page(buf[u], blk_of(min(u, n_w - 1)), koff, voff);
+  }
+  for (int j0 = 0; j0 < n_w; j0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
       const int j = j0 + u;
       if (j >= n_w) break;
-      load_b16_page(buf[(u + 2) % 3], blk_of(min(j + 2, n_w - 1)), koff, voff);
+      load_b16_page(buf[(u + kB16Ahead) % NB], blk_of(min(j + kB16Ahead, n_w - 1)), koff, voff);
       process(buf[u], j);
     }
   }
@@ -328,4 +330,34 @@ int launch_bf16_decode(const B16Launch& L, hipStream_t stream) {
   return hipGetLastError() != hipSuccess;
 }
 
+}  // namespace oscar
+
+// ---------------------------------------------------------------------------
+// Read-bandwidth probe: streams `bytes` (a multiple of 16) once with 16-byte
+// loads, 8 per thread in flight, grid-stride, and stores one xor-word per
+// thread.  Its duration gives the HBM read rate a plain stream reaches on the
+// device, the practical ceiling next to the 8 TB/s specification.
+// ---------------------------------------------------------------------------
+namespace oscar {
+namespace {
+constexpr int kProbeUnroll = 8;
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16, uint32_t* sink) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 256 * kProbeUnroll;
+  for (size_t i = (size_t)blockIdx.x * 256 * kProbeUnroll + threadIdx.x; i < n16; i += stride) {
+    uint4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) v[u] = i + 256 * u < n16 ? p[i + 256 * u] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+}  // namespace
+
+int launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<const uint4*>(buf),
+                     bytes / 16, sink);
+  return hipGetLastError() != hipSuccess;
+}
 }  // namespace oscar

@@ -67,5 +67,7 @@ struct B16Launch {
 int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream);
 int launch_decode(const DecodeLaunch& L, hipStream_t stream);
 int launch_bf16_decode(const B16Launch& L, hipStream_t stream);
+int launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+constexpr int kProbeBlocks = 4096;
 
 }  // namespace oscar

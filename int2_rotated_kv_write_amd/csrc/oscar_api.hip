@@ -193,4 +193,15 @@ int oscar_bf16_decode_attn(int32_t num_kv_heads, int32_t num_q_heads, const uint
   return OSCAR_OK;
 }
 
+size_t oscar_read_probe_sink_bytes(void) { return (size_t)oscar::kProbeBlocks * 256 * sizeof(uint32_t); }
+
+int oscar_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_bytes, hipStream_t stream) {
+  if (!buf || !sink) return fail(OSCAR_EINVAL, "NULL buffer%s");
+  if (bytes == 0 || bytes % 16 != 0) return fail(OSCAR_EINVAL, "bytes must be a positive multiple of 16%s");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return fail(OSCAR_EINVAL, "buffer not 16-byte aligned%s");
+  if (sink_bytes < oscar_read_probe_sink_bytes()) return fail(OSCAR_ENOWS, "sink smaller than required%s");
+  if (oscar::launch_read_probe(buf, bytes, sink, oscar::kProbeBlocks, stream)) return hip_fail("read probe launch");
+  return OSCAR_OK;
+}
+
 }  // extern "C"

@@ -143,3 +143,15 @@ def a_grows(L):
     b = L.oscar_bf16_decode_workspace_bytes(8, 32, 2, 100)
     c = L.oscar_bf16_decode_workspace_bytes(8, 32, 2, 10000)
     return 0 < a < b < c
+
+
+def test_read_probe_argument_checks():
+    L = lib.load()
+    need = L.oscar_read_probe_sink_bytes()
+    assert need > 0
+    assert L.oscar_read_probe(None, 1 << 20, 256, need, None) == 1
+    assert L.oscar_read_probe(256, 1 << 20, None, need, None) == 1
+    assert L.oscar_read_probe(256, 0, 256, need, None) == 1
+    assert L.oscar_read_probe(256, 100, 256, need, None) == 1
+    assert L.oscar_read_probe(264, 1 << 20, 256, need, None) == 1
+    assert L.oscar_read_probe(256, 1 << 20, 256, need - 1, None) == 2
