@@ -202,6 +202,25 @@ int oscar_bf16_decode_attn(int32_t num_kv_heads, int32_t num_q_heads, const uint
 size_t oscar_read_probe_sink_bytes(void);
 int oscar_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_bytes, hipStream_t stream);
 
+/* decode_step -- one decode step of a layer in one call: exactly
+ * oscar_kv_write(shape, layer, k, v, seq_idx, pos, num_tokens, page_table,
+ * max_pages, seq_lens_after) followed by oscar_decode_attn(shape, layer, q,
+ * page_table, max_pages, seq_lens, batch, sm_scale, out, workspace,
+ * workspace_bytes), with the same arguments, checks, results and return codes
+ * ([it] "Architettura del Sistema di Serving e Layout di Memoria": the new
+ * token is written rotated and quantized, then attention reads the mixed
+ * cache).  Every argument of both calls is checked before anything is
+ * launched.  The token writes and the query rotation share the first launch
+ * (they touch disjoint memory), which saves one dependent launch per layer;
+ * nothing else differs.  num_tokens == 0 (or k and v both NULL) decodes only;
+ * batch == 0 writes only. */
+int oscar_decode_step(const oscar_shape_t* shape, const oscar_layer_t* layer,
+                      const uint16_t* k, const uint16_t* v, const int32_t* seq_idx,
+                      const int32_t* pos, int32_t num_tokens, const int32_t* seq_lens_after,
+                      const uint16_t* q, const int32_t* page_table, int32_t max_pages,
+                      const int32_t* seq_lens, int32_t batch, float sm_scale, uint16_t* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* calibrate_layer -- HOST, offline: the calibration of [es] 2.2 A (steps 1-4)
  * and [ru] paragraph 2 for one layer, in fp64 on host memory.
  *   q_cal  host double [H_kv][gqa][num_samples][128] calibration queries

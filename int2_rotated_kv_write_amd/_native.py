@@ -23,7 +23,7 @@ class OscarLayer(ctypes.Structure):
                 ("clip_k", ctypes.c_float), ("clip_v", ctypes.c_float)]
 
 
-EXPORTS = ("oscar_kv_write", "oscar_decode_workspace_bytes", "oscar_decode_attn",
+EXPORTS = ("oscar_kv_write", "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_decode_step",
            "oscar_bf16_decode_workspace_bytes", "oscar_bf16_decode_attn",
            "oscar_read_probe_sink_bytes", "oscar_read_probe",
            "oscar_calibrate_layer", "oscar_status_string", "oscar_last_error")
@@ -50,6 +50,9 @@ def load() -> ctypes.CDLL:
     lib.oscar_decode_attn.argtypes = [SP, LP, c_ptr, c_ptr, c_i32, c_ptr, c_i32, ctypes.c_float,
                                       c_ptr, c_ptr, ctypes.c_size_t, c_ptr]
     lib.oscar_decode_attn.restype = ctypes.c_int
+    lib.oscar_decode_step.argtypes = [SP, LP, c_ptr, c_ptr, c_ptr, c_ptr, c_i32, c_ptr, c_ptr, c_ptr, c_i32,
+                                      c_ptr, c_i32, ctypes.c_float, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]
+    lib.oscar_decode_step.restype = ctypes.c_int
     lib.oscar_bf16_decode_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32]
     lib.oscar_bf16_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.oscar_bf16_decode_attn.argtypes = [c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_i32, c_ptr, c_i32,

@@ -203,6 +203,42 @@ def bf16_decode_attn(num_kv_heads: int, num_q_heads: int, pages, q, page_table, 
                                                             seq_lens, out, workspace, sm_scale, stream)))
 
 
+def _decode_step_args(shape: CacheShape, cache: CacheBuffers, k, v, seq_idx, pos, seq_lens_after, q, page_table,
+                      seq_lens, out, workspace, sm_scale, stream):
+    import torch
+    _check_cache(shape, cache)
+    T = int(seq_idx.numel())
+    H = shape.num_kv_heads
+    B = int(seq_lens.numel())
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if page_table.dim() != 2:
+        raise OscarError("page_table must be [num_slots][max_pages]")
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise OscarError("workspace must be a uint8 device tensor")
+    cs, cl = shape.c(), cache.c()
+    args = (ctypes.byref(cs), ctypes.byref(cl),
+            _dev(k, torch.bfloat16, "k", (T, H, HEAD_DIM)), _dev(v, torch.bfloat16, "v", (T, H, HEAD_DIM)),
+            _dev(seq_idx, torch.int32, "seq_idx", (T,)), _dev(pos, torch.int32, "pos", (T,)), T,
+            _dev(seq_lens_after, torch.int32, "seq_lens_after"),
+            _dev(q, torch.bfloat16, "q", (B, shape.num_q_heads, HEAD_DIM)),
+            _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
+            _dev(seq_lens, torch.int32, "seq_lens", (B,)), B, float(sm_scale),
+            _dev(out, torch.bfloat16, "out", (B, shape.num_q_heads, HEAD_DIM)),
+            workspace.data_ptr(), workspace.numel(), _stream(stream))
+    return args, (cs, cl, k, v, seq_idx, pos, seq_lens_after, q, page_table, seq_lens, out, workspace)
+
+
+def decode_step(shape: CacheShape, cache: CacheBuffers, k, v, seq_idx, pos, seq_lens_after, q, page_table,
+                seq_lens, out, workspace, sm_scale: float | None = None, stream=None) -> None:
+    """oscar_decode_step: kv_write of the new tokens (k, v bfloat16 [T][H_kv][128]
+    at (seq_idx, pos)), then decode_attn of q (bfloat16 [B][Hq][128]) over
+    seq_lens, in one call."""
+    args, _keep = _decode_step_args(shape, cache, k, v, seq_idx, pos, seq_lens_after, q, page_table, seq_lens,
+                                    out, workspace, sm_scale, stream)
+    _check(load().oscar_decode_step(*args))
+
+
 def calibrate_layer(q_cal: np.ndarray, k_cal: np.ndarray, v_cal: np.ndarray, sm_scale: float,
                     quantile: float = 0.999, num_threads: int = 0):
     """oscar_calibrate_layer (host, offline).  q_cal float64 [H][G][N][128],
@@ -287,3 +323,10 @@ def prepare_read_probe(buf, sink, stream=None) -> PreparedCall:
     nbytes = buf.numel() * buf.element_size()
     args = (buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * sink.element_size(), _stream(stream))
     return PreparedCall(load().oscar_read_probe, args, (buf, sink))
+
+
+def prepare_decode_step(shape: CacheShape, cache: CacheBuffers, k, v, seq_idx, pos, seq_lens_after, q, page_table,
+                        seq_lens, out, workspace, sm_scale: float | None = None, stream=None) -> PreparedCall:
+    args, keep = _decode_step_args(shape, cache, k, v, seq_idx, pos, seq_lens_after, q, page_table, seq_lens,
+                                   out, workspace, sm_scale, stream)
+    return PreparedCall(load().oscar_decode_step, args, keep)

@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "kv_write_body.h"
 
 namespace oscar {
 
@@ -67,12 +68,21 @@ __device__ __forceinline__ int int2_end(int L, int sink, int recent) {   // INT2
 // ---------------------------------------------------------------------------
 constexpr int kSideThreads = 256;
 
-__global__ __launch_bounds__(kSideThreads) void rotate_q_kernel(DecodeArgs a) {
-  __shared__ uint4 Us[kHeadDim * kHeadDim / 8];           // U_K[h], row-major bf16
-  __shared__ float qv[kMaxGqa][kHeadDim];
-  __shared__ float y[kMaxGqa][kHeadDim];
-  __shared__ uint16_t qh[kMaxGqa][kHeadDim], ql[kMaxGqa][kHeadDim];
-  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H, G = a.G;
+struct RotQSmem {
+  uint4 Us[kHeadDim * kHeadDim / 8];   // U_K[h], row-major bf16
+  float qv[kMaxGqa][kHeadDim];
+  float y[kMaxGqa][kHeadDim];
+  uint16_t qh[kMaxGqa][kHeadDim], ql[kMaxGqa][kHeadDim];
+};
+
+// block for (sequence, KV head) bh = b H + h
+__device__ __forceinline__ void rotate_q_block(const DecodeArgs& a, RotQSmem& sm, int bh) {
+  uint4* Us = sm.Us;
+  auto& qv = sm.qv;
+  auto& y = sm.y;
+  auto& qh = sm.qh;
+  auto& ql = sm.ql;
+  const int b = bh / a.H, h = bh % a.H, G = a.G;
   const int tid = threadIdx.x, j = tid & (kHeadDim - 1), hs = tid >> 7;
   const uint4* U = reinterpret_cast<const uint4*>(a.u_k + (size_t)h * kHeadDim * kHeadDim);
   // issue every global load before the first LDS store (one memory latency, not eight)
@@ -170,6 +180,34 @@ __global__ __launch_bounds__(kSideThreads) void rotate_q_kernel(DecodeArgs a) {
         rec->qsum[gr] = qs;
       }
     }
+  }
+}
+
+__global__ __launch_bounds__(kSideThreads) void rotate_q_kernel(DecodeArgs a) {
+  __shared__ RotQSmem sm;
+  rotate_q_block(a, sm, blockIdx.x);
+}
+
+// First launch of a decode step: blocks [0, n_write) write the step's new tokens
+// (kv_write blocks over a (gx, gy, gz) grid, flattened x fastest), the rest rotate
+// the queries (one per (sequence, KV head)).  The two touch disjoint memory: the
+// writes go to the page pool, sink and ring; the rotation reads q and U_K and
+// writes the workspace's query records.
+union StepFrontSmem {
+  KvWriteSmem kw;
+  RotQSmem rq;
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void step_front_kernel(
+    KvWriteArgs w, DecodeArgs d, int n_write, int gx, int gy) {
+  static_assert(kSideThreads == 256, "both halves run 256-thread blocks");
+  __shared__ StepFrontSmem sm;
+  const int bid = blockIdx.x;
+  if (bid < n_write) {
+    const int bx = bid % gx, rest = bid / gx;
+    kv_write_block(w, sm.kw, bx, gx, rest % gy, rest / gy);
+  } else {
+    rotate_q_block(d, sm.rq, bid - n_write);
   }
 }
 
@@ -856,8 +894,8 @@ DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   return p;
 }
 
-int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
-  if (L.batch == 0) return 0;
+namespace {
+DecodeArgs make_decode_args(const DecodeLaunch& L) {
   DecodeArgs a{};
   a.pages = L.pages;
   a.k_sink = L.k_sink;
@@ -893,19 +931,43 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.n_split = L.plan.n_split;
   a.n_bsplit = L.plan.n_bsplit;
   a.n_total = L.plan.n_total;
-  hipLaunchKernelGGL(rotate_q_kernel, dim3(L.batch * L.num_kv_heads), dim3(kSideThreads), 0, stream, a);
+  return a;
+}
+
+int launch_split_reduce(const DecodeArgs& a, int B, hipStream_t stream) {
   switch (a.G) {
-    case 1: launch_split<1>(a, L.batch, stream); break;
-    case 2: launch_split<2>(a, L.batch, stream); break;
-    case 3: launch_split<3>(a, L.batch, stream); break;
-    case 4: launch_split<4>(a, L.batch, stream); break;
-    case 5: launch_split<5>(a, L.batch, stream); break;
-    case 6: launch_split<6>(a, L.batch, stream); break;
-    case 7: launch_split<7>(a, L.batch, stream); break;
-    case 8: launch_split<8>(a, L.batch, stream); break;
+    case 1: launch_split<1>(a, B, stream); break;
+    case 2: launch_split<2>(a, B, stream); break;
+    case 3: launch_split<3>(a, B, stream); break;
+    case 4: launch_split<4>(a, B, stream); break;
+    case 5: launch_split<5>(a, B, stream); break;
+    case 6: launch_split<6>(a, B, stream); break;
+    case 7: launch_split<7>(a, B, stream); break;
+    case 8: launch_split<8>(a, B, stream); break;
     default: return 1;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+}  // namespace
+
+int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
+  if (L.batch == 0) return 0;
+  const DecodeArgs a = make_decode_args(L);
+  hipLaunchKernelGGL(rotate_q_kernel, dim3(L.batch * L.num_kv_heads), dim3(kSideThreads), 0, stream, a);
+  return launch_split_reduce(a, L.batch, stream);
+}
+
+int launch_decode_step(const KvWriteLaunch& W, const DecodeLaunch& D, hipStream_t stream) {
+  KvWriteArgs w{};
+  dim3 g;
+  const bool writes = kv_write_setup(W, device_cus(), w, g);
+  if (D.batch == 0) return writes ? launch_kv_write(W, stream) : 0;
+  if (!writes) return launch_decode(D, stream);
+  const DecodeArgs a = make_decode_args(D);
+  const int n_write = (int)(g.x * g.y * g.z);
+  hipLaunchKernelGGL(step_front_kernel, dim3(n_write + D.batch * D.num_kv_heads), dim3(256), 0, stream, w, a,
+                     n_write, (int)g.x, (int)g.y);
+  return launch_split_reduce(a, D.batch, stream);
 }
 
 }  // namespace oscar

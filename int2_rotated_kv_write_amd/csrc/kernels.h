@@ -64,7 +64,9 @@ struct B16Launch {
   B16Plan plan;
 };
 
+int device_cus();   // compute units of the current device
 int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream);
+int launch_decode_step(const KvWriteLaunch& W, const DecodeLaunch& D, hipStream_t stream);
 int launch_decode(const DecodeLaunch& L, hipStream_t stream);
 int launch_bf16_decode(const B16Launch& L, hipStream_t stream);
 int launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);

@@ -18,290 +18,15 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "kv_write_body.h"
 
 namespace oscar {
 
 namespace {
 
-constexpr int kUtRow = kHeadDim + 8;   // U^T row stride in LDS (272 B): conflict-free fragment reads
-constexpr float kInvSqrt128 = 0.08838834764831845f;
-
-// LDS row of channel j in the V transposition buffer: channel bits 3, 4 (the lane's
-// quarter when the codes are written) go to row bits 0, 1 and bits 1, 2 to row bits 2, 3,
-// so both the byte writes (4 quarters x 16 tokens) and the 16-byte row reads (16
-// consecutive channels) fall in distinct LDS banks.
-__device__ __forceinline__ int vrow(int j) {
-  return ((j >> 3) & 3) | (((j >> 1) & 3) << 2) | ((j & 1) << 4) | (j & 0x60);
-}
-
-struct KvWriteArgs {
-  const uint16_t* x[2];
-  const uint16_t* u[2];
-  float clip[2];
-  uint16_t* sink[2];
-  uint16_t* ring[2];
-  uint8_t* pages;
-  const int32_t* seq_idx;
-  const int32_t* pos;
-  const int32_t* page_table;
-  const int32_t* lens_after;
-  int32_t num_tokens, num_heads, max_pages, sink_len, recent, num_tiles;
-  int32_t kind_of_z[2];
-};
-
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void kv_write_kernel(KvWriteArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ut[kHeadDim * kUtRow];      // U^T, rows padded
-  __shared__ __attribute__((aligned(16))) uint8_t vbytes[4][kHeadDim][16];    // V transposition
-
-  const int kind = a.kind_of_z[blockIdx.z];
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15;   // token within the tile (MFMA N index)
-  const int q = lane >> 4;   // channel quarter: channels 16mt + 4q + r
-
-  const uint16_t* X = a.x[kind];
-  // per-tile inputs, loaded one tile ahead so their latency overlaps the previous tile's math
-  // (the first tile's before U^T is staged)
-  struct TileIn {
-    uint4 x[4];   // x[t][h][32ks + 8q .. +7]
-    int b, p;
-    bool valid;
-  };
-  auto load_tile = [&](int tg, TileIn& in) {   // tile 4 tg + wave
-    const int t = (tg * 4 + wave) * 16 + n;
-    in.valid = t < a.num_tokens;
-    in.b = in.valid ? a.seq_idx[t] : 0;
-    in.p = in.valid ? a.pos[t] : 0;
-    const uint16_t* xrow = X + ((size_t)(in.valid ? t : 0) * a.num_heads + h) * kHeadDim;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      in.x[ks] = in.valid ? *reinterpret_cast<const uint4*>(xrow + 32 * ks + 8 * q) : make_uint4(0, 0, 0, 0);
-  };
-  const int n_groups = (a.num_tiles + 3) / 4;   // groups of four 16-token tiles, one per wave
-  TileIn nxt;
-  load_tile(blockIdx.x, nxt);
-
-  // ---- stage U^T: ut[j][i] = U[i][j]; consecutive threads take consecutive rows i,
-  // so each LDS store instruction writes consecutive halfwords ----
-  const uint16_t* U = a.u[kind] + (size_t)h * kHeadDim * kHeadDim;
-  {
-    constexpr int kPer = kHeadDim * kHeadDim / 8 / 256;
-    uint4 v[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = tid + 256 * k, i = e & (kHeadDim - 1), jb = e >> 7;
-      v[k] = reinterpret_cast<const uint4*>(U + i * kHeadDim)[jb];
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = tid + 256 * k, i = e & (kHeadDim - 1), j0 = (e >> 7) * 8;
-      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        ut[(j0 + 2 * q2) * kUtRow + i] = (uint16_t)(w[q2] & 0xFFFFu);
-        ut[(j0 + 2 * q2 + 1) * kUtRow + i] = (uint16_t)(w[q2] >> 16);
-      }
-    }
-  }
-  __syncthreads();
-
-  // A fragment (mt, ks): rows = output channel 16mt + n', cols = input channels
-  // 32ks + 8q' .. +7 (the same k mapping as the B fragment below), read from LDS for
-  // every tile: holding all 32 in registers would cost 128 VGPRs and a third of the
-  // waves per SIMD.
-  auto afrag = [&](int mt, int ks) {
-    return *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kUtRow + 32 * ks + 8 * q]);
-  };
-
-  const float clip_s = a.clip[kind] * 11.313708498984761f;   // clip threshold before the 1/sqrt(128)
-  uint16_t* sink_buf = a.sink[kind];
-  uint16_t* ring_buf = a.ring[kind];
-  const int params_off = kind == 0 ? kKParams : kVParams;
-
-
-  // the block walks tile groups blockIdx.x, + gridDim.x, ...: U^T is staged once per block
-  for (int tg = blockIdx.x; tg < n_groups; tg += gridDim.x) {
-    const int tile = tg * 4 + wave;
-    if (tile >= a.num_tiles) break;   // wave-uniform (only in the last group)
-    const TileIn cur = nxt;
-    if (tg + (int)gridDim.x < n_groups) load_tile(tg + gridDim.x, nxt);
-    const bool valid = cur.valid;
-    const int b = cur.b, p = cur.p;
-    const bool is_int2 = valid && p >= a.sink_len;
-    // this token's page block (its id is loaded before the math that hides the latency)
-    const int32_t pid = is_int2 ? a.page_table[(size_t)b * a.max_pages + (p >> 4)] : 0;
-
-    bf16x8 bfrag[4];
-    uint4 xraw[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      xraw[ks] = cur.x[ks];
-      bfrag[ks] = __builtin_bit_cast(bf16x8, xraw[ks]);
-    }
-
-    // ---- bf16 copies (sink rows, recent ring) ----
-    if (valid) {
-      if (p < a.sink_len) {
-        uint16_t* row = sink_buf + (((size_t)b * a.num_heads + h) * a.sink_len + p) * kHeadDim;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(row + 32 * ks + 8 * q) = xraw[ks];
-      }
-      const int L_after = a.lens_after[b];
-      if (p >= max(a.sink_len, L_after - a.recent)) {
-        uint16_t* row = ring_buf + (((size_t)b * a.num_heads + h) * a.recent + (p % a.recent)) * kHeadDim;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(row + 32 * ks + 8 * q) = xraw[ks];
-      }
-    }
-
-    // ---- y^T = U^T x^T ----
-    float v[32];   // v[4*mt + r] = channel 16mt + 4q + r of token n
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag(mt, ks), bfrag[ks], acc, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * mt + r] = acc[r];
-    }
-
-    // ---- Walsh-Hadamard over the 128 channels (Sylvester order) ----
-    // in-register bits: index bits 0,1 (channel bits 0,1) and 2,3,4 (channel bits 4,5,6)
-#pragma unroll
-    for (int s = 1; s < 32; s <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i & s) continue;
-        const float x0 = v[i], x1 = v[i | s];
-        v[i] = x0 + x1;
-        v[i | s] = x0 - x1;
-      }
-    }
-    // cross-lane bits: channel bit 2 = lane bit 4, channel bit 3 = lane bit 5.  Registers
-    // x = v[i], y = v[i ^ 8] go through a permlane swap, which leaves in each lane the
-    // (bit-clear, bit-set) partner values of one of them; sum and difference are the
-    // butterfly outputs, and a second swap of (sum, difference) puts every result back
-    // in the lane and register it came from.
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i & 8) continue;
-      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
-      const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
-      r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
-      v[i] = __uint_as_float(r[0]);
-      v[i | 8] = __uint_as_float(r[1]);
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i & 8) continue;
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
-      const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
-      r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
-      v[i] = __uint_as_float(r[0]);
-      v[i | 8] = __uint_as_float(r[1]);
-    }
-
-    // ---- clip, group min/max (v holds the rotation times sqrt(128): the 1/sqrt(128)
-    // goes into the clip threshold, the group parameters and the code scale below) ----
-    // channel c = 16mt + 4q + r goes to post-rotation index j = bitrev7(c),
-    // whose group j/64 is bit 0 of c, i.e. r & 1.
-    float mn[2] = {INFINITY, INFINITY}, mx[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      v[i] = __builtin_amdgcn_fmed3f(v[i], -clip_s, clip_s);
-      mn[i & 1] = fminf(mn[i & 1], v[i]);
-      mx[i & 1] = fmaxf(mx[i & 1], v[i]);
-    }
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      mn[g] = wave_min_xor(mn[g], 16, 32);
-      mx[g] = wave_max_xor(mx[g], 16, 32);
-    }
-    uint32_t sbits[2], zbits[2];
-    float sf[2], zf[2], inv[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      sbits[g] = f32_to_f16_bits((mx[g] - mn[g]) * (kInvSqrt128 / 3.0f));
-      zbits[g] = f32_to_f16_bits(mn[g] * kInvSqrt128);   // = the smallest scaled value, rounded once
-      sf[g] = f16_bits_to_f32(sbits[g]);
-      zf[g] = f16_bits_to_f32(zbits[g]);
-      inv[g] = sf[g] > 0.f ? __builtin_amdgcn_rcpf(sf[g]) : 0.f;
-      zf[g] = -zf[g] * inv[g];          // t = w * inv - z * inv with w = v / sqrt(128)
-      inv[g] = inv[g] * kInvSqrt128;
-    }
-    float tq[32];   // (w - z) / s clamped to [0, 3]; rounded to the code where it is stored
-#pragma unroll
-    for (int i = 0; i < 32; ++i) tq[i] = __builtin_amdgcn_fmed3f(fmaf(v[i], inv[i & 1], zf[i & 1]), 0.f, 3.f);
-
-    // ---- store INT2 ----
-    // whole aligned page written by this tile?
-    const int b0 = __shfl(b, 0), p0 = __shfl(p, 0);
-    const bool full_page = __all(is_int2 && b == b0 && p == p0 + n && (p0 & 15) == 0);
-    uint8_t* blk = a.pages + ((size_t)pid * a.num_heads + h) * kBlockBytes;   // used only if is_int2
-    const int slot = p & 15;
-    if (kind == 0) {
-      // K, token-major: post-rotation channel j = 64 r0 + 32 r1 + 16 q0 + 8 q1 + bitrev3(mt)
-      // -> halfword (j / 8) = 8 r0 + 4 r1 + 2 q0 + q1, bit 2 * bitrev3(mt).
-      if (is_int2) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float hf = 0.f;   // sum of code * 4^k: exact in fp32 (16 bits)
-#pragma unroll
-          for (int mt = 0; mt < 8; ++mt) hf = fmaf(__builtin_rintf(tq[4 * mt + r]), (float)(1 << (2 * bitrev3(mt))), hf);
-          const uint32_t hw = (uint32_t)hf;
-          const int hidx = 8 * (r & 1) + 4 * (r >> 1) + 2 * (q & 1) + (q >> 1);
-          *reinterpret_cast<uint16_t*>(blk + kKCodes + 32 * slot + 2 * hidx) = (uint16_t)hw;
-        }
-      }
-    } else if (full_page) {
-      // V, channel-major, whole page: transpose through LDS, write whole words.  The code
-      // byte is the low byte of tq + 2^23 (adding 2^23 rounds to the nearest integer, ties
-      // to even, exactly like rint).
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int mt = i >> 2, r = i & 3;
-        const int j = 64 * (r & 1) + 32 * (r >> 1) + 16 * (q & 1) + 8 * (q >> 1) + bitrev3(mt);
-        vbytes[wave][vrow(j)][n] = (uint8_t)__float_as_uint(tq[i] + 8388608.0f);
-      }
-      wave_lds_sync();
-      // every lane of the tile holds the same page: lane 0's id
-      const uint8_t* page_blk = a.pages + ((size_t)__shfl(pid, 0) * a.num_heads + h) * kBlockBytes;
-      uint32_t words[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint4 by = *reinterpret_cast<const uint4*>(&vbytes[wave][vrow(2 * lane + c)][0]);
-        const uint32_t parts[4] = {by.x, by.y, by.z, by.w};
-        uint32_t wv = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t y = parts[k] | (parts[k] >> 6);
-          y = (y | (y >> 12)) & 0xFFu;   // 4 two-bit codes -> one byte
-          wv |= y << (8 * k);
-        }
-        words[c] = wv;
-      }
-      *reinterpret_cast<uint2*>(const_cast<uint8_t*>(page_blk) + kVCodes + 8 * lane) = make_uint2(words[0], words[1]);
-      wave_lds_sync();
-    } else if (is_int2) {
-      // V, partial page: merge this slot's two bits into each word atomically.
-      uint32_t* words = reinterpret_cast<uint32_t*>(blk + kVCodes);
-      const uint32_t clear = ~(3u << (2 * slot));
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int mt = i >> 2, r = i & 3;
-        const int j = 64 * (r & 1) + 32 * (r >> 1) + 16 * (q & 1) + 8 * (q >> 1) + bitrev3(mt);
-        const uint32_t code = (uint32_t)__builtin_rintf(tq[i]);
-        atomicAnd(&words[j], clear);
-        if (code) atomicOr(&words[j], code << (2 * slot));
-      }
-    }
-    if (is_int2 && q == 0) {
-      const uint32_t lo = sbits[0] | (zbits[0] << 16), hi = sbits[1] | (zbits[1] << 16);
-      *reinterpret_cast<uint2*>(blk + params_off + 8 * slot) = make_uint2(lo, hi);
-    }
-  }
+  __shared__ KvWriteSmem sm;
+  kv_write_block(a, sm, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z);
 }
 
 }  // namespace
@@ -320,37 +45,8 @@ int device_cus() {   // compute units of the current device (cached per device)
 
 int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream) {
   KvWriteArgs a{};
-  int nz = 0;
-  const uint16_t* xs[2] = {L.k, L.v};
-  for (int kind = 0; kind < 2; ++kind) {
-    a.x[kind] = xs[kind];
-    if (xs[kind]) a.kind_of_z[nz++] = kind;
-  }
-  if (nz == 0 || L.num_tokens == 0) return 0;
-  a.u[0] = L.u_k;
-  a.u[1] = L.u_v;
-  a.clip[0] = L.clip_k;
-  a.clip[1] = L.clip_v;
-  a.sink[0] = L.k_sink;
-  a.sink[1] = L.v_sink;
-  a.ring[0] = L.k_ring;
-  a.ring[1] = L.v_ring;
-  a.pages = L.pages;
-  a.seq_idx = L.seq_idx;
-  a.pos = L.pos;
-  a.page_table = L.page_table;
-  a.lens_after = L.seq_lens_after;
-  a.num_tokens = L.num_tokens;
-  a.num_heads = L.num_kv_heads;
-  a.max_pages = L.max_pages;
-  a.sink_len = L.sink;
-  a.recent = L.recent;
-  a.num_tiles = (L.num_tokens + 15) / 16;
-  // blocks per (KV head, K/V): enough for three resident blocks per CU over the whole
-  // grid (LDS and registers allow three), never more than there are tile groups
-  const int n_groups = (a.num_tiles + 3) / 4;
-  const int per_slice = std::max(1, (3 * device_cus() + L.num_kv_heads * nz - 1) / (L.num_kv_heads * nz));
-  dim3 grid(std::min(n_groups, per_slice), L.num_kv_heads, nz);
+  dim3 grid;
+  if (!kv_write_setup(L, device_cus(), a, grid)) return 0;   // nothing to write
   hipLaunchKernelGGL(kv_write_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -41,35 +41,27 @@ int hip_fail(const char* what) {
 
 }  // namespace
 
-extern "C" {
-
-const char* oscar_status_string(int status) {
-  switch (status) {
-    case OSCAR_OK: return "ok";
-    case OSCAR_EINVAL: return "invalid argument";
-    case OSCAR_ENOWS: return "workspace too small";
-    case OSCAR_EHIP: return "HIP error";
-    default: return "unknown status";
-  }
-}
-
-const char* oscar_last_error(void) { return g_last_error; }
-
-int oscar_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* k, const uint16_t* v,
-                   const int32_t* seq_idx, const int32_t* pos, int32_t num_tokens, const int32_t* page_table,
-                   int32_t max_pages, const int32_t* seq_lens_after, hipStream_t stream) {
+namespace {
+// Checks of a kv_write call; fills L.  *nothing is set when there is nothing to write.
+int prepare_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* k, const uint16_t* v,
+                     const int32_t* seq_idx, const int32_t* pos, int32_t num_tokens, const int32_t* page_table,
+                     int32_t max_pages, const int32_t* seq_lens_after, oscar::KvWriteLaunch& L, bool* nothing) {
+  *nothing = false;
   if (int rc = check_shape(shape)) return rc;
   if (!layer) return fail(OSCAR_EINVAL, "layer is NULL%s");
   if (num_tokens < 0) return fail(OSCAR_EINVAL, "num_tokens < 0%s");
   if (max_pages < 1) return fail(OSCAR_EINVAL, "max_pages must be >= 1%s");
-  if (num_tokens == 0 || (!k && !v)) return OSCAR_OK;
+  if (num_tokens == 0 || (!k && !v)) {
+    *nothing = true;
+    return OSCAR_OK;
+  }
   if (!seq_idx || !pos || !page_table || !seq_lens_after || !layer->pages)
     return fail(OSCAR_EINVAL, "NULL index array or pages%s");
   if (k && (!layer->u_k || !layer->k_ring || (shape->sink > 0 && !layer->k_sink) || !clip_ok(layer->clip_k)))
     return fail(OSCAR_EINVAL, "K half: NULL u_k/k_ring/k_sink or clip_k outside (0, 16384]%s");
   if (v && (!layer->u_v || !layer->v_ring || (shape->sink > 0 && !layer->v_sink) || !clip_ok(layer->clip_v)))
     return fail(OSCAR_EINVAL, "V half: NULL u_v/v_ring/v_sink or clip_v outside (0, 16384]%s");
-  oscar::KvWriteLaunch L{};
+  L = oscar::KvWriteLaunch{};
   L.k = k;
   L.v = v;
   L.u_k = layer->u_k;
@@ -90,26 +82,23 @@ int oscar_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer, const
   L.max_pages = max_pages;
   L.sink = shape->sink;
   L.recent = shape->recent;
-  if (oscar::launch_kv_write(L, stream)) return hip_fail("kv_write launch");
   return OSCAR_OK;
 }
 
-size_t oscar_decode_workspace_bytes(const oscar_shape_t* shape, int32_t batch, int32_t max_pages) {
-  if (check_shape(shape) || batch < 0 || max_pages < 1) return 0;
-  const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
-                                                         shape->recent, batch, max_pages);
-  return plan.n_total > oscar::kMaxItems ? 0 : plan.bytes;
-}
-
-int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q,
-                      const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t batch,
-                      float sm_scale, uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Checks of a decode_attn call; fills L.  *nothing is set for batch == 0.
+int prepare_decode(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q, const int32_t* page_table,
+                   int32_t max_pages, const int32_t* seq_lens, int32_t batch, float sm_scale, uint16_t* out,
+                   void* workspace, size_t workspace_bytes, oscar::DecodeLaunch& L, bool* nothing) {
+  *nothing = false;
   if (int rc = check_shape(shape)) return rc;
   if (!layer) return fail(OSCAR_EINVAL, "layer is NULL%s");
   if (batch < 0) return fail(OSCAR_EINVAL, "batch < 0%s");
   if (max_pages < 1) return fail(OSCAR_EINVAL, "max_pages must be >= 1%s");
   if (!std::isfinite(sm_scale)) return fail(OSCAR_EINVAL, "sm_scale is not finite%s");
-  if (batch == 0) return OSCAR_OK;
+  if (batch == 0) {
+    *nothing = true;
+    return OSCAR_OK;
+  }
   if (!q || !page_table || !seq_lens || !out || !layer->pages || !layer->k_ring || !layer->v_ring || !layer->u_k ||
       !layer->u_v || (shape->sink > 0 && (!layer->k_sink || !layer->v_sink)))
     return fail(OSCAR_EINVAL, "NULL tensor pointer%s");
@@ -119,7 +108,7 @@ int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, co
   if (plan.n_total > oscar::kMaxItems) return fail(OSCAR_EINVAL, "max_pages too large (sequences over ~8M tokens)%s");
   if (!workspace || workspace_bytes < plan.bytes) return fail(OSCAR_ENOWS, "workspace smaller than required%s");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned%s");
-  oscar::DecodeLaunch L{};
+  L = oscar::DecodeLaunch{};
   L.pages = layer->pages;
   L.k_sink = layer->k_sink;
   L.v_sink = layer->v_sink;
@@ -141,7 +130,78 @@ int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, co
   L.sink = shape->sink;
   L.recent = shape->recent;
   L.plan = plan;
+  return OSCAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* oscar_status_string(int status) {
+  switch (status) {
+    case OSCAR_OK: return "ok";
+    case OSCAR_EINVAL: return "invalid argument";
+    case OSCAR_ENOWS: return "workspace too small";
+    case OSCAR_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* oscar_last_error(void) { return g_last_error; }
+
+int oscar_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* k, const uint16_t* v,
+                   const int32_t* seq_idx, const int32_t* pos, int32_t num_tokens, const int32_t* page_table,
+                   int32_t max_pages, const int32_t* seq_lens_after, hipStream_t stream) {
+  oscar::KvWriteLaunch L;
+  bool nothing = false;
+  if (int rc = prepare_kv_write(shape, layer, k, v, seq_idx, pos, num_tokens, page_table, max_pages, seq_lens_after,
+                                L, &nothing))
+    return rc;
+  if (nothing) return OSCAR_OK;
+  if (oscar::launch_kv_write(L, stream)) return hip_fail("kv_write launch");
+  return OSCAR_OK;
+}
+
+size_t oscar_decode_workspace_bytes(const oscar_shape_t* shape, int32_t batch, int32_t max_pages) {
+  if (check_shape(shape) || batch < 0 || max_pages < 1) return 0;
+  const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
+                                                         shape->recent, batch, max_pages);
+  return plan.n_total > oscar::kMaxItems ? 0 : plan.bytes;
+}
+
+int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q,
+                      const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                      float sm_scale, uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  oscar::DecodeLaunch L;
+  bool nothing = false;
+  if (int rc = prepare_decode(shape, layer, q, page_table, max_pages, seq_lens, batch, sm_scale, out, workspace,
+                              workspace_bytes, L, &nothing))
+    return rc;
+  if (nothing) return OSCAR_OK;
   if (oscar::launch_decode(L, stream)) return hip_fail("decode launch");
+  return OSCAR_OK;
+}
+
+int oscar_decode_step(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* k, const uint16_t* v,
+                      const int32_t* seq_idx, const int32_t* pos, int32_t num_tokens, const int32_t* seq_lens_after,
+                      const uint16_t* q, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                      int32_t batch, float sm_scale, uint16_t* out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  oscar::KvWriteLaunch W;
+  oscar::DecodeLaunch D;
+  bool no_write = false, no_decode = false;
+  if (int rc = prepare_kv_write(shape, layer, k, v, seq_idx, pos, num_tokens, page_table, max_pages, seq_lens_after,
+                                W, &no_write))
+    return rc;
+  if (int rc = prepare_decode(shape, layer, q, page_table, max_pages, seq_lens, batch, sm_scale, out, workspace,
+                              workspace_bytes, D, &no_decode))
+    return rc;
+  int err = 0;
+  if (no_write && no_decode) return OSCAR_OK;
+  if (no_write) err = oscar::launch_decode(D, stream);
+  else if (no_decode) err = oscar::launch_kv_write(W, stream);
+  else err = oscar::launch_decode_step(W, D, stream);
+  if (err) return hip_fail("decode step launch");
   return OSCAR_OK;
 }
 

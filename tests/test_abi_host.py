@@ -155,3 +155,32 @@ def test_read_probe_argument_checks():
     assert L.oscar_read_probe(256, 100, 256, need, None) == 1
     assert L.oscar_read_probe(264, 1 << 20, 256, need, None) == 1
     assert L.oscar_read_probe(256, 1 << 20, 256, need - 1, None) == 2
+
+
+def test_decode_step_checks_both_halves_before_launching():
+    """decode_step = kv_write then decode_attn: a bad argument of either half is
+    rejected on the host (nothing launched); empty halves are no-ops."""
+    L = lib.load()
+    s = good_shape()
+    layer = OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1, clip_k=4.0, clip_v=4.0)
+    need = L.oscar_decode_workspace_bytes(ctypes.byref(s), 28, 6250)
+
+    def step(**kw):
+        a = dict(k=1, v=1, idx=1, pos=1, T=28, after=1, q=1, table=1, mp=6250, lens=1, B=28, sc=0.088, out=1,
+                 ws=256, n=need, shape=s, layer=layer)
+        a.update(kw)
+        return L.oscar_decode_step(ctypes.byref(a["shape"]), ctypes.byref(a["layer"]), a["k"], a["v"], a["idx"],
+                                   a["pos"], a["T"], a["after"], a["q"], a["table"], a["mp"], a["lens"], a["B"],
+                                   a["sc"], a["out"], a["ws"], a["n"], None)
+
+    assert step(shape=good_shape(head_dim=64)) == 1
+    assert step(T=-1) == 1                     # write half
+    assert step(idx=None) == 1
+    assert step(layer=OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1,
+                                 clip_k=0.0, clip_v=4.0)) == 1
+    assert step(sc=float("nan")) == 1          # decode half
+    assert step(q=None) == 1
+    assert step(n=need - 1) == 2
+    assert step(ws=257) == 1
+    assert step(T=0, B=0) == 0                 # both halves empty
+    assert step(k=None, v=None, B=0) == 0
