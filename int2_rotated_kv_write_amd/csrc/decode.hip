@@ -51,6 +51,7 @@ struct DecodeArgs {
   float sl2e;   // sm_scale * log2(e)
   float resc_thr;   // lazy rescale threshold tau: INT2 probabilities stay <= 2^tau
   int32_t H, Hq, G, B, max_pages, sink, recent, P, n_split, n_bsplit, n_total;
+  int32_t bchunk;   // BF16 tokens per BF16 item (a multiple of 64)
 };
 
 __device__ __forceinline__ int bf16_token_count(int L, int sink, int recent) {
@@ -262,7 +263,7 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, int b
   }
 }
 
-// BF16 sink + recent tokens, kBf16Chunk per item; the block's waves take 16-token
+// BF16 sink + recent tokens, a.bchunk per item; the block's waves take 16-token
 // groups round-robin and keep an online softmax across their groups; plain
 // (unrotated) q.
 template <int G>
@@ -298,7 +299,7 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
     uint32_t vv[16];   // V rows of the group's 16 tokens: channels 2 lane, + 1
   };
   auto load_round = [&](int round, RoundIn& in) {
-    const int jbase = chunk * kBf16Chunk + 16 * (4 * round + wave);
+    const int jbase = chunk * a.bchunk + 16 * (4 * round + wave);
     const int j = jbase + t;
 #pragma unroll
     for (int x = 0; x < 4; ++x) in.kd[x] = make_uint4(0, 0, 0, 0);
@@ -315,13 +316,14 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
   };
   RoundIn nxt;
   load_round(0, nxt);
-  for (int round = 0; round < kBf16Chunk / 64; ++round) {
-    const int jbase = chunk * kBf16Chunk + 16 * (4 * round + wave);
+  const int n_rounds = a.bchunk / 64;
+  for (int round = 0; round < n_rounds; ++round) {
+    const int jbase = chunk * a.bchunk + 16 * (4 * round + wave);
     if (jbase >= nb) break;   // wave-uniform
     const int j = jbase + t;
     const bool valid = j < nb;
     const RoundIn cur = nxt;
-    if (round + 1 < kBf16Chunk / 64 && jbase + 64 < nb) load_round(round + 1, nxt);
+    if (round + 1 < n_rounds && jbase + 64 < nb) load_round(round + 1, nxt);
     const uint4* kd = cur.kd;
     const uint32_t* vv = cur.vv;
     float lg[G];
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   const int b = bh / a.H, h = bh - b * a.H;
   const int L = a.seq_lens[b];
   if (item < a.n_bsplit) {
-    if (item * kBf16Chunk >= bf16_token_count(L, a.sink, a.recent)) return;
+    if (item * a.bchunk >= bf16_token_count(L, a.sink, a.recent)) return;
     bf16_item<G>(a, b, h, item, L, sm);
   } else {
     const int split = item - a.n_bsplit;
@@ -757,7 +759,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
 // with a running log-sum-exp in registers; then acc_rot R_V^T =
 // ((acc_rot P) H) U_V^T with U_V staged in LDS, bf16 out.
 // ---------------------------------------------------------------------------
-constexpr int kReduceBatch = 32;
+// partial records requested at once per thread: 64 where the block has 512 threads or
+// fewer (G <= 4: 256 VGPRs per thread available), 32 for G > 4
+template <int G>
+constexpr int reduce_batch() { return G <= 4 ? 64 : 32; }
 
 template <int G>
 __global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
@@ -784,13 +789,14 @@ __global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
     utmp[k] = i < kUChunks ? U[i] : make_uint4(0, 0, 0, 0);
   }
 
-  const int n_b = (bf16_token_count(L, a.sink, a.recent) + kBf16Chunk - 1) / kBf16Chunk;
+  const int n_b = (bf16_token_count(L, a.sink, a.recent) + a.bchunk - 1) / a.bchunk;
   const int i_hi = int2_end(L, a.sink, a.recent);
   const int int2_pages = i_hi > a.sink ? (i_hi + kPage - 1) / kPage - a.sink / kPage : 0;
   const int n_i = (int2_pages + a.P - 1) / a.P;
   const int n_used = n_b + n_i;   // used items: [0, n_b) BF16, then [n_bsplit, n_bsplit + n_i) INT2
   const size_t rec0 = ((size_t)b * a.Hq + h * G + g) * a.n_total;
   float M = -INFINITY, lsum = 0.f, plain = 0.f, rot = 0.f;
+  constexpr int kReduceBatch = reduce_batch<G>();
   for (int u0 = 0; u0 < n_used; u0 += kReduceBatch) {
     float mu[kReduceBatch], lu[kReduceBatch], vu[kReduceBatch];
 #pragma unroll
@@ -884,6 +890,17 @@ DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   if (per > kMaxPagesPerSplit) per = kMaxPagesPerSplit;
   p.pages_per_split = (int)per;
   p.n_split = int2_pages > 0 ? (int)((int2_pages + per - 1) / per) : 0;
+  p.bf16_chunk = kBf16Chunk;
+  // Few (sequence, KV head) pairs (a batch of one or two at 8 KV heads): the INT2 ranges are
+  // short, and a 320-token BF16 item, walked in five dependent rounds of loads, would
+  // finish last.  64-token items, one round each, as long as the records still fit.
+  if (bh > 0 && bh < 32) {
+    const int nb64 = (sink + recent + kBf16ChunkFew - 1) / kBf16ChunkFew;
+    if (p.n_split + nb64 <= kMaxItems) {
+      p.n_bsplit = nb64;
+      p.bf16_chunk = kBf16ChunkFew;
+    }
+  }
   p.n_total = p.n_split + p.n_bsplit;
   const size_t qrot = (size_t)batch * num_q_heads * kQrotBytes;
   p.qrot_off = 0;
@@ -931,6 +948,7 @@ DecodeArgs make_decode_args(const DecodeLaunch& L) {
   a.n_split = L.plan.n_split;
   a.n_bsplit = L.plan.n_bsplit;
   a.n_total = L.plan.n_total;
+  a.bchunk = L.plan.bf16_chunk;
   return a;
 }
 

@@ -18,15 +18,16 @@ struct KvWriteLaunch {
 
 // Split-K plan of one decode call: the INT2 history of each (sequence, KV
 // head) is cut into `n_split` ranges of `pages_per_split` logical pages; the
-// BF16 sink+recent tokens into `n_bsplit` chunks of 64 tokens.  Every
+// BF16 sink+recent tokens into `n_bsplit` chunks of `bf16_chunk` tokens.  Every
 // (sequence, query head) owns n_bsplit + n_split partial records.
 struct DecodePlan {
-  int32_t pages_per_split, n_split, n_bsplit, n_total;
+  int32_t pages_per_split, n_split, n_bsplit, n_total, bf16_chunk;
   size_t qrot_off, part_off, ml_off, bytes;
 };
 
 constexpr int kQrotBytes = 576;      // rotated-query record per (sequence, query head)
-constexpr int kBf16Chunk = 320;      // BF16 tokens per split item (multiple of 64)
+constexpr int kBf16Chunk = 320;      // BF16 tokens per split item (multiple of 64) ...
+constexpr int kBf16ChunkFew = 64;    // ... or this many when few (sequence, KV head) pairs share the GPU
 constexpr int kMaxItems = 1024;      // partial records per (sequence, query head) the reduce can merge
 
 DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t recent,
