@@ -759,21 +759,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
 // with a running log-sum-exp in registers; then acc_rot R_V^T =
 // ((acc_rot P) H) U_V^T with U_V staged in LDS, bf16 out.
 // ---------------------------------------------------------------------------
-// partial records requested at once per thread: 64 where the block has 512 threads or
-// fewer (G <= 4: 256 VGPRs per thread available), 32 for G > 4
-template <int G>
-constexpr int reduce_batch() { return G <= 4 ? 64 : 32; }
+constexpr int kReduceBatch = 32;   // partial records requested at once per thread
 
-template <int G>
-__global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
+// GB query heads per block (G, or 1 when few (sequence, KV head) pairs would leave most
+// CUs idle): block (b, h, gq) covers query heads h G + gq GB + [0, GB).
+template <int G, int GB>
+__global__ __launch_bounds__(GB * kHeadDim) void reduce_kernel(DecodeArgs a) {
+  static_assert(G % GB == 0, "whole head groups per block");
   constexpr int kURow = kHeadDim / 8 + 1;                 // uint4 per padded U row (272 B)
   __shared__ uint4 Us[kHeadDim * kURow];                  // U_V[h] rows, padded against bank conflicts
-  __shared__ float y[kMaxGqa][kHeadDim];
-  constexpr int nthr = G * kHeadDim;
-  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  __shared__ float y[GB][kHeadDim];
+  constexpr int nthr = GB * kHeadDim;
+  const int bhg = blockIdx.x, bh = bhg / (G / GB), gq = bhg % (G / GB), b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, g = tid >> 7, c = tid & (kHeadDim - 1);
+  const int head = h * G + gq * GB + g;   // query head of this thread
   const int L = a.seq_lens[b];
-  uint16_t* out = a.out + ((size_t)b * a.Hq + h * G + g) * kHeadDim;
+  uint16_t* out = a.out + ((size_t)b * a.Hq + head) * kHeadDim;
   if (L == 0) {
     out[c] = 0;
     return;
@@ -794,9 +795,8 @@ __global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
   const int int2_pages = i_hi > a.sink ? (i_hi + kPage - 1) / kPage - a.sink / kPage : 0;
   const int n_i = (int2_pages + a.P - 1) / a.P;
   const int n_used = n_b + n_i;   // used items: [0, n_b) BF16, then [n_bsplit, n_bsplit + n_i) INT2
-  const size_t rec0 = ((size_t)b * a.Hq + h * G + g) * a.n_total;
+  const size_t rec0 = ((size_t)b * a.Hq + head) * a.n_total;
   float M = -INFINITY, lsum = 0.f, plain = 0.f, rot = 0.f;
-  constexpr int kReduceBatch = reduce_batch<G>();
   for (int u0 = 0; u0 < n_used; u0 += kReduceBatch) {
     float mu[kReduceBatch], lu[kReduceBatch], vu[kReduceBatch];
 #pragma unroll
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
   y[g][bitrev7(c)] = rot;   // acc_rot P: z-space channel br(c) takes post-rotation channel c
   __syncthreads();
   for (int s = 1; s < kHeadDim; s <<= 1) {
-    for (int t = tid; t < G * 64; t += nthr) {
+    for (int t = tid; t < GB * 64; t += nthr) {
       const int gg = t >> 6, cc = t & 63;
       const int lo = ((cc & ~(s - 1)) << 1) | (cc & (s - 1)), hi = lo | s;
       const float x0 = y[gg][lo], x1 = y[gg][hi];
@@ -861,7 +861,10 @@ __global__ __launch_bounds__(G * kHeadDim) void reduce_kernel(DecodeArgs a) {
 template <int G>
 void launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
   hipLaunchKernelGGL(split_kernel<G>, dim3(a.n_total * a.H * B), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(reduce_kernel<G>, dim3(B * a.H), dim3(G * kHeadDim), 0, stream, a);
+  if (G > 1 && B * a.H < kFewPairs)
+    hipLaunchKernelGGL((reduce_kernel<G, 1>), dim3(B * a.H * G), dim3(kHeadDim), 0, stream, a);
+  else
+    hipLaunchKernelGGL((reduce_kernel<G, G>), dim3(B * a.H), dim3(G * kHeadDim), 0, stream, a);
 }
 
 }  // namespace
@@ -875,9 +878,12 @@ DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   // Items per (sequence, KV head): m ranges of ~400 pages (measured on MI355X at
   // 28 x 100K tokens: 16 to 20 items per (sequence, KV head) are within 0.7% of
   // each other, 13 items -- three rounds of block slots -- is 2.5% and 41 items 5%
-  // slower), but at least enough items to give every resident block slot work
-  // (4 per CU for G <= 4, 2 above, 256 CUs).
-  const long long slots = (num_q_heads / num_kv_heads <= 4 ? 4 : 2) * 256;
+  // slower), but at least enough items for half the resident block slots (2 per CU
+  // for G <= 4, 1 above, 256 CUs).  Measured with 1 and 2 sequences of 100K tokens
+  // (8 KV heads): filling every slot made ranges of ~50 pages whose records cost the
+  // reduce more than the extra blocks saved (45 against 51 us per call at batch 1,
+  // 53 against 59 at batch 2).
+  const long long slots = (num_q_heads / num_kv_heads <= 4 ? 2 : 1) * 256;
   const long long max_m = kMaxItems - p.n_bsplit;
   long long best_m = 0;
   if (int2_pages > 0 && bh > 0) {
@@ -894,7 +900,7 @@ DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   // Few (sequence, KV head) pairs (a batch of one or two at 8 KV heads): the INT2 ranges are
   // short, and a 320-token BF16 item, walked in five dependent rounds of loads, would
   // finish last.  64-token items, one round each, as long as the records still fit.
-  if (bh > 0 && bh < 32) {
+  if (bh > 0 && bh < kFewPairs) {
     const int nb64 = (sink + recent + kBf16ChunkFew - 1) / kBf16ChunkFew;
     if (p.n_split + nb64 <= kMaxItems) {
       p.n_bsplit = nb64;

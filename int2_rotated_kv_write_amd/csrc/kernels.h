@@ -28,6 +28,7 @@ struct DecodePlan {
 constexpr int kQrotBytes = 576;      // rotated-query record per (sequence, query head)
 constexpr int kBf16Chunk = 320;      // BF16 tokens per split item (multiple of 64) ...
 constexpr int kBf16ChunkFew = 64;    // ... or this many when few (sequence, KV head) pairs share the GPU
+constexpr int kFewPairs = 32;        // "few": fewer (sequence, KV head) pairs than this in one call
 constexpr int kMaxItems = 1024;      // partial records per (sequence, query head) the reduce can merge
 
 DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t recent,
