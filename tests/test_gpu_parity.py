@@ -118,6 +118,25 @@ def test_ragged_batch_permuted_pages(gpu, G):
     print("G", G, "decode", res, flush=True)
 
 
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_standard_plan_batch(gpu, G):
+    """8 sequences x 4 KV heads = 32 (sequence, KV head) pairs: the plan for many
+    pairs (320-token BF16 items, INT2 ranges for every block slot, one reduce
+    block per KV head), which the smaller cases above do not reach, compared in
+    full with the oracle."""
+    rng = np.random.default_rng(30 + G)
+    shape = O.Shape(num_kv_heads=4, num_q_heads=4 * G)
+    law = synth.heavy_tail_law(rng, 4)
+    layer = make_layer(rng, shape, law, 256)
+    lens = [0, 1, 65, 321, 700, 1000, 1500, 2049]
+    max_pages = 130
+    table = synth.permuted_page_table(rng, len(lens), max_pages)
+    seq_idx = np.concatenate([np.full(L, s) for s, L in enumerate(lens)])
+    pos = np.concatenate([np.arange(L) for L in lens])
+    stats, res = run_scenario(gpu, shape, layer, law, lens, table, [(seq_idx, pos)], rng)
+    print("G", G, "decode", res, flush=True)
+
+
 @pytest.mark.parametrize("sink,recent", [(16, 32), (0, 1), (128, 100)])
 def test_other_sink_and_recent_sizes(gpu, sink, recent):
     rng = np.random.default_rng(sink + recent)
