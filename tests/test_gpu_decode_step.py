@@ -73,7 +73,7 @@ def test_decode_step_equals_write_then_decode(gpu, H, G):
         assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
         _same_cache(host_cache(ca), host_cache(cb))
     # the last step against the oracle decoding the cache the GPU wrote (the decode
-    # parity rule: write-side near-tie code differences are judged by the kv_write
+    # parity rule: write-side near-tie code differences are checked by the kv_write
     # tests, not folded into the attention output)
     out_ref = O.decode(shape, host_cache(cb), layer, from_dev_bf16(q), table, Lf, SIG)
     print(compare_outputs(from_dev_bf16(out_b), out_ref), flush=True)
