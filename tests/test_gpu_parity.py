@@ -137,6 +137,27 @@ def test_standard_plan_batch(gpu, G):
     print("G", G, "decode", res, flush=True)
 
 
+def test_largest_max_pages(gpu):
+    """The largest page-table width one call accepts (sink 64, recent 256: 4 sink
+    pages + 1,023 ranges of 512 pages = 523,780 pages, about 8.4M tokens): the plan
+    at its item limit, a reduce over 1,024 records per query head, the largest
+    workspace.  One 1,000-token sequence uses the first 63 table entries (the rest
+    point at page 0), so the oracle checks the output in full."""
+    import int2_rotated_kv_write_amd as lib
+    rng = np.random.default_rng(77)
+    shape = O.Shape(num_kv_heads=1, num_q_heads=4)
+    top = 4 + 1023 * 512
+    assert lib.decode_workspace_bytes(lib_shape(shape), 1, top) > 0
+    assert lib.decode_workspace_bytes(lib_shape(shape), 1, top + 1) == 0
+    law = synth.outlier_law(rng, 1)
+    layer = make_layer(rng, shape, law, 256)
+    L = 1000
+    table = np.zeros((1, top), np.int32)
+    table[0, :63] = rng.permutation(63)
+    stats, res = run_scenario(gpu, shape, layer, law, [L], table, [(np.zeros(L, int), np.arange(L))], rng)
+    print("largest max_pages decode", res, flush=True)
+
+
 @pytest.mark.parametrize("sink,recent", [(16, 32), (0, 1), (128, 100)])
 def test_other_sink_and_recent_sizes(gpu, sink, recent):
     rng = np.random.default_rng(sink + recent)
