@@ -21,6 +21,10 @@
  *     default stream).  Return codes report argument errors found on the host
  *     and launch errors; nothing checks device memory contents.
  *   - bf16 values travel as uint16_t bit patterns; fp16 as uint16_t.
+ *   - Alignment: every bf16 / byte tensor (k, v, q, out, pages, sink, ring,
+ *     u_k, u_v) must start on a 16-byte boundary (the kernels move them in
+ *     16-byte vectors); int32 arrays on a 4-byte boundary; decode workspaces
+ *     on a 256-byte boundary.  A misaligned pointer is OSCAR_EINVAL.
  *   - Row-vector convention: a stored token is k' = k R.
  *
  * Page block format (one 1280-byte block per physical page id and KV head;

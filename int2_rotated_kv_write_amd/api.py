@@ -108,6 +108,9 @@ def _dev(t, dtype, name, shape=None):
         raise OscarError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise OscarError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    align = 4 if dtype == torch.int32 else 16     # the alignment rules of include/oscar.h
+    if t.data_ptr() % align:
+        raise OscarError(f"{name} must start on a {align}-byte boundary")
     return t.data_ptr()
 
 

@@ -29,6 +29,9 @@ FLAGS = [
     # code keeps its NaN checks on user arguments
     "-Xarch_device", "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
+    # inline assembly must not clobber reserved registers (M0 is saved and restored
+    # inside the statements that write it)
+    "-Werror=inline-asm",
 ]
 
 

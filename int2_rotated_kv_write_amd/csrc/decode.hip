@@ -395,10 +395,16 @@ __device__ __forceinline__ half8 half8_of(uint4 u) { return __builtin_bit_cast(h
 // slots being read (it would wait for every outstanding load before each LDS
 // read, defeating the prefetch); the loop's own s_waitcnt vmcnt orders it.
 __device__ __forceinline__ void dma_to_lds16(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  // one wait state between the M0 write and the load that reads it (the compiler puts the same
-  // s_nop in front of its own LDS-DMA loads; inline assembly is not checked for it)
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
-               : "memory", "m0");
+  // M0 is saved and restored inside the statement, so whatever value the compiler keeps in it
+  // survives; one wait state between the M0 write and the load that reads it (the compiler
+  // puts the same s_nop in front of its own LDS-DMA loads; inline assembly is not checked for
+  // it).  The load reads M0 when it issues, so M0 may be rewritten right after it.
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
 }
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -625,6 +631,11 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
         const bool ok = (k == 0 || has1) && (pp + k) * kPage + 4 * r + a4 < i_hi;
 #pragma unroll
         for (int qd = 0; qd < NQ; ++qd) lg[qd][k] = ok ? lg[qd][k] : -INFINITY;
+        // the value parameters of a masked slot (this lane's token in the value MFMA and
+        // the zero-point sum) may be anything, NaN included: slots at or past the
+        // sequence length were never written.  With s = z = 0 they contribute 0 * finite.
+        cur[k].vp[0] = ok ? cur[k].vp[0] : 0u;
+        cur[k].vp[1] = ok ? cur[k].vp[1] : 0u;
       }
     }
 

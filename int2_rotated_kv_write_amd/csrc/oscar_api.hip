@@ -33,6 +33,18 @@ int check_shape(const oscar_shape_t* s) {
 
 bool clip_ok(float c) { return std::isfinite(c) && c > 0.f && c <= 16384.f; }
 
+// The kernels move bf16 rows and page blocks in 16-byte vectors (and page blocks by
+// 16-byte direct-to-LDS loads); int32 index arrays are read as 32-bit words.
+bool al16(const void* p) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+bool al4(const void* p) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % 4 == 0; }
+
+int check_layer_alignment(const oscar_layer_t* l) {
+  if (!al16(l->pages) || !al16(l->k_sink) || !al16(l->v_sink) || !al16(l->k_ring) || !al16(l->v_ring) ||
+      !al16(l->u_k) || !al16(l->u_v))
+    return fail(OSCAR_EINVAL, "layer buffers must be 16-byte aligned%s");
+  return OSCAR_OK;
+}
+
 int hip_fail(const char* what) {
   const hipError_t e = hipGetLastError();
   std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
@@ -61,6 +73,10 @@ int prepare_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer, con
     return fail(OSCAR_EINVAL, "K half: NULL u_k/k_ring/k_sink or clip_k outside (0, 16384]%s");
   if (v && (!layer->u_v || !layer->v_ring || (shape->sink > 0 && !layer->v_sink) || !clip_ok(layer->clip_v)))
     return fail(OSCAR_EINVAL, "V half: NULL u_v/v_ring/v_sink or clip_v outside (0, 16384]%s");
+  if (int rc = check_layer_alignment(layer)) return rc;
+  if (!al16(k) || !al16(v)) return fail(OSCAR_EINVAL, "k and v must be 16-byte aligned%s");
+  if (!al4(seq_idx) || !al4(pos) || !al4(page_table) || !al4(seq_lens_after))
+    return fail(OSCAR_EINVAL, "int32 index arrays must be 4-byte aligned%s");
   L = oscar::KvWriteLaunch{};
   L.k = k;
   L.v = v;
@@ -103,6 +119,9 @@ int prepare_decode(const oscar_shape_t* shape, const oscar_layer_t* layer, const
       !layer->u_v || (shape->sink > 0 && (!layer->k_sink || !layer->v_sink)))
     return fail(OSCAR_EINVAL, "NULL tensor pointer%s");
   if (!clip_ok(layer->clip_v)) return fail(OSCAR_EINVAL, "clip_v outside (0, 16384]%s");
+  if (int rc = check_layer_alignment(layer)) return rc;
+  if (!al16(q) || !al16(out)) return fail(OSCAR_EINVAL, "q and out must be 16-byte aligned%s");
+  if (!al4(page_table) || !al4(seq_lens)) return fail(OSCAR_EINVAL, "int32 index arrays must be 4-byte aligned%s");
   const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
                                                          shape->recent, batch, max_pages);
   if (plan.n_total > oscar::kMaxItems) return fail(OSCAR_EINVAL, "max_pages too large (sequences over ~8M tokens)%s");
@@ -231,6 +250,8 @@ int oscar_bf16_decode_attn(int32_t num_kv_heads, int32_t num_q_heads, const uint
   if (!std::isfinite(sm_scale)) return fail(OSCAR_EINVAL, "sm_scale is not finite%s");
   if (batch == 0) return OSCAR_OK;
   if (!pages || !q || !page_table || !seq_lens || !out) return fail(OSCAR_EINVAL, "NULL tensor pointer%s");
+  if (!al16(pages) || !al16(q) || !al16(out)) return fail(OSCAR_EINVAL, "pages, q and out must be 16-byte aligned%s");
+  if (!al4(page_table) || !al4(seq_lens)) return fail(OSCAR_EINVAL, "int32 index arrays must be 4-byte aligned%s");
   const oscar::B16Plan plan = oscar::make_bf16_decode_plan(num_kv_heads, batch, max_pages, num_q_heads);
   if ((long long)batch * num_kv_heads * plan.n_split > 0x7FFFFFFFLL)
     return fail(OSCAR_EINVAL, "batch x num_kv_heads x ranges exceeds the grid limit%s");

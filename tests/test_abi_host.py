@@ -11,6 +11,9 @@ import int2_rotated_kv_write_amd as lib
 from int2_rotated_kv_write_amd._native import OscarLayer, OscarShape
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+# A stand-in device address: 256-byte aligned, never dereferenced (every call below
+# that passes it fails a host-side check, or has nothing to do, before any launch).
+A = 0x10000
 
 
 def header_functions():
@@ -60,7 +63,7 @@ def test_null_and_range_arguments_rejected():
     L = lib.load()
     s = good_shape()
     assert L.oscar_kv_write(None, None, 1, 1, 1, 1, 4, 1, 8, 1, None) == 1
-    layer = OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1,
+    layer = OscarLayer(pages=A, k_sink=A, v_sink=A, k_ring=A, v_ring=A, u_k=A, u_v=A,
                        clip_k=4.0, clip_v=4.0)
     # negative token count, zero max_pages, NULL index arrays
     assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), 1, 1, 1, 1, -1, 1, 8, 1, None) == 1
@@ -68,7 +71,7 @@ def test_null_and_range_arguments_rejected():
     assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), 1, 1, None, 1, 4, 1, 8, 1, None) == 1
     # clip thresholds must be finite and in (0, 16384]
     for c in (0.0, -1.0, float("inf"), float("nan"), 20000.0):
-        bad = OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1, clip_k=c, clip_v=4.0)
+        bad = OscarLayer(pages=A, k_sink=A, v_sink=A, k_ring=A, v_ring=A, u_k=A, u_v=A, clip_k=c, clip_v=4.0)
         assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(bad), 1, None, 1, 1, 4, 1, 8, 1, None) == 1
     # zero tokens, or neither k nor v: nothing to do
     assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), 1, 1, 1, 1, 0, 1, 8, 1, None) == 0
@@ -78,20 +81,20 @@ def test_null_and_range_arguments_rejected():
 def test_decode_workspace_checks():
     L = lib.load()
     s = good_shape()
-    layer = OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1,
+    layer = OscarLayer(pages=A, k_sink=A, v_sink=A, k_ring=A, v_ring=A, u_k=A, u_v=A,
                        clip_k=4.0, clip_v=4.0)
     need = L.oscar_decode_workspace_bytes(ctypes.byref(s), 28, 6250)
     assert need > 28 * 32 * 320
     # too small -> ENOWS; misaligned -> EINVAL; batch 0 -> OK without touching anything
-    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), 1, 1, 6250, 1, 28, 0.088, 1, 256, need - 1, None)
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), A, A, 6250, A, 28, 0.088, A, 256, need - 1, None)
     assert rc == 2
-    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), 1, 1, 6250, 1, 28, 0.088, 1, 257, need, None)
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), A, A, 6250, A, 28, 0.088, A, 257, need, None)
     assert rc == 1
-    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), 1, 1, 6250, 1, 0, 0.088, 1, None, 0, None)
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), A, A, 6250, A, 0, 0.088, A, None, 0, None)
     assert rc == 0
-    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), None, 1, 6250, 1, 28, 0.088, 1, 256, need, None)
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), None, A, 6250, A, 28, 0.088, A, 256, need, None)
     assert rc == 1
-    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), 1, 1, 6250, 1, 28, float("nan"), 1, 256, need,
+    rc = L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), A, A, 6250, A, 28, float("nan"), A, 256, need,
                              None)
     assert rc == 1
 
@@ -126,7 +129,7 @@ def test_bf16_decode_argument_checks():
         assert L.oscar_bf16_decode_workspace_bytes(h, hq, 2, 10) == 0
         assert L.oscar_bf16_decode_attn(h, hq, 1, 1, 1, 10, 1, 2, 0.088, 1, 256, 1 << 30, None) == 1
     assert L.oscar_bf16_decode_workspace_bytes(8, 32, 2, 0) == 0
-    args = lambda **kw: dict(dict(pages=1, q=1, table=1, mp=6250, lens=1, B=28, sc=0.088, out=1, ws=256, n=need), **kw)
+    args = lambda **kw: dict(dict(pages=A, q=A, table=A, mp=6250, lens=A, B=28, sc=0.088, out=A, ws=256, n=need), **kw)
     call = lambda a: L.oscar_bf16_decode_attn(8, 32, a["pages"], a["q"], a["table"], a["mp"], a["lens"], a["B"],
                                               a["sc"], a["out"], a["ws"], a["n"], None)
     assert call(args(n=need - 1)) == 2
@@ -162,11 +165,11 @@ def test_decode_step_checks_both_halves_before_launching():
     rejected on the host (nothing launched); empty halves are no-ops."""
     L = lib.load()
     s = good_shape()
-    layer = OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1, clip_k=4.0, clip_v=4.0)
+    layer = OscarLayer(pages=A, k_sink=A, v_sink=A, k_ring=A, v_ring=A, u_k=A, u_v=A, clip_k=4.0, clip_v=4.0)
     need = L.oscar_decode_workspace_bytes(ctypes.byref(s), 28, 6250)
 
     def step(**kw):
-        a = dict(k=1, v=1, idx=1, pos=1, T=28, after=1, q=1, table=1, mp=6250, lens=1, B=28, sc=0.088, out=1,
+        a = dict(k=A, v=A, idx=A, pos=A, T=28, after=A, q=A, table=A, mp=6250, lens=A, B=28, sc=0.088, out=A,
                  ws=256, n=need, shape=s, layer=layer)
         a.update(kw)
         return L.oscar_decode_step(ctypes.byref(a["shape"]), ctypes.byref(a["layer"]), a["k"], a["v"], a["idx"],
@@ -176,7 +179,7 @@ def test_decode_step_checks_both_halves_before_launching():
     assert step(shape=good_shape(head_dim=64)) == 1
     assert step(T=-1) == 1                     # write half
     assert step(idx=None) == 1
-    assert step(layer=OscarLayer(pages=1, k_sink=1, v_sink=1, k_ring=1, v_ring=1, u_k=1, u_v=1,
+    assert step(layer=OscarLayer(pages=A, k_sink=A, v_sink=A, k_ring=A, v_ring=A, u_k=A, u_v=A,
                                  clip_k=0.0, clip_v=4.0)) == 1
     assert step(sc=float("nan")) == 1          # decode half
     assert step(q=None) == 1
@@ -184,3 +187,29 @@ def test_decode_step_checks_both_halves_before_launching():
     assert step(ws=257) == 1
     assert step(T=0, B=0) == 0                 # both halves empty
     assert step(k=None, v=None, B=0) == 0
+
+
+def test_misaligned_pointers_rejected():
+    """16-byte alignment of bf16 / byte tensors and 4-byte alignment of int32
+    arrays are checked on the host before any launch."""
+    L = lib.load()
+    s = good_shape()
+    good = dict(pages=A, k_sink=A, v_sink=A, k_ring=A, v_ring=A, u_k=A, u_v=A, clip_k=4.0, clip_v=4.0)
+    need = L.oscar_decode_workspace_bytes(ctypes.byref(s), 28, 6250)
+    for f in ("pages", "k_sink", "v_sink", "k_ring", "v_ring", "u_k", "u_v"):
+        layer = OscarLayer(**dict(good, **{f: A + 8}))
+        assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), A, A, A, A, 4, A, 8, A, None) == 1
+        assert b"16-byte" in L.oscar_last_error()
+        assert L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), A, A, 6250, A, 28, 0.088, A, 256, need,
+                                   None) == 1
+    layer = OscarLayer(**good)
+    for k, v in ((A + 2, A), (A, A + 4)):
+        assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), k, v, A, A, 4, A, 8, A, None) == 1
+    for idx, pos, table, after in ((A + 2, A, A, A), (A, A + 1, A, A), (A, A, A + 2, A), (A, A, A, A + 3)):
+        assert L.oscar_kv_write(ctypes.byref(s), ctypes.byref(layer), A, A, idx, pos, 4, table, 8, after, None) == 1
+        assert b"4-byte" in L.oscar_last_error()
+    for q, table, lens, out in ((A + 8, A, A, A), (A, A + 2, A, A), (A, A, A + 2, A), (A, A, A, A + 2)):
+        assert L.oscar_decode_attn(ctypes.byref(s), ctypes.byref(layer), q, table, 6250, lens, 28, 0.088, out, 256,
+                                   need, None) == 1
+    assert L.oscar_bf16_decode_attn(8, 32, A + 8, A, A, 6250, A, 28, 0.088, A, 256, 1 << 40, None) == 1
+

@@ -27,17 +27,19 @@ def _same_cache(a: O.Cache, b: O.Cache):
         assert np.array_equal(getattr(a, f), getattr(b, f)), f
 
 
-@pytest.mark.parametrize("H,G", [(2, 4), (1, 8)])
-def test_decode_step_equals_write_then_decode(gpu, H, G):
+@pytest.mark.parametrize("H,G,B", [(2, 4, 3), (1, 8, 3), (8, 4, 28)])
+def test_decode_step_equals_write_then_decode(gpu, H, G, B):
+    """(8, 4, 28) is the benchmark's launch: 28 sequences x 8 KV heads, one new
+    token each, G = 4 (the many-pairs plan and the front kernel's flattened
+    write grid at that size)."""
     import torch
     import int2_rotated_kv_write_amd as lib
-    rng = np.random.default_rng(40 + G)
+    rng = np.random.default_rng(40 + G + B)
     shape = O.Shape(num_kv_heads=H, num_q_heads=H * G)
     law = synth.outlier_law(rng, H)
     layer = _layer(rng, law, G)
-    lens0 = np.array([700, 1301, 2000])
-    steps = 3
-    B = len(lens0)
+    lens0 = np.array([700, 1301, 2000]) if B == 3 else rng.integers(600, 2100, B)
+    steps = 3 if B == 3 else 2
     max_pages = int(np.ceil((lens0.max() + steps) / 16))
     table = synth.permuted_page_table(rng, B, max_pages)
     Lf = lens0 + steps - 1                       # lengths after the last step's write

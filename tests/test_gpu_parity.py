@@ -23,14 +23,20 @@ def make_layer(rng, shape, law, n_cal):
     return O.Layer(cal["u_k"], cal["u_v"], cal["clip_k"], cal["clip_v"])
 
 
-def run_scenario(device, shape, layer, law, lens, table, calls, rng, seed_q=0, check_each_call=True):
-    """calls: list of (seq_idx, pos) arrays; lens_after derived per call."""
+def run_scenario(device, shape, layer, law, lens, table, calls, rng, seed_q=0, check_each_call=True,
+                 poison=False):
+    """calls: list of (seq_idx, pos) arrays; lens_after derived per call.  poison:
+    the cache starts with every byte 0xFF (fp16 / bf16 NaN in every scale, zero
+    and BF16 row), so anything read from a slot that was never written shows up."""
     import torch
     import int2_rotated_kv_write_amd as lib
     n_slots = len(lens)
     num_pages = int(table.max()) + 1
     H = shape.num_kv_heads
     ref = O.new_cache(shape, num_pages, n_slots)
+    if poison:
+        for f in ("pages", "k_sink", "v_sink", "k_ring", "v_ring"):
+            getattr(ref, f)[...] = np.iinfo(getattr(ref, f).dtype).max
     dc = device_cache(shape, ref, layer, device)
     ls = lib_shape(shape)
     # token values for every (slot, pos)
@@ -169,6 +175,23 @@ def test_other_sink_and_recent_sizes(gpu, sink, recent):
     calls = [(np.full(L, s), np.arange(L)) for s, L in enumerate(lens)]
     stats, res = run_scenario(gpu, shape, layer, law, lens, table, calls, rng)
     print(sink, recent, "decode", res, flush=True)
+
+
+@pytest.mark.parametrize("sink,recent", [(0, 1), (16, 5), (64, 15), (64, 256)])
+def test_nan_poisoned_unwritten_slots(gpu, sink, recent):
+    """Every cache byte starts as 0xFF (NaN scales, zeros and BF16 rows).  With
+    recent < 16 the last INT2 page of a sequence holds slots at or past its
+    length that were never written; decode must mask their scales and zeros as
+    well as their logits, and match the oracle."""
+    rng = np.random.default_rng(500 + sink + recent)
+    shape = O.Shape(num_kv_heads=2, num_q_heads=8, sink=sink, recent=recent)
+    law = synth.outlier_law(rng, 2)
+    layer = make_layer(rng, shape, law, 256)
+    lens = [1, 17, sink + recent + 3, 333, 700]
+    table = synth.permuted_page_table(rng, len(lens), 50)
+    calls = [(np.full(L, s), np.arange(L)) for s, L in enumerate(lens)]
+    stats, res = run_scenario(gpu, shape, layer, law, lens, table, calls, rng, poison=True)
+    print(sink, recent, "poisoned decode", res, flush=True)
 
 
 def test_zero_length_and_empty_calls(gpu):
