@@ -244,6 +244,27 @@ int oscar_calibrate_layer(int32_t num_kv_heads, int32_t gqa, int32_t num_samples
                           uint16_t* u_v_out, float* clip_k_out, float* clip_v_out,
                           int32_t num_threads);
 
+/* decode_attn_noalloc -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): exactly oscar_decode_attn(shape, layer, q, page_table,
+ * max_pages, seq_lens, batch, sm_scale, out, <workspace>, <bytes>, stream),
+ * same kernels, checks and results, except that the workspace is a static
+ * device array inside the library of OSCAR_NOALLOC_SCRATCH_BYTES (64 MiB) per
+ * GPU, held from the library's first use of that GPU until the process ends.
+ * Calls whose oscar_decode_workspace_bytes(shape, batch, max_pages) exceeds it
+ * return OSCAR_EINVAL (at 32 query heads, 8 KV heads and 100K tokens per
+ * sequence the need is about 0.3 MB per sequence).  Nothing is allocated or
+ * freed and nothing in the scratch needs to start at zero.  Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads) race and must be serialised by the caller.  The first
+ * call on each GPU looks the array's address up (hipGetSymbolAddress) with
+ * that GPU current; a failure there is OSCAR_EHIP. */
+#define OSCAR_NOALLOC_SCRATCH_BYTES (64u << 20)
+int oscar_decode_attn_noalloc(const oscar_shape_t* shape, const oscar_layer_t* layer,
+                              const uint16_t* q, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_lens, int32_t batch, float sm_scale, uint16_t* out,
+                              hipStream_t stream);
+
 /* Static description of a return code. */
 const char* oscar_status_string(int status);
 

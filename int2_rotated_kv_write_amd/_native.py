@@ -7,6 +7,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "liboscar_gfx950.so"
 _lib = None
+NOALLOC_SCRATCH_BYTES = 64 << 20     # OSCAR_NOALLOC_SCRATCH_BYTES of include/oscar.h
 
 c_i32 = ctypes.c_int32
 c_ptr = ctypes.c_void_p
@@ -24,6 +25,7 @@ class OscarLayer(ctypes.Structure):
 
 
 EXPORTS = ("oscar_kv_write", "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_decode_step",
+           "oscar_decode_attn_noalloc",
            "oscar_bf16_decode_workspace_bytes", "oscar_bf16_decode_attn",
            "oscar_read_probe_sink_bytes", "oscar_read_probe",
            "oscar_calibrate_layer", "oscar_status_string", "oscar_last_error")
@@ -50,6 +52,9 @@ def load() -> ctypes.CDLL:
     lib.oscar_decode_attn.argtypes = [SP, LP, c_ptr, c_ptr, c_i32, c_ptr, c_i32, ctypes.c_float,
                                       c_ptr, c_ptr, ctypes.c_size_t, c_ptr]
     lib.oscar_decode_attn.restype = ctypes.c_int
+    lib.oscar_decode_attn_noalloc.argtypes = [SP, LP, c_ptr, c_ptr, c_i32, c_ptr, c_i32, ctypes.c_float, c_ptr,
+                                              c_ptr]
+    lib.oscar_decode_attn_noalloc.restype = ctypes.c_int
     lib.oscar_decode_step.argtypes = [SP, LP, c_ptr, c_ptr, c_ptr, c_ptr, c_i32, c_ptr, c_ptr, c_ptr, c_i32,
                                       c_ptr, c_i32, ctypes.c_float, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]
     lib.oscar_decode_step.restype = ctypes.c_int

@@ -173,6 +173,27 @@ def decode_attn(shape: CacheShape, cache: CacheBuffers, q, page_table, seq_lens,
     _check(rc)
 
 
+def decode_attn_noalloc(shape: CacheShape, cache: CacheBuffers, q, page_table, seq_lens, out,
+                        sm_scale: float | None = None, stream=None) -> None:
+    """oscar_decode_attn_noalloc: decode_attn with the library's static device
+    scratch instead of a workspace (no allocation anywhere; calls that overlap on
+    one GPU race)."""
+    import torch
+    _check_cache(shape, cache)
+    B = int(seq_lens.numel())
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if page_table.dim() != 2 or page_table.shape[0] < B:
+        raise OscarError("page_table must be [>= batch][max_pages]")
+    rc = load().oscar_decode_attn_noalloc(
+        ctypes.byref(shape.c()), ctypes.byref(cache.c()),
+        _dev(q, torch.bfloat16, "q", (B, shape.num_q_heads, HEAD_DIM)),
+        _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens", (B,)), B, float(sm_scale),
+        _dev(out, torch.bfloat16, "out", (B, shape.num_q_heads, HEAD_DIM)), _stream(stream))
+    _check(rc)
+
+
 def bf16_decode_workspace_bytes(num_kv_heads: int, num_q_heads: int, batch: int, max_pages: int) -> int:
     return int(load().oscar_bf16_decode_workspace_bytes(num_kv_heads, num_q_heads, batch, max_pages))
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liboscar_gfx950.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["oscar_api.hip", "kv_write.hip", "decode.hip", "decode_bf16.hip", "calibrate.cpp"]
+SOURCES = ["oscar_api.hip", "kv_write.hip", "decode.hip", "decode_bf16.hip", "decode_noalloc.hip", "calibrate.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

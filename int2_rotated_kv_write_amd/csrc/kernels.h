@@ -71,6 +71,8 @@ int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream);
 int launch_decode_step(const KvWriteLaunch& W, const DecodeLaunch& D, hipStream_t stream);
 int launch_decode(const DecodeLaunch& L, hipStream_t stream);
 int launch_bf16_decode(const B16Launch& L, hipStream_t stream);
+// Device address of the current device's static decode scratch (decode_noalloc.hip).
+hipError_t noalloc_scratch(void** out);
 int launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
 constexpr int kProbeBlocks = 4096;
 

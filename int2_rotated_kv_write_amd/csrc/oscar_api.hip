@@ -274,6 +274,36 @@ int oscar_bf16_decode_attn(int32_t num_kv_heads, int32_t num_q_heads, const uint
   return OSCAR_OK;
 }
 
+int oscar_decode_attn_noalloc(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                              float sm_scale, uint16_t* out, hipStream_t stream) {
+  oscar::DecodeLaunch L;
+  bool nothing = false;
+  if (int rc = check_shape(shape)) return rc;
+  if (batch <= 0 || max_pages < 1)   // argument errors or an empty batch: no scratch needed
+    return prepare_decode(shape, layer, q, page_table, max_pages, seq_lens, batch, sm_scale, out, nullptr, 0, L,
+                          &nothing);
+  const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
+                                                         shape->recent, batch, max_pages);
+  if (plan.n_total <= oscar::kMaxItems && plan.bytes > (size_t)OSCAR_NOALLOC_SCRATCH_BYTES) {
+    char need[64];
+    std::snprintf(need, sizeof(need), "%zu", plan.bytes);
+    return fail(OSCAR_EINVAL,
+                "decode of this batch x max_pages needs %s bytes of scratch, more than the library's static "
+                "OSCAR_NOALLOC_SCRATCH_BYTES; use oscar_decode_attn with a workspace",
+                need);
+  }
+  void* scratch = nullptr;
+  if (plan.n_total <= oscar::kMaxItems && oscar::noalloc_scratch(&scratch) != hipSuccess)
+    return hip_fail("static decode scratch lookup");
+  if (int rc = prepare_decode(shape, layer, q, page_table, max_pages, seq_lens, batch, sm_scale, out, scratch,
+                              OSCAR_NOALLOC_SCRATCH_BYTES, L, &nothing))
+    return rc;
+  if (nothing) return OSCAR_OK;
+  if (oscar::launch_decode(L, stream)) return hip_fail("decode launch");
+  return OSCAR_OK;
+}
+
 size_t oscar_read_probe_sink_bytes(void) { return (size_t)oscar::kProbeBlocks * 256 * sizeof(uint32_t); }
 
 int oscar_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_bytes, hipStream_t stream) {

@@ -213,3 +213,23 @@ def test_misaligned_pointers_rejected():
                                    need, None) == 1
     assert L.oscar_bf16_decode_attn(8, 32, A + 8, A, A, 6250, A, 28, 0.088, A, 256, 1 << 40, None) == 1
 
+
+def test_noalloc_decode_host_checks():
+    """decode_attn_noalloc: argument errors and a call whose scratch need exceeds
+    the static array are rejected on the host (nothing looked up or launched);
+    batch 0 is a no-op."""
+    L = lib.load()
+    s = good_shape()
+    layer = OscarLayer(pages=A, k_sink=A, v_sink=A, k_ring=A, v_ring=A, u_k=A, u_v=A, clip_k=4.0, clip_v=4.0)
+    call = lambda **kw: L.oscar_decode_attn_noalloc(
+        ctypes.byref(kw.get("shape", s)), ctypes.byref(layer), kw.get("q", A), A, kw.get("mp", 6250), A,
+        kw.get("B", 28), kw.get("sc", 0.088), A, None)
+    assert call(shape=good_shape(head_dim=64)) == 1
+    assert call(B=-1) == 1
+    assert call(mp=0) == 1
+    assert call(B=0) == 0
+    top = s.sink // 16 + 1023 * 512
+    assert L.oscar_decode_workspace_bytes(ctypes.byref(s), 64, top) > (64 << 20)
+    assert call(B=64, mp=top) == 1
+    assert b"OSCAR_NOALLOC_SCRATCH_BYTES" in L.oscar_last_error()
+    assert call(B=1, mp=top + 1) == 1            # beyond what one call can split at all
