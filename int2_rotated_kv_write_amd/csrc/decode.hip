@@ -389,21 +389,31 @@ __device__ __forceinline__ half8 half8_of(uint32_t a, uint32_t b, uint32_t c, ui
 }
 __device__ __forceinline__ half8 half8_of(uint4 u) { return __builtin_bit_cast(half8, u); }
 
-// 16 bytes per lane from global memory (wave-uniform base + per-lane offset)
-// straight into LDS at lds_base + 16 * lane (global_load_lds_dwordx4, LDS base in M0).  Issued as inline assembly so the
-// compiler does not see an LDS write it cannot disambiguate from the ring
-// slots being read (it would wait for every outstanding load before each LDS
-// read, defeating the prefetch); the loop's own s_waitcnt vmcnt orders it.
-__device__ __forceinline__ void dma_to_lds16(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  // M0 is saved and restored inside the statement, so whatever value the compiler keeps in it
-  // survives; one wait state between the M0 write and the load that reads it (the compiler
-  // puts the same s_nop in front of its own LDS-DMA loads; inline assembly is not checked for
-  // it).  The load reads M0 when it issues, so M0 may be rewritten right after it.
+// One 1280-byte page block from global memory (wave-uniform base + per-lane offsets)
+// straight into LDS at lds_base: 64 lanes x 16 bytes (global_load_lds_dwordx4), then
+// the last 256 bytes as 64 lanes x 4 bytes (global_load_lds_dword), the LDS base of each
+// in M0.  Issued as inline assembly so the compiler does not see an LDS write it cannot
+// disambiguate from the ring slots being read (it would wait for every outstanding
+// load before each LDS read, defeating the prefetch); the loop's own s_waitcnt vmcnt
+// orders it (two vector-memory instructions per page).  M0 is saved and restored inside
+// the statement, so whatever value the compiler keeps in it survives; one wait state
+// between each M0 write and the load that reads it (the compiler puts the same s_nop in
+// front of its own LDS-DMA loads; inline assembly is not checked for it).  A load reads
+// M0 when it issues, so M0 may be rewritten right after it.
+__device__ __forceinline__ void dma_page_to_lds(const void* sbase, uint32_t voff16, uint32_t voff4,
+                                                uint32_t lds_base, uint32_t lds_tail) {
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, %5\n\t"
+      "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "v"(voff16), "v"(voff4), "s"(lds_base), "s"(lds_tail), "s"(sbase)
       : "memory");
 }
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
@@ -500,39 +510,35 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   for (int d = 0; d < 4; ++d) wsel[d] = a4 == d ? 0x07060504u : ((a4 + 1) & 3) == d ? 0x03020100u : 0x0C0C0C0Cu;
 
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
-  const size_t head_off = (size_t)h * kBlockBytes;
-  const size_t page_stride = (size_t)a.H * kBlockBytes;
   // the wave's pages: j -> first + 8 (j / 2) + 2 wave + (j % 2)
   const int base0 = first + 2 * wave;
   int n_w = 0;
   if (base0 < end) n_w = 2 * ((end - base0 + 7) / 8) - ((end - base0 - 1) % 8 == 0 ? 1 : 0);
   auto page_of = [&](int j) { return base0 + 8 * (j >> 1) + (j & 1); };
-  const uint32_t lane_off = (uint32_t)(head_off + 16 * lane);   // byte offset of this lane in a page row
-  // physical page ids of the wave's pages, held in VGPRs: lane l keeps page j = l + 64 k
-  // (loaded and consumed here, so no load is pending inside the page loop)
+  const uint32_t off16 = 16 * lane, off4 = 1024 + 4 * lane;   // this lane's bytes of a page block
+  // the wave's page blocks as offsets from `pages` in 256-byte units (page id x H x 5 +
+  // h x 5: a block is 5 units), held in VGPRs: lane l keeps page j = l + 64 k (loaded and
+  // consumed here, so no load is pending inside the page loop).  32 bits suffice while
+  // the pool is below 1 TiB.
   constexpr int kIdRegs = kMaxPagesPerSplit / 4 / 64;
-  int32_t pid_reg[kIdRegs];
+  static_assert(kIdRegs == 2, "page offsets in two registers");
+  uint32_t unit_reg[kIdRegs];
   {
     const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+    const uint32_t per_page = (uint32_t)a.H * (kBlockBytes / 256), head_units = (uint32_t)h * (kBlockBytes / 256);
 #pragma unroll
     for (int k = 0; k < kIdRegs; ++k) {
       const int j = lane + 64 * k;
-      pid_reg[k] = j < n_w ? ptab[page_of(j)] : 0;
+      unit_reg[k] = j < n_w ? (uint32_t)ptab[page_of(j)] * per_page + head_units : 0u;
     }
 #pragma unroll
-    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(pid_reg[k]));
+    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(unit_reg[k]));
   }
-  auto pid_of = [&](int j) {   // wave-uniform j
-    int v = pid_reg[0];
-#pragma unroll
-    for (int q = 1; q < kIdRegs; ++q) v = (j >> 6) == q ? pid_reg[q] : v;
-    return __builtin_amdgcn_readlane(v, j & 63);
-  };
   auto issue = [&](int j, int slot) {   // 2 DMA instructions per page; slot = j % kRing
-    const uint8_t* row = a.pages + (size_t)pid_of(j) * page_stride;   // wave-uniform
+    const uint32_t u = __builtin_amdgcn_readlane(j < 64 ? unit_reg[0] : unit_reg[1], j & 63);   // wave-uniform
+    const uint8_t* row = a.pages + ((uint64_t)u << 8);
     const uint32_t dst = (uint32_t)(uintptr_t)&sm.ring[wave][slot][0];
-    dma_to_lds16(row, lane_off, dst);
-    if (lane < 16) dma_to_lds16(row, lane_off + 1024, dst + 1024);
+    dma_page_to_lds(row, off16, off4, dst, dst + 1024);
   };
   // A pair without its second page reads that page's slot anyway and weights it with p = 0;
   // the slot then holds an earlier page of this wave or, before the ring's first turn, the
@@ -682,17 +688,21 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
       lsum[qd] += p0 + p1;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const uint32_t v0 = cur[0].vp[g], v1 = cur[1].vp[g];   // (s_g | z_g << 16) of the token in each page
-        zs[qd][g] = fmaf(p0, f16_bits_to_f32(v0 >> 16), fmaf(p1, f16_bits_to_f32(v1 >> 16), zs[qd][g]));
-        const float ps0 = p0 * f16_bits_to_f32(v0), ps1 = p1 * f16_bits_to_f32(v1);
-        const half2v hi2 = half2v{(_Float16)ps0, (_Float16)ps1};
-        const half2v lo2 = half2v{(_Float16)(ps0 - (float)hi2[0]), (_Float16)(ps1 - (float)hi2[1])};
+        // (s_g, z_g) of the token in each page
+        const half2v sz0 = __builtin_bit_cast(half2v, cur[0].vp[g]), sz1 = __builtin_bit_cast(half2v, cur[1].vp[g]);
+        zs[qd][g] = fmaf(p0, (float)sz0[1], fmaf(p1, (float)sz1[1], zs[qd][g]));
+        const float ps0 = fmaf(p0, (float)sz0[0], 0.f), ps1 = fmaf(p1, (float)sz1[0], 0.f);
+        // hi = fp16(p s) rounded toward zero (one packed conversion for both pages), lo = the
+        // rest: hi + lo carries p s to about 2^-21 relative whatever hi's rounding
+        const half2v hi2 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ps0, ps1));
+        const half2v lo2 = half2v{(_Float16)fmaf(p0, (float)sz0[0], -(float)hi2[0]),
+                                  (_Float16)fmaf(p1, (float)sz1[0], -(float)hi2[1])};
         // the fp16 bases the value MFMA adds at this token's k-slot, times both limbs
         zs[qd][g] = __builtin_amdgcn_fdot2(hi2, nbase, zs[qd][g], false);
         zs[qd][g] = __builtin_amdgcn_fdot2(lo2, nbase, zs[qd][g], false);
         const uint32_t wh = __builtin_bit_cast(uint32_t, hi2);
-        const int lo_bits = __builtin_bit_cast(int, lo2);   // every quad lane has a source: old is unused
-        const uint32_t wl = (uint32_t)__builtin_amdgcn_update_dpp(lo_bits, lo_bits, kQuadRot1, 0xF, 0xF, false);
+        // lo of the next lane of the quad (every quad lane has a source)
+        const uint32_t wl = (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, lo2), kQuadRot1, 0xF, 0xF, true);
         A[qd][g] = half8_of(__builtin_amdgcn_perm(wh, wl, wsel[0]), __builtin_amdgcn_perm(wh, wl, wsel[1]),
                             __builtin_amdgcn_perm(wh, wl, wsel[2]), __builtin_amdgcn_perm(wh, wl, wsel[3]));
       }
