@@ -64,13 +64,16 @@ __device__ __forceinline__ int int2_end(int L, int sink, int recent) {   // INT2
 
 // ---------------------------------------------------------------------------
 // rotate_q: one 256-thread block per (sequence, KV head) for its G query
-// heads: U_K staged once in LDS, y = q U_K, FWHT, bit reversal, scale, then
-// the fp16 hi/lo MFMA fragments and offset sums of each head.
+// heads.  y = q U_K on v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32
+// sums): A rows = the G query heads (bf16 q straight from global memory), B =
+// U_K, whose columns each lane gathers as eight 16-bit loads (U_K's row-major
+// layout keeps a column strided); wave w makes output channels 32 w .. + 31.
+// Then FWHT, bit reversal and scale through LDS, and the fp16 hi/lo MFMA
+// fragments and offset sums of each head.
 // ---------------------------------------------------------------------------
 constexpr int kSideThreads = 256;
 
 struct RotQSmem {
-  uint4 Us[kHeadDim * kHeadDim / 8];   // U_K[h], row-major bf16
   float qv[kMaxGqa][kHeadDim];
   float y[kMaxGqa][kHeadDim];
   uint16_t qh[kMaxGqa][kHeadDim], ql[kMaxGqa][kHeadDim];
@@ -78,61 +81,42 @@ struct RotQSmem {
 
 // block for (sequence, KV head) bh = b H + h
 __device__ __forceinline__ void rotate_q_block(const DecodeArgs& a, RotQSmem& sm, int bh) {
-  uint4* Us = sm.Us;
   auto& qv = sm.qv;
   auto& y = sm.y;
   auto& qh = sm.qh;
   auto& ql = sm.ql;
   const int b = bh / a.H, h = bh % a.H, G = a.G;
-  const int tid = threadIdx.x, j = tid & (kHeadDim - 1), hs = tid >> 7;
-  const uint4* U = reinterpret_cast<const uint4*>(a.u_k + (size_t)h * kHeadDim * kHeadDim);
-  // issue every global load before the first LDS store (one memory latency, not eight)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kg = lane >> 4;
   {
-    constexpr int kPer = kHeadDim * kHeadDim / 8 / kSideThreads;
-    uint4 tmp[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) tmp[k] = U[tid + k * kSideThreads];
+    const uint16_t* U = a.u_k + (size_t)h * kHeadDim * kHeadDim;
     const uint16_t* qg = a.q + ((size_t)b * a.Hq + h * G) * kHeadDim;
-    uint16_t qb[kMaxGqa * kHeadDim / kSideThreads];
+    bf16x8 bq[4];   // A: query head n, input channels 32 ks + 8 kg .. + 7 (zero beyond G)
 #pragma unroll
-    for (int k = 0; k < kMaxGqa * kHeadDim / kSideThreads; ++k) {
-      const int e = tid + k * kSideThreads;
-      qb[k] = e < G * kHeadDim ? qg[e] : (uint16_t)0;
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 v = n < G ? *reinterpret_cast<const uint4*>(qg + n * kHeadDim + 32 * ks + 8 * kg)
+                            : make_uint4(0, 0, 0, 0);
+      bq[ks] = __builtin_bit_cast(bf16x8, v);
     }
+    bf16x8 bu[2][4];   // B: U_K[32 ks + 8 kg + d][16 nt + n], nt = 2 wave + t
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) Us[tid + k * kSideThreads] = tmp[k];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int k = 0; k < kMaxGqa * kHeadDim / kSideThreads; ++k) {
-      const int e = tid + k * kSideThreads;
-      if (e < G * kHeadDim) qv[e >> 7][e & 127] = bf16_bits_to_f32(qb[k]);
-    }
-  }
-  __syncthreads();
-  // y[g][j] = sum_i q_g[i] U[i][j]; this thread: column j of heads hs, hs + 2, ... (hs is
-  // wave-uniform); eight independent LDS loads per step, two partial sums per head
-  const uint16_t* Uh = reinterpret_cast<const uint16_t*>(Us);
-  float acc[kMaxGqa / 2][2];
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-  for (int k = 0; k < kMaxGqa / 2; ++k) acc[k][0] = acc[k][1] = 0.f;
+        for (int d = 0; d < 8; ++d)
+          bu[t][ks][d] = __builtin_bit_cast(__bf16, U[(32 * ks + 8 * kg + d) * kHeadDim + 16 * (2 * wave + t) + n]);
 #pragma unroll
-  for (int i = 0; i < kHeadDim; i += 8) {
-    float u[8];
+    for (int t = 0; t < 2; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int di = 0; di < 8; ++di) u[di] = bf16_bits_to_f32(Uh[(i + di) * kHeadDim + j]);
+      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[ks], bu[t][ks], acc, 0, 0, 0);
+      // lane (n, kg) holds heads 4 kg .. 4 kg + 3 of channel 16 nt + n
 #pragma unroll
-    for (int k = 0; k < kMaxGqa / 2; ++k) {
-      const int g = hs + 2 * k;
-      if (g < G) {
-        const float4 q0 = *reinterpret_cast<const float4*>(&qv[g][i]);
-        const float4 q1 = *reinterpret_cast<const float4*>(&qv[g][i + 4]);
-        acc[k][0] = fmaf(q0.x, u[0], fmaf(q0.y, u[1], fmaf(q0.z, u[2], fmaf(q0.w, u[3], acc[k][0]))));
-        acc[k][1] = fmaf(q1.x, u[4], fmaf(q1.y, u[5], fmaf(q1.z, u[6], fmaf(q1.w, u[7], acc[k][1]))));
-      }
+      for (int i = 0; i < 4; ++i)
+        if (4 * kg + i < G) y[4 * kg + i][16 * (2 * wave + t) + n] = acc[i];
     }
   }
-#pragma unroll
-  for (int k = 0; k < kMaxGqa / 2; ++k)
-    if (hs + 2 * k < G) y[hs + 2 * k][j] = acc[k][0] + acc[k][1];
   __syncthreads();
   // FWHT of every head, 64 butterflies per head and stage
   for (int s = 1; s < kHeadDim; s <<= 1) {
@@ -165,7 +149,6 @@ __device__ __forceinline__ void rotate_q_block(const DecodeArgs& a, RotQSmem& sm
     (&rec->frag[0][0][0][0][0])[jj] = (uint32_t)src[ch] | ((uint32_t)src[ch + 8] << 16);
   }
   // offset sums, one wave per head: lane l takes channel 64 gr + l
-  const int lane = tid & 63;
   for (int g = tid >> 6; g < G; g += kSideThreads / 64) {
     QrotRecord* rec = a.qrot + (size_t)b * a.Hq + h * G + g;
     const float base = (float)pair_base(pair_of_k(lane & 7));
@@ -774,118 +757,203 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
 }
 
 // ---------------------------------------------------------------------------
-// reduce: one block of G x 128 threads per (sequence, KV head); thread (g, c)
-// owns output channel c of query head g.  Every partial record of a batch of
-// up to 32 items is requested at once (one memory latency per batch), merged
-// with a running log-sum-exp in registers; then acc_rot R_V^T =
-// ((acc_rot P) H) U_V^T with U_V staged in LDS, bf16 out.
+// reduce: one 256-thread block per (sequence, KV head, group of GB query
+// heads).  The (m, l) of every used record are staged in LDS and each head's
+// maximum taken first, so the merge needs no running rescale; wave w then
+// requests every record u = w (mod 4) of the GB heads at once (lane l:
+// channels 2l, 2l + 1) and sums them with weights 2^(m_u - M).  The four
+// waves' sums meet in LDS; wave g finishes head g: acc_rot P H by an in-wave
+// Walsh-Hadamard transform, split into three bf16 limbs (hi + mid + lo carry
+// the fp32 value).  (acc_rot P H) U_V^T runs on v_mfma_f32_16x16x32_bf16: A
+// rows = (head, limb), B = rows of U_V read straight from global memory (row c
+// of U_V is column c of U_V^T, contiguous), so each wave produces 32 output
+// channels of all GB heads; plain (BF16-region) sum added, divided by l, bf16.
 // ---------------------------------------------------------------------------
-constexpr int kReduceBatch = 32;   // partial records requested at once per thread
+constexpr int kRedMaxRec = kMaxItems;   // records per (sequence, query head) the reduce accepts
 
-// GB query heads per block (G, or 1 when few (sequence, KV head) pairs would leave most
-// CUs idle): block (b, h, gq) covers query heads h G + gq GB + [0, GB).
+template <int GB>
+struct ReduceSmem {
+  float2 ml[GB][kRedMaxRec];                 // (m, l) of every used record
+  float part_rot[4][GB][kHeadDim];           // per-wave sums
+  float part_pl[4][GB][kHeadDim];
+  float part_l[4][GB];
+  float y[4][kHeadDim];                      // per-wave scratch of the bit reversal
+  __attribute__((aligned(16))) uint16_t ya[16][kHeadDim + 8];   // A operand: row 4 g + limb (bf16)
+  float plain[GB][kHeadDim];
+  float lsum[GB];
+};
+
 template <int G, int GB>
-__global__ __launch_bounds__(GB * kHeadDim) void reduce_kernel(DecodeArgs a) {
-  static_assert(G % GB == 0, "whole head groups per block");
-  constexpr int kURow = kHeadDim / 8 + 1;                 // uint4 per padded U row (272 B)
-  __shared__ uint4 Us[kHeadDim * kURow];                  // U_V[h] rows, padded against bank conflicts
-  __shared__ float y[GB][kHeadDim];
-  constexpr int nthr = GB * kHeadDim;
+__global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
+  static_assert(G % GB == 0 && GB <= 4, "whole head groups of at most four heads per block");
+  __shared__ ReduceSmem<GB> sm;
   const int bhg = blockIdx.x, bh = bhg / (G / GB), gq = bhg % (G / GB), b = bh / a.H, h = bh % a.H;
-  const int tid = threadIdx.x, g = tid >> 7, c = tid & (kHeadDim - 1);
-  const int head = h * G + gq * GB + g;   // query head of this thread
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, kg = lane >> 4;
+  const int head0 = h * G + gq * GB;   // first query head of this block
   const int L = a.seq_lens[b];
-  uint16_t* out = a.out + ((size_t)b * a.Hq + head) * kHeadDim;
   if (L == 0) {
-    out[c] = 0;
+    for (int e = tid; e < GB * kHeadDim; e += 256) a.out[((size_t)b * a.Hq + head0) * kHeadDim + e] = 0;
     return;
   }
-  // U_V loads first (stored to LDS after the record loads are also in flight)
-  constexpr int kUChunks = kHeadDim * kHeadDim / 8;       // uint4 per U
-  const uint4* U = reinterpret_cast<const uint4*>(a.u_v + (size_t)h * kHeadDim * kHeadDim);
-  constexpr int kUPer = (kUChunks + nthr - 1) / nthr;
-  uint4 utmp[kUPer];
+  // B fragments of the final product, requested first: wave w makes output channels
+  // 32 w .. 32 w + 31 (column tiles nt = 2 w + t); lane (n, kg) holds U_V[16 nt + n][32 ks + 8 kg, + 8)
+  bf16x8 ub[2][4];
+  {
+    const uint16_t* U = a.u_v + (size_t)h * kHeadDim * kHeadDim;
 #pragma unroll
-  for (int k = 0; k < kUPer; ++k) {
-    const int i = tid + k * nthr;
-    utmp[k] = i < kUChunks ? U[i] : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        ub[t][ks] = *reinterpret_cast<const bf16x8*>(U + (32 * wave + 16 * t + n) * kHeadDim + 32 * ks + 8 * kg);
   }
-
   const int n_b = (bf16_token_count(L, a.sink, a.recent) + a.bchunk - 1) / a.bchunk;
   const int i_hi = int2_end(L, a.sink, a.recent);
   const int int2_pages = i_hi > a.sink ? (i_hi + kPage - 1) / kPage - a.sink / kPage : 0;
   const int n_i = (int2_pages + a.P - 1) / a.P;
   const int n_used = n_b + n_i;   // used items: [0, n_b) BF16, then [n_bsplit, n_bsplit + n_i) INT2
-  const size_t rec0 = ((size_t)b * a.Hq + head) * a.n_total;
-  float M = -INFINITY, lsum = 0.f, plain = 0.f, rot = 0.f;
-  for (int u0 = 0; u0 < n_used; u0 += kReduceBatch) {
-    float mu[kReduceBatch], lu[kReduceBatch], vu[kReduceBatch];
-#pragma unroll
-    for (int d = 0; d < kReduceBatch; ++d) {
-      const int u = u0 + d;
-      const bool ok = u < n_used;
-      const size_t rec = rec0 + (!ok ? 0 : u < n_b ? u : a.n_bsplit + (u - n_b));
-      const float2 ml = ok ? a.part_ml[rec] : make_float2(-INFINITY, 0.f);   // same address across a head
-      mu[d] = ml.x;
-      lu[d] = ml.y;
-      vu[d] = ok ? a.part[rec * kHeadDim + c] : 0.f;
-    }
-    float bm = M;
-#pragma unroll
-    for (int d = 0; d < kReduceBatch; ++d) bm = fmaxf(bm, mu[d]);
-    const float sc = M == -INFINITY ? 0.f : exp2f(M - bm);
-    lsum *= sc;
-    plain *= sc;
-    rot *= sc;
-    M = bm;
-#pragma unroll
-    for (int d = 0; d < kReduceBatch; ++d) {
-      const float e = mu[d] == -INFINITY ? 0.f : exp2f(mu[d] - M);
-      lsum = fmaf(e, lu[d], lsum);
-      if (u0 + d < n_b) plain = fmaf(e, vu[d], plain);
-      else rot = fmaf(e, vu[d], rot);
-    }
+  auto rec_of = [&](int g, int u) {
+    return ((size_t)b * a.Hq + head0 + g) * a.n_total + (u < n_b ? u : a.n_bsplit + (u - n_b));
+  };
+  // ---- (m, l) of every record into LDS; each head's maximum ----
+  for (int e = tid; e < GB * n_used; e += 256) {
+    const int g = e / n_used, u = e - g * n_used;
+    sm.ml[g][u] = a.part_ml[rec_of(g, u)];
   }
-#pragma unroll
-  for (int k = 0; k < kUPer; ++k) {
-    const int i = tid + k * nthr;
-    if (i < kUChunks) Us[(i >> 4) * kURow + (i & 15)] = utmp[k];
-  }
-  y[g][bitrev7(c)] = rot;   // acc_rot P: z-space channel br(c) takes post-rotation channel c
   __syncthreads();
-  for (int s = 1; s < kHeadDim; s <<= 1) {
-    for (int t = tid; t < GB * 64; t += nthr) {
-      const int gg = t >> 6, cc = t & 63;
-      const int lo = ((cc & ~(s - 1)) << 1) | (cc & (s - 1)), hi = lo | s;
-      const float x0 = y[gg][lo], x1 = y[gg][hi];
-      y[gg][lo] = x0 + x1;
-      y[gg][hi] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  // (y U_V^T)_c = sum_k y_k U_V[c][k]
-  float o0 = 0.f, o1 = 0.f;
+  float M[GB];
 #pragma unroll
-  for (int kb = 0; kb < kHeadDim / 8; ++kb) {
-    const uint4 u8 = Us[c * kURow + kb];
-    const uint32_t uu[4] = {u8.x, u8.y, u8.z, u8.w};
+  for (int g = 0; g < GB; ++g) {
+    float m = -INFINITY;
+    for (int u = lane; u < n_used; u += 64) m = fmaxf(m, sm.ml[g][u].x);
+    M[g] = wave_max_xor(m, 1, 32);   // finite: every used BF16 item has a token
+  }
+  // ---- this wave's records, all requested before any is used ----
+  float rot[GB][2], pl[GB][2], lw[GB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      o0 = fmaf(y[g][8 * kb + 2 * q], bf16_bits_to_f32(uu[q] & 0xFFFFu), o0);
-      o1 = fmaf(y[g][8 * kb + 2 * q + 1], bf16_bits_to_f32(uu[q] >> 16), o1);
+  for (int g = 0; g < GB; ++g) rot[g][0] = rot[g][1] = pl[g][0] = pl[g][1] = lw[g] = 0.f;
+  constexpr int kBatch = GB == 1 ? 16 : 32 / GB;   // records per head requested at once by a wave
+  for (int u0 = wave; u0 < n_used; u0 += 4 * kBatch) {
+    float2 v[GB][kBatch];
+#pragma unroll
+    for (int g = 0; g < GB; ++g)
+#pragma unroll
+      for (int d = 0; d < kBatch; ++d) {
+        const int u = u0 + 4 * d;
+        v[g][d] = u < n_used ? *reinterpret_cast<const float2*>(a.part + rec_of(g, u) * kHeadDim + 2 * lane)
+                             : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+    for (int g = 0; g < GB; ++g)
+#pragma unroll
+      for (int d = 0; d < kBatch; ++d) {
+        const int u = u0 + 4 * d;
+        if (u < n_used) {   // wave-uniform
+          const float2 ml = sm.ml[g][u];
+          const float e = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M[g]);
+          lw[g] = fmaf(e, ml.y, lw[g]);
+          if (u < n_b) {
+            pl[g][0] = fmaf(e, v[g][d].x, pl[g][0]);
+            pl[g][1] = fmaf(e, v[g][d].y, pl[g][1]);
+          } else {
+            rot[g][0] = fmaf(e, v[g][d].x, rot[g][0]);
+            rot[g][1] = fmaf(e, v[g][d].y, rot[g][1]);
+          }
+        }
+      }
+  }
+#pragma unroll
+  for (int g = 0; g < GB; ++g) {
+    *reinterpret_cast<float2*>(&sm.part_rot[wave][g][2 * lane]) = make_float2(rot[g][0], rot[g][1]);
+    *reinterpret_cast<float2*>(&sm.part_pl[wave][g][2 * lane]) = make_float2(pl[g][0], pl[g][1]);
+    if (lane == 0) sm.part_l[wave][g] = lw[g];
+  }
+  __syncthreads();
+  // ---- wave g: head g's sums, bit reversal, Walsh-Hadamard, bf16 limbs ----
+  if (wave < GB) {
+    const int g = wave;
+    float r0 = 0.f, r1 = 0.f, p0 = 0.f, p1 = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float2 rr = *reinterpret_cast<const float2*>(&sm.part_rot[w][g][2 * lane]);
+      const float2 pp = *reinterpret_cast<const float2*>(&sm.part_pl[w][g][2 * lane]);
+      r0 += rr.x;
+      r1 += rr.y;
+      p0 += pp.x;
+      p1 += pp.y;
+      l += sm.part_l[w][g];
+    }
+    *reinterpret_cast<float2*>(&sm.plain[g][2 * lane]) = make_float2(p0, p1);
+    if (lane == 0) sm.lsum[g] = l;
+    // acc_rot P: z-space channel br(c) takes post-rotation channel c
+    sm.y[g][bitrev7(2 * lane)] = r0;
+    sm.y[g][bitrev7(2 * lane + 1)] = r1;
+    wave_lds_sync();
+    float y0 = sm.y[g][2 * lane], y1 = sm.y[g][2 * lane + 1];
+    {   // Walsh-Hadamard: index bit 0 in registers, bits 1..6 = lane bits 0..5
+      const float t0 = y0 + y1, t1 = y0 - y1;
+      y0 = t0;
+      y1 = t1;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float sgn = (lane & m) ? -1.f : 1.f;   // upper partner: partner - own
+      y0 = fmaf(sgn, y0, __shfl_xor(y0, m));
+      y1 = fmaf(sgn, y1, __shfl_xor(y1, m));
+    }
+    // three bf16 limbs of each value: rows 4 g + limb of the A operand
+    const float ys[2] = {y0, y1};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t hi = f32_to_bf16_bits(ys[k]);
+      const float r1v = ys[k] - bf16_bits_to_f32(hi);
+      const uint32_t mid = f32_to_bf16_bits(r1v);
+      const uint32_t lo = f32_to_bf16_bits(r1v - bf16_bits_to_f32(mid));
+      sm.ya[4 * g][2 * lane + k] = (uint16_t)hi;
+      sm.ya[4 * g + 1][2 * lane + k] = (uint16_t)mid;
+      sm.ya[4 * g + 2][2 * lane + k] = (uint16_t)lo;
+      sm.ya[4 * g + 3][2 * lane + k] = 0;
+    }
+  } else if (wave < 4) {
+    for (int r = 4 * GB; r < 16; ++r) {   // rows of heads this block does not have
+      sm.ya[r][2 * lane] = 0;
+      sm.ya[r][2 * lane + 1] = 0;
     }
   }
-  const float res = (plain + (o0 + o1) * 0.08838834764831845f) / lsum;
-  out[c] = (uint16_t)f32_to_bf16_bits(res);
+  __syncthreads();
+  // ---- (acc_rot P H) U_V^T: lane (n, kg) ends with rows 4 kg .. 4 kg + 3 = head kg's limbs ----
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&sm.ya[n][32 * ks + 8 * kg]);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ub[t][ks], d, 0, 0, 0);
+    }
+    const int c = 32 * wave + 16 * t + n;
+    if (kg < GB) {
+      const float o = (d[0] + d[1]) + d[2];
+      const float res = (sm.plain[kg][c] + o * 0.08838834764831845f) / sm.lsum[kg];
+      a.out[((size_t)b * a.Hq + head0 + kg) * kHeadDim + c] = (uint16_t)f32_to_bf16_bits(res);
+    }
+  }
+}
+
+// query heads per reduce block: one when few (sequence, KV head) pairs would leave most CUs
+// idle, else the largest divisor of G that is at most four
+template <int G>
+constexpr int reduce_group() {
+  return G <= 4 ? G : G % 4 == 0 ? 4 : G % 3 == 0 ? 3 : G % 2 == 0 ? 2 : 1;
 }
 
 template <int G>
 void launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
   hipLaunchKernelGGL(split_kernel<G>, dim3(a.n_total * a.H * B), dim3(256), 0, stream, a);
-  if (G > 1 && B * a.H < kFewPairs)
-    hipLaunchKernelGGL((reduce_kernel<G, 1>), dim3(B * a.H * G), dim3(kHeadDim), 0, stream, a);
+  constexpr int GB = reduce_group<G>();
+  if (GB > 1 && B * a.H < kFewPairs)
+    hipLaunchKernelGGL((reduce_kernel<G, 1>), dim3(B * a.H * G), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((reduce_kernel<G, G>), dim3(B * a.H), dim3(G * kHeadDim), 0, stream, a);
+    hipLaunchKernelGGL((reduce_kernel<G, GB>), dim3(B * a.H * (G / GB)), dim3(256), 0, stream, a);
 }
 
 }  // namespace
