@@ -34,7 +34,9 @@ SIG = 1.0 / math.sqrt(128)
 WORKLOADS = {
     "concurrent_28x100k_36l": dict(batch=28, seq_len=100_000, q_heads=32, kv_heads=8, layers=36,
                                    table="permuted", law="heavy"),
-    "qwen3_8b_layer_100k": dict(batch=1, seq_len=100_000, q_heads=32, kv_heads=8, layers=1,
+    # one layer's shape; 8 copies of its cache (525 MB, twice the 256 MB MALL) are cycled
+    # through, so every call reads its pages from HBM
+    "qwen3_8b_layer_100k": dict(batch=1, seq_len=100_000, q_heads=32, kv_heads=8, layers=8,
                                 table="contiguous", law="heavy"),
     "ragged_64x4k_128k": dict(batch=64, seq_len=(4096, 131072), q_heads=64, kv_heads=8, layers=1,
                               table="shared_prefix", law="outlier"),

@@ -155,6 +155,14 @@ __device__ __forceinline__ float tok_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A wave-uniform int32 read through the scalar cache (constant address space), for arrays
+// the kernel never writes: counted by lgkmcnt, so waiting for it does not also wait for
+// the vector loads issued before it.
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p, size_t i) {
+  typedef __attribute__((address_space(4))) const int32_t* cptr;
+  return ((cptr)(p))[i];
+}
+
 // Make this wave's earlier LDS writes visible to its own other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");

@@ -206,7 +206,10 @@ static_assert(2 * (kRing - 2) == 12, "s_waitcnt vmcnt immediate below assumes kR
 struct __attribute__((aligned(16))) SplitSmem {
   union {
     uint8_t ring[4][kRing][kBlockBytes];   // INT2 items: per-wave ring of page blocks
-    float p[4][kMaxGqa][16];               // BF16 items: probabilities per token (inside wave 0's ring)
+    struct {                               // BF16 items (inside wave 0's ring):
+      float p[4][kMaxGqa][16];             //   probabilities per token
+      uint4 q[kMaxGqa][kHeadDim / 8];      //   the G query rows (bf16)
+    } b16;
   };
 };
 
@@ -218,7 +221,8 @@ struct WaveResult {
   float m[kMaxGqa], l[kMaxGqa];
 };
 static_assert(sizeof(WaveResult) <= (kRing - kRing / 2) * kBlockBytes, "wave result fits its ring's upper half");
-static_assert(sizeof(float) * 4 * kMaxGqa * 16 <= (kRing / 2) * kBlockBytes, "BF16 scratch below wave 0's results");
+static_assert(sizeof(float) * 4 * kMaxGqa * 16 + 2 * kMaxGqa * kHeadDim <= (kRing / 2) * kBlockBytes,
+              "BF16 scratch below wave 0's results");
 __device__ __forceinline__ WaveResult& wave_result(SplitSmem& sm, int w) {
   return *reinterpret_cast<WaveResult*>(&sm.ring[w][kRing / 2][0]);
 }
@@ -299,6 +303,12 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
   };
   RoundIn nxt;
   load_round(0, nxt);
+  // the G query rows, staged in LDS once (read per round without a memory latency)
+  {
+    const uint4* qg = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h * G) * kHeadDim);
+    if (threadIdx.x < G * kHeadDim / 8) (&sm.b16.q[0][0])[threadIdx.x] = qg[threadIdx.x];
+    __syncthreads();
+  }
   const int n_rounds = a.bchunk / 64;
   for (int round = 0; round < n_rounds; ++round) {
     const int jbase = chunk * a.bchunk + 16 * (4 * round + wave);
@@ -312,11 +322,10 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
     float lg[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const uint16_t* qv = a.q + ((size_t)b * a.Hq + h * G + hh) * kHeadDim + 32 * q;
       float d = 0.f;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const uint4 qd = reinterpret_cast<const uint4*>(qv)[x];
+        const uint4 qd = sm.b16.q[hh][4 * q + x];
         d = dot2_bf16(qd.x, kd[x].x, d);
         d = dot2_bf16(qd.y, kd[x].y, d);
         d = dot2_bf16(qd.z, kd[x].z, d);
@@ -336,7 +345,7 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
       acc[hh][0] *= al;
       acc[hh][1] *= al;
       m[hh] = m_new;
-      if (q == 0) sm.p[wave][hh][t] = p;
+      if (q == 0) sm.b16.p[wave][hh][t] = p;
     }
     wave_lds_sync();
 #pragma unroll
@@ -344,7 +353,7 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
       const float v0 = bf16_bits_to_f32(vv[tt] & 0xFFFFu), v1 = bf16_bits_to_f32(vv[tt] >> 16);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float p = sm.p[wave][hh][tt];   // 0 beyond the last token
+        const float p = sm.b16.p[wave][hh][tt];   // 0 beyond the last token
         acc[hh][0] = fmaf(p, v0, acc[hh][0]);
         acc[hh][1] = fmaf(p, v1, acc[hh][1]);
       }
@@ -441,28 +450,64 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   const int n = lane & 15, r = lane >> 4;
   const int hh = n >> 2, a4 = n & 3, gp = a4 & 1, limb = a4 >> 1;
 
-  // q' fragments of column n: head 4 qd + hh, group gp, limb (zero beyond G)
+  // The wave's pages: j -> first + 8 (j / 2) + 2 wave + (j % 2).
+  const int base0 = first + 2 * wave;
+  int n_w = 0;
+  if (base0 < end) n_w = 2 * ((end - base0 + 7) / 8) - ((end - base0 - 1) % 8 == 0 ? 1 : 0);
+  auto page_of = [&](int j) { return base0 + 8 * (j >> 1) + (j & 1); };
+  constexpr int kIdRegs = kMaxPagesPerSplit / 4 / 64;
+  static_assert(kIdRegs == 2, "page offsets in two registers");
+  // Every prologue load is issued before any is used, from addresses that are always valid
+  // (selects come after), so the block waits one memory latency before its first page DMA:
+  // the physical page ids of the wave's pages (lane l: page j = l + 64 k) and the q'
+  // fragments of column n (head 4 qd + hh, group gp, limb; zero beyond G).
+  int32_t pid_raw[kIdRegs];
+  {
+    const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) {
+      const int j = lane + 64 * k;
+      pid_raw[k] = ptab[n_w > 0 ? page_of(min(j, n_w - 1)) : first];
+    }
+  }
+  uint4 qraw[NQ][2][2];
+  float craw[NQ], sraw[NQ];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    const int head = 4 * qd + hh;
+    const QrotRecord* rec = a.qrot + ((size_t)b * a.Hq + h * G + (head < G ? head : 0));
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) qraw[qd][g][kh] = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][limb][r][0]);
+    craw[qd] = rec->negc[gp][limb];
+    sraw[qd] = rec->qsum[gp];
+  }
+  // consume them all here: no wait for them may land inside the page loop, where it would
+  // also wait for every page DMA in flight
+#pragma unroll
+  for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(pid_raw[k]));
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+        asm volatile("" : "+v"(qraw[qd][g][kh].x), "+v"(qraw[qd][g][kh].y), "+v"(qraw[qd][g][kh].z),
+                     "+v"(qraw[qd][g][kh].w));
+    asm volatile("" : "+v"(craw[qd]), "+v"(sraw[qd]));
+  }
   half8 qb[NQ][2][2];
   float cinit[NQ], qs[NQ];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
-    const int head = 4 * qd + hh;
-    const bool ok = head < G;
-    const QrotRecord* rec = a.qrot + ((size_t)b * a.Hq + h * G + (ok ? head : 0));
+    const bool ok = 4 * qd + hh < G;
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        uint4 u = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][limb][r][0]);
-        u = ok && g == gp ? u : make_uint4(0, 0, 0, 0);
-        // consume the load here: its wait must not land inside the page loop, where it
-        // would also wait for every page DMA in flight
-        asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-        qb[qd][g][kh] = half8_of(u);
-      }
-    cinit[qd] = ok ? rec->negc[gp][limb] : 0.f;
-    qs[qd] = ok ? rec->qsum[gp] : 0.f;
-    asm volatile("" : "+v"(cinit[qd]), "+v"(qs[qd]));
+      for (int kh = 0; kh < 2; ++kh) qb[qd][g][kh] = half8_of(ok && g == gp ? qraw[qd][g][kh] : make_uint4(0, 0, 0, 0));
+    cinit[qd] = ok ? craw[qd] : 0.f;
+    qs[qd] = ok ? sraw[qd] : 0.f;
   }
 
   // zs[g]: per-head correction of group g's channels, sum over tokens of p z_g minus the
@@ -493,29 +538,15 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   for (int d = 0; d < 4; ++d) wsel[d] = a4 == d ? 0x07060504u : ((a4 + 1) & 3) == d ? 0x03020100u : 0x0C0C0C0Cu;
 
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
-  // the wave's pages: j -> first + 8 (j / 2) + 2 wave + (j % 2)
-  const int base0 = first + 2 * wave;
-  int n_w = 0;
-  if (base0 < end) n_w = 2 * ((end - base0 + 7) / 8) - ((end - base0 - 1) % 8 == 0 ? 1 : 0);
-  auto page_of = [&](int j) { return base0 + 8 * (j >> 1) + (j & 1); };
   const uint32_t off16 = 16 * lane, off4 = 1024 + 4 * lane;   // this lane's bytes of a page block
   // the wave's page blocks as offsets from `pages` in 256-byte units (page id x H x 5 +
-  // h x 5: a block is 5 units), held in VGPRs: lane l keeps page j = l + 64 k (loaded and
-  // consumed here, so no load is pending inside the page loop).  32 bits suffice while
-  // the pool is below 1 TiB.
-  constexpr int kIdRegs = kMaxPagesPerSplit / 4 / 64;
-  static_assert(kIdRegs == 2, "page offsets in two registers");
+  // h x 5: a block is 5 units), held in VGPRs: lane l keeps page j = l + 64 k.  32 bits
+  // suffice while the pool is below 1 TiB.
   uint32_t unit_reg[kIdRegs];
   {
-    const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
     const uint32_t per_page = (uint32_t)a.H * (kBlockBytes / 256), head_units = (uint32_t)h * (kBlockBytes / 256);
 #pragma unroll
-    for (int k = 0; k < kIdRegs; ++k) {
-      const int j = lane + 64 * k;
-      unit_reg[k] = j < n_w ? (uint32_t)ptab[page_of(j)] * per_page + head_units : 0u;
-    }
-#pragma unroll
-    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(unit_reg[k]));
+    for (int k = 0; k < kIdRegs; ++k) unit_reg[k] = (uint32_t)pid_raw[k] * per_page + head_units;
   }
   auto issue = [&](int j, int slot) {   // 2 DMA instructions per page; slot = j % kRing
     const uint32_t u = __builtin_amdgcn_readlane(j < 64 ? unit_reg[0] : unit_reg[1], j & 63);   // wave-uniform
@@ -791,11 +822,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, kg = lane >> 4;
   const int head0 = h * G + gq * GB;   // first query head of this block
-  const int L = a.seq_lens[b];
-  if (L == 0) {
-    for (int e = tid; e < GB * kHeadDim; e += 256) a.out[((size_t)b * a.Hq + head0) * kHeadDim + e] = 0;
-    return;
-  }
+  const int L = scalar_load_i32(a.seq_lens, b);
   // B fragments of the final product, requested first: wave w makes output channels
   // 32 w .. 32 w + 31 (column tiles nt = 2 w + t); lane (n, kg) holds U_V[16 nt + n][32 ks + 8 kg, + 8)
   bf16x8 ub[2][4];
@@ -807,6 +834,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
       for (int ks = 0; ks < 4; ++ks)
         ub[t][ks] = *reinterpret_cast<const bf16x8*>(U + (32 * wave + 16 * t + n) * kHeadDim + 32 * ks + 8 * kg);
   }
+  if (L == 0) {
+    for (int e = tid; e < GB * kHeadDim; e += 256) a.out[((size_t)b * a.Hq + head0) * kHeadDim + e] = 0;
+    return;
+  }
   const int n_b = (bf16_token_count(L, a.sink, a.recent) + a.bchunk - 1) / a.bchunk;
   const int i_hi = int2_end(L, a.sink, a.recent);
   const int int2_pages = i_hi > a.sink ? (i_hi + kPage - 1) / kPage - a.sink / kPage : 0;
@@ -815,8 +846,32 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
   auto rec_of = [&](int g, int u) {
     return ((size_t)b * a.Hq + head0 + g) * a.n_total + (u < n_b ? u : a.n_bsplit + (u - n_b));
   };
-  // ---- (m, l) of every record into LDS; each head's maximum ----
-  for (int e = tid; e < GB * n_used; e += 256) {
+  // ---- this wave's records u = wave + 4 d, requested first (they do not depend on the maxima):
+  // per head one base address, the record index and lane in a 32-bit offset ----
+  constexpr int kBatch = GB == 1 ? 32 : 8;   // records per head requested at once by a wave
+  const float* head_base[GB];
+#pragma unroll
+  for (int g = 0; g < GB; ++g) head_base[g] = a.part + ((size_t)b * a.Hq + head0 + g) * a.n_total * kHeadDim;
+  auto load_batch = [&](int u0, float2 (&v)[GB][kBatch]) {
+#pragma unroll
+    for (int g = 0; g < GB; ++g)
+#pragma unroll
+      for (int d = 0; d < kBatch; ++d) {
+        const int u = u0 + 4 * d;
+        const int idx = u < n_b ? u : a.n_bsplit + (u - n_b);
+        v[g][d] = u < n_used ? *reinterpret_cast<const float2*>(head_base[g] + (idx * kHeadDim + 2 * lane))
+                             : make_float2(0.f, 0.f);
+      }
+  };
+  // ---- (m, l) of every record into LDS; each head's maximum.  The first 256 are requested
+  // before this wave's records, so the wait for them leaves the record loads in flight ----
+  const bool ml0_ok = tid < GB * n_used;
+  const int g0 = ml0_ok ? tid / n_used : 0, u0_ = ml0_ok ? tid - g0 * n_used : 0;
+  const float2 ml0 = a.part_ml[rec_of(g0, u0_)];
+  float2 v[GB][kBatch];
+  load_batch(wave, v);
+  if (ml0_ok) sm.ml[g0][u0_] = ml0;
+  for (int e = tid + 256; e < GB * n_used; e += 256) {   // more than 256 records: long sequences
     const int g = e / n_used, u = e - g * n_used;
     sm.ml[g][u] = a.part_ml[rec_of(g, u)];
   }
@@ -828,21 +883,11 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
     for (int u = lane; u < n_used; u += 64) m = fmaxf(m, sm.ml[g][u].x);
     M[g] = wave_max_xor(m, 1, 32);   // finite: every used BF16 item has a token
   }
-  // ---- this wave's records, all requested before any is used ----
   float rot[GB][2], pl[GB][2], lw[GB];
 #pragma unroll
   for (int g = 0; g < GB; ++g) rot[g][0] = rot[g][1] = pl[g][0] = pl[g][1] = lw[g] = 0.f;
-  constexpr int kBatch = GB == 1 ? 16 : 32 / GB;   // records per head requested at once by a wave
   for (int u0 = wave; u0 < n_used; u0 += 4 * kBatch) {
-    float2 v[GB][kBatch];
-#pragma unroll
-    for (int g = 0; g < GB; ++g)
-#pragma unroll
-      for (int d = 0; d < kBatch; ++d) {
-        const int u = u0 + 4 * d;
-        v[g][d] = u < n_used ? *reinterpret_cast<const float2*>(a.part + rec_of(g, u) * kHeadDim + 2 * lane)
-                             : make_float2(0.f, 0.f);
-      }
+    if (u0 != wave) load_batch(u0, v);   // more records than one batch (long sequences)
 #pragma unroll
     for (int g = 0; g < GB; ++g)
 #pragma unroll
