@@ -163,11 +163,9 @@ __device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p, size_t i) {
   return ((cptr)(p))[i];
 }
 
-// Make this wave's earlier LDS writes visible to its own other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
+// Make this wave's earlier LDS writes visible to its own other lanes: wait for the wave's
+// LDS operations only (a workgroup-scope fence would also wait for every global load in
+// flight, draining any prefetch), and keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 }  // namespace oscar

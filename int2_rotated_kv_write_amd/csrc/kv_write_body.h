@@ -64,8 +64,12 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
   const int q = lane >> 4;   // channel quarter: channels 16mt + 4q + r
 
   const uint16_t* X = a.x[kind];
-  // per-tile inputs, loaded one tile ahead so their latency overlaps the previous tile's math
-  // (the first tile's before U^T is staged)
+  // Per-tile inputs, loaded one tile ahead so their latency overlaps the previous tile's
+  // math (the first tile's before U^T is staged).  Every load reads a valid token (tokens
+  // past the end read the last one), so none needs a branch.  The loads that depend on a
+  // tile's indices (its page id, its sequence's length after the call) are issued at the
+  // start of the tile, before the next tile's prefetch, so waiting for them leaves the
+  // prefetch in flight.
   struct TileIn {
     uint4 x[4];   // x[t][h][32ks + 8q .. +7]
     int b, p;
@@ -74,12 +78,12 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
   auto load_tile = [&](int tg, TileIn& in) {   // tile 4 tg + wave
     const int t = (tg * 4 + wave) * 16 + n;
     in.valid = t < a.num_tokens;
-    in.b = in.valid ? a.seq_idx[t] : 0;
-    in.p = in.valid ? a.pos[t] : 0;
-    const uint16_t* xrow = X + ((size_t)(in.valid ? t : 0) * a.num_heads + h) * kHeadDim;
+    const int tc = in.valid ? t : a.num_tokens - 1;
+    in.b = a.seq_idx[tc];
+    in.p = a.pos[tc];
+    const uint16_t* xrow = X + ((size_t)tc * a.num_heads + h) * kHeadDim;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      in.x[ks] = in.valid ? *reinterpret_cast<const uint4*>(xrow + 32 * ks + 8 * q) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) in.x[ks] = *reinterpret_cast<const uint4*>(xrow + 32 * ks + 8 * q);
   };
   const int n_groups = (a.num_tiles + 3) / 4;   // groups of four 16-token tiles, one per wave
   TileIn nxt;
@@ -123,39 +127,25 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
   const int params_off = kind == 0 ? kKParams : kVParams;
 
 
-  // the block walks tile groups bx, bx + gdx, ...: U^T is staged once per block
-  for (int tg = bx; tg < n_groups; tg += gdx) {
-    const int tile = tg * 4 + wave;
-    if (tile >= a.num_tiles) break;   // wave-uniform (only in the last group)
-    const TileIn cur = nxt;
-    if (tg + gdx < n_groups) load_tile(tg + gdx, nxt);
+  // The block walks tile groups bx, bx + gdx, ...: U^T is staged once per block.  Two tile
+  // buffers alternate (the loop below is unrolled twice), so the tile being processed is
+  // never copied out of the registers its loads landed in while the next tile's loads fly.
+  int tg = bx;
+  auto step = [&](const TileIn& cur, TileIn& nxt_buf) {
+    if (tg >= n_groups || tg * 4 + wave >= a.num_tiles) return false;   // wave-uniform
     const bool valid = cur.valid;
     const int b = cur.b, p = cur.p;
     const bool is_int2 = valid && p >= a.sink_len;
-    // this token's page block (its id is loaded before the math that hides the latency)
-    const int32_t pid = is_int2 ? a.page_table[(size_t)b * a.max_pages + (p >> 4)] : 0;
-
+    const int32_t pid = a.page_table[(size_t)b * a.max_pages + max(0, min(p >> 4, a.max_pages - 1))];
+    const int L_after = a.lens_after[b];
+    asm volatile("" ::: "memory");   // keep those two loads ahead of the prefetch
+    if (tg + gdx < n_groups) load_tile(tg + gdx, nxt_buf);
     bf16x8 bfrag[4];
     uint4 xraw[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       xraw[ks] = cur.x[ks];
       bfrag[ks] = __builtin_bit_cast(bf16x8, xraw[ks]);
-    }
-
-    // ---- bf16 copies (sink rows, recent ring) ----
-    if (valid) {
-      if (p < a.sink_len) {
-        uint16_t* row = sink_buf + (((size_t)b * a.num_heads + h) * a.sink_len + p) * kHeadDim;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(row + 32 * ks + 8 * q) = xraw[ks];
-      }
-      const int L_after = a.lens_after[b];
-      if (p >= max(a.sink_len, L_after - a.recent)) {
-        uint16_t* row = ring_buf + (((size_t)b * a.num_heads + h) * a.recent + (p % a.recent)) * kHeadDim;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(row + 32 * ks + 8 * q) = xraw[ks];
-      }
     }
 
     // ---- y^T = U^T x^T ----
@@ -304,6 +294,26 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
       const uint32_t lo = sbits[0] | (zbits[0] << 16), hi = sbits[1] | (zbits[1] << 16);
       *reinterpret_cast<uint2*>(blk + params_off + 8 * slot) = make_uint2(lo, hi);
     }
+
+    // ---- bf16 copies (sink rows, recent ring), last: the sequence length they need was
+    // requested at the start of the tile ----
+    if (valid) {
+      if (p < a.sink_len) {
+        uint16_t* row = sink_buf + (((size_t)b * a.num_heads + h) * a.sink_len + p) * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(row + 32 * ks + 8 * q) = xraw[ks];
+      }
+      if (p >= max(a.sink_len, L_after - a.recent)) {
+        uint16_t* row = ring_buf + (((size_t)b * a.num_heads + h) * a.recent + (p % a.recent)) * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(row + 32 * ks + 8 * q) = xraw[ks];
+      }
+    }
+    tg += gdx;
+    return true;
+  };
+  TileIn nxt2;
+  while (step(nxt, nxt2) && step(nxt2, nxt)) {
   }
 }
 
