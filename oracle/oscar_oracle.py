@@ -35,7 +35,7 @@ __all__ = [
     "Shape", "Cache", "Layer", "bf16_to_f64", "f64_to_bf16", "fp16_rne",
     "hadamard", "bitrev7", "bitrev_permutation", "rotate", "rotation", "quantize",
     "pack_k_codes", "unpack_k_codes", "regions", "kv_write", "gather_sequence",
-    "decode", "decode_folded", "query_covariance", "score_weighted_covariance",
+    "decode", "decode_folded", "extend", "query_covariance", "score_weighted_covariance",
     "eigenbasis", "calibrate_layer", "new_cache", "BF16_BLOCK", "new_bf16_pages",
     "bf16_pages_write", "bf16_pages_gather", "decode_bf16_paged",
 ]
@@ -434,6 +434,45 @@ def decode_folded(shape: Shape, cache: Cache, layer: Layer, q_bits, page_table,
                 npl = len(plainK)
                 acc = p[:npl] @ plainV + (p[npl:] @ Vr) @ Rv.T
                 out[b, hq] = acc / p.sum()
+    return out
+
+
+def extend(shape: Shape, cache: Cache, layer: Layer, q_bits, k_bits, v_bits, cu_seqlens,
+           prefix_lens, page_table, sm_scale: float):
+    """Chunked-prefill (extend) attention over the mixed cache, fp64.
+
+    The read path of the Italian page's section "Architettura del Sistema di
+    Serving e Layout di Memoria" and of the Spanish summary's 2.2 B (paged
+    attention over the mixed cache, prefix caching) for a chunk of new tokens
+    instead of one.  Reading taken where the pages are silent: the chunk of
+    sequence slot b is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of q (bf16
+    [T][Hq][128]) and of k, v (bf16 [T][H_kv][128]); its i-th token sits at
+    position prefix_lens[b] + i and attends to
+      - the cached prefix [0, L_prev), L_prev = prefix_lens[b], as the cache
+        stores it for a sequence of that length (gather_sequence: sink and
+        ring rows exact, INT2 history dequantized and inverse-rotated), and
+      - the chunk's own keys 0..i, in BF16 as given (causal),
+    with softmax(sm_scale q . k) over all of them.  The chunk is not in the
+    cache yet (it is written afterwards).  Returns out [T][Hq][128]."""
+    q = bf16_to_f64(q_bits)
+    kn = bf16_to_f64(k_bits)
+    vn = bf16_to_f64(v_bits)
+    T, Hq, _ = q.shape
+    G = shape.gqa
+    out = np.zeros((T, Hq, D))
+    cu = np.asarray(cu_seqlens, np.int64)
+    for b in range(len(cu) - 1):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        L = int(prefix_lens[b])
+        for h in range(shape.num_kv_heads):
+            Kp, Vp, _ = gather_sequence(shape, cache, layer, b, h, L, page_table)
+            for t in range(t0, t1):
+                K = np.concatenate([Kp, kn[t0:t + 1, h]])
+                V = np.concatenate([Vp, vn[t0:t + 1, h]])
+                for hq in range(h * G, (h + 1) * G):
+                    logits = sm_scale * (K @ q[t, hq])
+                    p = np.exp(logits - logits.max())
+                    out[t, hq] = (p @ V) / p.sum()
     return out
 
 

@@ -72,3 +72,45 @@ def test_oracle_imports_no_product_code():
     r = subprocess.run([sys.executable, "-c", code], cwd=TR.__file__.rsplit("/tests/", 1)[0],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def _extend_mutant(causal_end):
+    """The oracle's extend with the chunk-key bound replaced (t0 .. causal_end(t, t1))."""
+    def ext(shape, cache, layer, q_bits, k_bits, v_bits, cu_seqlens, prefix_lens, page_table, sm_scale):
+        q, kn, vn = OO.bf16_to_f64(q_bits), OO.bf16_to_f64(k_bits), OO.bf16_to_f64(v_bits)
+        T, Hq, _ = q.shape
+        G = shape.gqa
+        out = np.zeros((T, Hq, OO.D))
+        for b in range(len(cu_seqlens) - 1):
+            t0, t1, L = int(cu_seqlens[b]), int(cu_seqlens[b + 1]), int(prefix_lens[b])
+            for h in range(shape.num_kv_heads):
+                Kp, Vp, _ = OO.gather_sequence(shape, cache, layer, b, h, L, page_table)
+                for t in range(t0, t1):
+                    e = causal_end(t, t1)
+                    K, V = np.concatenate([Kp, kn[t0:e, h]]), np.concatenate([Vp, vn[t0:e, h]])
+                    for hq in range(h * G, (h + 1) * G):
+                        lg = sm_scale * (K @ q[t, hq])
+                        p = np.exp(lg - lg.max())
+                        out[t, hq] = (p @ V) / p.sum()
+        return out
+    return ext
+
+
+def test_extend_without_causal_mask_is_caught(monkeypatch):
+    import test_oracle_extend as TE
+    _patch(monkeypatch, "extend", _extend_mutant(lambda t, t1: t1))
+    assert _fails(TE.test_bf16_only_prefix_equals_brute_force_causal, 10, 7)
+
+
+def test_extend_excluding_its_own_key_is_caught(monkeypatch):
+    import test_oracle_extend as TE
+    _patch(monkeypatch, "extend", _extend_mutant(lambda t, t1: t))
+    assert _fails(TE.test_bf16_only_prefix_equals_brute_force_causal, 10, 7)
+
+
+def test_extend_with_a_short_prefix_is_caught(monkeypatch):
+    import test_oracle_extend as TE
+    orig = OO.gather_sequence
+    monkeypatch.setattr(OO, "gather_sequence",
+                        lambda shape, cache, layer, b, h, L, table: orig(shape, cache, layer, b, h, max(L - 1, 0), table))
+    assert _fails(TE.test_bf16_only_prefix_equals_brute_force_causal, 150, 20)
