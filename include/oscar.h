@@ -141,7 +141,8 @@ size_t oscar_decode_workspace_bytes(const oscar_shape_t* shape, int32_t batch, i
  *
  *   q          bf16 [batch][num_q_heads][128]
  *   page_table int32 [batch][max_pages]
- *   seq_lens   int32 [batch], 0 <= L <= 16 * max_pages
+ *   seq_lens   int32 [batch], 0 <= L <= 16 * max_pages (a device value
+ *              outside is clamped to that range)
  *   sm_scale   softmax scale (1/sqrt(128) for standard attention)
  *   out        bf16 [batch][num_q_heads][128] (written, round to nearest even)
  *   workspace  device scratch of at least oscar_decode_workspace_bytes(shape,
@@ -184,7 +185,8 @@ size_t oscar_bf16_decode_workspace_bytes(int32_t num_kv_heads, int32_t num_q_hea
  *   pages      bf16 [num_pages][num_kv_heads][4096] (format above)
  *   q          bf16 [batch][num_q_heads][128]
  *   page_table int32 [batch][max_pages]
- *   seq_lens   int32 [batch], 0 <= L <= 16 * max_pages (not checked on device)
+ *   seq_lens   int32 [batch], 0 <= L <= 16 * max_pages (a device value
+ *              outside is clamped to that range)
  *   out        bf16 [batch][num_q_heads][128] (round to nearest even); L == 0
  *              writes zeros
  *   workspace  >= oscar_bf16_decode_workspace_bytes(...) bytes, 256-byte
@@ -243,6 +245,41 @@ int oscar_calibrate_layer(int32_t num_kv_heads, int32_t gqa, int32_t num_samples
                           double sm_scale, double quantile, uint16_t* u_k_out,
                           uint16_t* u_v_out, float* clip_k_out, float* clip_v_out,
                           int32_t num_threads);
+
+/* extend_attn -- chunked prefill (extend) attention over the mixed cache: the
+ * read path of [it] "Architettura del Sistema di Serving e Layout di Memoria"
+ * and [es] 2.2 B (paged attention with prefix caching) for a chunk of new
+ * tokens per sequence instead of one.  The chunk of sequence b is tokens
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, k, v; its i-th token sits at
+ * position prefix_lens[b] + i and attends to
+ *   - the cached prefix [0, L), L = prefix_lens[b], as the cache stores it for
+ *     a sequence of length L (sink rows [0, min(sink, L)), ring rows
+ *     [max(sink, L - recent), L), INT2 history in between, dequantized and
+ *     inverse-rotated by folding as in decode_attn), and
+ *   - the chunk's own keys 0..i, in BF16 as given (causal),
+ * with softmax(sm_scale q . k) over all of them.  The chunk is not in the
+ * cache yet: call oscar_kv_write for it afterwards (on the same stream; the
+ * write replaces ring rows this call reads).
+ *   q          bf16 [num_tokens][num_q_heads][128]
+ *   k, v       bf16 [num_tokens][num_kv_heads][128]
+ *   cu_seqlens int32 [batch + 1], nondecreasing, cu_seqlens[0] = 0,
+ *              cu_seqlens[batch] = num_tokens, each chunk at most max_chunk
+ *              tokens.  On the device a chunk is clamped to [0, num_tokens)
+ *              and to max_chunk tokens; out rows no chunk covers are undefined
+ *   prefix_lens int32 [batch], 0 <= L <= 16 * max_pages (clamped on the device)
+ *   page_table int32 [batch][max_pages]; batch entry b uses sink/ring slot b
+ *   out        bf16 [num_tokens][num_q_heads][128]
+ *   workspace  >= oscar_extend_workspace_bytes(shape, num_tokens, max_pages,
+ *              max_chunk) bytes, 256-byte aligned; clobbered
+ * Returns OSCAR_OK, OSCAR_EINVAL, OSCAR_ENOWS or OSCAR_EHIP; num_tokens == 0
+ * is a no-op. */
+size_t oscar_extend_workspace_bytes(const oscar_shape_t* shape, int32_t num_tokens, int32_t max_pages,
+                                    int32_t max_chunk);
+int oscar_extend_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q,
+                      const uint16_t* k, const uint16_t* v, const int32_t* cu_seqlens,
+                      const int32_t* prefix_lens, int32_t batch, int32_t num_tokens, int32_t max_chunk,
+                      const int32_t* page_table, int32_t max_pages, float sm_scale, uint16_t* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* decode_attn_noalloc -- for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid

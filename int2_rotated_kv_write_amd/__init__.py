@@ -9,7 +9,8 @@ the first call does, and raises if the library is missing.
 """
 from ._native import load, library_path
 from .api import (
-    CacheBuffers, CacheShape, OscarError, allocate_cache, bf16_decode_attn, decode_attn_noalloc,
+    CacheBuffers, CacheShape, OscarError, allocate_cache, bf16_decode_attn, decode_attn_noalloc, extend_attn,
+    extend_workspace_bytes,
     bf16_decode_workspace_bytes, calibrate_layer, decode_attn, decode_step, decode_workspace_bytes, kv_write,
     prepare_bf16_decode_attn, prepare_decode_attn, prepare_decode_step, prepare_kv_write, prepare_read_probe,
     read_probe_sink_bytes, status_string,
@@ -21,5 +22,5 @@ __all__ = [
     "calibrate_layer", "status_string", "prepare_kv_write", "prepare_decode_attn",
     "bf16_decode_attn", "bf16_decode_workspace_bytes", "prepare_bf16_decode_attn",
     "prepare_read_probe", "read_probe_sink_bytes", "decode_step", "prepare_decode_step",
-    "decode_attn_noalloc",
+    "decode_attn_noalloc", "extend_attn", "extend_workspace_bytes",
 ]

@@ -194,6 +194,39 @@ def decode_attn_noalloc(shape: CacheShape, cache: CacheBuffers, q, page_table, s
     _check(rc)
 
 
+def extend_workspace_bytes(shape: CacheShape, num_tokens: int, max_pages: int, max_chunk: int) -> int:
+    return int(load().oscar_extend_workspace_bytes(ctypes.byref(shape.c()), num_tokens, max_pages, max_chunk))
+
+
+def extend_attn(shape: CacheShape, cache: CacheBuffers, q, k, v, cu_seqlens, prefix_lens, page_table, out,
+                workspace, max_chunk: int, sm_scale: float | None = None, stream=None) -> None:
+    """oscar_extend_attn: chunked-prefill attention.  q (bfloat16 [T][Hq][128]) of the chunk
+    tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 (int32 [B+1]) attends to the cached prefix of
+    prefix_lens[b] (int32 [B]) tokens as stored and causally to the chunk's own k, v
+    (bfloat16 [T][H_kv][128]); out bfloat16 [T][Hq][128].  The chunk is not yet in the
+    cache: write it with kv_write afterwards."""
+    import torch
+    _check_cache(shape, cache)
+    T = int(q.shape[0]) if q is not None else 0
+    B = int(prefix_lens.numel())
+    H = shape.num_kv_heads
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if page_table.dim() != 2 or page_table.shape[0] < B:
+        raise OscarError("page_table must be [>= batch][max_pages]")
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise OscarError("workspace must be a uint8 device tensor")
+    rc = load().oscar_extend_attn(
+        ctypes.byref(shape.c()), ctypes.byref(cache.c()),
+        _dev(q, torch.bfloat16, "q", (T, shape.num_q_heads, HEAD_DIM)),
+        _dev(k, torch.bfloat16, "k", (T, H, HEAD_DIM)), _dev(v, torch.bfloat16, "v", (T, H, HEAD_DIM)),
+        _dev(cu_seqlens, torch.int32, "cu_seqlens", (B + 1,)), _dev(prefix_lens, torch.int32, "prefix_lens", (B,)),
+        B, T, int(max_chunk), _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
+        float(sm_scale), _dev(out, torch.bfloat16, "out", (T, shape.num_q_heads, HEAD_DIM)),
+        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(rc)
+
+
 def bf16_decode_workspace_bytes(num_kv_heads: int, num_q_heads: int, batch: int, max_pages: int) -> int:
     return int(load().oscar_bf16_decode_workspace_bytes(num_kv_heads, num_q_heads, batch, max_pages))
 

@@ -163,9 +163,21 @@ __device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p, size_t i) {
   return ((cptr)(p))[i];
 }
 
+// A sequence length as the kernels use it: clamped to [0, the tokens a page table row of
+// max_pages pages holds], so a length outside the documented range cannot send a read
+// past the row or past the records a plan provides.
+__device__ __forceinline__ int clamp_len(int L, int max_pages) { return min(max(L, 0), kPage * max_pages); }
+
 // Make this wave's earlier LDS writes visible to its own other lanes: wait for the wave's
 // LDS operations only (a workgroup-scope fence would also wait for every global load in
 // flight, draining any prefetch), and keep the compiler from moving memory accesses across.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Block barrier for LDS data only: this wave's LDS operations complete, then s_barrier.
+// Unlike __syncthreads it does not wait for global loads in flight (a workgroup-scope fence
+// would), so a prefetch into registers or LDS keeps streaming across it.  Data a wave loaded
+// into LDS by DMA is visible to the others once that wave has waited for it (vmcnt) before
+// the barrier.
+__device__ __forceinline__ void block_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 }  // namespace oscar

@@ -52,6 +52,9 @@ struct DecodeArgs {
   float resc_thr;   // lazy rescale threshold tau: INT2 probabilities stay <= 2^tau
   int32_t H, Hq, G, B, max_pages, sink, recent, P, n_split, n_bsplit, n_total;
   int32_t bchunk;   // BF16 tokens per BF16 item (a multiple of 64)
+  // extend (chunked prefill) reduce: every row (chunk token) has exactly one BF16 record,
+  // index 0, and seq_lens holds the prefix length of the row's sequence
+  int32_t ext;
 };
 
 __device__ __forceinline__ int bf16_token_count(int L, int sink, int recent) {
@@ -418,6 +421,222 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 __device__ __forceinline__ float rows_max(float x) { return swap32(swap16(x, true), true); }
 __device__ __forceinline__ float rows_sum(float x) { return swap32(swap16(x, false), false); }
 
+// Per-lane constants of the INT2 page math (lane l: n = l % 16, r = l / 16; logit MFMA
+// column n = 4 hh + a4 with a4 = group gp + 2 limb) and the q' operands of its NQ quads.
+template <int NQ>
+struct Int2Lane {
+  int r, a4, gp, limb;
+  int off_kc, off_kp, off_vp, off_vw;   // this lane's byte offsets inside a page block
+  uint32_t perm_sel;
+  uint32_t wsel[4];
+  PairConsts pk;
+  half2v nbase;
+  float tau;
+  half8 qb[NQ][2][2];
+  float cinit[NQ], qs[NQ];
+};
+
+// Running softmax state of the lane's NQ quads: m (reference maximum), hm = -m / 2, the
+// lane's share of l, the zero-point sums and the value accumulators.
+template <int NQ>
+struct Int2State {
+  float m[NQ], hm[NQ], lsum[NQ], zs[NQ][2];
+  f32x4 acc[NQ][8];
+};
+
+// Lane constants (everything but the q' operands) and a zero state.
+template <int NQ>
+__device__ __forceinline__ void int2_lane_init(Int2Lane<NQ>& L, int lane, float tau) {
+  const int n = lane & 15;
+  L.r = lane >> 4;
+  L.a4 = n & 3;
+  L.gp = L.a4 & 1;
+  L.limb = L.a4 >> 1;
+  const int t0 = 4 * L.r + 2 * L.limb;
+  L.off_kc = kKCodes + 32 * n + 4 * L.r;        // token n: code word r of group 0 (+16: group 1)
+  L.off_kp = kKParams + 8 * t0 + 4 * L.gp;      // (s, z) of group gp, tokens t0 and t0 + 1
+  L.off_vp = kVParams + 8 * (4 * L.r + L.a4);   // (s0, z0, s1, z1) of token 4r + a4
+  L.off_vw = kVCodes + 4 * n;                   // value code word of channel 16t + n at + 64t
+  L.perm_sel = (uint32_t)L.r | (0x0Cu << 8) | ((4u + L.r) << 16) | (0x0Cu << 24);
+  // the value B operand's dword a4 carries fp16 base 64 (a4 even) or 16 (odd) on both
+  // halves: this lane's weights (dword a4 of A) pick up -base each
+  L.nbase = L.a4 & 1 ? half2v{(_Float16)-16.f, (_Float16)-16.f} : half2v{(_Float16)-64.f, (_Float16)-64.f};
+  L.tau = tau;
+  // byte selectors placing the weight limbs in the A operand (v_perm: bytes 4-7 = hi, 0-3 =
+  // lo, 0x0C = zero): dword a4 takes the hi limb, dword (a4 + 1) % 4 the lo limb from lane a4 + 1
+#pragma unroll
+  for (int d = 0; d < 4; ++d) L.wsel[d] = L.a4 == d ? 0x07060504u : ((L.a4 + 1) & 3) == d ? 0x03020100u : 0x0C0C0C0Cu;
+}
+
+template <int NQ>
+__device__ __forceinline__ void int2_state_init(Int2State<NQ>& st) {
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    st.m[qd] = 0.f;   // set by the first pair, which always takes the rescale branch
+    st.hm[qd] = 0.f;
+    st.lsum[qd] = 0.f;
+    st.zs[qd][0] = st.zs[qd][1] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.acc[qd][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// One pair of INT2 pages (blocks blk0 = logical page pp, blk1 = pp + 1, both in LDS): logits,
+// online softmax and value accumulation for the lane's quads.  has1: page pp + 1 exists
+// (otherwise its block holds stale bytes and is weighted 0); i_hi: first position past the
+// INT2 tokens; first: the pair starts the item (forces the first rescale).
+template <int NQ>
+__device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>& L, const uint8_t* blk0,
+                                          const uint8_t* blk1, bool has1, int pp, int i_hi, bool first) {
+  struct PageRegs {
+    uint32_t kc[2];   // token n: code words r of group 0 and of group 1
+    uint32_t kp[2];   // (s, z) of group gp for tokens 4r + 2 limb and + 1
+    uint32_t vp[2];   // (s0, z0), (s1, z1) of token 4r + a4
+    uint32_t vw[8];   // value code words of channels 16t + n
+  } cur[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint8_t* blk = k ? blk1 : blk0;   // without page pp + 1 its block holds stale bytes
+    cur[k].kc[0] = *reinterpret_cast<const uint32_t*>(blk + L.off_kc);
+    cur[k].kc[1] = *reinterpret_cast<const uint32_t*>(blk + L.off_kc + 16);
+    cur[k].kp[0] = *reinterpret_cast<const uint32_t*>(blk + L.off_kp);
+    cur[k].kp[1] = *reinterpret_cast<const uint32_t*>(blk + L.off_kp + 8);
+    const uint2 v2 = *reinterpret_cast<const uint2*>(blk + L.off_vp);
+    cur[k].vp[0] = v2.x;
+    cur[k].vp[1] = v2.y;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cur[k].vw[t] = *reinterpret_cast<const uint32_t*>(blk + L.off_vw + 64 * t);
+  }
+
+  // ---- logits: lane (r, hh, a4) ends with token 4r + a4 of head 4 qd + hh ----
+  // all MFMA chains of both pages first, so they overlap each other's latency
+  f32x4 dq[2][NQ];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    uint32_t e0[8], e1[8];
+    unpack16(cur[k].kc[0], e0, L.pk);
+    unpack16(cur[k].kc[1], e1, L.pk);
+    const half8 a00 = half8_of(e0[0], e0[1], e0[2], e0[3]), a01 = half8_of(e0[4], e0[5], e0[6], e0[7]);
+    const half8 a10 = half8_of(e1[0], e1[1], e1[2], e1[3]), a11 = half8_of(e1[4], e1[5], e1[6], e1[7]);
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      f32x4 d = f32x4{L.cinit[qd], L.cinit[qd], L.cinit[qd], L.cinit[qd]};
+      d = mfma16(a00, L.qb[qd][0][0], d);
+      d = mfma16(a01, L.qb[qd][0][1], d);
+      d = mfma16(a10, L.qb[qd][1][0], d);
+      d = mfma16(a11, L.qb[qd][1][1], d);
+      dq[k][qd] = d;
+    }
+  }
+  float lg[NQ][2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const PageRegs& P = cur[k];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const f32x4 d = dq[k][qd];
+      // limbs: partner lane ^ 2 holds the other limb of the same group
+      const float u0 = d[0] + dpp<kQuadXor2>(d[0]), u1 = d[1] + dpp<kQuadXor2>(d[1]);
+      const float u2 = d[2] + dpp<kQuadXor2>(d[2]), u3 = d[3] + dpp<kQuadXor2>(d[3]);
+      const float y0 = L.limb ? u2 : u0, y1 = L.limb ? u3 : u1;
+      // scale and zero-point term of group gp (tokens 4r + 2 limb, + 1)
+      const float x0 = fmaf(f16_bits_to_f32(P.kp[0]), y0, fmaf(f16_bits_to_f32(P.kp[0] >> 16), L.qs[qd], st.hm[qd]));
+      const float x1 = fmaf(f16_bits_to_f32(P.kp[1]), y1, fmaf(f16_bits_to_f32(P.kp[1] >> 16), L.qs[qd], st.hm[qd]));
+      // groups: partner lane ^ 1 holds the other group of the same tokens
+      const float v0 = x0 + dpp<kQuadXor1>(x0), v1 = x1 + dpp<kQuadXor1>(x1);
+      lg[qd][k] = L.gp ? v1 : v0;
+    }
+  }
+  if (!has1 || (pp + 2) * kPage > i_hi) {   // wave-uniform: only the last pair can hold missing tokens
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const bool ok = (k == 0 || has1) && (pp + k) * kPage + 4 * L.r + L.a4 < i_hi;
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) lg[qd][k] = ok ? lg[qd][k] : -INFINITY;
+      // the value parameters of a masked slot (this lane's token in the value MFMA and
+      // the zero-point sum) may be anything, NaN included: slots at or past the
+      // sequence length were never written.  With s = z = 0 they contribute 0 * finite.
+      cur[k].vp[0] = ok ? cur[k].vp[0] : 0u;
+      cur[k].vp[1] = ok ? cur[k].vp[1] : 0u;
+    }
+  }
+
+  // ---- online softmax per head (logits are relative to m); rescale only when the max
+  // grows by more than tau.  A lane test first: the head maxima are reduced only on the
+  // rare pairs that rescale.
+  bool need_any = first;
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) need_any |= fmaxf(lg[qd][0], lg[qd][1]) > L.tau;
+  if (__any(need_any)) {
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      float pm = fmaxf(lg[qd][0], lg[qd][1]);
+      pm = fmaxf(pm, dpp<kQuadXor1>(pm));
+      pm = fmaxf(pm, dpp<kQuadXor2>(pm));
+      pm = rows_max(pm);   // finite: every pair has a valid token
+      const float dm = first || pm > L.tau ? pm : 0.f;
+      const float al = fast_exp2(-dm);
+      st.m[qd] += dm;
+      st.hm[qd] = -0.5f * st.m[qd];
+      lg[qd][0] -= dm;
+      lg[qd][1] -= dm;
+      st.lsum[qd] *= al;
+      st.zs[qd][0] *= al;
+      st.zs[qd][1] *= al;
+      const float ai = __shfl(al, 4 * L.r);   // accumulator rows of this lane belong to head hh' = r
+#pragma unroll
+      for (int t = 0; t < 8; ++t) st.acc[qd][t] *= ai;
+    }
+  }
+
+  // ---- weights W_g = p s_g of this lane's token in both pages as fp16 hi + lo ----
+  // A single fp16 rounding of p s_g would leave a relative error on the code part of the
+  // token's value but not on its zero-point part p z_g; the codes' common level (about 1.5)
+  // turns that into an error shared by all 64 channels of the group, which the inverse
+  // rotation concentrates in one or two output channels.  With hi + lo the products are
+  // exact to about 2^-22.  Row (hh, a4) of the value MFMA carries the hi limb of token a4
+  // at k-slot a4 and the lo limb of token (a4 + 1) % 4 (from the next lane of the quad)
+  // at that token's k-slot; the four rows of a head are summed at the end.
+  half8 A[NQ][2];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    const float p0 = fast_exp2(lg[qd][0]), p1 = fast_exp2(lg[qd][1]);
+    st.lsum[qd] += p0 + p1;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      // (s_g, z_g) of the token in each page
+      const half2v sz0 = __builtin_bit_cast(half2v, cur[0].vp[g]), sz1 = __builtin_bit_cast(half2v, cur[1].vp[g]);
+      st.zs[qd][g] = fmaf(p0, (float)sz0[1], fmaf(p1, (float)sz1[1], st.zs[qd][g]));
+      const float ps0 = fmaf(p0, (float)sz0[0], 0.f), ps1 = fmaf(p1, (float)sz1[0], 0.f);
+      // hi = fp16(p s) rounded toward zero (one packed conversion for both pages), lo = the
+      // rest: hi + lo carries p s to about 2^-21 relative whatever hi's rounding
+      const half2v hi2 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ps0, ps1));
+      const half2v lo2 = half2v{(_Float16)fmaf(p0, (float)sz0[0], -(float)hi2[0]),
+                                (_Float16)fmaf(p1, (float)sz1[0], -(float)hi2[1])};
+      // the fp16 bases the value MFMA adds at this token's k-slot, times both limbs
+      st.zs[qd][g] = __builtin_amdgcn_fdot2(hi2, L.nbase, st.zs[qd][g], false);
+      st.zs[qd][g] = __builtin_amdgcn_fdot2(lo2, L.nbase, st.zs[qd][g], false);
+      const uint32_t wh = __builtin_bit_cast(uint32_t, hi2);
+      // lo of the next lane of the quad (every quad lane has a source)
+      const uint32_t wl = (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, lo2), kQuadRot1, 0xF, 0xF, true);
+      A[qd][g] = half8_of(__builtin_amdgcn_perm(wh, wl, L.wsel[0]), __builtin_amdgcn_perm(wh, wl, L.wsel[1]),
+                          __builtin_amdgcn_perm(wh, wl, L.wsel[2]), __builtin_amdgcn_perm(wh, wl, L.wsel[3]));
+    }
+  }
+
+  // ---- values ----
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    // slots 4r + d of both pages: d = 0, 1 from x << 4 (bits 4-5, 6-7), d = 2, 3 from x
+    const uint32_t x = __builtin_amdgcn_perm(cur[1].vw[t], cur[0].vw[t], L.perm_sel);
+    const uint32_t l4 = x << 4;
+    const half8 bv = half8_of((l4 & L.pk.m64) | L.pk.b64, (l4 & L.pk.m16) | L.pk.b16, (x & L.pk.m64) | L.pk.b64,
+                              (x & L.pk.m16) | L.pk.b16);
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) st.acc[qd][t] = mfma16(A[qd][t >> 2], bv, st.acc[qd][t]);
+  }
+}
+
 // INT2 history pages [first, end), two pages (32 tokens) per step; wave w
 // takes the pairs starting at first + 2w, + 8, ...  The G query heads are
 // handled in quads (NQ = ceil(G / 4)); lane l: n = l % 16, r = l / 16, and
@@ -497,46 +716,25 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
                      "+v"(qraw[qd][g][kh].w));
     asm volatile("" : "+v"(craw[qd]), "+v"(sraw[qd]));
   }
-  half8 qb[NQ][2][2];
-  float cinit[NQ], qs[NQ];
+  Int2Lane<NQ> ln;
+  int2_lane_init(ln, lane, a.resc_thr);
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
     const bool ok = 4 * qd + hh < G;
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) qb[qd][g][kh] = half8_of(ok && g == gp ? qraw[qd][g][kh] : make_uint4(0, 0, 0, 0));
-    cinit[qd] = ok ? craw[qd] : 0.f;
-    qs[qd] = ok ? sraw[qd] : 0.f;
+      for (int kh = 0; kh < 2; ++kh)
+        ln.qb[qd][g][kh] = half8_of(ok && g == gp ? qraw[qd][g][kh] : make_uint4(0, 0, 0, 0));
+    ln.cinit[qd] = ok ? craw[qd] : 0.f;
+    ln.qs[qd] = ok ? sraw[qd] : 0.f;
   }
-
   // zs[g]: per-head correction of group g's channels, sum over tokens of p z_g minus the
-  // fp16 bases the value MFMA adds (base * W_g), accumulated by v_dot2
-  // m: running reference maximum of the head's logits; logits are formed relative to it
-  // (each of the two group terms carries hm = -m / 2)
-  float m[NQ], hm[NQ], lsum[NQ], zs[NQ][2];
-  f32x4 acc[NQ][8];
-#pragma unroll
-  for (int qd = 0; qd < NQ; ++qd) {
-    m[qd] = 0.f;     // set by the first pair, which always takes the rescale branch
-    hm[qd] = 0.f;
-    lsum[qd] = 0.f;
-    zs[qd][0] = zs[qd][1] = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[qd][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const uint32_t perm_sel = (uint32_t)r | (0x0Cu << 8) | ((4u + r) << 16) | (0x0Cu << 24);
-  const PairConsts pk;
-  // the value B operand's dword a4 carries fp16 base 64 (a4 even) or 16 (odd) on both
-  // halves: this lane's weights (dword a4 of A) pick up -base each
-  const half2v nbase = a4 & 1 ? half2v{(_Float16)-16.f, (_Float16)-16.f} : half2v{(_Float16)-64.f, (_Float16)-64.f};
-  const float tau = a.resc_thr;
-  // byte selectors placing the weight limbs in the A operand (v_perm: bytes 4-7 = hi, 0-3 = lo,
-  // 0x0C = zero): dword a4 takes the hi limb, dword (a4 + 1) % 4 the lo limb from lane a4 + 1
-  uint32_t wsel[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) wsel[d] = a4 == d ? 0x07060504u : ((a4 + 1) & 3) == d ? 0x03020100u : 0x0C0C0C0Cu;
-
+  // fp16 bases the value MFMA adds (base * W_g), accumulated by v_dot2; m: running reference
+  // maximum of the head's logits, which are formed relative to it (each of the two group
+  // terms carries hm = -m / 2)
+  Int2State<NQ> st;
+  int2_state_init(st);
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
   const uint32_t off16 = 16 * lane, off4 = 1024 + 4 * lane;   // this lane's bytes of a page block
   // the wave's page blocks as offsets from `pages` in 256-byte units (page id x H x 5 +
@@ -563,12 +761,6 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // before any page lands in these slots
   }
   for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(j, j);
-  // this lane's byte offsets inside a page block
-  const int t0 = 4 * r + 2 * limb;
-  const int off_kc = kKCodes + 32 * n + 4 * r;            // token n: code word r of group 0 (+16: group 1)
-  const int off_kp = kKParams + 8 * t0 + 4 * gp;          // (s, z) of group gp, tokens t0 and t0 + 1
-  const int off_vp = kVParams + 8 * (4 * r + a4);         // (s0, z0, s1, z1) of token 4r + a4
-  const int off_vw = kVCodes + 4 * n;                     // value code word of channel 16t + n at + 64t
 
   // unrolled over one turn of the ring, so every slot offset is an immediate
   for (int j0 = 0; j0 < n_w; j0 += kRing)
@@ -586,153 +778,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    struct PageRegs {
-      uint32_t kc[2];   // token n: code words r of group 0 and of group 1
-      uint32_t kp[2];   // (s, z) of group gp for tokens 4r + 2 limb and + 1
-      uint32_t vp[2];   // (s0, z0), (s1, z1) of token 4r + a4
-      uint32_t vw[8];   // value code words of channels 16t + n
-    } cur[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint8_t* blk = &sm.ring[wave][2 * u + k][0];   // without page j + 1 its slot holds stale bytes
-      cur[k].kc[0] = *reinterpret_cast<const uint32_t*>(blk + off_kc);
-      cur[k].kc[1] = *reinterpret_cast<const uint32_t*>(blk + off_kc + 16);
-      cur[k].kp[0] = *reinterpret_cast<const uint32_t*>(blk + off_kp);
-      cur[k].kp[1] = *reinterpret_cast<const uint32_t*>(blk + off_kp + 8);
-      const uint2 v2 = *reinterpret_cast<const uint2*>(blk + off_vp);
-      cur[k].vp[0] = v2.x;
-      cur[k].vp[1] = v2.y;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) cur[k].vw[t] = *reinterpret_cast<const uint32_t*>(blk + off_vw + 64 * t);
-    }
-
-    // ---- logits: lane (r, hh, a4) ends with token 4r + a4 of head 4 qd + hh ----
-    // all MFMA chains of both pages first, so they overlap each other's latency
-    f32x4 dq[2][NQ];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      uint32_t e0[8], e1[8];
-      unpack16(cur[k].kc[0], e0, pk);
-      unpack16(cur[k].kc[1], e1, pk);
-      const half8 a00 = half8_of(e0[0], e0[1], e0[2], e0[3]), a01 = half8_of(e0[4], e0[5], e0[6], e0[7]);
-      const half8 a10 = half8_of(e1[0], e1[1], e1[2], e1[3]), a11 = half8_of(e1[4], e1[5], e1[6], e1[7]);
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
-        f32x4 d = f32x4{cinit[qd], cinit[qd], cinit[qd], cinit[qd]};
-        d = mfma16(a00, qb[qd][0][0], d);
-        d = mfma16(a01, qb[qd][0][1], d);
-        d = mfma16(a10, qb[qd][1][0], d);
-        d = mfma16(a11, qb[qd][1][1], d);
-        dq[k][qd] = d;
-      }
-    }
-    float lg[NQ][2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const PageRegs& P = cur[k];
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
-        const f32x4 d = dq[k][qd];
-        // limbs: partner lane ^ 2 holds the other limb of the same group
-        const float u0 = d[0] + dpp<kQuadXor2>(d[0]), u1 = d[1] + dpp<kQuadXor2>(d[1]);
-        const float u2 = d[2] + dpp<kQuadXor2>(d[2]), u3 = d[3] + dpp<kQuadXor2>(d[3]);
-        const float y0 = limb ? u2 : u0, y1 = limb ? u3 : u1;
-        // scale and zero-point term of group gp (tokens 4r + 2 limb, + 1)
-        const float x0 = fmaf(f16_bits_to_f32(P.kp[0]), y0, fmaf(f16_bits_to_f32(P.kp[0] >> 16), qs[qd], hm[qd]));
-        const float x1 = fmaf(f16_bits_to_f32(P.kp[1]), y1, fmaf(f16_bits_to_f32(P.kp[1] >> 16), qs[qd], hm[qd]));
-        // groups: partner lane ^ 1 holds the other group of the same tokens
-        const float v0 = x0 + dpp<kQuadXor1>(x0), v1 = x1 + dpp<kQuadXor1>(x1);
-        lg[qd][k] = gp ? v1 : v0;
-      }
-    }
-    if (!has1 || (pp + 2) * kPage > i_hi) {   // wave-uniform: only the last pair can hold missing tokens
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const bool ok = (k == 0 || has1) && (pp + k) * kPage + 4 * r + a4 < i_hi;
-#pragma unroll
-        for (int qd = 0; qd < NQ; ++qd) lg[qd][k] = ok ? lg[qd][k] : -INFINITY;
-        // the value parameters of a masked slot (this lane's token in the value MFMA and
-        // the zero-point sum) may be anything, NaN included: slots at or past the
-        // sequence length were never written.  With s = z = 0 they contribute 0 * finite.
-        cur[k].vp[0] = ok ? cur[k].vp[0] : 0u;
-        cur[k].vp[1] = ok ? cur[k].vp[1] : 0u;
-      }
-    }
-
-    // ---- online softmax per head (logits are relative to m); rescale only when the max
-    // grows by more than tau.  A lane test first: the head maxima are reduced only on the
-    // rare pairs that rescale.
-    bool need_any = j == 0;
-#pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) need_any |= fmaxf(lg[qd][0], lg[qd][1]) > tau;
-    if (__any(need_any)) {
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
-        float pm = fmaxf(lg[qd][0], lg[qd][1]);
-        pm = fmaxf(pm, dpp<kQuadXor1>(pm));
-        pm = fmaxf(pm, dpp<kQuadXor2>(pm));
-        pm = rows_max(pm);   // finite: every pair has a valid token
-        const float dm = j == 0 || pm > tau ? pm : 0.f;
-        const float al = fast_exp2(-dm);
-        m[qd] += dm;
-        hm[qd] = -0.5f * m[qd];
-        lg[qd][0] -= dm;
-        lg[qd][1] -= dm;
-        lsum[qd] *= al;
-        zs[qd][0] *= al;
-        zs[qd][1] *= al;
-        const float ai = __shfl(al, 4 * r);   // accumulator rows of this lane belong to head hh' = r
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[qd][t] *= ai;
-      }
-    }
-
-    // ---- weights W_g = p s_g of this lane's token in both pages as fp16 hi + lo ----
-    // A single fp16 rounding of p s_g would leave a relative error on the code part of the
-    // token's value but not on its zero-point part p z_g; the codes' common level (about 1.5)
-    // turns that into an error shared by all 64 channels of the group, which the inverse
-    // rotation concentrates in one or two output channels.  With hi + lo the products are
-    // exact to about 2^-22.  Row (hh, a4) of the value MFMA carries the hi limb of token a4
-    // at k-slot a4 and the lo limb of token (a4 + 1) % 4 (from the next lane of the quad)
-    // at that token's k-slot; the four rows of a head are summed at the end.
-    half8 A[NQ][2];
-#pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) {
-      const float p0 = fast_exp2(lg[qd][0]), p1 = fast_exp2(lg[qd][1]);
-      lsum[qd] += p0 + p1;
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        // (s_g, z_g) of the token in each page
-        const half2v sz0 = __builtin_bit_cast(half2v, cur[0].vp[g]), sz1 = __builtin_bit_cast(half2v, cur[1].vp[g]);
-        zs[qd][g] = fmaf(p0, (float)sz0[1], fmaf(p1, (float)sz1[1], zs[qd][g]));
-        const float ps0 = fmaf(p0, (float)sz0[0], 0.f), ps1 = fmaf(p1, (float)sz1[0], 0.f);
-        // hi = fp16(p s) rounded toward zero (one packed conversion for both pages), lo = the
-        // rest: hi + lo carries p s to about 2^-21 relative whatever hi's rounding
-        const half2v hi2 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ps0, ps1));
-        const half2v lo2 = half2v{(_Float16)fmaf(p0, (float)sz0[0], -(float)hi2[0]),
-                                  (_Float16)fmaf(p1, (float)sz1[0], -(float)hi2[1])};
-        // the fp16 bases the value MFMA adds at this token's k-slot, times both limbs
-        zs[qd][g] = __builtin_amdgcn_fdot2(hi2, nbase, zs[qd][g], false);
-        zs[qd][g] = __builtin_amdgcn_fdot2(lo2, nbase, zs[qd][g], false);
-        const uint32_t wh = __builtin_bit_cast(uint32_t, hi2);
-        // lo of the next lane of the quad (every quad lane has a source)
-        const uint32_t wl = (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, lo2), kQuadRot1, 0xF, 0xF, true);
-        A[qd][g] = half8_of(__builtin_amdgcn_perm(wh, wl, wsel[0]), __builtin_amdgcn_perm(wh, wl, wsel[1]),
-                            __builtin_amdgcn_perm(wh, wl, wsel[2]), __builtin_amdgcn_perm(wh, wl, wsel[3]));
-      }
-    }
-
-    // ---- values ----
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      // slots 4r + d of both pages: d = 0, 1 from x << 4 (bits 4-5, 6-7), d = 2, 3 from x
-      const uint32_t x = __builtin_amdgcn_perm(cur[1].vw[t], cur[0].vw[t], perm_sel);
-      const uint32_t l4 = x << 4;
-      const half8 bv = half8_of((l4 & pk.m64) | pk.b64, (l4 & pk.m16) | pk.b16, (x & pk.m64) | pk.b64,
-                                (x & pk.m16) | pk.b16);
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) acc[qd][t] = mfma16(A[qd][t >> 2], bv, acc[qd][t]);
-    }
+    int2_pair<NQ>(st, ln, &sm.ring[wave][2 * u][0], &sm.ring[wave][2 * u + 1][0], has1, pp, i_hi, j == 0);
   }
 
   // ---- finish the wave: its result goes to its own ring (all of its page loads have landed) ----
@@ -740,13 +786,13 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
     // per-head totals over the 16 lanes of head hh (quad, then rows)
-    float L_h = lsum[qd], Z0 = zs[qd][0], Z1 = zs[qd][1];
+    float L_h = st.lsum[qd], Z0 = st.zs[qd][0], Z1 = st.zs[qd][1];
     L_h = rows_sum(quad_sum(L_h));
     Z0 = rows_sum(quad_sum(Z0));
     Z1 = rows_sum(quad_sum(Z1));
     const int head = 4 * qd + hh;
     if (r == 0 && a4 == 0 && head < G) {
-      res.m[head] = n_w > 0 ? m[qd] : -INFINITY;   // a wave without pages contributes nothing
+      res.m[head] = n_w > 0 ? st.m[qd] : -INFINITY;   // a wave without pages contributes nothing
       res.l[head] = L_h;
     }
     // accumulator rows of this lane: head 4 qd + r, subsets j = 0..3
@@ -755,7 +801,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     if (row_head < G) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float s = (acc[qd][t][0] + acc[qd][t][1]) + (acc[qd][t][2] + acc[qd][t][3]);
+        const float s = (st.acc[qd][t][0] + st.acc[qd][t][1]) + (st.acc[qd][t][2] + st.acc[qd][t][3]);
         res.acc[row_head][16 * t + n] = s + (t < 4 ? z0 : z1);
       }
     }
@@ -773,7 +819,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   const int bh = w < n_int2 ? w / a.n_split : (w - n_int2) / a.n_bsplit;
   const int item = w < n_int2 ? a.n_bsplit + (w - bh * a.n_split) : (w - n_int2) - bh * a.n_bsplit;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int L = a.seq_lens[b];
+  const int L = clamp_len(a.seq_lens[b], a.max_pages);
   if (item < a.n_bsplit) {
     if (item * a.bchunk >= bf16_token_count(L, a.sink, a.recent)) return;
     bf16_item<G>(a, b, h, item, L, sm);
@@ -822,7 +868,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, kg = lane >> 4;
   const int head0 = h * G + gq * GB;   // first query head of this block
-  const int L = scalar_load_i32(a.seq_lens, b);
+  const int L = clamp_len(scalar_load_i32(a.seq_lens, b), a.max_pages);
   // B fragments of the final product, requested first: wave w makes output channels
   // 32 w .. 32 w + 31 (column tiles nt = 2 w + t); lane (n, kg) holds U_V[16 nt + n][32 ks + 8 kg, + 8)
   bf16x8 ub[2][4];
@@ -834,11 +880,11 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
       for (int ks = 0; ks < 4; ++ks)
         ub[t][ks] = *reinterpret_cast<const bf16x8*>(U + (32 * wave + 16 * t + n) * kHeadDim + 32 * ks + 8 * kg);
   }
-  if (L == 0) {
+  if (L == 0 && !a.ext) {
     for (int e = tid; e < GB * kHeadDim; e += 256) a.out[((size_t)b * a.Hq + head0) * kHeadDim + e] = 0;
     return;
   }
-  const int n_b = (bf16_token_count(L, a.sink, a.recent) + a.bchunk - 1) / a.bchunk;
+  const int n_b = a.ext ? 1 : (bf16_token_count(L, a.sink, a.recent) + a.bchunk - 1) / a.bchunk;
   const int i_hi = int2_end(L, a.sink, a.recent);
   const int int2_pages = i_hi > a.sink ? (i_hi + kPage - 1) / kPage - a.sink / kPage : 0;
   const int n_i = (int2_pages + a.P - 1) / a.P;
@@ -984,6 +1030,274 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// extend (chunked prefill): the queries of a chunk attend to the cached
+// prefix as stored and causally to the chunk's own BF16 keys.  Rows are chunk
+// tokens (global index t); each (row, query head) gets one BF16 record (index
+// 0: sink rows, ring rows and chunk keys) and one record per INT2 range of the
+// prefix (indices 1 ..), merged by reduce_kernel in extend mode.
+// ---------------------------------------------------------------------------
+struct ExtArgs {
+  DecodeArgs d;                 // qrot / part / part_ml over rows = chunk tokens; seq_lens -> row_len
+  const uint16_t *k_new, *v_new;   // bf16 [T][H][128]
+  const int32_t *cu, *prefix_lens;
+  int32_t* row_len;             // [T]: prefix length of the row's sequence (written by the BF16 kernel)
+  int32_t n_seq, n_tok, max_chunk;
+  int32_t n_qt;                 // 16-query-head tiles per (sequence, KV head)
+};
+
+// Sequence b's chunk: tokens t0 .. t0 + chunk - 1, clamped to [0, n_tok) and to at most
+// max_chunk tokens (the grids cover no more), so inconsistent offsets cannot send a write
+// past the output.
+__device__ __forceinline__ void chunk_of(const ExtArgs& e, int b, int& t0, int& chunk) {
+  t0 = min(max(scalar_load_i32(e.cu, b), 0), e.n_tok);
+  chunk = min(min(scalar_load_i32(e.cu, b + 1) - t0, e.max_chunk), e.n_tok - t0);
+  chunk = max(chunk, 0);
+}
+
+constexpr int kMqRing = 8;   // pages per block ring of the multi-query INT2 kernel
+
+struct __attribute__((aligned(16))) MqSmem {
+  uint8_t ring[kMqRing][kBlockBytes];
+};
+
+// INT2 prefix pages of one range of one (sequence, KV head), read once per block and used by
+// all four waves: wave w owns query heads 16 qt + 4 w .. + 3 of the sequence's chunk (query
+// head e = chunk position * G + head in the group).  Page j is loaded by wave j % 4; before a
+// pair is read every wave waits for its own loads of it and the block synchronises, which
+// also frees the slots of the previous pair for the next loads.
+template <int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void ext_int2_kernel(ExtArgs e) {
+  __shared__ MqSmem sm;
+  const DecodeArgs& a = e.d;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, r = lane >> 4, hh = n >> 2;
+  int job = blockIdx.x;
+  const int qt = job % e.n_qt;
+  job /= e.n_qt;
+  const int split = job % a.n_split;
+  job /= a.n_split;
+  const int h = job % a.H, b = job / a.H;
+  int t0, chunk;
+  chunk_of(e, b, t0, chunk);
+  const int L = clamp_len(scalar_load_i32(e.prefix_lens, b), a.max_pages);
+  const int i_hi = int2_end(L, a.sink, a.recent);
+  const int first = a.sink / kPage + split * a.P;
+  const int end = min(first + a.P, (i_hi + kPage - 1) / kPage);
+  const int e_block = 16 * qt;
+  if (i_hi <= a.sink || first >= end || e_block >= chunk * G) return;   // block-uniform
+  const int np = end - first;
+
+  // this lane's query head (column n of the logit MFMA: head hh of the wave's quad)
+  const int e_q = e_block + 4 * wave + hh;
+  const bool q_ok = e_q < chunk * G;
+  const int row = t0 + (q_ok ? e_q / G : 0), hq = h * G + (q_ok ? e_q % G : 0);
+  Int2Lane<1> ln;
+  int2_lane_init(ln, lane, a.resc_thr);
+  // the block offsets (256-byte units) of the pages this wave loads, j = wave + 4 m: lane l
+  // holds m = l + 64 k
+  constexpr int kIdRegs = kMaxPagesPerSplit / 4 / 64;
+  uint32_t unit_reg[kIdRegs];
+  {
+    const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+    const uint32_t per_page = (uint32_t)a.H * (kBlockBytes / 256), head_units = (uint32_t)h * (kBlockBytes / 256);
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k)
+      unit_reg[k] = (uint32_t)ptab[first + min(wave + 4 * (lane + 64 * k), np - 1)] * per_page + head_units;
+    const QrotRecord* rec = a.qrot + ((size_t)row * a.Hq + hq);
+    uint4 qraw[2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) qraw[g][kh] = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][ln.limb][r][0]);
+    float craw = rec->negc[ln.gp][ln.limb], sraw = rec->qsum[ln.gp];
+    // consumed here, before any page load: no wait for them lands in the page loop
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(unit_reg[k]));
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        asm volatile("" : "+v"(qraw[g][kh].x), "+v"(qraw[g][kh].y), "+v"(qraw[g][kh].z), "+v"(qraw[g][kh].w));
+        ln.qb[0][g][kh] = half8_of(q_ok && g == ln.gp ? qraw[g][kh] : make_uint4(0, 0, 0, 0));
+      }
+    asm volatile("" : "+v"(craw), "+v"(sraw));
+    ln.cinit[0] = q_ok ? craw : 0.f;
+    ln.qs[0] = q_ok ? sraw : 0.f;
+  }
+  Int2State<1> st;
+  int2_state_init(st);
+  auto issue = [&](int j) {   // page j of the range (first + j) into slot j % kMqRing, by wave j % 4
+    if ((j & 3) != wave) return;
+    const int m = j >> 2;
+    const uint32_t u = __builtin_amdgcn_readlane(m < 64 ? unit_reg[0] : unit_reg[1], m & 63);
+    const uint8_t* blk = a.pages + ((uint64_t)u << 8);
+    const uint32_t dst = (uint32_t)(uintptr_t)&sm.ring[j % kMqRing][0];
+    dma_page_to_lds(blk, 16 * lane, 1024 + 4 * lane, dst, dst + 1024);
+  };
+  // the V parameters of every slot start at zero (a missing second page of the last pair is
+  // read anyway and weighted 0; its scales must be finite)
+  if (threadIdx.x < kMqRing * 8)
+    *reinterpret_cast<uint4*>(&sm.ring[threadIdx.x >> 3][kVParams + 16 * (threadIdx.x & 7)]) = make_uint4(0, 0, 0, 0);
+  block_lds_barrier();
+  for (int j = 0; j < kMqRing - 2 && j < np; ++j) issue(j);
+  for (int j = 0; j < np; j += 2) {
+    // this wave's loads of pages j, j + 1 have landed: of its later loads, exactly one page
+    // (two instructions) is among j + 2 .. j + 5 when all of those exist
+    if (j + 5 < np) {
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    block_lds_barrier();   // pages j, j + 1 visible to every wave; slots of pair j - 2 no longer read
+    if (j + kMqRing - 2 < np) issue(j + kMqRing - 2);
+    if (j + kMqRing - 1 < np) issue(j + kMqRing - 1);
+    int2_pair<1>(st, ln, &sm.ring[j % kMqRing][0], &sm.ring[(j + 1) % kMqRing][0], j + 1 < np, first + j, i_hi,
+                 j == 0);
+  }
+  // ---- the wave's quad: one record per query head ----
+  float L_h = rows_sum(quad_sum(st.lsum[0]));
+  float Z0 = rows_sum(quad_sum(st.zs[0][0])), Z1 = rows_sum(quad_sum(st.zs[0][1]));
+  const size_t rec_base = (size_t)a.n_total;
+  if (r == 0 && ln.a4 == 0 && q_ok)
+    a.part_ml[((size_t)row * a.Hq + hq) * rec_base + 1 + split] = make_float2(st.m[0], L_h);
+  // accumulator rows of this lane: head r of the quad
+  const float z0 = __shfl(Z0, 4 * r), z1 = __shfl(Z1, 4 * r);
+  const int e_r = e_block + 4 * wave + r;
+  if (e_r < chunk * G) {
+    const int row_r = t0 + e_r / G, hq_r = h * G + e_r % G;
+    float* dst = a.part + (((size_t)row_r * a.Hq + hq_r) * rec_base + 1 + split) * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float sum = (st.acc[0][t][0] + st.acc[0][t][1]) + (st.acc[0][t][2] + st.acc[0][t][3]);
+      dst[16 * t + n] = sum + (t < 4 ? z0 : z1);
+    }
+  }
+}
+
+// BF16 keys of a chunk query: the prefix's sink rows [0, min(sink, L)), its ring rows
+// [max(sink, L - recent), L) as stored, and the chunk's keys 0..i from the input (causal).
+// Block (sequence, KV head, group of 4 chunk positions); wave w takes position 4 ig + w and
+// all G query heads, 16 keys per round (lane: key lane / 4, channels 32 (lane % 4) ..; for
+// the values channels 2 lane, + 1), the next round's rows requested before this round's math.
+struct __attribute__((aligned(16))) ExtB16Smem {
+  uint4 q[4][kMaxGqa][kHeadDim / 8];
+  float p[4][kMaxGqa][16];
+};
+
+template <int G>
+__global__ __launch_bounds__(256) void ext_bf16_kernel(ExtArgs e) {
+  __shared__ ExtB16Smem sm;
+  const DecodeArgs& a = e.d;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tt = lane >> 2, q4 = lane & 3;
+  const int n_ig = (e.max_chunk + 3) / 4;   // groups of 4 positions per (sequence, KV head)
+  int job = blockIdx.x;
+  const int ig = job % n_ig;
+  job /= n_ig;
+  const int h = job % a.H, b = job / a.H;
+  int t0, chunk;
+  chunk_of(e, b, t0, chunk);
+  const int L = clamp_len(scalar_load_i32(e.prefix_lens, b), a.max_pages);
+  const int i = 4 * ig + wave;
+  if (i >= chunk) return;   // wave-uniform; nothing below synchronises the block
+  const int t = t0 + i;
+  if (h == 0 && lane == 0) e.row_len[t] = L;
+  const int ns = min(a.sink, L);
+  const int r_lo = L > a.sink ? max(a.sink, L - a.recent) : L;
+  const int nr = L - r_lo;
+  const int nk = ns + nr + i + 1;
+  const size_t head_row = (size_t)b * a.H + h;
+  const int ring0 = a.recent > 0 ? r_lo % a.recent : 0;
+  auto key_row = [&](int j, const uint16_t* sink_buf, const uint16_t* ring_buf, const uint16_t* chunk_buf) {
+    if (j < ns) return sink_buf + (head_row * a.sink + j) * kHeadDim;
+    if (j < ns + nr) {
+      int rr = ring0 + (j - ns);
+      rr = rr >= a.recent ? rr - a.recent : rr;
+      return ring_buf + (head_row * a.recent + rr) * kHeadDim;
+    }
+    return chunk_buf + ((size_t)(t0 + j - ns - nr) * a.H + h) * kHeadDim;
+  };
+  {
+    const uint4* qg = reinterpret_cast<const uint4*>(a.q + ((size_t)t * a.Hq + h * G) * kHeadDim);
+    for (int x = lane; x < G * kHeadDim / 8; x += 64) (&sm.q[wave][0][0])[x] = qg[x];
+  }
+  float m[G], lsum[G], acc[G][2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    lsum[g] = 0.f;
+    acc[g][0] = acc[g][1] = 0.f;
+  }
+  struct RoundIn {
+    uint4 kd[4];
+    uint32_t vv[16];
+  };
+  auto load_round = [&](int jbase, RoundIn& in) {
+    const int j = jbase + tt;
+    const uint16_t* krow = key_row(min(j, nk - 1), a.k_sink, a.k_ring, e.k_new) + 32 * q4;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) in.kd[x] = reinterpret_cast<const uint4*>(krow)[x];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      in.vv[u] = *reinterpret_cast<const uint32_t*>(key_row(min(jbase + u, nk - 1), a.v_sink, a.v_ring, e.v_new) +
+                                                    2 * lane);
+  };
+  RoundIn nxt;
+  load_round(0, nxt);
+  wave_lds_sync();   // the query rows are in LDS
+  for (int jbase = 0; jbase < nk; jbase += 16) {
+    const RoundIn cur = nxt;
+    if (jbase + 16 < nk) load_round(jbase + 16, nxt);
+    const bool valid = jbase + tt < nk;
+    float lg[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float d = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint4 qd = sm.q[wave][g][4 * q4 + x];
+        d = dot2_bf16(qd.x, cur.kd[x].x, d);
+        d = dot2_bf16(qd.y, cur.kd[x].y, d);
+        d = dot2_bf16(qd.z, cur.kd[x].z, d);
+        d = dot2_bf16(qd.w, cur.kd[x].w, d);
+      }
+      d += __shfl_xor(d, 1);
+      d += __shfl_xor(d, 2);
+      lg[g] = valid ? d * a.sl2e : -INFINITY;
+    }
+    wave_lds_sync();   // the previous round's weights have been read
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float m_new = fmaxf(m[g], wave_max_xor(lg[g], 4, 32));   // finite: the round has a key
+      const float al = exp2f(m[g] - m_new);
+      const float p = valid ? exp2f(lg[g] - m_new) : 0.f;
+      lsum[g] = lsum[g] * al + wave_sum_xor(p, 4, 32);
+      acc[g][0] *= al;
+      acc[g][1] *= al;
+      m[g] = m_new;
+      if (q4 == 0) sm.p[wave][g][tt] = p;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float v0 = bf16_bits_to_f32(cur.vv[u] & 0xFFFFu), v1 = bf16_bits_to_f32(cur.vv[u] >> 16);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = sm.p[wave][g][u];   // 0 beyond the last key
+        acc[g][0] = fmaf(p, v0, acc[g][0]);
+        acc[g][1] = fmaf(p, v1, acc[g][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const size_t rec = ((size_t)t * a.Hq + h * G + g) * a.n_total;   // record 0: the BF16 keys
+    *reinterpret_cast<float2*>(a.part + rec * kHeadDim + 2 * lane) = make_float2(acc[g][0], acc[g][1]);
+    if (lane == 0) a.part_ml[rec] = make_float2(m[g], lsum[g]);
+  }
+}
+
 // query heads per reduce block: one when few (sequence, KV head) pairs would leave most CUs
 // idle, else the largest divisor of G that is at most four
 template <int G>
@@ -1113,6 +1427,100 @@ int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   const DecodeArgs a = make_decode_args(L);
   hipLaunchKernelGGL(rotate_q_kernel, dim3(L.batch * L.num_kv_heads), dim3(kSideThreads), 0, stream, a);
   return launch_split_reduce(a, L.batch, stream);
+}
+
+ExtendPlan make_extend_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t num_tokens,
+                            int32_t max_pages, int32_t max_chunk) {
+  ExtendPlan p{};
+  const long long int2_pages = max(0, max_pages - sink / kPage);
+  // ranges of about 400 pages (at most 512, whole page pairs)
+  long long n_split = int2_pages > 0 ? max(1LL, (int2_pages + 399) / 400) : 0;
+  long long per = n_split > 0 ? (int2_pages + n_split - 1) / n_split : 2;
+  per = (per + 1) / 2 * 2;
+  if (per > kMaxPagesPerSplit) per = kMaxPagesPerSplit;
+  p.pages_per_split = (int)per;
+  p.n_split = int2_pages > 0 ? (int)((int2_pages + per - 1) / per) : 0;
+  p.n_total = 1 + p.n_split;
+  p.n_qt = (int)(((long long)max_chunk * (num_q_heads / num_kv_heads) + 15) / 16);
+  const size_t rows = (size_t)num_tokens * num_q_heads;
+  p.qrot_off = 0;
+  p.part_off = (rows * kQrotBytes + 511) / 512 * 512;
+  p.ml_off = p.part_off + rows * p.n_total * kHeadDim * sizeof(float);
+  p.len_off = (p.ml_off + rows * p.n_total * sizeof(float2) + 255) / 256 * 256;
+  p.bytes = p.len_off + (size_t)num_tokens * sizeof(int32_t);
+  return p;
+}
+
+namespace {
+template <int G>
+void launch_extend_g(const ExtArgs& e, hipStream_t stream) {
+  const DecodeArgs& a = e.d;
+  if (a.n_split > 0)
+    hipLaunchKernelGGL(ext_int2_kernel<G>, dim3(e.n_seq * a.H * a.n_split * e.n_qt), dim3(256), 0, stream, e);
+  hipLaunchKernelGGL(ext_bf16_kernel<G>, dim3(e.n_seq * a.H * ((e.max_chunk + 3) / 4)), dim3(256), 0, stream, e);
+  constexpr int GB = reduce_group<G>();
+  hipLaunchKernelGGL((reduce_kernel<G, GB>), dim3(e.n_tok * a.H * (G / GB)), dim3(256), 0, stream, a);
+}
+}  // namespace
+
+int launch_extend(const ExtendLaunch& X, hipStream_t stream) {
+  if (X.num_tokens == 0) return 0;
+  DecodeLaunch D{};
+  D.pages = X.pages;
+  D.k_sink = X.k_sink;
+  D.v_sink = X.v_sink;
+  D.k_ring = X.k_ring;
+  D.v_ring = X.v_ring;
+  D.u_k = X.u_k;
+  D.u_v = X.u_v;
+  D.q = X.q;
+  D.page_table = X.page_table;
+  D.seq_lens = reinterpret_cast<const int32_t*>(X.workspace + X.plan.len_off);   // row prefix lengths
+  D.out = X.out;
+  D.workspace = X.workspace;
+  D.sm_scale = X.sm_scale;
+  D.clip_v = X.clip_v;
+  D.num_kv_heads = X.num_kv_heads;
+  D.num_q_heads = X.num_q_heads;
+  D.max_pages = X.max_pages;
+  D.batch = X.num_tokens;
+  D.sink = X.sink;
+  D.recent = X.recent;
+  D.plan.pages_per_split = X.plan.pages_per_split;
+  D.plan.n_split = X.plan.n_split;
+  D.plan.n_bsplit = 1;
+  D.plan.n_total = X.plan.n_total;
+  D.plan.bf16_chunk = kBf16Chunk;
+  D.plan.qrot_off = X.plan.qrot_off;
+  D.plan.part_off = X.plan.part_off;
+  D.plan.ml_off = X.plan.ml_off;
+  ExtArgs e{};
+  e.d = make_decode_args(D);
+  e.d.ext = 1;
+  e.k_new = X.k;
+  e.v_new = X.v;
+  e.cu = X.cu_seqlens;
+  e.prefix_lens = X.prefix_lens;
+  e.row_len = reinterpret_cast<int32_t*>(X.workspace + X.plan.len_off);
+  e.n_seq = X.batch;
+  e.n_tok = X.num_tokens;
+  e.max_chunk = X.max_chunk;
+  e.n_qt = X.plan.n_qt;
+  // rows = chunk tokens: the rotation of every chunk query, then the INT2 ranges, the BF16 keys
+  // and the merge (which reads row_len, written by the BF16 kernel)
+  hipLaunchKernelGGL(rotate_q_kernel, dim3(X.num_tokens * X.num_kv_heads), dim3(kSideThreads), 0, stream, e.d);
+  switch (e.d.G) {
+    case 1: launch_extend_g<1>(e, stream); break;
+    case 2: launch_extend_g<2>(e, stream); break;
+    case 3: launch_extend_g<3>(e, stream); break;
+    case 4: launch_extend_g<4>(e, stream); break;
+    case 5: launch_extend_g<5>(e, stream); break;
+    case 6: launch_extend_g<6>(e, stream); break;
+    case 7: launch_extend_g<7>(e, stream); break;
+    case 8: launch_extend_g<8>(e, stream); break;
+    default: return 1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
 int launch_decode_step(const KvWriteLaunch& W, const DecodeLaunch& D, hipStream_t stream) {

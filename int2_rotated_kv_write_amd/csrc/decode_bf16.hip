@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void b16_split_kernel(B16Args a) {
   const int w_blk = blockIdx.x;
   const int bh = w_blk / a.n_split, split = w_blk - bh * a.n_split;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int L = a.seq_lens[b];
+  const int L = clamp_len(a.seq_lens[b], a.max_pages);
   const int n_pages = (L + kPage - 1) / kPage;
   const int first = split * a.P;
   const int end = min(first + a.P, n_pages);
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void b16_split_kernel(B16Args a) {
 __global__ __launch_bounds__(kHeadDim) void b16_reduce_kernel(B16Args a) {
   const int bhq = blockIdx.x, b = bhq / a.Hq, c = threadIdx.x;
   uint16_t* out = a.out + (size_t)bhq * kHeadDim;
-  const int L = a.seq_lens[b];
+  const int L = clamp_len(a.seq_lens[b], a.max_pages);
   if (L <= 0) {
     out[c] = 0;
     return;

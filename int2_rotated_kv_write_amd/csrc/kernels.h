@@ -66,10 +66,34 @@ struct B16Launch {
   B16Plan plan;
 };
 
+// Extend (chunked prefill) plan: the INT2 pages of a prefix in n_split ranges of
+// pages_per_split pages; n_qt tiles of 16 query heads per (sequence, KV head); every
+// (chunk token, query head) owns n_total = 1 + n_split partial records.
+struct ExtendPlan {
+  int32_t pages_per_split, n_split, n_total, n_qt;
+  size_t qrot_off, part_off, ml_off, len_off, bytes;
+};
+
+ExtendPlan make_extend_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t num_tokens,
+                            int32_t max_pages, int32_t max_chunk);
+
+struct ExtendLaunch {
+  const uint8_t* pages;
+  const uint16_t *k_sink, *v_sink, *k_ring, *v_ring, *u_k, *u_v;
+  const uint16_t *q, *k, *v;
+  const int32_t *cu_seqlens, *prefix_lens, *page_table;
+  uint16_t* out;
+  uint8_t* workspace;
+  float sm_scale, clip_v;
+  int32_t num_kv_heads, num_q_heads, max_pages, batch, num_tokens, max_chunk, sink, recent;
+  ExtendPlan plan;
+};
+
 int device_cus();   // compute units of the current device
 int launch_kv_write(const KvWriteLaunch& L, hipStream_t stream);
 int launch_decode_step(const KvWriteLaunch& W, const DecodeLaunch& D, hipStream_t stream);
 int launch_decode(const DecodeLaunch& L, hipStream_t stream);
+int launch_extend(const ExtendLaunch& L, hipStream_t stream);
 int launch_bf16_decode(const B16Launch& L, hipStream_t stream);
 // Device address of the current device's static decode scratch (decode_noalloc.hip).
 hipError_t noalloc_scratch(void** out);

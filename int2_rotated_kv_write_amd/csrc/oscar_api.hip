@@ -1,5 +1,6 @@
 // C ABI entry points (include/oscar.h): host-side argument checks, the
 // split-K plan and kernel launches.  No allocation, no synchronisation.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -271,6 +272,71 @@ int oscar_bf16_decode_attn(int32_t num_kv_heads, int32_t num_q_heads, const uint
   L.batch = batch;
   L.plan = plan;
   if (oscar::launch_bf16_decode(L, stream)) return hip_fail("bf16 decode launch");
+  return OSCAR_OK;
+}
+
+size_t oscar_extend_workspace_bytes(const oscar_shape_t* shape, int32_t num_tokens, int32_t max_pages,
+                                    int32_t max_chunk) {
+  if (check_shape(shape) || num_tokens < 0 || max_pages < 1 || max_chunk < 1) return 0;
+  return oscar::make_extend_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink, num_tokens, max_pages,
+                                 max_chunk)
+      .bytes;
+}
+
+int oscar_extend_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v, const int32_t* cu_seqlens, const int32_t* prefix_lens, int32_t batch,
+                      int32_t num_tokens, int32_t max_chunk, const int32_t* page_table, int32_t max_pages,
+                      float sm_scale, uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int rc = check_shape(shape)) return rc;
+  if (!layer) return fail(OSCAR_EINVAL, "layer is NULL%s");
+  if (batch < 0 || num_tokens < 0) return fail(OSCAR_EINVAL, "batch and num_tokens must be >= 0%s");
+  if (max_pages < 1 || max_chunk < 1) return fail(OSCAR_EINVAL, "max_pages and max_chunk must be >= 1%s");
+  if (!std::isfinite(sm_scale)) return fail(OSCAR_EINVAL, "sm_scale is not finite%s");
+  if (num_tokens == 0) return OSCAR_OK;
+  if (batch == 0) return fail(OSCAR_EINVAL, "num_tokens > 0 with batch == 0%s");
+  if ((long long)max_chunk * batch < num_tokens) return fail(OSCAR_EINVAL, "num_tokens exceeds batch x max_chunk%s");
+  if (!q || !k || !v || !cu_seqlens || !prefix_lens || !page_table || !out || !layer->pages || !layer->k_ring ||
+      !layer->v_ring || !layer->u_k || !layer->u_v || (shape->sink > 0 && (!layer->k_sink || !layer->v_sink)))
+    return fail(OSCAR_EINVAL, "NULL tensor pointer%s");
+  if (!clip_ok(layer->clip_v)) return fail(OSCAR_EINVAL, "clip_v outside (0, 16384]%s");
+  if (int rc = check_layer_alignment(layer)) return rc;
+  if (!al16(q) || !al16(k) || !al16(v) || !al16(out)) return fail(OSCAR_EINVAL, "q, k, v and out must be 16-byte aligned%s");
+  if (!al4(cu_seqlens) || !al4(prefix_lens) || !al4(page_table))
+    return fail(OSCAR_EINVAL, "int32 index arrays must be 4-byte aligned%s");
+  const oscar::ExtendPlan plan = oscar::make_extend_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
+                                                         num_tokens, max_pages, max_chunk);
+  const long long blocks = (long long)batch * shape->num_kv_heads * std::max(1, plan.n_split) * plan.n_qt;
+  if (blocks > 0x7FFFFFFFLL) return fail(OSCAR_EINVAL, "batch x KV heads x ranges x query tiles exceeds the grid limit%s");
+  if (!workspace || workspace_bytes < plan.bytes) return fail(OSCAR_ENOWS, "workspace smaller than required%s");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned%s");
+  oscar::ExtendLaunch L{};
+  L.pages = layer->pages;
+  L.k_sink = layer->k_sink;
+  L.v_sink = layer->v_sink;
+  L.k_ring = layer->k_ring;
+  L.v_ring = layer->v_ring;
+  L.u_k = layer->u_k;
+  L.u_v = layer->u_v;
+  L.q = q;
+  L.k = k;
+  L.v = v;
+  L.cu_seqlens = cu_seqlens;
+  L.prefix_lens = prefix_lens;
+  L.page_table = page_table;
+  L.out = out;
+  L.workspace = static_cast<uint8_t*>(workspace);
+  L.sm_scale = sm_scale;
+  L.clip_v = layer->clip_v;
+  L.num_kv_heads = shape->num_kv_heads;
+  L.num_q_heads = shape->num_q_heads;
+  L.max_pages = max_pages;
+  L.batch = batch;
+  L.num_tokens = num_tokens;
+  L.max_chunk = max_chunk;
+  L.sink = shape->sink;
+  L.recent = shape->recent;
+  L.plan = plan;
+  if (oscar::launch_extend(L, stream)) return hip_fail("extend launch");
   return OSCAR_OK;
 }
 
