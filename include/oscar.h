@@ -246,6 +246,39 @@ int oscar_calibrate_layer(int32_t num_kv_heads, int32_t gqa, int32_t num_samples
                           uint16_t* u_v_out, float* clip_k_out, float* clip_v_out,
                           int32_t num_threads);
 
+/* decode_attn_cascade -- decode_attn for a batch in which groups of sequences
+ * share the physical pages of a common prefix (prefix caching: [es] 2.2 B and
+ * section 3, item 3; [it] "Architettura del Sistema di Serving e Layout di
+ * Memoria").  Computes exactly what oscar_decode_attn computes; only the reads
+ * differ: the shared INT2 pages of a group are read once per block of 16
+ * (G <= 4) or 32 (G >= 5) of the members' query heads instead of once per
+ * member and KV head.
+ *   cu_groups   int32 [num_groups + 1], nondecreasing: group g is batch entries
+ *               cu_groups[g] .. cu_groups[g+1] - 1 (at most max_group of them
+ *               take part; entries in no group decode alone)
+ *   group_pages int32 [num_groups]: the group's members share INT2 pages
+ *               sink/16 .. sink/16 + group_pages[g] - 1 of their page-table
+ *               rows (the same physical pages, read through the first
+ *               member's row); clamped on the device to [0, max_shared_pages]
+ *               rounded up to whole ranges
+ * A member whose own INT2 history does not hold every shared page whole
+ * (seq_len < sink + 16 group_pages + recent) reads its pages itself, and so
+ * does every member of a group whose first member is such a sequence; so any
+ * device values give the decode_attn result as long as the members' rows do
+ * name the same physical pages where they are shared.
+ *   max_group        host bound on the members per group
+ *   max_shared_pages host bound on group_pages
+ *   workspace        >= oscar_cascade_workspace_bytes(shape, batch, max_pages,
+ *                    max_shared_pages) bytes, 256-byte aligned; clobbered
+ * Other arguments, errors and outputs as oscar_decode_attn. */
+size_t oscar_cascade_workspace_bytes(const oscar_shape_t* shape, int32_t batch, int32_t max_pages,
+                                     int32_t max_shared_pages);
+int oscar_decode_attn_cascade(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                              const int32_t* cu_groups, const int32_t* group_pages, int32_t num_groups,
+                              int32_t max_group, int32_t max_shared_pages, float sm_scale, uint16_t* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* extend_attn -- chunked prefill (extend) attention over the mixed cache: the
  * read path of [it] "Architettura del Sistema di Serving e Layout di Memoria"
  * and [es] 2.2 B (paged attention with prefix caching) for a chunk of new

@@ -26,6 +26,7 @@ class OscarLayer(ctypes.Structure):
 
 EXPORTS = ("oscar_kv_write", "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_decode_step",
            "oscar_decode_attn_noalloc", "oscar_extend_workspace_bytes", "oscar_extend_attn",
+           "oscar_cascade_workspace_bytes", "oscar_decode_attn_cascade",
            "oscar_bf16_decode_workspace_bytes", "oscar_bf16_decode_attn",
            "oscar_read_probe_sink_bytes", "oscar_read_probe",
            "oscar_calibrate_layer", "oscar_status_string", "oscar_last_error")
@@ -55,6 +56,11 @@ def load() -> ctypes.CDLL:
     lib.oscar_decode_attn_noalloc.argtypes = [SP, LP, c_ptr, c_ptr, c_i32, c_ptr, c_i32, ctypes.c_float, c_ptr,
                                               c_ptr]
     lib.oscar_decode_attn_noalloc.restype = ctypes.c_int
+    lib.oscar_cascade_workspace_bytes.argtypes = [SP, c_i32, c_i32, c_i32]
+    lib.oscar_cascade_workspace_bytes.restype = ctypes.c_size_t
+    lib.oscar_decode_attn_cascade.argtypes = [SP, LP, c_ptr, c_ptr, c_i32, c_ptr, c_i32, c_ptr, c_ptr, c_i32, c_i32,
+                                              c_i32, ctypes.c_float, c_ptr, c_ptr, ctypes.c_size_t, c_ptr]
+    lib.oscar_decode_attn_cascade.restype = ctypes.c_int
     lib.oscar_extend_workspace_bytes.argtypes = [SP, c_i32, c_i32, c_i32]
     lib.oscar_extend_workspace_bytes.restype = ctypes.c_size_t
     lib.oscar_extend_attn.argtypes = [SP, LP, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_i32, c_i32, c_i32, c_ptr, c_i32,

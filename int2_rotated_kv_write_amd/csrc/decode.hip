@@ -55,6 +55,14 @@ struct DecodeArgs {
   // extend (chunked prefill) reduce: every row (chunk token) has exactly one BF16 record,
   // index 0, and seq_lens holds the prefix length of the row's sequence
   int32_t ext;
+  // cascade decode: groups of sequences (batch entries cu_groups[g] .. cu_groups[g+1] - 1, at
+  // most max_group of them) share their first group_pages[g] INT2 pages.  The first n_cas
+  // split blocks read each shared range once for all members' query heads (n_cqt tiles of
+  // 16 NQ heads) into records n_bsplit + n_split + k; cas_eff[b] is the number of shared
+  // pages sequence b takes from its group (0: none), written by the query rotation.
+  const int32_t *cu_groups, *group_pages;
+  int32_t* cas_eff;
+  int32_t n_groups, max_group, n_sh, n_cqt, n_cas;
 };
 
 __device__ __forceinline__ int bf16_token_count(int L, int sink, int recent) {
@@ -63,6 +71,38 @@ __device__ __forceinline__ int bf16_token_count(int L, int sink, int recent) {
 }
 __device__ __forceinline__ int int2_end(int L, int sink, int recent) {   // INT2 tokens [sink, end)
   return L <= sink ? sink : max(sink, L - recent);
+}
+
+__device__ __forceinline__ int whole_int2_pages(const DecodeArgs& a, int L) {   // pages sink/16 .. wholly INT2
+  return int2_end(L, a.sink, a.recent) / kPage - a.sink / kPage;
+}
+
+// Members and shared pages of cascade group g, clamped so that no read leaves the batch, the
+// records the plan provides or the part of the first member's page-table row its own length
+// covers (the shared pages are read through that row): a group whose first member does not
+// hold every shared page whole in its INT2 history shares nothing.
+__device__ __forceinline__ void cascade_group(const DecodeArgs& a, int g, int& m0, int& members, int& shared) {
+  m0 = min(max(scalar_load_i32(a.cu_groups, g), 0), a.B);
+  const int m1 = min(max(scalar_load_i32(a.cu_groups, g + 1), m0), a.B);
+  members = min(m1 - m0, a.max_group);
+  shared = min(max(scalar_load_i32(a.group_pages, g), 0), a.n_sh * a.P);
+  if (members == 0 || shared > whole_int2_pages(a, clamp_len(scalar_load_i32(a.seq_lens, m0), a.max_pages)))
+    shared = 0;
+}
+
+// Shared pages sequence b (length L) takes from its group: the group's count when b is one
+// of its members and every shared page lies whole inside b's INT2 history, else 0 (b then
+// reads all of its pages itself).
+__device__ int cascade_pages_of(const DecodeArgs& a, int b, int L) {
+  int lo = 0, hi = a.n_groups - 1;   // the last group whose first member is <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_groups[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  int m0, members, shared;
+  cascade_group(a, lo, m0, members, shared);
+  if (b < m0 || b >= m0 + members) return 0;
+  return shared <= whole_int2_pages(a, L) ? shared : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -91,6 +131,8 @@ __device__ __forceinline__ void rotate_q_block(const DecodeArgs& a, RotQSmem& sm
   const int b = bh / a.H, h = bh % a.H, G = a.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4;
+  if (a.cas_eff && h == 0 && tid == 0)
+    a.cas_eff[b] = a.n_groups > 0 ? cascade_pages_of(a, b, clamp_len(a.seq_lens[b], a.max_pages)) : 0;
   {
     const uint16_t* U = a.u_k + (size_t)h * kHeadDim * kHeadDim;
     const uint16_t* qg = a.q + ((size_t)b * a.Hq + h * G) * kHeadDim;
@@ -809,13 +851,164 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   merge_waves_and_store<G>(a, b, h, a.n_bsplit + split, sm);
 }
 
+// ---------------------------------------------------------------------------
+// Many queries over one range of INT2 pages: pages [first, first + np) of one KV
+// head (physical ids in the page-table row ptab) are read once per block into an
+// LDS ring of R page slots shared by the four waves, and every wave applies them
+// to its own 4 NQ query heads.  Query head e (of n_e) is head h G + e % G of row
+// t0 + e / G; the block takes e_block .. e_block + 16 NQ - 1 and wave w the
+// heads e_block + 4 NQ w + 4 qd + hh.  Page j is loaded by wave j % 4: before
+// a pair is read each wave waits for its own loads of it and the block
+// synchronises, which also frees the slots of the pair before for new loads.
+// Each (row, head) gets one record, index rec.  Used by extend (rows = chunk
+// tokens over the prefix) and by cascade decode (rows = sequences sharing the
+// range's pages).
+// ---------------------------------------------------------------------------
+template <int R>
+__device__ __forceinline__ void mq_wait_own_pair(bool all_issued) {
+  // of this wave's later loads, (R - 4) / 4 pages (two instructions each) lie among
+  // j + 2 .. j + R - 3 once all of those are issued
+  static_assert(R == 8 || R == 16, "ring of 8 or 16 slots");
+  if (all_issued) {
+    if constexpr (R == 8) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+template <int G, int NQ, int R>
+__device__ void mq_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, int first, int np, int i_hi,
+                              int t0, int n_e, int e_block, int rec, uint8_t (*ring)[kBlockBytes]) {
+  static_assert(R % 4 == 0 && R * 8 <= 256, "whole rounds of the four waves; one thread per V-parameter line");
+  i_hi = __builtin_amdgcn_readfirstlane(i_hi);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, r = lane >> 4, hh = n >> 2;
+  const int e_wave = e_block + 4 * NQ * wave;
+  Int2Lane<NQ> ln;
+  int2_lane_init(ln, lane, a.resc_thr);
+  // the block offsets (256-byte units) of the pages this wave loads, j = wave + 4 m: lane l
+  // holds m = l + 64 k
+  constexpr int kIdRegs = kMaxPagesPerSplit / 4 / 64;
+  static_assert(kIdRegs == 2, "page offsets in two registers");
+  uint32_t unit_reg[kIdRegs];
+  {
+    const uint32_t per_page = (uint32_t)a.H * (kBlockBytes / 256), head_units = (uint32_t)h * (kBlockBytes / 256);
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k)
+      unit_reg[k] = (uint32_t)ptab[first + min(wave + 4 * (lane + 64 * k), np - 1)] * per_page + head_units;
+    uint4 qraw[NQ][2][2];
+    float craw[NQ], sraw[NQ];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const int e_q = e_wave + 4 * qd + hh;
+      const bool ok = e_q < n_e;
+      const int row = t0 + (ok ? e_q / G : 0), hq = h * G + (ok ? e_q % G : 0);
+      const QrotRecord* qr = a.qrot + ((size_t)row * a.Hq + hq);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) qraw[qd][g][kh] = *reinterpret_cast<const uint4*>(&qr->frag[g][kh][ln.limb][r][0]);
+      craw[qd] = qr->negc[ln.gp][ln.limb];
+      sraw[qd] = qr->qsum[ln.gp];
+    }
+    // consumed here, before any page load: no wait for them lands in the page loop
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(unit_reg[k]));
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const bool ok = e_wave + 4 * qd + hh < n_e;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          asm volatile("" : "+v"(qraw[qd][g][kh].x), "+v"(qraw[qd][g][kh].y), "+v"(qraw[qd][g][kh].z),
+                       "+v"(qraw[qd][g][kh].w));
+          ln.qb[qd][g][kh] = half8_of(ok && g == ln.gp ? qraw[qd][g][kh] : make_uint4(0, 0, 0, 0));
+        }
+      asm volatile("" : "+v"(craw[qd]), "+v"(sraw[qd]));
+      ln.cinit[qd] = ok ? craw[qd] : 0.f;
+      ln.qs[qd] = ok ? sraw[qd] : 0.f;
+    }
+  }
+  Int2State<NQ> st;
+  int2_state_init(st);
+  auto issue = [&](int j) {   // page j of the range (first + j) into slot j % R, by wave j % 4
+    if ((j & 3) != wave) return;
+    const int m = j >> 2;
+    const uint32_t u = __builtin_amdgcn_readlane(m < 64 ? unit_reg[0] : unit_reg[1], m & 63);
+    const uint8_t* blk = a.pages + ((uint64_t)u << 8);
+    const uint32_t dst = (uint32_t)(uintptr_t)&ring[j % R][0];
+    dma_page_to_lds(blk, 16 * lane, 1024 + 4 * lane, dst, dst + 1024);
+  };
+  // the V parameters of every slot start at zero (a missing second page of the last pair is
+  // read anyway and weighted 0; its scales must be finite)
+  if (threadIdx.x < R * 8)
+    *reinterpret_cast<uint4*>(&ring[threadIdx.x >> 3][kVParams + 16 * (threadIdx.x & 7)]) = make_uint4(0, 0, 0, 0);
+  block_lds_barrier();
+  for (int j = 0; j < R - 2 && j < np; ++j) issue(j);
+  for (int j = 0; j < np; j += 2) {
+    mq_wait_own_pair<R>(j + R - 3 < np);
+    block_lds_barrier();   // pages j, j + 1 visible to every wave; slots of pair j - 2 no longer read
+    if (j + R - 2 < np) issue(j + R - 2);
+    if (j + R - 1 < np) issue(j + R - 1);
+    int2_pair<NQ>(st, ln, &ring[j % R][0], &ring[(j + 1) % R][0], j + 1 < np, first + j, i_hi, j == 0);
+  }
+  // ---- one record per (row, query head) ----
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    const float L_h = rows_sum(quad_sum(st.lsum[qd]));
+    const float Z0 = rows_sum(quad_sum(st.zs[qd][0])), Z1 = rows_sum(quad_sum(st.zs[qd][1]));
+    const int e_q = e_wave + 4 * qd + hh;
+    if (r == 0 && ln.a4 == 0 && e_q < n_e)
+      a.part_ml[((size_t)(t0 + e_q / G) * a.Hq + h * G + e_q % G) * a.n_total + rec] = make_float2(st.m[qd], L_h);
+    // accumulator rows of this lane: head 4 qd + r of the wave
+    const float z0 = __shfl(Z0, 4 * r), z1 = __shfl(Z1, 4 * r);
+    const int e_r = e_wave + 4 * qd + r;
+    if (e_r < n_e) {
+      float* dst = a.part + (((size_t)(t0 + e_r / G) * a.Hq + h * G + e_r % G) * a.n_total + rec) * kHeadDim;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float sum = (st.acc[qd][t][0] + st.acc[qd][t][1]) + (st.acc[qd][t][2] + st.acc[qd][t][3]);
+        dst[16 * t + n] = sum + (t < 4 ? z0 : z1);
+      }
+    }
+  }
+}
+
+// Cascade block w (< n_cas): shared range k of group g, KV head h, query tile qt, with the
+// pages of the group's first member's table row.
+template <int G>
+__device__ void cascade_block(const DecodeArgs& a, int w, SplitSmem& sm) {
+  constexpr int NQ = (G + 3) / 4;
+  const int qt = w % a.n_cqt;
+  w /= a.n_cqt;
+  const int k = w % a.n_sh;
+  w /= a.n_sh;
+  const int h = w % a.H, g = w / a.H;
+  int m0, members, shared;
+  cascade_group(a, g, m0, members, shared);
+  const int first = a.sink / kPage + k * a.P;
+  const int end = min(first + a.P, a.sink / kPage + shared);
+  const int e_block = 16 * NQ * qt;
+  if (first >= end || e_block >= members * G) return;   // block-uniform
+  static_assert(sizeof(sm.ring) >= 16 * kBlockBytes, "a 16-slot ring inside the split kernel's LDS");
+  mq_int2_range<G, NQ, 16>(a, a.page_table + (size_t)m0 * a.max_pages, h, first, end - first,
+                           (a.sink / kPage + shared) * kPage, m0, members * G, e_block, a.n_bsplit + a.n_split + k,
+                           reinterpret_cast<uint8_t(*)[kBlockBytes]>(&sm.ring[0][0][0]));
+}
+
 template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void split_kernel(DecodeArgs a) {
   __shared__ SplitSmem sm;
   // 1D grid: every (sequence, KV head)'s INT2 ranges first, then all BF16 chunks, which are
   // short and fill the block slots the last INT2 ranges leave idle (measured 1.7% faster
   // than a (sequence, KV head)-major order at 28 x 100K)
-  const int nbh = a.B * a.H, w = blockIdx.x, n_int2 = nbh * a.n_split;
+  if ((int)blockIdx.x < a.n_cas) {   // cascade decode: shared prefix ranges come first
+    cascade_block<G>(a, blockIdx.x, sm);
+    return;
+  }
+  const int nbh = a.B * a.H, w = blockIdx.x - a.n_cas, n_int2 = nbh * a.n_split;
   const int bh = w < n_int2 ? w / a.n_split : (w - n_int2) / a.n_bsplit;
   const int item = w < n_int2 ? a.n_bsplit + (w - bh * a.n_split) : (w - n_int2) - bh * a.n_bsplit;
   const int b = bh / a.H, h = bh - b * a.H;
@@ -826,7 +1019,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
   } else {
     const int split = item - a.n_bsplit;
     const int i_hi = int2_end(L, a.sink, a.recent);
-    const int first = a.sink / kPage + split * a.P;
+    const int shared = a.cas_eff ? a.cas_eff[b] : 0;   // pages a cascade block reads for this sequence
+    const int first = a.sink / kPage + shared + split * a.P;
     const int end = min(first + a.P, (i_hi + kPage - 1) / kPage);
     if (i_hi <= a.sink || first >= end) return;
     int2_item<G>(a, b, h, split, first, end, i_hi, sm);
@@ -887,11 +1081,14 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
   const int n_b = a.ext ? 1 : (bf16_token_count(L, a.sink, a.recent) + a.bchunk - 1) / a.bchunk;
   const int i_hi = int2_end(L, a.sink, a.recent);
   const int int2_pages = i_hi > a.sink ? (i_hi + kPage - 1) / kPage - a.sink / kPage : 0;
-  const int n_i = (int2_pages + a.P - 1) / a.P;
-  const int n_used = n_b + n_i;   // used items: [0, n_b) BF16, then [n_bsplit, n_bsplit + n_i) INT2
-  auto rec_of = [&](int g, int u) {
-    return ((size_t)b * a.Hq + head0 + g) * a.n_total + (u < n_b ? u : a.n_bsplit + (u - n_b));
-  };
+  const int shared = a.cas_eff ? a.cas_eff[b] : 0;   // of which read by cascade blocks
+  const int n_i = (int2_pages - shared + a.P - 1) / a.P;
+  const int n_bi = n_b + n_i;
+  const int n_used = n_bi + (shared + a.P - 1) / a.P;
+  // used records: [0, n_b) BF16, [n_bsplit, n_bsplit + n_i) the sequence's own INT2 ranges,
+  // then from n_bsplit + n_split the shared ranges
+  auto idx_of = [&](int u) { return u < n_b ? u : u < n_bi ? a.n_bsplit + (u - n_b) : a.n_bsplit + a.n_split + (u - n_bi); };
+  auto rec_of = [&](int g, int u) { return ((size_t)b * a.Hq + head0 + g) * a.n_total + idx_of(u); };
   // ---- this wave's records u = wave + 4 d, requested first (they do not depend on the maxima):
   // per head one base address, the record index and lane in a 32-bit offset ----
   constexpr int kBatch = GB == 1 ? 32 : 8;   // records per head requested at once by a wave
@@ -904,7 +1101,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
 #pragma unroll
       for (int d = 0; d < kBatch; ++d) {
         const int u = u0 + 4 * d;
-        const int idx = u < n_b ? u : a.n_bsplit + (u - n_b);
+        const int idx = idx_of(u);
         v[g][d] = u < n_used ? *reinterpret_cast<const float2*>(head_base[g] + (idx * kHeadDim + 2 * lane))
                              : make_float2(0.f, 0.f);
       }
@@ -1061,17 +1258,12 @@ struct __attribute__((aligned(16))) MqSmem {
   uint8_t ring[kMqRing][kBlockBytes];
 };
 
-// INT2 prefix pages of one range of one (sequence, KV head), read once per block and used by
-// all four waves: wave w owns query heads 16 qt + 4 w .. + 3 of the sequence's chunk (query
-// head e = chunk position * G + head in the group).  Page j is loaded by wave j % 4; before a
-// pair is read every wave waits for its own loads of it and the block synchronises, which
-// also frees the slots of the previous pair for the next loads.
+// INT2 prefix pages of one range of one (sequence, KV head), read once per block for 16 query
+// heads of the sequence's chunk (query head e = chunk position * G + head in the group).
 template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void ext_int2_kernel(ExtArgs e) {
   __shared__ MqSmem sm;
   const DecodeArgs& a = e.d;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15, r = lane >> 4, hh = n >> 2;
   int job = blockIdx.x;
   const int qt = job % e.n_qt;
   job /= e.n_qt;
@@ -1086,93 +1278,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   const int end = min(first + a.P, (i_hi + kPage - 1) / kPage);
   const int e_block = 16 * qt;
   if (i_hi <= a.sink || first >= end || e_block >= chunk * G) return;   // block-uniform
-  const int np = end - first;
-
-  // this lane's query head (column n of the logit MFMA: head hh of the wave's quad)
-  const int e_q = e_block + 4 * wave + hh;
-  const bool q_ok = e_q < chunk * G;
-  const int row = t0 + (q_ok ? e_q / G : 0), hq = h * G + (q_ok ? e_q % G : 0);
-  Int2Lane<1> ln;
-  int2_lane_init(ln, lane, a.resc_thr);
-  // the block offsets (256-byte units) of the pages this wave loads, j = wave + 4 m: lane l
-  // holds m = l + 64 k
-  constexpr int kIdRegs = kMaxPagesPerSplit / 4 / 64;
-  uint32_t unit_reg[kIdRegs];
-  {
-    const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
-    const uint32_t per_page = (uint32_t)a.H * (kBlockBytes / 256), head_units = (uint32_t)h * (kBlockBytes / 256);
-#pragma unroll
-    for (int k = 0; k < kIdRegs; ++k)
-      unit_reg[k] = (uint32_t)ptab[first + min(wave + 4 * (lane + 64 * k), np - 1)] * per_page + head_units;
-    const QrotRecord* rec = a.qrot + ((size_t)row * a.Hq + hq);
-    uint4 qraw[2][2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) qraw[g][kh] = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][ln.limb][r][0]);
-    float craw = rec->negc[ln.gp][ln.limb], sraw = rec->qsum[ln.gp];
-    // consumed here, before any page load: no wait for them lands in the page loop
-#pragma unroll
-    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(unit_reg[k]));
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        asm volatile("" : "+v"(qraw[g][kh].x), "+v"(qraw[g][kh].y), "+v"(qraw[g][kh].z), "+v"(qraw[g][kh].w));
-        ln.qb[0][g][kh] = half8_of(q_ok && g == ln.gp ? qraw[g][kh] : make_uint4(0, 0, 0, 0));
-      }
-    asm volatile("" : "+v"(craw), "+v"(sraw));
-    ln.cinit[0] = q_ok ? craw : 0.f;
-    ln.qs[0] = q_ok ? sraw : 0.f;
-  }
-  Int2State<1> st;
-  int2_state_init(st);
-  auto issue = [&](int j) {   // page j of the range (first + j) into slot j % kMqRing, by wave j % 4
-    if ((j & 3) != wave) return;
-    const int m = j >> 2;
-    const uint32_t u = __builtin_amdgcn_readlane(m < 64 ? unit_reg[0] : unit_reg[1], m & 63);
-    const uint8_t* blk = a.pages + ((uint64_t)u << 8);
-    const uint32_t dst = (uint32_t)(uintptr_t)&sm.ring[j % kMqRing][0];
-    dma_page_to_lds(blk, 16 * lane, 1024 + 4 * lane, dst, dst + 1024);
-  };
-  // the V parameters of every slot start at zero (a missing second page of the last pair is
-  // read anyway and weighted 0; its scales must be finite)
-  if (threadIdx.x < kMqRing * 8)
-    *reinterpret_cast<uint4*>(&sm.ring[threadIdx.x >> 3][kVParams + 16 * (threadIdx.x & 7)]) = make_uint4(0, 0, 0, 0);
-  block_lds_barrier();
-  for (int j = 0; j < kMqRing - 2 && j < np; ++j) issue(j);
-  for (int j = 0; j < np; j += 2) {
-    // this wave's loads of pages j, j + 1 have landed: of its later loads, exactly one page
-    // (two instructions) is among j + 2 .. j + 5 when all of those exist
-    if (j + 5 < np) {
-      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    block_lds_barrier();   // pages j, j + 1 visible to every wave; slots of pair j - 2 no longer read
-    if (j + kMqRing - 2 < np) issue(j + kMqRing - 2);
-    if (j + kMqRing - 1 < np) issue(j + kMqRing - 1);
-    int2_pair<1>(st, ln, &sm.ring[j % kMqRing][0], &sm.ring[(j + 1) % kMqRing][0], j + 1 < np, first + j, i_hi,
-                 j == 0);
-  }
-  // ---- the wave's quad: one record per query head ----
-  float L_h = rows_sum(quad_sum(st.lsum[0]));
-  float Z0 = rows_sum(quad_sum(st.zs[0][0])), Z1 = rows_sum(quad_sum(st.zs[0][1]));
-  const size_t rec_base = (size_t)a.n_total;
-  if (r == 0 && ln.a4 == 0 && q_ok)
-    a.part_ml[((size_t)row * a.Hq + hq) * rec_base + 1 + split] = make_float2(st.m[0], L_h);
-  // accumulator rows of this lane: head r of the quad
-  const float z0 = __shfl(Z0, 4 * r), z1 = __shfl(Z1, 4 * r);
-  const int e_r = e_block + 4 * wave + r;
-  if (e_r < chunk * G) {
-    const int row_r = t0 + e_r / G, hq_r = h * G + e_r % G;
-    float* dst = a.part + (((size_t)row_r * a.Hq + hq_r) * rec_base + 1 + split) * kHeadDim;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float sum = (st.acc[0][t][0] + st.acc[0][t][1]) + (st.acc[0][t][2] + st.acc[0][t][3]);
-      dst[16 * t + n] = sum + (t < 4 ? z0 : z1);
-    }
-  }
+  mq_int2_range<G, 1, kMqRing>(a, a.page_table + (size_t)b * a.max_pages, h, first, end - first, i_hi, t0, chunk * G,
+                               e_block, 1 + split, sm.ring);
 }
 
 // BF16 keys of a chunk query: the prefix's sink rows [0, min(sink, L)), its ring rows
@@ -1307,7 +1414,7 @@ constexpr int reduce_group() {
 
 template <int G>
 void launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(split_kernel<G>, dim3(a.n_total * a.H * B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(split_kernel<G>, dim3(a.n_cas + (a.n_split + a.n_bsplit) * a.H * B), dim3(256), 0, stream, a);
   constexpr int GB = reduce_group<G>();
   if (GB > 1 && B * a.H < kFewPairs)
     hipLaunchKernelGGL((reduce_kernel<G, 1>), dim3(B * a.H * G), dim3(256), 0, stream, a);
@@ -1361,7 +1468,25 @@ DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   p.part_off = (qrot + 511) / 512 * 512;   // records on 128-byte line boundaries
   const size_t n_rec = (size_t)batch * num_q_heads * p.n_total;
   p.ml_off = p.part_off + n_rec * kHeadDim * sizeof(float);
-  p.bytes = p.ml_off + n_rec * sizeof(float2);
+  p.eff_off = p.bytes = p.ml_off + n_rec * sizeof(float2);
+  return p;
+}
+
+DecodePlan make_cascade_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t recent,
+                             int32_t batch, int32_t max_pages, int32_t max_shared_pages) {
+  DecodePlan p = make_decode_plan(num_kv_heads, num_q_heads, sink, recent, batch, max_pages);
+  const int int2_pages = max(0, max_pages - sink / kPage);
+  const int shared = min(max(max_shared_pages, 0), int2_pages);
+  p.n_sh = shared > 0 ? (shared + p.pages_per_split - 1) / p.pages_per_split : 0;
+  p.n_total += p.n_sh;
+  if (p.n_total > kMaxItems) {
+    p.bytes = 0;
+    return p;
+  }
+  const size_t n_rec = (size_t)batch * num_q_heads * p.n_total;
+  p.ml_off = p.part_off + n_rec * kHeadDim * sizeof(float);
+  p.eff_off = (p.ml_off + n_rec * sizeof(float2) + 255) / 256 * 256;
+  p.bytes = p.eff_off + (size_t)batch * sizeof(int32_t);
   return p;
 }
 
@@ -1403,6 +1528,18 @@ DecodeArgs make_decode_args(const DecodeLaunch& L) {
   a.n_bsplit = L.plan.n_bsplit;
   a.n_total = L.plan.n_total;
   a.bchunk = L.plan.bf16_chunk;
+  if (L.n_groups > 0 && L.plan.n_sh > 0) {   // cascade decode
+    constexpr int kHeadsPerTile = 16;          // per NQ: a block's 4 waves x 4 NQ query heads
+    const int nq = (a.G + 3) / 4;
+    a.cu_groups = L.cu_groups;
+    a.group_pages = L.group_pages;
+    a.cas_eff = reinterpret_cast<int32_t*>(L.workspace + L.plan.eff_off);
+    a.n_groups = L.n_groups;
+    a.max_group = L.max_group;
+    a.n_sh = L.plan.n_sh;
+    a.n_cqt = (L.max_group * a.G + kHeadsPerTile * nq - 1) / (kHeadsPerTile * nq);
+    a.n_cas = L.n_groups * a.H * a.n_sh * a.n_cqt;
+  }
   return a;
 }
 

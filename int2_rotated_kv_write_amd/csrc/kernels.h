@@ -22,7 +22,8 @@ struct KvWriteLaunch {
 // (sequence, query head) owns n_bsplit + n_split partial records.
 struct DecodePlan {
   int32_t pages_per_split, n_split, n_bsplit, n_total, bf16_chunk;
-  size_t qrot_off, part_off, ml_off, bytes;
+  int32_t n_sh;     // cascade decode: shared-prefix ranges per (sequence, query head), else 0
+  size_t qrot_off, part_off, ml_off, eff_off, bytes;
 };
 
 constexpr int kQrotBytes = 576;      // rotated-query record per (sequence, query head)
@@ -33,6 +34,10 @@ constexpr int kMaxItems = 1024;      // partial records per (sequence, query hea
 
 DecodePlan make_decode_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t recent,
                             int32_t batch, int32_t max_pages);
+// decode_attn's plan with records for the shared ranges of cascade groups whose shared
+// prefix is at most max_shared_pages INT2 pages; bytes == 0 when that exceeds the reduce's limit
+DecodePlan make_cascade_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t sink, int32_t recent,
+                             int32_t batch, int32_t max_pages, int32_t max_shared_pages);
 
 struct DecodeLaunch {
   const uint8_t* pages;
@@ -44,6 +49,9 @@ struct DecodeLaunch {
   float sm_scale, clip_v;
   int32_t num_kv_heads, num_q_heads, max_pages, batch, sink, recent;
   DecodePlan plan;
+  // cascade decode only (n_groups == 0 otherwise)
+  const int32_t *cu_groups, *group_pages;
+  int32_t n_groups, max_group;
 };
 
 // BF16 paged decode (the comparison kernel): `n_split` ranges of

@@ -105,7 +105,8 @@ int prepare_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer, con
 // Checks of a decode_attn call; fills L.  *nothing is set for batch == 0.
 int prepare_decode(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q, const int32_t* page_table,
                    int32_t max_pages, const int32_t* seq_lens, int32_t batch, float sm_scale, uint16_t* out,
-                   void* workspace, size_t workspace_bytes, oscar::DecodeLaunch& L, bool* nothing) {
+                   void* workspace, size_t workspace_bytes, oscar::DecodeLaunch& L, bool* nothing,
+                   int32_t max_shared_pages = -1) {
   *nothing = false;
   if (int rc = check_shape(shape)) return rc;
   if (!layer) return fail(OSCAR_EINVAL, "layer is NULL%s");
@@ -123,8 +124,12 @@ int prepare_decode(const oscar_shape_t* shape, const oscar_layer_t* layer, const
   if (int rc = check_layer_alignment(layer)) return rc;
   if (!al16(q) || !al16(out)) return fail(OSCAR_EINVAL, "q and out must be 16-byte aligned%s");
   if (!al4(page_table) || !al4(seq_lens)) return fail(OSCAR_EINVAL, "int32 index arrays must be 4-byte aligned%s");
-  const oscar::DecodePlan plan = oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink,
-                                                         shape->recent, batch, max_pages);
+  const oscar::DecodePlan plan =
+      max_shared_pages < 0
+          ? oscar::make_decode_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink, shape->recent, batch,
+                                    max_pages)
+          : oscar::make_cascade_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink, shape->recent, batch,
+                                     max_pages, max_shared_pages);
   if (plan.n_total > oscar::kMaxItems) return fail(OSCAR_EINVAL, "max_pages too large (sequences over ~8M tokens)%s");
   if (!workspace || workspace_bytes < plan.bytes) return fail(OSCAR_ENOWS, "workspace smaller than required%s");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(OSCAR_EINVAL, "workspace not 256-byte aligned%s");
@@ -202,13 +207,51 @@ int oscar_decode_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, co
   return OSCAR_OK;
 }
 
+size_t oscar_cascade_workspace_bytes(const oscar_shape_t* shape, int32_t batch, int32_t max_pages,
+                                     int32_t max_shared_pages) {
+  if (check_shape(shape) || batch < 0 || max_pages < 1 || max_shared_pages < 0) return 0;
+  return oscar::make_cascade_plan(shape->num_kv_heads, shape->num_q_heads, shape->sink, shape->recent, batch,
+                                  max_pages, max_shared_pages)
+      .bytes;
+}
+
+int oscar_decode_attn_cascade(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* q,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                              const int32_t* cu_groups, const int32_t* group_pages, int32_t num_groups,
+                              int32_t max_group, int32_t max_shared_pages, float sm_scale, uint16_t* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_groups < 0) return fail(OSCAR_EINVAL, "num_groups < 0%s");
+  if (max_shared_pages < 0) return fail(OSCAR_EINVAL, "max_shared_pages < 0%s");
+  if (num_groups > 0 && max_group < 1) return fail(OSCAR_EINVAL, "max_group must be >= 1%s");
+  if (num_groups > 0 && (!cu_groups || !group_pages)) return fail(OSCAR_EINVAL, "NULL group array%s");
+  if (num_groups > 0 && (!al4(cu_groups) || !al4(group_pages)))
+    return fail(OSCAR_EINVAL, "int32 index arrays must be 4-byte aligned%s");
+  oscar::DecodeLaunch L;
+  bool nothing = false;
+  if (int rc = prepare_decode(shape, layer, q, page_table, max_pages, seq_lens, batch, sm_scale, out, workspace,
+                              workspace_bytes, L, &nothing, max_shared_pages))
+    return rc;
+  if (nothing) return OSCAR_OK;
+  const long long G = shape->num_q_heads / shape->num_kv_heads, nq = (G + 3) / 4;
+  const long long tiles = ((long long)std::min(max_group, batch) * G + 16 * nq - 1) / (16 * nq);
+  const long long blocks = (long long)num_groups * shape->num_kv_heads * L.plan.n_sh * tiles +
+                           (long long)batch * shape->num_kv_heads * (L.plan.n_split + L.plan.n_bsplit);
+  if (blocks > 0x7FFFFFFFLL) return fail(OSCAR_EINVAL, "groups x KV heads x shared ranges exceed the grid limit%s");
+  L.cu_groups = cu_groups;
+  L.group_pages = group_pages;
+  L.n_groups = num_groups;
+  L.max_group = (int32_t)std::min(max_group, batch);
+  if (oscar::launch_decode(L, stream)) return hip_fail("cascade decode launch");
+  return OSCAR_OK;
+}
+
 int oscar_decode_step(const oscar_shape_t* shape, const oscar_layer_t* layer, const uint16_t* k, const uint16_t* v,
                       const int32_t* seq_idx, const int32_t* pos, int32_t num_tokens, const int32_t* seq_lens_after,
                       const uint16_t* q, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
                       int32_t batch, float sm_scale, uint16_t* out, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   oscar::KvWriteLaunch W;
-  oscar::DecodeLaunch D;
+  oscar::DecodeLaunch D{};
   bool no_write = false, no_decode = false;
   if (int rc = prepare_kv_write(shape, layer, k, v, seq_idx, pos, num_tokens, page_table, max_pages, seq_lens_after,
                                 W, &no_write))
