@@ -10,6 +10,16 @@ then decode_attn over the 100,000 cached tokens.  value = decoded tokens/s
 (28 per step); each layer's write and decode go through one decode_step
 call.  Inputs are seeded synthetic data already resident in HBM.
 
+Besides the headline line's fields, the JSON carries (unless --no-extras):
+  single_1x100k     one Qwen3-8B-shaped layer, batch 1, 100,000 tokens,
+                    decode_attn over 8 cycled cache copies (HBM-resident);
+  ragged_64x4k_128k 64 sequences of 4,096..131,072 tokens, 64 q / 8 kv
+                    heads, a quarter of them sharing a 4,096-token prefix:
+                    decode_attn and decode_attn_cascade, with the page bytes
+                    the shared reads save;
+  kv_write_prefill  one kv_write of 100,000 prefill tokens x 8 KV heads;
+  bf16_baseline     the all-BF16 paged decode at the headline shape.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -42,6 +52,7 @@ WORKLOADS = {
                               table="shared_prefix", law="outlier"),
 }
 SHARED_PREFIX_TOKENS = 4096     # ragged workload: 25% of the sequences share their first 4,096 tokens
+SINK, RECENT = 64, 256
 PREFILL_TOKENS = 100_000        # write-path workload: one kv_write of 100,000 prefill tokens x 8 KV heads
 
 
@@ -129,7 +140,7 @@ def cpu_baseline(H, layers, seq_len, budget_s=20.0):
     the whole step (batch x KV heads x layers units)."""
     import oracle as O
     import synth
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
     rng = np.random.default_rng(1234)
     shape = O.Shape(num_kv_heads=1, num_q_heads=4)
     law = synth.heavy_tail_law(rng, 1)
@@ -143,18 +154,210 @@ def cpu_baseline(H, layers, seq_len, budget_s=20.0):
     v = law.sample_bf16(rng, seq_len)
     O.kv_write(shape, cache, layer, k, v, np.zeros(seq_len, int), np.arange(seq_len), table, [seq_len])
     q = synth.decode_queries(rng, 1, 4)
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < 3 or (time.perf_counter() - t_start < budget_s and len(times) < 50):
-        t0 = time.perf_counter()
-        O.decode(shape, cache, layer, q, table, [seq_len], SIG)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > 3 * budget_s:
-            break
-    t_unit = statistics.median(times)
-    threads = sum(int(i.get("num_threads", 0)) for i in threadpool_info() if i.get("user_api") == "blas")
-    return t_unit, len(times), max(threads, 1)
 
+    def timed(budget):
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < 3 or (time.perf_counter() - t_start < budget and len(times) < 50):
+            t0 = time.perf_counter()
+            O.decode(shape, cache, layer, q, table, [seq_len], SIG)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > 3 * budget:
+                break
+        return statistics.median(times), len(times)
+
+    t_unit, reps = timed(budget_s)
+    threads = sum(int(i.get("num_threads", 0)) for i in threadpool_info() if i.get("user_api") == "blas")
+    with threadpool_limits(1):
+        t_one, reps_one = timed(budget_s / 2)
+    return t_unit, reps, max(threads, 1), t_one, reps_one
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+
+def build_workload(name, rng, gen, dev, n_fill_minus=0):
+    """Sequences, page tables and per-layer caches of a named workload, prefilled
+    through kv_write with positions [0, L - n_fill_minus) of every sequence
+    (seeded synthetic K/V drawn on the device).  Ragged workloads share the
+    first SHARED_PREFIX_TOKENS tokens (same values, same physical pages) among a
+    contiguous quarter of the batch."""
+    import torch
+    from types import SimpleNamespace
+
+    import int2_rotated_kv_write_amd as lib
+    import synth
+    from synth.device import sample_kv_device
+    wl = WORKLOADS[name]
+    B, Hq, H, NL = wl["batch"], wl["q_heads"], wl["kv_heads"], wl["layers"]
+    if isinstance(wl["seq_len"], tuple):
+        lens = synth.ragged_lengths(rng, B, *wl["seq_len"])
+    else:
+        lens = np.full(B, wl["seq_len"], np.int32)
+    max_pages = int(math.ceil(lens.max() / 16))
+    shape = lib.CacheShape(H, Hq)
+    law = synth.heavy_tail_law(rng, H) if wl["law"] == "heavy" else synth.outlier_law(rng, H)
+
+    # ---- offline calibration (host, native library), one set replicated per layer ----
+    t0 = time.perf_counter()
+    qc, kc, vc = synth.calibration_samples(rng, law, Hq // H, 2048)
+    u_k, u_v, ck, cv = lib.calibrate_layer(qc, kc, vc, SIG, 0.999)
+    log(f"{name}: calibration {time.perf_counter() - t0:.1f}s clip_k={ck:.3f} clip_v={cv:.3f}")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    u_k_d, u_v_d = bf(u_k), bf(u_v)
+
+    # ---- page table (shared by the layers' separate cache pools) ----
+    sharers = []
+    if wl["table"] == "permuted":
+        table = synth.permuted_page_table(rng, B, max_pages)
+    elif wl["table"] == "shared_prefix":
+        n_share = B // 4
+        s0 = int(rng.integers(0, B - n_share + 1))
+        sharers = list(range(s0, s0 + n_share))
+        table, _, _ = synth.shared_prefix_page_table(rng, lens, max_pages, SHARED_PREFIX_TOKENS, sharers)
+    else:
+        table = synth.contiguous_page_table(B, max_pages)
+    num_pages = int(table.max()) + 1
+    table_d = torch.from_numpy(table).to(dev)
+
+    # ---- caches ----
+    caches = []
+    t0 = time.perf_counter()
+    after = torch.from_numpy(np.maximum(lens - n_fill_minus, 0).astype(np.int32)).to(dev)
+    for layer in range(NL):
+        c = lib.allocate_cache(shape, num_pages, B, dev, u_k=u_k_d.clone(), u_v=u_v_d.clone(),
+                               clip_k=float(ck), clip_v=float(cv))
+        prefix_kv = None
+        for b in range(B):
+            n = int(lens[b]) - n_fill_minus
+            for s0 in range(0, n, 1 << 16):
+                m = min(1 << 16, n - s0)
+                k = sample_kv_device(law, m, gen, dev)
+                v = sample_kv_device(law, m, gen, dev)
+                if s0 == 0 and b in sharers:   # shared prefix: same tokens, same physical pages
+                    if prefix_kv is None:
+                        prefix_kv = (k[:SHARED_PREFIX_TOKENS].clone(), v[:SHARED_PREFIX_TOKENS].clone())
+                    k[:SHARED_PREFIX_TOKENS] = prefix_kv[0]
+                    v[:SHARED_PREFIX_TOKENS] = prefix_kv[1]
+                idx = torch.full((m,), b, dtype=torch.int32, device=dev)
+                pos = torch.arange(s0, s0 + m, dtype=torch.int32, device=dev)
+                lib.kv_write(shape, c, k, v, idx, pos, table_d, after)
+        caches.append(c)
+        if layer % 6 == 5 or layer == NL - 1:
+            torch.cuda.synchronize()
+            log(f"{name}: prefilled {layer + 1}/{NL} layers ({time.perf_counter() - t0:.1f}s)")
+    return SimpleNamespace(B=B, Hq=Hq, H=H, NL=NL, lens=lens, max_pages=max_pages, shape=shape, law=law,
+                           table=table, table_d=table_d, num_pages=num_pages, caches=caches, sharers=sharers)
+
+
+def event_us(calls, reps):
+    """Mean and median device time (us) of `reps` calls cycled over `calls`, each
+    bracketed by HIP events on the stream the library launches on (torch's
+    current stream), after one untimed pass over `calls`."""
+    import torch
+    for c in calls:
+        c()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        calls[i % len(calls)]()
+        e1.record()
+    torch.cuda.synchronize()
+    t = [1e3 * e0.elapsed_time(e1) for e0, e1 in ev]
+    return statistics.mean(t), statistics.median(t)
+
+
+def shared_pages_saved(lens, sharers, H, G):
+    """INT2 page blocks (1,280 B per page and KV head) that cascade decode does
+    not read on the ragged workload: every sharer whose INT2 history holds the
+    shared pages whole takes them from one read per block of 16 ceil(G / 4) of
+    the sharers' query heads instead of its own."""
+    pages = (SHARED_PREFIX_TOKENS - SINK) // 16
+    users = [b for b in sharers if max(SINK, int(lens[b]) - RECENT) // 16 - SINK // 16 >= pages]
+    if not users:
+        return 0, 0, 0
+    per_block = 16 * ((G + 3) // 4)
+    reads = -(-len(users) * G // per_block)
+    return pages, len(users), (len(users) - reads) * pages * H
+
+
+def bench_single(rng, gen, dev):
+    """One Qwen3-8B-shaped layer at batch 1 and 100,000 tokens: decode_attn over
+    8 separate cache copies in turn (525 MB, twice the 256 MB MALL), so every
+    call reads its pages from HBM."""
+    import torch
+
+    import int2_rotated_kv_write_amd as lib
+    from synth.device import sample_queries_device
+    name = "qwen3_8b_layer_100k"
+    W = build_workload(name, rng, gen, dev)
+    q = sample_queries_device(W.B, W.Hq, gen, dev)
+    lens_d = torch.from_numpy(W.lens.astype(np.int32)).to(dev)
+    out = torch.empty((W.B, W.Hq, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.decode_workspace_bytes(W.shape, W.B, W.max_pages), dtype=torch.uint8, device=dev)
+    calls = [lib.prepare_decode_attn(W.shape, c, q, W.table_d, lens_d, out, ws, SIG) for c in W.caches]
+    mean, med = event_us(calls, 20 * len(calls))
+    nbytes = decode_bytes(W.lens, W.H, W.Hq)
+    gbs = nbytes / (mean * 1e-6) / 1e9
+    log(f"{name}: decode_attn {mean:.1f} us (median {med:.1f}), {gbs:.0f} GB/s")
+    return {"workload": name, "batch": W.B, "seq_len": int(W.lens[0]), "num_q_heads": W.Hq, "num_kv_heads": W.H,
+            "page_table": "contiguous", "cache_copies_cycled": W.NL,
+            "kernel": "decode_attn (rotate_q + split + reduce)", "us": mean, "us_median": med,
+            "bytes_per_launch": nbytes, "achieved_gbs": gbs, "frac": gbs / PEAK_HBM_GBS,
+            "tokens_per_s_36_layers": 1.0 / (36 * mean * 1e-6)}
+
+
+def bench_ragged(rng, gen, dev):
+    """64 sequences of 4,096..131,072 tokens, G = 8, a contiguous quarter of the
+    batch sharing a 4,096-token prefix (same physical pages): decode_attn, and
+    decode_attn_cascade with that quarter as one group."""
+    import torch
+
+    import int2_rotated_kv_write_amd as lib
+    from synth.device import sample_queries_device
+    name = "ragged_64x4k_128k"
+    W = build_workload(name, rng, gen, dev)
+    G = W.Hq // W.H
+    q = sample_queries_device(W.B, W.Hq, gen, dev)
+    lens_d = torch.from_numpy(W.lens.astype(np.int32)).to(dev)
+    out = torch.empty((W.B, W.Hq, 128), dtype=torch.bfloat16, device=dev)
+    out_c = torch.empty_like(out)
+    ws = torch.empty(lib.decode_workspace_bytes(W.shape, W.B, W.max_pages), dtype=torch.uint8, device=dev)
+    sh_pages = (SHARED_PREFIX_TOKENS - SINK) // 16
+    ws_c = torch.empty(lib.cascade_workspace_bytes(W.shape, W.B, W.max_pages, sh_pages), dtype=torch.uint8,
+                       device=dev)
+    s0, n_sh = W.sharers[0], len(W.sharers)
+    cu = torch.tensor([s0, s0 + n_sh], dtype=torch.int32, device=dev)
+    gp = torch.tensor([sh_pages], dtype=torch.int32, device=dev)
+    plain = lib.prepare_decode_attn(W.shape, W.caches[0], q, W.table_d, lens_d, out, ws, SIG)
+    cas = lib.prepare_decode_attn_cascade(W.shape, W.caches[0], q, W.table_d, lens_d, cu, gp, out_c, ws_c, n_sh,
+                                          sh_pages, SIG)
+    t_plain, m_plain = event_us([plain], 20)
+    t_cas, m_cas = event_us([cas], 20)
+    diff = (out.float() - out_c.float()).abs().max().item()
+    nbytes = decode_bytes(W.lens, W.H, W.Hq)
+    pages, users, saved_blocks = shared_pages_saved(W.lens, W.sharers, W.H, G)
+    saved = saved_blocks * 1280
+    gbs = nbytes / (t_plain * 1e-6) / 1e9
+    log(f"{name}: decode_attn {t_plain:.1f} us ({gbs:.0f} GB/s), cascade {t_cas:.1f} us, "
+        f"{saved / 1e6:.1f} MB of shared pages not re-read, max |out diff| {diff:.3g}")
+    return {"workload": name, "batch": W.B, "seq_len_min": int(W.lens.min()), "seq_len_max": int(W.lens.max()),
+            "seq_len_total": int(W.lens.sum()), "num_q_heads": W.Hq, "num_kv_heads": W.H,
+            "page_table": "permuted, shared prefix", "sharers": n_sh, "shared_prefix_tokens": SHARED_PREFIX_TOKENS,
+            "decode_attn": {"us": t_plain, "us_median": m_plain, "bytes_per_launch": nbytes, "achieved_gbs": gbs,
+                            "frac": gbs / PEAK_HBM_GBS},
+            "decode_attn_cascade": {"us": t_cas, "us_median": m_cas, "bytes_per_launch": nbytes - saved,
+                                    "shared_int2_pages": pages, "sharers_using_shared_reads": users,
+                                    "page_bytes_saved": saved, "bytes_saved_frac": saved / nbytes,
+                                    "speedup": t_plain / t_cas, "max_abs_diff_vs_decode_attn": diff}}
 
 def main():
     ap = argparse.ArgumentParser()
@@ -163,6 +366,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="concurrent_28x100k_36l", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the single-sequence and ragged workloads")
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -181,65 +385,14 @@ def main():
     dev = torch.device("cuda:0")
     lib.load()
     wl = WORKLOADS[args.workload]
-    B, Hq, H, NL = wl["batch"], wl["q_heads"], wl["kv_heads"], wl["layers"]
-    rng = np.random.default_rng(args.seed)
-    if isinstance(wl["seq_len"], tuple):
-        lens = synth.ragged_lengths(rng, B, *wl["seq_len"])
-    else:
-        lens = np.full(B, wl["seq_len"], np.int32)
-    max_pages = int(math.ceil(lens.max() / 16))
-    shape = lib.CacheShape(H, Hq)
-    law = synth.heavy_tail_law(rng, H) if wl["law"] == "heavy" else synth.outlier_law(rng, H)
-
-    # ---- offline calibration (host, native library), one set replicated per layer ----
-    t0 = time.perf_counter()
-    qc, kc, vc = synth.calibration_samples(rng, law, Hq // H, 2048)
-    u_k, u_v, ck, cv = lib.calibrate_layer(qc, kc, vc, SIG, 0.999)
-    log(f"calibration: {time.perf_counter() - t0:.1f}s clip_k={ck:.3f} clip_v={cv:.3f}")
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-    u_k_d, u_v_d = bf(u_k), bf(u_v)
-
-    # ---- page tables (one per layer, like separate cache pools) ----
-    sharers = []
-    if wl["table"] == "permuted":
-        table = synth.permuted_page_table(rng, B, max_pages)
-    elif wl["table"] == "shared_prefix":
-        sharers = sorted(int(x) for x in rng.choice(B, B // 4, replace=False))
-        table, _, _ = synth.shared_prefix_page_table(rng, lens, max_pages, SHARED_PREFIX_TOKENS, sharers)
-    else:
-        table = synth.contiguous_page_table(B, max_pages)
-    num_pages = int(table.max()) + 1
-    table_d = torch.from_numpy(table).to(dev)
-
-    # ---- caches: prefill positions [0, L-1) of every sequence through kv_write ----
+    rng = np.random.default_rng(args.seed)
     gen = torch.Generator(device=dev)
     gen.manual_seed(args.seed)
-    caches = []
-    t0 = time.perf_counter()
-    for layer in range(NL):
-        c = lib.allocate_cache(shape, num_pages, B, dev, u_k=u_k_d.clone(), u_v=u_v_d.clone(),
-                               clip_k=float(ck), clip_v=float(cv))
-        prefix_kv = None
-        for b in range(B):
-            n = int(lens[b]) - 1
-            for s0 in range(0, n, 1 << 16):
-                m = min(1 << 16, n - s0)
-                k = sample_kv_device(law, m, gen, dev)
-                v = sample_kv_device(law, m, gen, dev)
-                if s0 == 0 and b in sharers:   # shared prefix: same tokens, same physical pages
-                    if prefix_kv is None:
-                        prefix_kv = (k[:SHARED_PREFIX_TOKENS].clone(), v[:SHARED_PREFIX_TOKENS].clone())
-                    k[:SHARED_PREFIX_TOKENS] = prefix_kv[0]
-                    v[:SHARED_PREFIX_TOKENS] = prefix_kv[1]
-                idx = torch.full((m,), b, dtype=torch.int32, device=dev)
-                pos = torch.arange(s0, s0 + m, dtype=torch.int32, device=dev)
-                after = torch.from_numpy(np.maximum(lens - 1, 0).astype(np.int32)).to(dev)
-                lib.kv_write(shape, c, k, v, idx, pos, table_d, after)
-        caches.append(c)
-        if layer % 6 == 5 or layer == NL - 1:
-            torch.cuda.synchronize()
-            log(f"prefilled {layer + 1}/{NL} layers ({time.perf_counter() - t0:.1f}s)")
-
+    W = build_workload(args.workload, rng, gen, dev, n_fill_minus=1)
+    B, Hq, H, NL = W.B, W.Hq, W.H, W.NL
+    lens, max_pages, shape, law, table_d, caches = W.lens, W.max_pages, W.shape, W.law, W.table_d, W.caches
+    num_pages = W.num_pages
     # ---- per-step inputs: the new token of every sequence and the queries ----
     new_k = [sample_kv_device(law, B, gen, dev) for _ in range(NL)]
     new_v = [sample_kv_device(law, B, gen, dev) for _ in range(NL)]
@@ -301,6 +454,7 @@ def main():
 
     # ---- write path: one kv_write of 100,000 prefill tokens x H KV heads (K and V),
     # outlier law, its own calibration; HIP events around each call ----
+    W.caches = None
     del caches, layer_steps, decodes
     torch.cuda.empty_cache()
     pw_law = synth.outlier_law(rng, H)
@@ -374,15 +528,26 @@ def main():
     log(f"read probe: {read_gbs:.0f} GB/s (decode_attn at {achieved / read_gbs:.1%} of it)")
     del probe_buf, probe_sink, probe
 
+    extras = {}
+    if not args.no_extras:
+        torch.cuda.empty_cache()
+        extras["single_1x100k"] = bench_single(rng, gen, dev)
+        torch.cuda.empty_cache()
+        extras["ragged_64x4k_128k"] = bench_ragged(rng, gen, dev)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
-        t_unit, reps, threads = cpu_baseline(H, NL, int(lens.max()))
+        t_unit, reps, threads, t_one, reps_one = cpu_baseline(H, NL, int(lens.max()))
         units = B * H * NL
         cpu = {"value": B / (t_unit * units), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
                "sample": (f"fp64 oracle decode of 1 sequence x 1 KV head (4 query heads) at "
-                          f"L={int(lens.max())}, median of {reps} runs = {t_unit:.3f}s, "
-                          f"extrapolated x{units} (batch x KV heads x layers)")}
-        log(f"cpu baseline: {t_unit:.3f}s per unit, {threads} threads")
+                          f"L={int(lens.max())}, median of {reps} runs = {t_unit:.3f}s with {threads} BLAS "
+                          f"threads, extrapolated x{units} (batch x KV heads x layers)"),
+               "one_thread": {"value": B / (t_one * units), "unit": "tokens/s", "cores": 1,
+                              "sample": f"the same unit with 1 BLAS thread, median of {reps_one} runs = {t_one:.3f}s"}}
+        log(f"cpu baseline: {t_unit:.3f}s per unit with {threads} threads, {t_one:.3f}s with 1")
 
     traffic = None
     if args.workload == "concurrent_28x100k_36l":
@@ -409,6 +574,7 @@ def main():
                           "frac": b16_gbs / PEAK_HBM_GBS, "int2_speedup": b16_us / (dec_avg_ms * 1e3),
                           "cache_bytes_ratio": b16_bytes / dbytes},
         "step_hbm_gbs": step_bytes / (elapsed / args.steps) / 1e9,
+        **extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -10,7 +10,7 @@ the first call does, and raises if the library is missing.
 from ._native import load, library_path
 from .api import (
     CacheBuffers, CacheShape, OscarError, allocate_cache, bf16_decode_attn, decode_attn_noalloc, extend_attn,
-    extend_workspace_bytes, cascade_workspace_bytes, decode_attn_cascade,
+    extend_workspace_bytes, cascade_workspace_bytes, decode_attn_cascade, prepare_decode_attn_cascade,
     bf16_decode_workspace_bytes, calibrate_layer, decode_attn, decode_step, decode_workspace_bytes, kv_write,
     prepare_bf16_decode_attn, prepare_decode_attn, prepare_decode_step, prepare_kv_write, prepare_read_probe,
     read_probe_sink_bytes, status_string,
@@ -23,5 +23,5 @@ __all__ = [
     "bf16_decode_attn", "bf16_decode_workspace_bytes", "prepare_bf16_decode_attn",
     "prepare_read_probe", "read_probe_sink_bytes", "decode_step", "prepare_decode_step",
     "decode_attn_noalloc", "extend_attn", "extend_workspace_bytes",
-    "cascade_workspace_bytes", "decode_attn_cascade",
+    "cascade_workspace_bytes", "decode_attn_cascade", "prepare_decode_attn_cascade",
 ]

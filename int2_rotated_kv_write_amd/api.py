@@ -177,13 +177,8 @@ def cascade_workspace_bytes(shape: CacheShape, batch: int, max_pages: int, max_s
     return int(load().oscar_cascade_workspace_bytes(ctypes.byref(shape.c()), batch, max_pages, max_shared_pages))
 
 
-def decode_attn_cascade(shape: CacheShape, cache: CacheBuffers, q, page_table, seq_lens, cu_groups, group_pages,
-                        out, workspace, max_group: int, max_shared_pages: int, sm_scale: float | None = None,
-                        stream=None) -> None:
-    """oscar_decode_attn_cascade: decode_attn where groups of sequences (batch
-    entries cu_groups[g] .. cu_groups[g+1]-1, int32 [n_groups+1]) share their first
-    group_pages[g] (int32 [n_groups]) INT2 pages; those pages are read once per
-    block of the members' query heads.  Same result as decode_attn."""
+def _cascade_args(shape, cache, q, page_table, seq_lens, cu_groups, group_pages, out, workspace, max_group,
+                  max_shared_pages, sm_scale, stream):
     import torch
     _check_cache(shape, cache)
     B = int(seq_lens.numel())
@@ -194,16 +189,35 @@ def decode_attn_cascade(shape: CacheShape, cache: CacheBuffers, q, page_table, s
         raise OscarError("page_table must be [>= batch][max_pages]")
     if workspace.dtype != torch.uint8 or not workspace.is_cuda:
         raise OscarError("workspace must be a uint8 device tensor")
-    rc = load().oscar_decode_attn_cascade(
-        ctypes.byref(shape.c()), ctypes.byref(cache.c()),
-        _dev(q, torch.bfloat16, "q", (B, shape.num_q_heads, HEAD_DIM)),
-        _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
-        _dev(seq_lens, torch.int32, "seq_lens", (B,)), B,
-        _dev(cu_groups, torch.int32, "cu_groups", (n_groups + 1,)), _dev(group_pages, torch.int32, "group_pages"),
-        n_groups, int(max_group), int(max_shared_pages), float(sm_scale),
-        _dev(out, torch.bfloat16, "out", (B, shape.num_q_heads, HEAD_DIM)),
-        workspace.data_ptr(), workspace.numel(), _stream(stream))
-    _check(rc)
+    cs, cl = shape.c(), cache.c()
+    args = (ctypes.byref(cs), ctypes.byref(cl), _dev(q, torch.bfloat16, "q", (B, shape.num_q_heads, HEAD_DIM)),
+            _dev(page_table, torch.int32, "page_table"), int(page_table.shape[1]),
+            _dev(seq_lens, torch.int32, "seq_lens", (B,)), B,
+            _dev(cu_groups, torch.int32, "cu_groups", (n_groups + 1,)), _dev(group_pages, torch.int32, "group_pages"),
+            n_groups, int(max_group), int(max_shared_pages), float(sm_scale),
+            _dev(out, torch.bfloat16, "out", (B, shape.num_q_heads, HEAD_DIM)),
+            workspace.data_ptr(), workspace.numel(), _stream(stream))
+    return args, (cs, cl, q, page_table, seq_lens, cu_groups, group_pages, out, workspace)
+
+
+def decode_attn_cascade(shape: CacheShape, cache: CacheBuffers, q, page_table, seq_lens, cu_groups, group_pages,
+                        out, workspace, max_group: int, max_shared_pages: int, sm_scale: float | None = None,
+                        stream=None) -> None:
+    """oscar_decode_attn_cascade: decode_attn where groups of sequences (batch
+    entries cu_groups[g] .. cu_groups[g+1]-1, int32 [n_groups+1]) share their first
+    group_pages[g] (int32 [n_groups]) INT2 pages; those pages are read once per
+    block of the members' query heads.  Same result as decode_attn."""
+    args, _ = _cascade_args(shape, cache, q, page_table, seq_lens, cu_groups, group_pages, out, workspace,
+                            max_group, max_shared_pages, sm_scale, stream)
+    _check(load().oscar_decode_attn_cascade(*args))
+
+
+def prepare_decode_attn_cascade(shape: CacheShape, cache: CacheBuffers, q, page_table, seq_lens, cu_groups,
+                                group_pages, out, workspace, max_group: int, max_shared_pages: int,
+                                sm_scale: float | None = None, stream=None) -> PreparedCall:
+    args, keep = _cascade_args(shape, cache, q, page_table, seq_lens, cu_groups, group_pages, out, workspace,
+                               max_group, max_shared_pages, sm_scale, stream)
+    return PreparedCall(load().oscar_decode_attn_cascade, args, keep)
 
 
 def decode_attn_noalloc(shape: CacheShape, cache: CacheBuffers, q, page_table, seq_lens, out,
