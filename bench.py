@@ -18,7 +18,10 @@ Besides the headline line's fields, the JSON carries (unless --no-extras):
                     decode_attn and decode_attn_cascade, with the page bytes
                     the shared reads save;
   kv_write_prefill  one kv_write of 100,000 prefill tokens x 8 KV heads;
-  bf16_baseline     the all-BF16 paged decode at the headline shape.
+  bf16_baseline     the all-BF16 paged decode at the headline shape;
+  rotation_ablation attention-output error against BF16 of OSCAR,
+                    Hadamard-only and naive INT2 rotations through the
+                    library's kernels on two synthetic laws.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -359,6 +362,88 @@ def bench_ragged(rng, gen, dev):
                                     "page_bytes_saved": saved, "bytes_saved_frac": saved / nbytes,
                                     "speedup": t_plain / t_cas, "max_abs_diff_vs_decode_attn": diff}}
 
+
+ABLATION = dict(batch=8, seq_len=16384, q_heads=8, kv_heads=2, rank=8)
+
+
+def naive_basis():
+    """U = P H (Sylvester Hadamard / sqrt(128), rows in 7-bit-reversed order), so that
+    R = U H P = P H H P = I: INT2 then quantizes the raw channels (the naive
+    INT2 baseline), up to the bf16 rounding of U."""
+    h = np.array([[1.0]])
+    while h.shape[0] < 128:
+        h = np.block([[h, h], [h, -h]])
+    br = [int(format(i, "07b")[::-1], 2) for i in range(128)]
+    return h[br, :] / math.sqrt(128)
+
+
+def bench_ablation(rng, gen, dev):
+    """Attention-output error against BF16 attention of three rotations, all through
+    kv_write + decode_attn with only U and the clips changed: OSCAR (calibrated U_Q,
+    U_S), Hadamard-only (U = I) and naive INT2 (U = bf16(P H), R ~ I); clips are the
+    0.999 quantile of the calibration set rotated by each U.  Three synthetic laws:
+    the outlier law with N(0,1) queries; the same K/V with rank-8 queries whose
+    directions avoid the outlier channels; and the outlier law turned by a random
+    orthogonal matrix per head (outliers along dense directions) with N(0,1)
+    queries.  The reference is fp32 softmax attention over the same bf16 K/V."""
+    import torch
+
+    import int2_rotated_kv_write_amd as lib
+    import synth
+    from synth.device import sample_kv_device
+    B, L, Hq, H = ABLATION["batch"], ABLATION["seq_len"], ABLATION["q_heads"], ABLATION["kv_heads"]
+    G = Hq // H
+    shape = lib.CacheShape(H, Hq)
+    pages = L // 16
+    table_d = torch.arange(B * pages, dtype=torch.int32, device=dev).view(B, pages)
+    lens_d = torch.full((B,), L, dtype=torch.int32, device=dev)
+    seq = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(L)
+    pos = torch.arange(L, dtype=torch.int32, device=dev).repeat(B)
+    ws = torch.empty(lib.decode_workspace_bytes(shape, B, pages), dtype=torch.uint8, device=dev)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    eye = synth.f32_to_bf16_bits(np.broadcast_to(np.eye(128), (H, 128, 128)))
+    naive = synth.f32_to_bf16_bits(np.broadcast_to(naive_basis(), (H, 128, 128)))
+    result = {"setup": {"batch": B, "seq_len": L, "num_q_heads": Hq, "num_kv_heads": H,
+                        "calibration_samples": 2048, "clip_quantile": 0.999, "query_rank": ABLATION["rank"],
+                        "metric": "||out - ref||_F / ||ref||_F and mean |out - ref| over all outputs; "
+                                  "ref = fp32 attention over the bf16 K/V"}}
+    for law_name in ("outlier_iid_queries", "outlier_lowrank_misaligned_queries", "dense_outlier_iid_queries"):
+        kv_law = synth.dense_outlier_law(rng, H) if law_name.startswith("dense") else synth.outlier_law(rng, H)
+        q_law = synth.lowrank_query_law(rng, kv_law, ABLATION["rank"]) if "lowrank" in law_name else None
+        qc, kc, vc = synth.calibration_samples(rng, kv_law, G, 2048, q_law)
+        u_k, u_v, ck, cv = lib.calibrate_layer(qc, kc, vc, SIG, 0.999)
+        variants = {"oscar": (u_k, u_v, ck, cv),
+                    "hadamard_only": (eye, eye, lib.calibrate_clip(kc, eye), lib.calibrate_clip(vc, eye)),
+                    "naive_int2": (naive, naive, lib.calibrate_clip(kc, naive), lib.calibrate_clip(vc, naive))}
+        k = sample_kv_device(kv_law, B * L, gen, dev)
+        v = sample_kv_device(kv_law, B * L, gen, dev)
+        if q_law is None:
+            q = torch.randn((B, Hq, 128), generator=gen, device=dev).to(torch.bfloat16)
+        else:
+            q = bf(q_law.decode_queries(rng, B, Hq))
+        ref = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+        kf, vf = k.float().view(B, L, H, 128), v.float().view(B, L, H, 128)
+        for b in range(B):
+            for h in range(H):
+                lg = (q[b, h * G:(h + 1) * G].float() @ kf[b, :, h].t().contiguous()) * SIG
+                ref[b, h * G:(h + 1) * G] = torch.softmax(lg, dim=-1) @ vf[b, :, h]
+        res = {}
+        for name, (uk, uv, c_k, c_v) in variants.items():
+            cache = lib.allocate_cache(shape, B * pages, B, dev, u_k=bf(uk), u_v=bf(uv), clip_k=float(c_k),
+                                       clip_v=float(c_v))
+            lib.kv_write(shape, cache, k, v, seq, pos, table_d, lens_d)
+            out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+            lib.decode_attn(shape, cache, q, table_d, lens_d, out, ws, SIG)
+            err = out.float() - ref
+            res[name] = {"rel_fro_err": (err.norm() / ref.norm()).item(), "mean_abs_err": err.abs().mean().item(),
+                         "max_abs_err": err.abs().max().item(), "clip_k": float(c_k), "clip_v": float(c_v)}
+            del cache
+        for name in res:
+            res[name]["err_vs_oscar"] = res[name]["rel_fro_err"] / res["oscar"]["rel_fro_err"]
+        log(f"ablation {law_name}: " + ", ".join(f"{n} {r['rel_fro_err']:.4f}" for n, r in res.items()))
+        result[law_name] = res
+    return result
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -366,7 +451,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="concurrent_28x100k_36l", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the single-sequence and ragged workloads")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the single-sequence and ragged workloads and the rotation ablation")
+    ap.add_argument("--only-ablation", action="store_true", help="run the rotation ablation alone and print it")
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -384,6 +471,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     lib.load()
+    if args.only_ablation:
+        rng = np.random.default_rng(args.seed)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        print(json.dumps({"rotation_ablation": bench_ablation(rng, gen, dev)}), flush=True)
+        return
     wl = WORKLOADS[args.workload]
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     rng = np.random.default_rng(args.seed)
@@ -534,6 +627,8 @@ def main():
         extras["single_1x100k"] = bench_single(rng, gen, dev)
         torch.cuda.empty_cache()
         extras["ragged_64x4k_128k"] = bench_ragged(rng, gen, dev)
+        torch.cuda.empty_cache()
+        extras["rotation_ablation"] = bench_ablation(rng, gen, dev)
         torch.cuda.empty_cache()
 
     cpu = None

@@ -246,6 +246,16 @@ int oscar_calibrate_layer(int32_t num_kv_heads, int32_t gqa, int32_t num_samples
                           uint16_t* u_v_out, float* clip_k_out, float* clip_v_out,
                           int32_t num_threads);
 
+/* calibrate_clip -- HOST, offline: the clip threshold of [es] 2.2 A step 4
+ * for a rotation basis the caller chooses (the clip oscar_calibrate_layer
+ * returns, for any U: e.g. U = I, the Hadamard-only rotation of [es] section
+ * 4).  x_cal host double [H_kv][num_samples][128] calibration keys or values,
+ * u host uint16 bf16 [H_kv][128][128]; *clip_out = the `quantile` (linear
+ * interpolation) of |x U H P| over all samples, channels and heads.  Returns
+ * OSCAR_OK or OSCAR_EINVAL. */
+int oscar_calibrate_clip(int32_t num_kv_heads, int32_t num_samples, const double* x_cal, const uint16_t* u,
+                         double quantile, float* clip_out);
+
 /* decode_attn_cascade -- decode_attn for a batch in which groups of sequences
  * share the physical pages of a common prefix (prefix caching: [es] 2.2 B and
  * section 3, item 3; [it] "Architettura del Sistema di Serving e Layout di

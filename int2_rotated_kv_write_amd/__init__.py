@@ -11,7 +11,7 @@ from ._native import load, library_path
 from .api import (
     CacheBuffers, CacheShape, OscarError, allocate_cache, bf16_decode_attn, decode_attn_noalloc, extend_attn,
     extend_workspace_bytes, cascade_workspace_bytes, decode_attn_cascade, prepare_decode_attn_cascade,
-    bf16_decode_workspace_bytes, calibrate_layer, decode_attn, decode_step, decode_workspace_bytes, kv_write,
+    bf16_decode_workspace_bytes, calibrate_clip, calibrate_layer, decode_attn, decode_step, decode_workspace_bytes, kv_write,
     prepare_bf16_decode_attn, prepare_decode_attn, prepare_decode_step, prepare_kv_write, prepare_read_probe,
     read_probe_sink_bytes, status_string,
 )
@@ -19,7 +19,7 @@ from .api import (
 __all__ = [
     "load", "library_path", "CacheShape", "CacheBuffers", "OscarError",
     "allocate_cache", "kv_write", "decode_attn", "decode_workspace_bytes",
-    "calibrate_layer", "status_string", "prepare_kv_write", "prepare_decode_attn",
+    "calibrate_layer", "calibrate_clip", "status_string", "prepare_kv_write", "prepare_decode_attn",
     "bf16_decode_attn", "bf16_decode_workspace_bytes", "prepare_bf16_decode_attn",
     "prepare_read_probe", "read_probe_sink_bytes", "decode_step", "prepare_decode_step",
     "decode_attn_noalloc", "extend_attn", "extend_workspace_bytes",

@@ -29,7 +29,7 @@ EXPORTS = ("oscar_kv_write", "oscar_decode_workspace_bytes", "oscar_decode_attn"
            "oscar_cascade_workspace_bytes", "oscar_decode_attn_cascade",
            "oscar_bf16_decode_workspace_bytes", "oscar_bf16_decode_attn",
            "oscar_read_probe_sink_bytes", "oscar_read_probe",
-           "oscar_calibrate_layer", "oscar_status_string", "oscar_last_error")
+           "oscar_calibrate_layer", "oscar_calibrate_clip", "oscar_status_string", "oscar_last_error")
 
 
 def library_path() -> str:
@@ -84,6 +84,8 @@ def load() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_float),
                                           ctypes.POINTER(ctypes.c_float), c_i32]
     lib.oscar_calibrate_layer.restype = ctypes.c_int
+    lib.oscar_calibrate_clip.argtypes = [c_i32, c_i32, dp, c_ptr, ctypes.c_double, ctypes.POINTER(ctypes.c_float)]
+    lib.oscar_calibrate_clip.restype = ctypes.c_int
     lib.oscar_status_string.argtypes = [ctypes.c_int]
     lib.oscar_status_string.restype = ctypes.c_char_p
     lib.oscar_last_error.argtypes = []

@@ -366,6 +366,22 @@ def calibrate_layer(q_cal: np.ndarray, k_cal: np.ndarray, v_cal: np.ndarray, sm_
     return u_k, u_v, np.float32(ck.value), np.float32(cv.value)
 
 
+def calibrate_clip(x_cal: np.ndarray, u: np.ndarray, quantile: float = 0.999) -> np.float32:
+    """oscar_calibrate_clip (host, offline): the clip threshold for the rotation
+    basis u (uint16 bf16 bits [H][128][128]) from calibration rows x_cal
+    (float64 [H][N][128])."""
+    x_cal = np.ascontiguousarray(x_cal, np.float64)
+    u = np.ascontiguousarray(u, np.uint16)
+    H, N, D = x_cal.shape
+    if D != HEAD_DIM or u.shape != (H, D, D):
+        raise OscarError("x_cal [H][N][128], u [H][128][128]")
+    c = ctypes.c_float()
+    rc = load().oscar_calibrate_clip(H, N, x_cal.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), u.ctypes.data,
+                                     float(quantile), ctypes.byref(c))
+    _check(rc)
+    return np.float32(c.value)
+
+
 class PreparedCall:
     """A library call with its ctypes arguments built once (for tight loops);
     calling it re-issues the same launch on the same stream."""

@@ -248,3 +248,19 @@ extern "C" int oscar_calibrate_layer(int32_t num_kv_heads, int32_t gqa, int32_t 
   *clip_v_out = (float)quantile_linear(rv, quantile);
   return OSCAR_OK;
 }
+
+extern "C" int oscar_calibrate_clip(int32_t num_kv_heads, int32_t num_samples, const double* x_cal,
+                                    const uint16_t* u, double quantile, float* clip_out) {
+  if (num_kv_heads < 1 || num_samples < 1 || !x_cal || !u || !clip_out || !(quantile >= 0.0 && quantile <= 1.0))
+    return OSCAR_EINVAL;
+  const int H = num_kv_heads, N = num_samples;
+  std::vector<double> r;
+  r.reserve((size_t)H * N * D);
+  for (int h = 0; h < H; ++h) {
+    std::vector<double> ub(D * D);
+    for (int i = 0; i < D * D; ++i) ub[i] = from_bf16(u[(size_t)h * D * D + i]);
+    rotated_abs(x_cal + (size_t)h * N * D, N, ub, r);
+  }
+  *clip_out = (float)quantile_linear(r, quantile);
+  return OSCAR_OK;
+}

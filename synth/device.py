@@ -20,6 +20,9 @@ def sample_kv_device(law, n_tokens: int, gen, device):
             z = torch.randn((n_tokens, len(ch)), generator=gen, device=device)
             c = torch.randn((n_tokens, len(ch), nu), generator=gen, device=device).square().sum(-1)
             x[:, h, ch] = z / torch.sqrt(c / law.nu) * law.scale
+    if law.mix is not None:
+        mix = torch.as_tensor(law.mix, device=device, dtype=torch.float32)
+        x = torch.einsum("nhc,hcd->nhd", x, mix).contiguous()
     return x.to(torch.bfloat16)
 
 

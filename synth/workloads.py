@@ -22,7 +22,8 @@ HEAD_DIM = 128
 
 __all__ = [
     "HEAD_DIM", "f32_to_bf16_bits", "bf16_bits_to_f32", "KVLaw", "outlier_law",
-    "heavy_tail_law", "calibration_samples", "decode_queries",
+    "heavy_tail_law", "calibration_samples", "decode_queries", "QueryLaw", "lowrank_query_law",
+    "dense_outlier_law",
     "contiguous_page_table", "permuted_page_table", "shared_prefix_page_table",
     "ragged_lengths", "WORKLOADS",
 ]
@@ -53,6 +54,7 @@ class KVLaw:
     channels: np.ndarray           # [H_kv][n_special] channel indices
     scale: float = 20.0
     nu: float = 3.0
+    mix: np.ndarray | None = None  # [H_kv][128][128] orthogonal: samples x -> x mix (dense outlier directions)
 
     @property
     def num_heads(self) -> int:
@@ -71,6 +73,8 @@ class KVLaw:
                 x[:, h, ch] = (t * self.scale).astype(np.float32)
             else:
                 raise ValueError(self.kind)
+        if self.mix is not None:
+            x = np.einsum("nhc,hcd->nhd", x, self.mix).astype(np.float32)
         return x
 
     def sample_bf16(self, rng: np.random.Generator, n_tokens: int) -> np.ndarray:
@@ -85,6 +89,15 @@ def outlier_law(rng: np.random.Generator, num_heads: int, n_channels: int = 4,
     return KVLaw("outlier", ch, scale=scale)
 
 
+def dense_outlier_law(rng: np.random.Generator, num_heads: int, n_channels: int = 4,
+                      scale: float = 20.0) -> KVLaw:
+    """The outlier law seen through a random orthogonal matrix per head: the
+    x20 outliers lie along dense directions instead of single channels."""
+    base = outlier_law(rng, num_heads, n_channels, scale)
+    mix = np.stack([np.linalg.qr(rng.standard_normal((HEAD_DIM, HEAD_DIM)))[0] for _ in range(num_heads)])
+    return KVLaw("outlier", base.channels, scale=scale, mix=mix)
+
+
 def heavy_tail_law(rng: np.random.Generator, num_heads: int, frac: float = 0.02,
                    scale: float = 10.0, nu: float = 3.0) -> KVLaw:
     n = int(math.ceil(frac * HEAD_DIM))  # 2.56 -> 3 channels per head
@@ -93,16 +106,57 @@ def heavy_tail_law(rng: np.random.Generator, num_heads: int, frac: float = 0.02,
     return KVLaw("heavy", ch, scale=scale, nu=nu)
 
 
+@dataclass
+class QueryLaw:
+    """Anisotropic queries: per KV head, q = z B + noise e with z ~ N(0, (128/r) I_r)
+    over an orthonormal basis B of r directions (rows) and e ~ N(0, I), so that
+    E|q|^2 is about 128 as for N(0,1) queries but concentrated in r directions."""
+    basis: np.ndarray              # [H_kv][r][128]
+    noise: float = 0.05
+
+    def sample(self, rng: np.random.Generator, num_heads_per_kv: int, n: int) -> np.ndarray:
+        """float32 [H_kv][G][n][128]."""
+        H, r, _ = self.basis.shape
+        z = rng.standard_normal((H, num_heads_per_kv, n, r)) * math.sqrt(HEAD_DIM / r)
+        q = np.einsum("hgnr,hrd->hgnd", z, self.basis)
+        q += self.noise * rng.standard_normal(q.shape)
+        return q.astype(np.float32)
+
+    def decode_queries(self, rng: np.random.Generator, batch: int, num_q_heads: int) -> np.ndarray:
+        """bf16 bits [B][Hq][128]; query head h G + g follows KV head h's basis."""
+        H = self.basis.shape[0]
+        G = num_q_heads // H
+        q = self.sample(rng, G, batch)                       # [H][G][B][128]
+        return f32_to_bf16_bits(q.transpose(2, 0, 1, 3).reshape(batch, num_q_heads, HEAD_DIM))
+
+
+def lowrank_query_law(rng: np.random.Generator, kv_law: KVLaw, rank: int = 8, noise: float = 0.05) -> QueryLaw:
+    """Queries of rank `rank` per KV head whose directions avoid the K/V law's
+    special channels (random Gaussian directions with those channels zeroed,
+    then orthonormalised): low-rank and misaligned with the outliers."""
+    bases = []
+    for h in range(kv_law.num_heads):
+        a = rng.standard_normal((HEAD_DIM, rank))
+        a[kv_law.channels[h], :] = 0.0
+        qmat, _ = np.linalg.qr(a)
+        bases.append(qmat.T)
+    return QueryLaw(np.stack(bases), noise)
+
+
 def calibration_samples(rng: np.random.Generator, law: KVLaw, group_size: int,
-                        n_samples: int = 2048):
+                        n_samples: int = 2048, q_law: QueryLaw | None = None):
     """Calibration activations for one layer.
 
-    Returns float64 arrays (q_cal [H][G][N][128] ~ N(0,1), k_cal [H][N][128],
-    v_cal [H][N][128]) with K and V drawn from ``law``, each value rounded to
-    bf16 first (they stand in for activations a bf16 model would produce).
+    Returns float64 arrays (q_cal [H][G][N][128] ~ N(0,1), or from ``q_law``,
+    k_cal [H][N][128], v_cal [H][N][128]) with K and V drawn from ``law``, each
+    value rounded to bf16 first (they stand in for activations a bf16 model
+    would produce).
     """
     H = law.num_heads
-    q = rng.standard_normal((H, group_size, n_samples, HEAD_DIM), dtype=np.float32)
+    if q_law is None:
+        q = rng.standard_normal((H, group_size, n_samples, HEAD_DIM), dtype=np.float32)
+    else:
+        q = q_law.sample(rng, group_size, n_samples)
     q = bf16_bits_to_f32(f32_to_bf16_bits(q)).astype(np.float64)
     k = law.sample(rng, n_samples).transpose(1, 0, 2)
     v = law.sample(rng, n_samples).transpose(1, 0, 2)

@@ -37,3 +37,26 @@ def test_native_calibration_matches_oracle(H, G, N, law):
 def test_native_calibration_rejects_bad_arguments():
     with pytest.raises(lib.OscarError):
         lib.calibrate_layer(np.zeros((1, 1, 1, 128)), np.zeros((1, 1, 128)), np.zeros((1, 1, 128)), SIG)
+
+
+@pytest.mark.parametrize("basis", ["identity", "naive", "calibrated"])
+def test_native_clip_for_a_chosen_basis(basis):
+    """oscar_calibrate_clip: the clip quantile of |x U H P| for any bf16 U, against
+    the oracle's rotation and NumPy's linear-interpolation quantile; with the
+    calibrated U it reproduces oscar_calibrate_layer's clip."""
+    rng = np.random.default_rng(11)
+    law = synth.outlier_law(rng, 2)
+    qc, kc, vc = synth.calibration_samples(rng, law, 2, 400)
+    if basis == "identity":
+        u = O.f64_to_bf16(np.broadcast_to(np.eye(128), (2, 128, 128)))
+    elif basis == "naive":
+        # U = bf16(P H): R = U H P is the identity up to the bf16 rounding of U
+        ph = O.bitrev_permutation() @ O.hadamard()
+        u = O.f64_to_bf16(np.broadcast_to(ph, (2, 128, 128)))
+        assert np.abs(O.rotation(u[0]) - np.eye(128)).max() < 2e-3
+    else:
+        u, _, ck, _ = lib.calibrate_layer(qc, kc, vc, SIG, 0.999)
+        assert lib.calibrate_clip(kc, u) == ck
+    want = np.quantile(np.concatenate([np.abs(kc[h] @ O.rotation(u[h])).ravel() for h in range(2)]), 0.999)
+    got = float(lib.calibrate_clip(kc, u, 0.999))
+    assert abs(got - want) <= 2e-7 * want
