@@ -8,19 +8,20 @@
 //
 // The inverse rotation is folded instead of applied per token: with
 // k_hat = k_hat' R_K^T, q . k_hat = (q R_K) . k_hat', and
-// sum_i p_i v_hat_i = (sum_i p_i v_hat'_i) R_V^T.  Three launches:
-//   rotate_q  q' = q U_K H P (times sm_scale*log2 e) once per (sequence, head),
-//             stored as fp16 hi/lo MFMA fragments
+// sum_i p_i v_hat_i = (sum_i p_i v_hat'_i) R_V^T.  Two launches:
 //   split     split-K over the pages: BF16 chunks with the plain q; INT2 page
-//             ranges on v_mfma_f32_16x16x32_f16 -- logits = codes x q' (the
-//             G query heads of a KV head share every code) and acc = (p s) x
-//             codes; online softmax in base 2
+//             ranges on v_mfma_f32_16x16x32_f16 -- each block first forms
+//             q' = q U_K H P (times sm_scale*log2 e) of its G query heads as
+//             fp16 hi/lo MFMA fragments while its first pages load, then
+//             logits = codes x q' (the G query heads of a KV head share every
+//             code) and acc = (p s) x codes; online softmax in base 2
 //   reduce    log-sum-exp merge, acc_rot R_V^T = ((acc_rot P) H) U_V^T, bf16 out
+// The extend and cascade kernels, whose blocks serve query heads of many rows,
+// read q' from records a separate rotate_q launch stores.
 #include <cmath>
 
 #include "common.h"
 #include "kernels.h"
-#include "kv_write_body.h"
 
 namespace oscar {
 
@@ -55,6 +56,8 @@ struct DecodeArgs {
   // extend (chunked prefill) reduce: every row (chunk token) has exactly one BF16 record,
   // index 0, and seq_lens holds the prefix length of the row's sequence
   int32_t ext;
+  // 1: the split kernel's INT2 items rotate their own queries (no stored records)
+  int32_t qrot_inline;
   // cascade decode: groups of sequences (batch entries cu_groups[g] .. cu_groups[g+1] - 1, at
   // most max_group of them) share their first group_pages[g] INT2 pages.  The first n_cas
   // split blocks read each shared range once for all members' query heads (n_cqt tiles of
@@ -106,138 +109,156 @@ __device__ int cascade_pages_of(const DecodeArgs& a, int b, int L) {
 }
 
 // ---------------------------------------------------------------------------
-// rotate_q: one 256-thread block per (sequence, KV head) for its G query
-// heads.  y = q U_K on v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32
-// sums): A rows = the G query heads (bf16 q straight from global memory), B =
-// U_K, whose columns each lane gathers as eight 16-bit loads (U_K's row-major
-// layout keeps a column strided); wave w makes output channels 32 w .. + 31.
-// Then FWHT, bit reversal and scale through LDS, and the fp16 hi/lo MFMA
-// fragments and offset sums of each head.
+// Query rotation of the G query heads of one (sequence, KV head), by one
+// 256-thread block, in three steps shared by the split kernel's INT2 items
+// (which rotate their own queries while their first page loads are in flight)
+// and by rotate_q_kernel (which stores records for the extend and cascade
+// kernels, whose blocks serve the query heads of many rows):
+//   qrot_load     q rows and U_K columns into registers (A: head n, input
+//                 channels 32 ks + 8 kg ..; B: each lane gathers eight 16-bit
+//                 entries of a U_K column, U_K being row-major)
+//   qrot_product  y = q U_K on v_mfma_f32_16x16x32_bf16 (exact bf16 products,
+//                 fp32 sums); wave w makes output channels 32 w .. + 31
+//   qrot_finish   per head, in one wave: Walsh-Hadamard transform (channel
+//                 2 l + e in lane l: stage 1 in registers, the others across
+//                 lanes), w_c = y_br(c) / sqrt(128) * sm_scale * log2(e), its
+//                 fp16 hi / lo limbs, and per group the offset sums of the
+//                 limbs and sum w (the accumulator starts of the logit MFMA)
 // ---------------------------------------------------------------------------
 constexpr int kSideThreads = 256;
 
-struct RotQSmem {
-  float qv[kMaxGqa][kHeadDim];
-  float y[kMaxGqa][kHeadDim];
-  uint16_t qh[kMaxGqa][kHeadDim], ql[kMaxGqa][kHeadDim];
+struct QRotIn {
+  bf16x8 bq[4];      // A: query head n, input channels 32 ks + 8 kg .. + 7 (zero beyond G)
+  bf16x8 bu[2][4];   // B: U_K[32 ks + 8 kg + d][16 nt + n], nt = 2 wave + t
 };
 
-// block for (sequence, KV head) bh = b H + h
-__device__ __forceinline__ void rotate_q_block(const DecodeArgs& a, RotQSmem& sm, int bh) {
-  auto& qv = sm.qv;
-  auto& y = sm.y;
-  auto& qh = sm.qh;
-  auto& ql = sm.ql;
-  const int b = bh / a.H, h = bh % a.H, G = a.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// LDS of the rotation (a view, so that the split kernel can place it in free ring slots)
+struct QRotLds {
+  float (*y)[kHeadDim];                 // [G][128]: q U_K, then w
+  uint16_t (*qh)[kHeadDim], (*ql)[kHeadDim];   // [G][128]: fp16 limbs of w
+  float (*negc)[2][2];                  // [G][group][limb]: -sum over the group of limb * base
+  float (*qsum)[2];                     // [G][group]: sum over the group of w
+};
+
+__device__ __forceinline__ void qrot_load(const DecodeArgs& a, int b, int h, QRotIn& in) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kg = lane >> 4, G = a.G;
+  const uint16_t* U = a.u_k + (size_t)h * kHeadDim * kHeadDim;
+  const uint16_t* qg = a.q + ((size_t)b * a.Hq + h * G) * kHeadDim;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 v = *reinterpret_cast<const uint4*>(qg + min(n, G - 1) * kHeadDim + 32 * ks + 8 * kg);
+    in.bq[ks] = __builtin_bit_cast(bf16x8, n < G ? v : make_uint4(0, 0, 0, 0));
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        in.bu[t][ks][d] = __builtin_bit_cast(__bf16, U[(32 * ks + 8 * kg + d) * kHeadDim + 16 * (2 * wave + t) + n]);
+}
+
+__device__ __forceinline__ void qrot_product(const DecodeArgs& a, const QRotIn& in, QRotLds v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(in.bq[ks], in.bu[t][ks], acc, 0, 0, 0);
+    // lane (n, kg) holds heads 4 kg .. 4 kg + 3 of channel 16 nt + n
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * kg + i < a.G) v.y[4 * kg + i][16 * (2 * wave + t) + n] = acc[i];
+  }
+}
+
+// after a block barrier that makes every y visible; wave w finishes heads w, w + 4
+__device__ __forceinline__ void qrot_finish(const DecodeArgs& a, QRotLds v) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int g = wave; g < a.G; g += 4) {
+    const float2 yy = *reinterpret_cast<const float2*>(&v.y[g][2 * lane]);
+    float y0 = yy.x + yy.y, y1 = yy.x - yy.y;   // stage 1: channels 2 l, 2 l + 1
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {           // stages 2 .. 64: lane bit m
+      const float sgn = (lane & m) ? -1.f : 1.f;   // upper partner: partner - own
+      y0 = fmaf(sgn, y0, __shfl_xor(y0, m));
+      y1 = fmaf(sgn, y1, __shfl_xor(y1, m));
+    }
+    *reinterpret_cast<float2*>(&v.y[g][2 * lane]) = make_float2(y0, y1);
+    wave_lds_sync();
+    float w[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = 2 * lane + e;
+      w[e] = v.y[g][bitrev7(c)] * 0.08838834764831845f * a.sl2e;
+      const uint32_t hb = f32_to_f16_bits(w[e]);
+      v.qh[g][c] = (uint16_t)hb;
+      v.ql[g][c] = (uint16_t)f32_to_f16_bits(w[e] - f16_bits_to_f32(hb));
+    }
+    *reinterpret_cast<float2*>(&v.y[g][2 * lane]) = make_float2(w[0], w[1]);   // after every lane's reads
+    wave_lds_sync();
+    const float base = (float)pair_base(pair_of_k(lane & 7));
+#pragma unroll
+    for (int gr = 0; gr < 2; ++gr) {   // lane l takes channel 64 gr + l
+      const int c = 64 * gr + lane;
+      const float nh = wave_sum_xor(-base * f16_bits_to_f32(v.qh[g][c]), 1, 32);
+      const float nl = wave_sum_xor(-base * f16_bits_to_f32(v.ql[g][c]), 1, 32);
+      const float qs = wave_sum_xor(v.y[g][c], 1, 32);
+      if (lane == 0) {
+        v.negc[g][gr][0] = nh;
+        v.negc[g][gr][1] = nl;
+        v.qsum[g][gr] = qs;
+      }
+    }
+  }
+}
+
+// The two fp16 values of register v of fragment (group gr, k-half kh, k-group c) of head g.
+__device__ __forceinline__ uint32_t qrot_frag_dword(const QRotLds& v, int g, int gr, int kh, int limb, int c, int vi) {
+  const int ch = 64 * gr + 16 * c + pair_k(4 * kh + vi);
+  const uint16_t* src = limb ? v.ql[g] : v.qh[g];
+  return (uint32_t)src[ch] | ((uint32_t)src[ch + 8] << 16);
+}
+
+struct RotQSmem {
+  float y[kMaxGqa][kHeadDim];
+  uint16_t qh[kMaxGqa][kHeadDim], ql[kMaxGqa][kHeadDim];
+  float negc[kMaxGqa][2][2], qsum[kMaxGqa][2];
+};
+
+// block for (sequence, KV head) bh = b H + h: the records of its G query heads
+__device__ __forceinline__ void rotate_q_block(const DecodeArgs& a, RotQSmem& sm, int bh) {
+  const int b = bh / a.H, h = bh % a.H, G = a.G;
+  const int tid = threadIdx.x;
   if (a.cas_eff && h == 0 && tid == 0)
     a.cas_eff[b] = a.n_groups > 0 ? cascade_pages_of(a, b, clamp_len(a.seq_lens[b], a.max_pages)) : 0;
-  {
-    const uint16_t* U = a.u_k + (size_t)h * kHeadDim * kHeadDim;
-    const uint16_t* qg = a.q + ((size_t)b * a.Hq + h * G) * kHeadDim;
-    bf16x8 bq[4];   // A: query head n, input channels 32 ks + 8 kg .. + 7 (zero beyond G)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 v = n < G ? *reinterpret_cast<const uint4*>(qg + n * kHeadDim + 32 * ks + 8 * kg)
-                            : make_uint4(0, 0, 0, 0);
-      bq[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-    bf16x8 bu[2][4];   // B: U_K[32 ks + 8 kg + d][16 nt + n], nt = 2 wave + t
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-          bu[t][ks][d] = __builtin_bit_cast(__bf16, U[(32 * ks + 8 * kg + d) * kHeadDim + 16 * (2 * wave + t) + n]);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[ks], bu[t][ks], acc, 0, 0, 0);
-      // lane (n, kg) holds heads 4 kg .. 4 kg + 3 of channel 16 nt + n
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * kg + i < G) y[4 * kg + i][16 * (2 * wave + t) + n] = acc[i];
-    }
-  }
-  __syncthreads();
-  // FWHT of every head, 64 butterflies per head and stage
-  for (int s = 1; s < kHeadDim; s <<= 1) {
-    for (int t = tid; t < G * 64; t += kSideThreads) {
-      const int g = t >> 6, c = t & 63;
-      const int lo = ((c & ~(s - 1)) << 1) | (c & (s - 1)), hi = lo | s;
-      const float x0 = y[g][lo], x1 = y[g][hi];
-      y[g][lo] = x0 + x1;
-      y[g][hi] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  // w_j = z_br(j) / sqrt(128) * sm_scale * log2(e), split into fp16 hi + lo
-  for (int e = tid; e < G * kHeadDim; e += kSideThreads) {
-    const int g = e >> 7, c = e & 127;
-    const float w = y[g][bitrev7(c)] * 0.08838834764831845f * a.sl2e;
-    const uint32_t hb = f32_to_f16_bits(w);
-    qv[g][c] = w;
-    qh[g][c] = (uint16_t)hb;
-    ql[g][c] = (uint16_t)f32_to_f16_bits(w - f16_bits_to_f32(hb));
-  }
-  __syncthreads();
+  const QRotLds v{sm.y, sm.qh, sm.ql, sm.negc, sm.qsum};
+  QRotIn in;
+  qrot_load(a, b, h, in);
+  qrot_product(a, in, v);
+  block_lds_barrier();
+  qrot_finish(a, v);
+  block_lds_barrier();
   for (int e = tid; e < G * kHeadDim; e += kSideThreads) {
     // dword e of head g: frag index (((gr*2 + kh)*2 + limb)*4 + c)*4 + v
     const int g = e >> 7, jj = e & 127;
-    const int v = jj & 3, c = (jj >> 2) & 3, limb = (jj >> 4) & 1, kh = (jj >> 5) & 1, gr = (jj >> 6) & 1;
-    const int ch = 64 * gr + 16 * c + pair_k(4 * kh + v);
-    const uint16_t* src = limb ? ql[g] : qh[g];
     QrotRecord* rec = a.qrot + (size_t)b * a.Hq + h * G + g;
-    (&rec->frag[0][0][0][0][0])[jj] = (uint32_t)src[ch] | ((uint32_t)src[ch + 8] << 16);
+    (&rec->frag[0][0][0][0][0])[jj] =
+        qrot_frag_dword(v, g, (jj >> 6) & 1, (jj >> 5) & 1, (jj >> 4) & 1, (jj >> 2) & 3, jj & 3);
   }
-  // offset sums, one wave per head: lane l takes channel 64 gr + l
-  for (int g = tid >> 6; g < G; g += kSideThreads / 64) {
+  if (tid < G * 6) {
+    const int g = tid / 6, k = tid % 6;
     QrotRecord* rec = a.qrot + (size_t)b * a.Hq + h * G + g;
-    const float base = (float)pair_base(pair_of_k(lane & 7));
-#pragma unroll
-    for (int gr = 0; gr < 2; ++gr) {
-      const int c = 64 * gr + lane;
-      const float nh = wave_sum_xor(-base * f16_bits_to_f32(qh[g][c]), 1, 32);
-      const float nl = wave_sum_xor(-base * f16_bits_to_f32(ql[g][c]), 1, 32);
-      const float qs = wave_sum_xor(qv[g][c], 1, 32);
-      if (lane == 0) {
-        rec->negc[gr][0] = nh;
-        rec->negc[gr][1] = nl;
-        rec->qsum[gr] = qs;
-      }
-    }
+    if (k < 4) rec->negc[k >> 1][k & 1] = sm.negc[g][k >> 1][k & 1];
+    else rec->qsum[k - 4] = sm.qsum[g][k - 4];
   }
 }
 
 __global__ __launch_bounds__(kSideThreads) void rotate_q_kernel(DecodeArgs a) {
   __shared__ RotQSmem sm;
   rotate_q_block(a, sm, blockIdx.x);
-}
-
-// First launch of a decode step: blocks [0, n_write) write the step's new tokens
-// (kv_write blocks over a (gx, gy, gz) grid, flattened x fastest), the rest rotate
-// the queries (one per (sequence, KV head)).  The two touch disjoint memory: the
-// writes go to the page pool, sink and ring; the rotation reads q and U_K and
-// writes the workspace's query records.
-union StepFrontSmem {
-  KvWriteSmem kw;
-  RotQSmem rq;
-};
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void step_front_kernel(
-    KvWriteArgs w, DecodeArgs d, int n_write, int gx, int gy) {
-  static_assert(kSideThreads == 256, "both halves run 256-thread blocks");
-  __shared__ StepFrontSmem sm;
-  const int bid = blockIdx.x;
-  if (bid < n_write) {
-    const int bx = bid % gx, rest = bid / gx;
-    kv_write_block(w, sm.kw, bx, gx, rest % gy, rest / gy);
-  } else {
-    rotate_q_block(d, sm.rq, bid - n_write);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -720,8 +741,8 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   static_assert(kIdRegs == 2, "page offsets in two registers");
   // Every prologue load is issued before any is used, from addresses that are always valid
   // (selects come after), so the block waits one memory latency before its first page DMA:
-  // the physical page ids of the wave's pages (lane l: page j = l + 64 k) and the q'
-  // fragments of column n (head 4 qd + hh, group gp, limb; zero beyond G).
+  // the physical page ids of the wave's pages (lane l: page j = l + 64 k), the q rows and
+  // the U_K columns of the block's query rotation.
   int32_t pid_raw[kIdRegs];
   {
     const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
@@ -731,46 +752,8 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
       pid_raw[k] = ptab[n_w > 0 ? page_of(min(j, n_w - 1)) : first];
     }
   }
-  uint4 qraw[NQ][2][2];
-  float craw[NQ], sraw[NQ];
-#pragma unroll
-  for (int qd = 0; qd < NQ; ++qd) {
-    const int head = 4 * qd + hh;
-    const QrotRecord* rec = a.qrot + ((size_t)b * a.Hq + h * G + (head < G ? head : 0));
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) qraw[qd][g][kh] = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][limb][r][0]);
-    craw[qd] = rec->negc[gp][limb];
-    sraw[qd] = rec->qsum[gp];
-  }
-  // consume them all here: no wait for them may land inside the page loop, where it would
-  // also wait for every page DMA in flight
-#pragma unroll
-  for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(pid_raw[k]));
-#pragma unroll
-  for (int qd = 0; qd < NQ; ++qd) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-        asm volatile("" : "+v"(qraw[qd][g][kh].x), "+v"(qraw[qd][g][kh].y), "+v"(qraw[qd][g][kh].z),
-                     "+v"(qraw[qd][g][kh].w));
-    asm volatile("" : "+v"(craw[qd]), "+v"(sraw[qd]));
-  }
   Int2Lane<NQ> ln;
   int2_lane_init(ln, lane, a.resc_thr);
-#pragma unroll
-  for (int qd = 0; qd < NQ; ++qd) {
-    const bool ok = 4 * qd + hh < G;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-        ln.qb[qd][g][kh] = half8_of(ok && g == gp ? qraw[qd][g][kh] : make_uint4(0, 0, 0, 0));
-    ln.cinit[qd] = ok ? craw[qd] : 0.f;
-    ln.qs[qd] = ok ? sraw[qd] : 0.f;
-  }
   // zs[g]: per-head correction of group g's channels, sum over tokens of p z_g minus the
   // fp16 bases the value MFMA adds (base * W_g), accumulated by v_dot2; m: running reference
   // maximum of the head's logits, which are formed relative to it (each of the two group
@@ -779,30 +762,128 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   int2_state_init(st);
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
   const uint32_t off16 = 16 * lane, off4 = 1024 + 4 * lane;   // this lane's bytes of a page block
-  // the wave's page blocks as offsets from `pages` in 256-byte units (page id x H x 5 +
-  // h x 5: a block is 5 units), held in VGPRs: lane l keeps page j = l + 64 k.  32 bits
-  // suffice while the pool is below 1 TiB.
-  uint32_t unit_reg[kIdRegs];
-  {
-    const uint32_t per_page = (uint32_t)a.H * (kBlockBytes / 256), head_units = (uint32_t)h * (kBlockBytes / 256);
-#pragma unroll
-    for (int k = 0; k < kIdRegs; ++k) unit_reg[k] = (uint32_t)pid_raw[k] * per_page + head_units;
-  }
-  auto issue = [&](int j, int slot) {   // 2 DMA instructions per page; slot = j % kRing
+  auto issue = [&](const uint32_t (&unit_reg)[kIdRegs], int j, int slot) {   // 2 DMA instructions per page
     const uint32_t u = __builtin_amdgcn_readlane(j < 64 ? unit_reg[0] : unit_reg[1], j & 63);   // wave-uniform
     const uint8_t* row = a.pages + ((uint64_t)u << 8);
     const uint32_t dst = (uint32_t)(uintptr_t)&sm.ring[wave][slot][0];
     dma_page_to_lds(row, off16, off4, dst, dst + 1024);
   };
+  // the wave's page blocks as offsets from `pages` in 256-byte units (page id x H x 5 +
+  // h x 5: a block is 5 units), held in VGPRs: lane l keeps page j = l + 64 k.  32 bits
+  // suffice while the pool is below 1 TiB.
+  auto unit_offsets = [&](uint32_t (&unit_reg)[kIdRegs]) {
+    const uint32_t per_page = (uint32_t)a.H * (kBlockBytes / 256), head_units = (uint32_t)h * (kBlockBytes / 256);
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) unit_reg[k] = (uint32_t)pid_raw[k] * per_page + head_units;
+  };
   // A pair without its second page reads that page's slot anyway and weights it with p = 0;
   // the slot then holds an earlier page of this wave or, before the ring's first turn, the
   // zeros written here, so the value scales it multiplies stay finite.
-  {
-    static_assert(kRing * 16 == 128, "one 16-byte store per lane covers the V parameters of every slot");
-    *reinterpret_cast<uint4*>(&sm.ring[wave][lane >> 3][kVParams + 16 * (lane & 7)]) = make_uint4(0, 0, 0, 0);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // before any page lands in these slots
+  static_assert(kRing == 8, "one 16-byte store per lane covers the V parameters of all eight slots");
+  auto zero_vparams = [&](bool lower, bool upper) {
+    if ((lane >= 32) ? upper : lower)
+      *reinterpret_cast<uint4*>(&sm.ring[wave][lane >> 3][kVParams + 16 * (lane & 7)]) = make_uint4(0, 0, 0, 0);
+    wave_lds_sync();   // before any page lands in these slots
+  };
+  uint32_t unit_reg[kIdRegs];
+  if (a.qrot_inline) {
+    // ---- the block rotates its own G queries while its first four pages per wave load:
+    // scratch in slots 4..7 of the rings of waves 0 (y), 1 (limbs) and 2 (offset sums),
+    // which are cleared and filled once every wave holds its fragments ----
+    QRotIn qin;
+    qrot_load(a, b, h, qin);
+    // consume them all here: no wait for them may land after the first page DMA, where it
+    // would also wait for every DMA in flight
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(pid_raw[k]));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      asm volatile("" : "+v"(qin.bq[ks]));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) asm volatile("" : "+v"(qin.bu[t][ks]));
+    }
+    unit_offsets(unit_reg);
+    zero_vparams(true, false);
+    for (int j = 0; j < 4 && j < n_w; ++j) issue(unit_reg, j, j);
+    static_assert(sizeof(float) * kMaxGqa * kHeadDim <= 4 * kBlockBytes &&
+                      2 * sizeof(uint16_t) * kMaxGqa * kHeadDim <= 4 * kBlockBytes,
+                  "rotation scratch fits four ring slots");
+    uint8_t* limbs = &sm.ring[1][4][0];
+    uint8_t* sums = &sm.ring[2][4][0];
+    const QRotLds qv{reinterpret_cast<float(*)[kHeadDim]>(&sm.ring[0][4][0]),
+                     reinterpret_cast<uint16_t(*)[kHeadDim]>(limbs),
+                     reinterpret_cast<uint16_t(*)[kHeadDim]>(limbs + sizeof(uint16_t) * kMaxGqa * kHeadDim),
+                     reinterpret_cast<float(*)[2][2]>(sums),
+                     reinterpret_cast<float(*)[2]>(sums + sizeof(float) * kMaxGqa * 4)};
+    qrot_product(a, qin, qv);
+    block_lds_barrier();
+    qrot_finish(a, qv);
+    block_lds_barrier();
+    // B fragments of column n: head 4 qd + hh, group gp, limb; zero on the other group
+    // and beyond G
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const int head = 4 * qd + hh;
+      const bool ok = head < G;
+      const int hs = ok ? head : 0;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const uint4 f = make_uint4(qrot_frag_dword(qv, hs, gp, kh, limb, r, 0), qrot_frag_dword(qv, hs, gp, kh, limb, r, 1),
+                                   qrot_frag_dword(qv, hs, gp, kh, limb, r, 2), qrot_frag_dword(qv, hs, gp, kh, limb, r, 3));
+#pragma unroll
+        for (int g = 0; g < 2; ++g) ln.qb[qd][g][kh] = half8_of(ok && g == gp ? f : make_uint4(0, 0, 0, 0));
+      }
+      ln.cinit[qd] = ok ? qv.negc[hs][gp][limb] : 0.f;
+      ln.qs[qd] = ok ? qv.qsum[hs][gp] : 0.f;
+    }
+    block_lds_barrier();   // every wave holds its fragments: slots 4..7 are free
+    zero_vparams(false, true);
+    for (int j = 4; j < kRing - 2 && j < n_w; ++j) issue(unit_reg, j, j);
+  } else {
+    // ---- the q' fragments of column n from the stored records (head 4 qd + hh, group gp,
+    // limb; zero beyond G), loaded with the page ids ----
+    uint4 qraw[NQ][2][2];
+    float craw[NQ], sraw[NQ];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const int head = 4 * qd + hh;
+      const QrotRecord* rec = a.qrot + ((size_t)b * a.Hq + h * G + (head < G ? head : 0));
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) qraw[qd][g][kh] = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][limb][r][0]);
+      craw[qd] = rec->negc[gp][limb];
+      sraw[qd] = rec->qsum[gp];
+    }
+    // consume them all here: no wait for them may land inside the page loop, where it would
+    // also wait for every page DMA in flight
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(pid_raw[k]));
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          asm volatile("" : "+v"(qraw[qd][g][kh].x), "+v"(qraw[qd][g][kh].y), "+v"(qraw[qd][g][kh].z),
+                       "+v"(qraw[qd][g][kh].w));
+      asm volatile("" : "+v"(craw[qd]), "+v"(sraw[qd]));
+    }
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const bool ok = 4 * qd + hh < G;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          ln.qb[qd][g][kh] = half8_of(ok && g == gp ? qraw[qd][g][kh] : make_uint4(0, 0, 0, 0));
+      ln.cinit[qd] = ok ? craw[qd] : 0.f;
+      ln.qs[qd] = ok ? sraw[qd] : 0.f;
+    }
+    unit_offsets(unit_reg);
+    zero_vparams(true, true);
+    for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(unit_reg, j, j);
   }
-  for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(j, j);
 
   // unrolled over one turn of the ring, so every slot offset is an immediate
   for (int j0 = 0; j0 < n_w; j0 += kRing)
@@ -813,8 +894,8 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     const int pp = page_of(j);
     const bool has1 = j + 1 < n_w;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of the slots being refilled
-    if (j + kRing - 2 < n_w) issue(j + kRing - 2, (2 * u + kRing - 2) % kRing);
-    if (j + kRing - 1 < n_w) issue(j + kRing - 1, (2 * u + kRing - 1) % kRing);
+    if (j + kRing - 2 < n_w) issue(unit_reg, j + kRing - 2, (2 * u + kRing - 2) % kRing);
+    if (j + kRing - 1 < n_w) issue(unit_reg, j + kRing - 1, (2 * u + kRing - 1) % kRing);
     if (j + kRing - 1 < n_w) {
       asm volatile("s_waitcnt vmcnt(12)" ::: "memory");   // pages j, j+1 landed: 2*(kRing-2) still in flight
     } else {
@@ -1561,8 +1642,15 @@ int launch_split_reduce(const DecodeArgs& a, int B, hipStream_t stream) {
 
 int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   if (L.batch == 0) return 0;
-  const DecodeArgs a = make_decode_args(L);
-  hipLaunchKernelGGL(rotate_q_kernel, dim3(L.batch * L.num_kv_heads), dim3(kSideThreads), 0, stream, a);
+  DecodeArgs a = make_decode_args(L);
+  // With few (sequence, KV head) pairs the GPU idles through a separate rotation launch,
+  // so the split kernel's INT2 items rotate their own queries while their first pages
+  // load (measured at 1 x 100K: 32.5 against 34.4 us per call); with many, that per-block
+  // prologue costs more than the launch (366.6 against 356.7 us at 28 x 100K).  Cascade
+  // blocks serve the query heads of many sequences and always read stored records.
+  a.qrot_inline = (long long)L.batch * L.num_kv_heads < kFewPairs && a.n_cas == 0;
+  if (!a.qrot_inline)
+    hipLaunchKernelGGL(rotate_q_kernel, dim3(L.batch * L.num_kv_heads), dim3(kSideThreads), 0, stream, a);
   return launch_split_reduce(a, L.batch, stream);
 }
 
@@ -1661,16 +1749,8 @@ int launch_extend(const ExtendLaunch& X, hipStream_t stream) {
 }
 
 int launch_decode_step(const KvWriteLaunch& W, const DecodeLaunch& D, hipStream_t stream) {
-  KvWriteArgs w{};
-  dim3 g;
-  const bool writes = kv_write_setup(W, device_cus(), w, g);
-  if (D.batch == 0) return writes ? launch_kv_write(W, stream) : 0;
-  if (!writes) return launch_decode(D, stream);
-  const DecodeArgs a = make_decode_args(D);
-  const int n_write = (int)(g.x * g.y * g.z);
-  hipLaunchKernelGGL(step_front_kernel, dim3(n_write + D.batch * D.num_kv_heads), dim3(256), 0, stream, w, a,
-                     n_write, (int)g.x, (int)g.y);
-  return launch_split_reduce(a, D.batch, stream);
+  if (launch_kv_write(W, stream)) return 1;
+  return launch_decode(D, stream);
 }
 
 }  // namespace oscar
