@@ -216,9 +216,8 @@ int oscar_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_
  * ([it] "Architettura del Sistema di Serving e Layout di Memoria": the new
  * token is written rotated and quantized, then attention reads the mixed
  * cache).  Every argument of both calls is checked before anything is
- * launched.  The token writes and the query rotation share the first launch
- * (they touch disjoint memory), which saves one dependent launch per layer;
- * nothing else differs.  num_tokens == 0 (or k and v both NULL) decodes only;
+ * launched, so a bad argument of either leaves the cache untouched; nothing
+ * else differs.  num_tokens == 0 (or k and v both NULL) decodes only;
  * batch == 0 writes only. */
 int oscar_decode_step(const oscar_shape_t* shape, const oscar_layer_t* layer,
                       const uint16_t* k, const uint16_t* v, const int32_t* seq_idx,
