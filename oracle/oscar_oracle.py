@@ -15,14 +15,19 @@ Pages cited (title, then the short tag used below):
 Readings taken where the pages are silent are listed with each function and
 collected in the repository's design notes.
 
-Page block format (one block per physical page id and KV head, 1280 bytes);
-the pages only say the cache is paged, so the layout is this library's own:
+Page block format (one block per physical page id and KV head); the pages
+only say the cache is paged, so the layout is this library's own.  With
+groups of 64 channels (2 groups per token) the block is 1280 bytes:
   [   0,  512)  K codes, token-major: slot t at byte 32*t; channel j (post-P
                 index) at byte j//4, bits 2*(j%4).
   [ 512, 1024)  V codes, channel-major: channel j is the little-endian uint32 at
                 512 + 4*j; slot t at bits 2*t.
   [1024, 1152)  K group parameters: slot t at 1024 + 8*t: fp16 s0, z0, s1, z1.
   [1152, 1280)  V group parameters: slot t at 1152 + 8*t: fp16 s0, z0, s1, z1.
+With one group of 128 channels per token (2.25 bits per element: the format
+behind [ru] paragraph 4's "2.28 bits per KV element") it is 1152 bytes: the
+same codes, then K parameters at 1024 + 4*t (fp16 s, z) and V parameters at
+1088 + 4*t.
 """
 from __future__ import annotations
 
@@ -31,7 +36,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = [
-    "D", "PAGE_BLOCK", "K_CODES", "V_CODES", "K_PARAMS", "V_PARAMS",
+    "D", "PAGE_BLOCK", "K_CODES", "V_CODES", "K_PARAMS", "V_PARAMS", "block_layout",
     "Shape", "Cache", "Layer", "bf16_to_f64", "f64_to_bf16", "fp16_rne",
     "hadamard", "bitrev7", "bitrev_permutation", "rotate", "rotation", "quantize",
     "pack_k_codes", "unpack_k_codes", "regions", "kv_write", "gather_sequence",
@@ -41,8 +46,19 @@ __all__ = [
 ]
 
 D = 128                      # head_dim
-PAGE_BLOCK = 1280
+PAGE_BLOCK = 1280            # block bytes with 64-channel groups
 K_CODES, V_CODES, K_PARAMS, V_PARAMS = 0, 512, 1024, 1152
+
+
+def block_layout(group: int):
+    """(block bytes, K params offset, V params offset, parameter bytes per slot)
+    of the page block for `group`-channel quantization groups (64 or 128);
+    the codes are at K_CODES and V_CODES for both."""
+    if group == 64:
+        return PAGE_BLOCK, K_PARAMS, V_PARAMS, 8
+    if group == 128:
+        return 1152, 1024, 1088, 4
+    raise ValueError("group must be 64 or 128")
 
 
 # ----------------------------------------------------------------------------
@@ -53,7 +69,8 @@ class Shape:
     """Cache geometry.  Sink 64 / recent 256 are the sizes [it] gives in
     "Architettura del Sistema di Serving e Layout di Memoria"; groups of 64
     channels with an fp16 scale and zero per token-group are this build's
-    quantizer format (the pages only say "INT2")."""
+    quantizer format (the pages only say "INT2"); group = 128 (one scale and
+    zero per token) is the 2.25-bit variant."""
     num_kv_heads: int
     num_q_heads: int
     head_dim: int = 128
@@ -69,7 +86,7 @@ class Shape:
 
 @dataclass
 class Cache:
-    pages: np.ndarray      # uint8 [num_pages][H_kv][1280]
+    pages: np.ndarray      # uint8 [num_pages][H_kv][block bytes: 1280, or 1152 with 128-channel groups]
     k_sink: np.ndarray     # uint16 bf16 [slots][H_kv][sink][128]
     v_sink: np.ndarray
     k_ring: np.ndarray     # uint16 bf16 [slots][H_kv][recent][128], row = pos % recent
@@ -87,7 +104,7 @@ class Layer:
 def new_cache(shape: Shape, num_pages: int, num_slots: int) -> Cache:
     H = shape.num_kv_heads
     return Cache(
-        pages=np.zeros((num_pages, H, PAGE_BLOCK), np.uint8),
+        pages=np.zeros((num_pages, H, block_layout(shape.group)[0]), np.uint8),
         k_sink=np.zeros((num_slots, H, shape.sink, D), np.uint16),
         v_sink=np.zeros((num_slots, H, shape.sink, D), np.uint16),
         k_ring=np.zeros((num_slots, H, shape.recent, D), np.uint16),
@@ -192,12 +209,13 @@ def rotation(u_bits: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# INT2 quantizer (64-channel groups, fp16 scale and fp16 zero per token-group)
+# INT2 quantizer (groups of 64 or 128 channels, fp16 scale and fp16 zero per token-group)
 # ----------------------------------------------------------------------------
 def quantize(w: np.ndarray, group: int = 64):
     """Asymmetric min/max INT2 of already-clipped rotated values.
 
-    For every 64-channel group: s = fp16(max - min) / 3, z = fp16(min), and
+    For every `group`-channel group (64: two per token, 128: one):
+    s = fp16((max - min) / 3), z = fp16(min), and
     code = clamp(rne((w - z) / s), 0, 3), using the fp16-rounded s and z so
     the stored parameters decode what was encoded.  s == 0 gives all-zero
     codes (the group decodes to z).
@@ -270,9 +288,10 @@ def kv_write(shape: Shape, cache: Cache, layer: Layer, k_bits, v_bits, seq_idx,
     S0, W, PG = shape.sink, shape.recent, shape.page_size
     L_after = np.asarray(seq_lens_after, np.int64)[seq_idx] if T else np.zeros(0, np.int64)
     info = {}
+    _, k_par, v_par, pb = block_layout(shape.group)
     for name, bits, R_bits, clip, sink_buf, ring_buf, codes_off, par_off in (
-            ("K", k_bits, layer.u_k, layer.clip_k, cache.k_sink, cache.k_ring, K_CODES, K_PARAMS),
-            ("V", v_bits, layer.u_v, layer.clip_v, cache.v_sink, cache.v_ring, V_CODES, V_PARAMS)):
+            ("K", k_bits, layer.u_k, layer.clip_k, cache.k_sink, cache.k_ring, K_CODES, k_par),
+            ("V", v_bits, layer.u_v, layer.clip_v, cache.v_sink, cache.v_ring, V_CODES, v_par)):
         if bits is None or T == 0:
             continue
         bits = np.asarray(bits, np.uint16)
@@ -294,10 +313,11 @@ def kv_write(shape: Shape, cache: Cache, layer: Layer, k_bits, v_bits, seq_idx,
         pid = np.asarray(page_table)[seq_idx[tq], pos[tq] // PG].astype(np.int64)
         slot = pos[tq] % PG
         hh = np.arange(H)
-        params = np.stack([s16[..., 0], z16[..., 0], s16[..., 1], z16[..., 1]], -1)
-        pbytes = params.view(np.uint16).astype("<u2").view(np.uint8).reshape(len(tq), H, 8)
+        # per group g: fp16 s_g then z_g
+        params = np.stack([s16, z16], -1).reshape(s16.shape[:-1] + (2 * s16.shape[-1],))
+        pbytes = np.ascontiguousarray(params).view(np.uint16).astype("<u2").view(np.uint8).reshape(len(tq), H, pb)
         cache.pages[pid[:, None, None], hh[None, :, None],
-                    (par_off + 8 * slot)[:, None, None] + np.arange(8)[None, None, :]] = pbytes
+                    (par_off + pb * slot)[:, None, None] + np.arange(pb)[None, None, :]] = pbytes
         if name == "K":
             kb = pack_k_codes(codes)                       # [Tq][H][32]
             cache.pages[pid[:, None, None], hh[None, :, None],
@@ -326,17 +346,18 @@ def kv_write(shape: Shape, cache: Cache, layer: Layer, k_bits, v_bits, seq_idx,
 def _dequant_rotated(shape: Shape, cache: Cache, h: int, pid, slot, which: str):
     """Rotated-basis reconstruction k_hat'_j = z_g + s_g * code_j (fp64) for the
     INT2 tokens at (pid, slot)."""
-    blk = cache.pages[pid, h]                              # [n][1280]
+    blk = cache.pages[pid, h]                              # [n][block bytes]
     n = len(pid)
+    _, k_par, v_par, pb = block_layout(shape.group)
     if which == "K":
         kb = blk[np.arange(n)[:, None], K_CODES + 32 * slot[:, None] + np.arange(32)[None, :]]
         codes = unpack_k_codes(kb)                         # [n][128]
-        par = blk[np.arange(n)[:, None], K_PARAMS + 8 * slot[:, None] + np.arange(8)[None, :]]
+        par = blk[np.arange(n)[:, None], k_par + pb * slot[:, None] + np.arange(pb)[None, :]]
     else:
         words = np.ascontiguousarray(blk[:, V_CODES:V_CODES + 512]).view("<u4")  # [n][128]
         codes = (words >> (2 * slot[:, None]).astype(np.uint32)) & 3
-        par = blk[np.arange(n)[:, None], V_PARAMS + 8 * slot[:, None] + np.arange(8)[None, :]]
-    par = np.ascontiguousarray(par).view("<f2").astype(np.float64)   # [n][4] s0 z0 s1 z1
+        par = blk[np.arange(n)[:, None], v_par + pb * slot[:, None] + np.arange(pb)[None, :]]
+    par = np.ascontiguousarray(par).view("<f2").astype(np.float64)   # [n][2 per group]: s_g, z_g
     g = np.arange(D) // shape.group
     s = par[:, 0::2][:, g]
     z = par[:, 1::2][:, g]
