@@ -67,13 +67,19 @@ def test_qwen3_8b_layer_100k_full_compare(gpu):
     del info
     q = synth.decode_queries(rng, 1, Hq)
     want = O.decode(shape, ref, layer, q, table, [L], SIG)
+    # the library-written cache is held to the oracle's decode of its own bytes (excused
+    # write near-ties may move an output by a code step times an attention weight)
+    gpu_cache = host_cache(dc)
+    want_gpu = want if np.array_equal(gpu_cache.pages, ref.pages) else O.decode(shape, gpu_cache, layer, q, table,
+                                                                              [L], SIG)
     ws = torch.empty(lib.decode_workspace_bytes(ls, 1, P), dtype=torch.uint8, device=gpu)
     res = {}
-    for name, cache in (("gpu-written", dc), ("oracle-written", device_cache(shape, ref, layer, gpu))):
+    for name, cache, want_c in (("gpu-written", dc, want_gpu), ("oracle-written", device_cache(shape, ref, layer, gpu),
+                                                                want)):
         out = torch.full((1, Hq, 128), float("nan"), dtype=torch.bfloat16, device=gpu)
         lib.decode_attn(ls, cache, to_dev_bf16(q, gpu), table_d, lens_d, out, ws, SIG)
         torch.cuda.synchronize()
-        res[name] = compare_outputs(from_dev_bf16(out), want)
+        res[name] = compare_outputs(from_dev_bf16(out), want_c)
     print("decode", res, flush=True)
 
 

@@ -69,12 +69,20 @@ def run_scenario(device, shape, layer, law, lens, table, calls, rng, seed_q=0, c
     q_d = to_dev_bf16(q, device)
     lens_d = to_dev_i32(lens, device)
     results = {}
-    for name, cache in (("oracle-written", device_cache(shape, ref, layer, device)), ("gpu-written", dc)):
+    # Each decode is held to the oracle's decode of the same cache bytes: the library-written
+    # cache may differ from the oracle's by excused near-ties (a code one step away, an fp16
+    # scale one ulp away), which move an output by up to that step times the token's
+    # attention weight -- a write difference the write rule has already judged.
+    gpu_cache = host_cache(dc)
+    out_ref_gpu = out_ref if np.array_equal(gpu_cache.pages, ref.pages) else O.decode(
+        shape, gpu_cache, layer, q, table, lens, SIG)
+    for name, cache, want in (("oracle-written", device_cache(shape, ref, layer, device), out_ref),
+                              ("gpu-written", dc, out_ref_gpu)):
         out = torch.empty((B, shape.num_q_heads, 128), dtype=torch.bfloat16, device=device)
         out.fill_(float("nan"))
         lib.decode_attn(ls, cache, q_d, table_d, lens_d, out, ws, SIG)
         torch.cuda.synchronize()
-        results[name] = compare_outputs(from_dev_bf16(out), out_ref)
+        results[name] = compare_outputs(from_dev_bf16(out), want)
     return stats_all, results
 
 
