@@ -27,16 +27,22 @@
  *     on a 256-byte boundary.  A misaligned pointer is OSCAR_EINVAL.
  *   - Row-vector convention: a stored token is k' = k R.
  *
- * Page block format (one 1280-byte block per physical page id and KV head;
- * `pages` is [num_pages][num_kv_heads][1280]):
+ * Page block format (one block per physical page id and KV head; `pages` is
+ * [num_pages][num_kv_heads][B] with B = 1280 bytes for group == 64 and 1152
+ * for group == 128):
  *   [   0,  512) K codes, token-major: slot t at byte 32*t; post-rotation
  *                channel j at byte j/4, bits 2*(j%4).
  *   [ 512, 1024) V codes, channel-major: channel j is the little-endian uint32
  *                at 512 + 4*j; slot t at bits 2*t.
+ *   group == 64 (2.5 bits per element):
  *   [1024, 1152) K group parameters, slot t at 1024 + 8*t: fp16 s0, z0, s1, z1
  *   [1152, 1280) V group parameters, slot t at 1152 + 8*t: fp16 s0, z0, s1, z1
- * Group g covers post-rotation channels [64g, 64g+64); a code c decodes to
- * z_g + s_g * c.
+ *   group == 128 (2.25 bits per element, the format of the Russian page's
+ *   paragraph 4 "2.28 bits per KV element"):
+ *   [1024, 1088) K parameters, slot t at 1024 + 4*t: fp16 s, z
+ *   [1088, 1152) V parameters, slot t at 1088 + 4*t: fp16 s, z
+ * Group g covers post-rotation channels [group*g, group*(g+1)); a code c
+ * decodes to z_g + s_g * c.
  */
 #ifndef OSCAR_H
 #define OSCAR_H
@@ -58,9 +64,10 @@ extern "C" {
 
 /* Cache geometry.  The Italian page's section "Architettura del Sistema di
  * Serving e Layout di Memoria" gives 64 BF16 sink tokens and 256 BF16 recent
- * tokens (also configurable server flags on that page); group = 64 channels
- * with an fp16 scale and zero per token-group is this library's INT2 format.
- * Supported: head_dim == 128, page_size == 16, group == 64,
+ * tokens (also configurable server flags on that page); group = 64 (or 128)
+ * channels with an fp16 scale and zero per token-group is this library's INT2
+ * format.
+ * Supported: head_dim == 128, page_size == 16, group == 64 or 128,
  * 1 <= num_kv_heads, num_q_heads % num_kv_heads == 0,
  * 1 <= num_q_heads / num_kv_heads <= 8, 0 <= sink <= 1024 with
  * sink % 16 == 0, 1 <= recent <= 4096. */
@@ -76,7 +83,7 @@ typedef struct oscar_shape {
 
 /* One layer's cache and rotation.  Sequence "slot" b indexes the sink and ring
  * buffers; for decode, batch entry b uses slot b.
- *   pages          [num_pages][H_kv][1280] bytes (format above)
+ *   pages          [num_pages][H_kv][1280 or 1152] bytes (format above)
  *   k_sink, v_sink bf16 [num_slots][H_kv][sink][128]; row p holds position p
  *   k_ring, v_ring bf16 [num_slots][H_kv][recent][128]; row p % recent holds
  *                  position p while p is inside the recent window

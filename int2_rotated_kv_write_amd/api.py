@@ -15,7 +15,8 @@ import numpy as np
 from ._native import OscarLayer, OscarShape, load
 
 HEAD_DIM = 128
-PAGE_BLOCK = 1280
+PAGE_BLOCK = 1280          # page block bytes with 64-channel groups
+PAGE_BLOCK_G128 = 1152     # ... with one 128-channel group per token
 BF16_PAGE_ELEMS = 4096     # bf16 elements per (page, KV head) of the BF16 baseline cache
 
 
@@ -47,6 +48,10 @@ class CacheShape:
     def gqa(self) -> int:
         return self.num_q_heads // self.num_kv_heads
 
+    @property
+    def block_bytes(self) -> int:
+        return PAGE_BLOCK_G128 if self.group == 128 else PAGE_BLOCK
+
     def c(self) -> OscarShape:
         return OscarShape(self.num_kv_heads, self.num_q_heads, self.head_dim, self.page_size,
                           self.sink, self.recent, self.group)
@@ -55,7 +60,7 @@ class CacheShape:
 @dataclass
 class CacheBuffers:
     """One layer's device buffers (layouts in include/oscar.h)."""
-    pages: "torch.Tensor"      # uint8 [num_pages][H_kv][1280]
+    pages: "torch.Tensor"      # uint8 [num_pages][H_kv][1280, or 1152 with 128-channel groups]
     k_sink: "torch.Tensor"     # bfloat16 [slots][H_kv][sink][128]
     v_sink: "torch.Tensor"
     k_ring: "torch.Tensor"     # bfloat16 [slots][H_kv][recent][128]
@@ -81,7 +86,7 @@ def allocate_cache(shape: CacheShape, num_pages: int, num_slots: int, device,
     if u_v is None:
         u_v = z(H, HEAD_DIM, HEAD_DIM)
     return CacheBuffers(
-        pages=z(num_pages, H, PAGE_BLOCK, dt=torch.uint8),
+        pages=z(num_pages, H, shape.block_bytes, dt=torch.uint8),
         k_sink=z(num_slots, H, max(shape.sink, 1), HEAD_DIM),
         v_sink=z(num_slots, H, max(shape.sink, 1), HEAD_DIM),
         k_ring=z(num_slots, H, shape.recent, HEAD_DIM),
@@ -117,8 +122,8 @@ def _dev(t, dtype, name, shape=None):
 def _check_cache(shape: CacheShape, cache: CacheBuffers):
     import torch
     H = shape.num_kv_heads
-    if cache.pages.dim() != 3 or cache.pages.shape[1:] != (H, PAGE_BLOCK):
-        raise OscarError("pages must be [num_pages][H_kv][1280]")
+    if cache.pages.dim() != 3 or cache.pages.shape[1:] != (H, shape.block_bytes):
+        raise OscarError(f"pages must be [num_pages][H_kv][{shape.block_bytes}]")
     _dev(cache.pages, torch.uint8, "pages")
     for n in ("k_sink", "v_sink", "k_ring", "v_ring"):
         _dev(getattr(cache, n), torch.bfloat16, n)

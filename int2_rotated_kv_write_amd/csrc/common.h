@@ -8,11 +8,23 @@ namespace oscar {
 
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
-constexpr int kBlockBytes = 1280;   // one page block per (physical page, KV head)
+constexpr int kBlockBytes = 1280;   // one page block per (physical page, KV head), 64-channel groups
 constexpr int kKCodes = 0;          // K codes, token-major [16][32 B]
 constexpr int kVCodes = 512;        // V codes, channel-major [128] uint32, slot t at bits 2t
 constexpr int kKParams = 1024;      // [16] x {fp16 s0, z0, s1, z1}
 constexpr int kVParams = 1152;
+// One 128-channel group per token (2.25 bits per element): the same codes, then
+// [16] x {fp16 s, z} for K at 1024 and for V at 1088; 1152 bytes per block.
+constexpr int kBlockBytes128 = 1152;
+constexpr int kVParams128 = 1088;
+
+struct PageFormat {
+  int block_bytes, k_params, v_params, param_bytes;
+};
+__host__ __device__ constexpr PageFormat page_format(int group) {
+  return group == 128 ? PageFormat{kBlockBytes128, kKParams, kVParams128, 4}
+                      : PageFormat{kBlockBytes, kKParams, kVParams, 8};
+}
 constexpr int kMaxGqa = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

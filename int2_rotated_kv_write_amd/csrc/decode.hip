@@ -58,6 +58,8 @@ struct DecodeArgs {
   int32_t ext;
   // 1: the split kernel's INT2 items rotate their own queries (no stored records)
   int32_t qrot_inline;
+  // 1: one 128-channel quantization group per token (1152-byte page blocks)
+  int32_t one_group;
   // cascade decode: groups of sequences (batch entries cu_groups[g] .. cu_groups[g+1] - 1, at
   // most max_group of them) share their first group_pages[g] INT2 pages.  The first n_cas
   // split blocks read each shared range once for all members' query heads (n_cqt tiles of
@@ -508,7 +510,7 @@ struct Int2State {
 };
 
 // Lane constants (everything but the q' operands) and a zero state.
-template <int NQ>
+template <int NQ, bool kOne>
 __device__ __forceinline__ void int2_lane_init(Int2Lane<NQ>& L, int lane, float tau) {
   const int n = lane & 15;
   L.r = lane >> 4;
@@ -517,8 +519,10 @@ __device__ __forceinline__ void int2_lane_init(Int2Lane<NQ>& L, int lane, float 
   L.limb = L.a4 >> 1;
   const int t0 = 4 * L.r + 2 * L.limb;
   L.off_kc = kKCodes + 32 * n + 4 * L.r;        // token n: code word r of group 0 (+16: group 1)
-  L.off_kp = kKParams + 8 * t0 + 4 * L.gp;      // (s, z) of group gp, tokens t0 and t0 + 1
-  L.off_vp = kVParams + 8 * (4 * L.r + L.a4);   // (s0, z0, s1, z1) of token 4r + a4
+  // (s, z) of group gp, tokens t0 and t0 + 1; (s0, z0, s1, z1) of token 4r + a4 -- with one
+  // 128-channel group per token, its single (s, z) serves both groups
+  L.off_kp = kOne ? kKParams + 4 * t0 : kKParams + 8 * t0 + 4 * L.gp;
+  L.off_vp = kOne ? kVParams128 + 4 * (4 * L.r + L.a4) : kVParams + 8 * (4 * L.r + L.a4);
   L.off_vw = kVCodes + 4 * n;                   // value code word of channel 16t + n at + 64t
   L.perm_sel = (uint32_t)L.r | (0x0Cu << 8) | ((4u + L.r) << 16) | (0x0Cu << 24);
   // the value B operand's dword a4 carries fp16 base 64 (a4 even) or 16 (odd) on both
@@ -548,7 +552,7 @@ __device__ __forceinline__ void int2_state_init(Int2State<NQ>& st) {
 // online softmax and value accumulation for the lane's quads.  has1: page pp + 1 exists
 // (otherwise its block holds stale bytes and is weighted 0); i_hi: first position past the
 // INT2 tokens; first: the pair starts the item (forces the first rescale).
-template <int NQ>
+template <int NQ, bool kOne>
 __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>& L, const uint8_t* blk0,
                                           const uint8_t* blk1, bool has1, int pp, int i_hi, bool first) {
   struct PageRegs {
@@ -563,10 +567,14 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
     cur[k].kc[0] = *reinterpret_cast<const uint32_t*>(blk + L.off_kc);
     cur[k].kc[1] = *reinterpret_cast<const uint32_t*>(blk + L.off_kc + 16);
     cur[k].kp[0] = *reinterpret_cast<const uint32_t*>(blk + L.off_kp);
-    cur[k].kp[1] = *reinterpret_cast<const uint32_t*>(blk + L.off_kp + 8);
-    const uint2 v2 = *reinterpret_cast<const uint2*>(blk + L.off_vp);
-    cur[k].vp[0] = v2.x;
-    cur[k].vp[1] = v2.y;
+    cur[k].kp[1] = *reinterpret_cast<const uint32_t*>(blk + L.off_kp + (kOne ? 4 : 8));
+    if constexpr (kOne) {
+      cur[k].vp[0] = cur[k].vp[1] = *reinterpret_cast<const uint32_t*>(blk + L.off_vp);
+    } else {
+      const uint2 v2 = *reinterpret_cast<const uint2*>(blk + L.off_vp);
+      cur[k].vp[0] = v2.x;
+      cur[k].vp[1] = v2.y;
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) cur[k].vw[t] = *reinterpret_cast<const uint32_t*>(blk + L.off_vw + 64 * t);
   }
@@ -723,7 +731,7 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
 //   words of channel 16t + n, byte r of each page.  The base offsets are
 //   summed by one more MFMA per group against constant bases; the zero-point
 //   term sum p z_g is a per-head scalar.
-template <int G>
+template <int G, bool kOne>
 __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int first, int end, int i_hi,
                           SplitSmem& sm) {
   constexpr int NQ = (G + 3) / 4;
@@ -753,7 +761,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     }
   }
   Int2Lane<NQ> ln;
-  int2_lane_init(ln, lane, a.resc_thr);
+  int2_lane_init<NQ, kOne>(ln, lane, a.resc_thr);
   // zs[g]: per-head correction of group g's channels, sum over tokens of p z_g minus the
   // fp16 bases the value MFMA adds (base * W_g), accumulated by v_dot2; m: running reference
   // maximum of the head's logits, which are formed relative to it (each of the two group
@@ -761,18 +769,21 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   Int2State<NQ> st;
   int2_state_init(st);
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
-  const uint32_t off16 = 16 * lane, off4 = 1024 + 4 * lane;   // this lane's bytes of a page block
+  // this lane's bytes of a page block: 16 at 16 lane, then 4 at 1024 + 4 lane (a 1152-byte
+  // block's last 128 bytes are read twice, the copy landing past it in the 1280-byte slot)
+  const uint32_t off16 = 16 * lane, off4 = 1024 + 4 * (kOne ? (lane & 31) : lane);
   auto issue = [&](const uint32_t (&unit_reg)[kIdRegs], int j, int slot) {   // 2 DMA instructions per page
     const uint32_t u = __builtin_amdgcn_readlane(j < 64 ? unit_reg[0] : unit_reg[1], j & 63);   // wave-uniform
-    const uint8_t* row = a.pages + ((uint64_t)u << 8);
+    const uint8_t* row = a.pages + ((uint64_t)u << 7);
     const uint32_t dst = (uint32_t)(uintptr_t)&sm.ring[wave][slot][0];
     dma_page_to_lds(row, off16, off4, dst, dst + 1024);
   };
-  // the wave's page blocks as offsets from `pages` in 256-byte units (page id x H x 5 +
-  // h x 5: a block is 5 units), held in VGPRs: lane l keeps page j = l + 64 k.  32 bits
-  // suffice while the pool is below 1 TiB.
+  // the wave's page blocks as offsets from `pages` in 128-byte units (page id x H x 10 +
+  // h x 10: a block is 10 units, 9 with one 128-channel group), held in VGPRs: lane l
+  // keeps page j = l + 64 k.  32 bits suffice while the pool is below 512 GiB.
+  constexpr uint32_t kUnits = (kOne ? kBlockBytes128 : kBlockBytes) / 128;
   auto unit_offsets = [&](uint32_t (&unit_reg)[kIdRegs]) {
-    const uint32_t per_page = (uint32_t)a.H * (kBlockBytes / 256), head_units = (uint32_t)h * (kBlockBytes / 256);
+    const uint32_t per_page = (uint32_t)a.H * kUnits, head_units = (uint32_t)h * kUnits;
 #pragma unroll
     for (int k = 0; k < kIdRegs; ++k) unit_reg[k] = (uint32_t)pid_raw[k] * per_page + head_units;
   };
@@ -782,7 +793,8 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   static_assert(kRing == 8, "one 16-byte store per lane covers the V parameters of all eight slots");
   auto zero_vparams = [&](bool lower, bool upper) {
     if ((lane >= 32) ? upper : lower)
-      *reinterpret_cast<uint4*>(&sm.ring[wave][lane >> 3][kVParams + 16 * (lane & 7)]) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sm.ring[wave][lane >> 3][(kOne ? kVParams128 : kVParams) + 16 * (lane & 7)]) =
+          make_uint4(0, 0, 0, 0);
     wave_lds_sync();   // before any page lands in these slots
   };
   uint32_t unit_reg[kIdRegs];
@@ -901,7 +913,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    int2_pair<NQ>(st, ln, &sm.ring[wave][2 * u][0], &sm.ring[wave][2 * u + 1][0], has1, pp, i_hi, j == 0);
+    int2_pair<NQ, kOne>(st, ln, &sm.ring[wave][2 * u][0], &sm.ring[wave][2 * u + 1][0], has1, pp, i_hi, j == 0);
   }
 
   // ---- finish the wave: its result goes to its own ring (all of its page loads have landed) ----
@@ -958,7 +970,7 @@ __device__ __forceinline__ void mq_wait_own_pair(bool all_issued) {
   }
 }
 
-template <int G, int NQ, int R>
+template <int G, int NQ, int R, bool kOne>
 __device__ void mq_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, int first, int np, int i_hi,
                               int t0, int n_e, int e_block, int rec, uint8_t (*ring)[kBlockBytes]) {
   static_assert(R % 4 == 0 && R * 8 <= 256, "whole rounds of the four waves; one thread per V-parameter line");
@@ -967,14 +979,15 @@ __device__ void mq_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, i
   const int n = lane & 15, r = lane >> 4, hh = n >> 2;
   const int e_wave = e_block + 4 * NQ * wave;
   Int2Lane<NQ> ln;
-  int2_lane_init(ln, lane, a.resc_thr);
-  // the block offsets (256-byte units) of the pages this wave loads, j = wave + 4 m: lane l
+  int2_lane_init<NQ, kOne>(ln, lane, a.resc_thr);
+  // the block offsets (128-byte units) of the pages this wave loads, j = wave + 4 m: lane l
   // holds m = l + 64 k
   constexpr int kIdRegs = kMaxPagesPerSplit / 4 / 64;
   static_assert(kIdRegs == 2, "page offsets in two registers");
   uint32_t unit_reg[kIdRegs];
   {
-    const uint32_t per_page = (uint32_t)a.H * (kBlockBytes / 256), head_units = (uint32_t)h * (kBlockBytes / 256);
+    constexpr uint32_t kUnits = (kOne ? kBlockBytes128 : kBlockBytes) / 128;
+    const uint32_t per_page = (uint32_t)a.H * kUnits, head_units = (uint32_t)h * kUnits;
 #pragma unroll
     for (int k = 0; k < kIdRegs; ++k)
       unit_reg[k] = (uint32_t)ptab[first + min(wave + 4 * (lane + 64 * k), np - 1)] * per_page + head_units;
@@ -1018,14 +1031,15 @@ __device__ void mq_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, i
     if ((j & 3) != wave) return;
     const int m = j >> 2;
     const uint32_t u = __builtin_amdgcn_readlane(m < 64 ? unit_reg[0] : unit_reg[1], m & 63);
-    const uint8_t* blk = a.pages + ((uint64_t)u << 8);
+    const uint8_t* blk = a.pages + ((uint64_t)u << 7);
     const uint32_t dst = (uint32_t)(uintptr_t)&ring[j % R][0];
-    dma_page_to_lds(blk, 16 * lane, 1024 + 4 * lane, dst, dst + 1024);
+    dma_page_to_lds(blk, 16 * lane, 1024 + 4 * (kOne ? (lane & 31) : lane), dst, dst + 1024);
   };
   // the V parameters of every slot start at zero (a missing second page of the last pair is
   // read anyway and weighted 0; its scales must be finite)
   if (threadIdx.x < R * 8)
-    *reinterpret_cast<uint4*>(&ring[threadIdx.x >> 3][kVParams + 16 * (threadIdx.x & 7)]) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&ring[threadIdx.x >> 3][(kOne ? kVParams128 : kVParams) + 16 * (threadIdx.x & 7)]) =
+        make_uint4(0, 0, 0, 0);
   block_lds_barrier();
   for (int j = 0; j < R - 2 && j < np; ++j) issue(j);
   for (int j = 0; j < np; j += 2) {
@@ -1033,7 +1047,7 @@ __device__ void mq_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, i
     block_lds_barrier();   // pages j, j + 1 visible to every wave; slots of pair j - 2 no longer read
     if (j + R - 2 < np) issue(j + R - 2);
     if (j + R - 1 < np) issue(j + R - 1);
-    int2_pair<NQ>(st, ln, &ring[j % R][0], &ring[(j + 1) % R][0], j + 1 < np, first + j, i_hi, j == 0);
+    int2_pair<NQ, kOne>(st, ln, &ring[j % R][0], &ring[(j + 1) % R][0], j + 1 < np, first + j, i_hi, j == 0);
   }
   // ---- one record per (row, query head) ----
 #pragma unroll
@@ -1059,7 +1073,7 @@ __device__ void mq_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, i
 
 // Cascade block w (< n_cas): shared range k of group g, KV head h, query tile qt, with the
 // pages of the group's first member's table row.
-template <int G>
+template <int G, bool kOne>
 __device__ void cascade_block(const DecodeArgs& a, int w, SplitSmem& sm) {
   constexpr int NQ = (G + 3) / 4;
   const int qt = w % a.n_cqt;
@@ -1074,19 +1088,19 @@ __device__ void cascade_block(const DecodeArgs& a, int w, SplitSmem& sm) {
   const int e_block = 16 * NQ * qt;
   if (first >= end || e_block >= members * G) return;   // block-uniform
   static_assert(sizeof(sm.ring) >= 16 * kBlockBytes, "a 16-slot ring inside the split kernel's LDS");
-  mq_int2_range<G, NQ, 16>(a, a.page_table + (size_t)m0 * a.max_pages, h, first, end - first,
+  mq_int2_range<G, NQ, 16, kOne>(a, a.page_table + (size_t)m0 * a.max_pages, h, first, end - first,
                            (a.sink / kPage + shared) * kPage, m0, members * G, e_block, a.n_bsplit + a.n_split + k,
                            reinterpret_cast<uint8_t(*)[kBlockBytes]>(&sm.ring[0][0][0]));
 }
 
-template <int G>
+template <int G, bool kOne>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void split_kernel(DecodeArgs a) {
   __shared__ SplitSmem sm;
   // 1D grid: every (sequence, KV head)'s INT2 ranges first, then all BF16 chunks, which are
   // short and fill the block slots the last INT2 ranges leave idle (measured 1.7% faster
   // than a (sequence, KV head)-major order at 28 x 100K)
   if ((int)blockIdx.x < a.n_cas) {   // cascade decode: shared prefix ranges come first
-    cascade_block<G>(a, blockIdx.x, sm);
+    cascade_block<G, kOne>(a, blockIdx.x, sm);
     return;
   }
   const int nbh = a.B * a.H, w = blockIdx.x - a.n_cas, n_int2 = nbh * a.n_split;
@@ -1104,7 +1118,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 
     const int first = a.sink / kPage + shared + split * a.P;
     const int end = min(first + a.P, (i_hi + kPage - 1) / kPage);
     if (i_hi <= a.sink || first >= end) return;
-    int2_item<G>(a, b, h, split, first, end, i_hi, sm);
+    int2_item<G, kOne>(a, b, h, split, first, end, i_hi, sm);
   }
 }
 
@@ -1341,7 +1355,7 @@ struct __attribute__((aligned(16))) MqSmem {
 
 // INT2 prefix pages of one range of one (sequence, KV head), read once per block for 16 query
 // heads of the sequence's chunk (query head e = chunk position * G + head in the group).
-template <int G>
+template <int G, bool kOne>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void ext_int2_kernel(ExtArgs e) {
   __shared__ MqSmem sm;
   const DecodeArgs& a = e.d;
@@ -1359,7 +1373,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   const int end = min(first + a.P, (i_hi + kPage - 1) / kPage);
   const int e_block = 16 * qt;
   if (i_hi <= a.sink || first >= end || e_block >= chunk * G) return;   // block-uniform
-  mq_int2_range<G, 1, kMqRing>(a, a.page_table + (size_t)b * a.max_pages, h, first, end - first, i_hi, t0, chunk * G,
+  mq_int2_range<G, 1, kMqRing, kOne>(a, a.page_table + (size_t)b * a.max_pages, h, first, end - first, i_hi, t0, chunk * G,
                                e_block, 1 + split, sm.ring);
 }
 
@@ -1495,7 +1509,11 @@ constexpr int reduce_group() {
 
 template <int G>
 void launch_split(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(split_kernel<G>, dim3(a.n_cas + (a.n_split + a.n_bsplit) * a.H * B), dim3(256), 0, stream, a);
+  const dim3 grid(a.n_cas + (a.n_split + a.n_bsplit) * a.H * B);
+  if (a.one_group)
+    hipLaunchKernelGGL((split_kernel<G, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((split_kernel<G, false>), grid, dim3(256), 0, stream, a);
   constexpr int GB = reduce_group<G>();
   if (GB > 1 && B * a.H < kFewPairs)
     hipLaunchKernelGGL((reduce_kernel<G, 1>), dim3(B * a.H * G), dim3(256), 0, stream, a);
@@ -1609,6 +1627,7 @@ DecodeArgs make_decode_args(const DecodeLaunch& L) {
   a.n_bsplit = L.plan.n_bsplit;
   a.n_total = L.plan.n_total;
   a.bchunk = L.plan.bf16_chunk;
+  a.one_group = L.group == 128;
   if (L.n_groups > 0 && L.plan.n_sh > 0) {   // cascade decode
     constexpr int kHeadsPerTile = 16;          // per NQ: a block's 4 waves x 4 NQ query heads
     const int nq = (a.G + 3) / 4;
@@ -1680,8 +1699,13 @@ namespace {
 template <int G>
 void launch_extend_g(const ExtArgs& e, hipStream_t stream) {
   const DecodeArgs& a = e.d;
-  if (a.n_split > 0)
-    hipLaunchKernelGGL(ext_int2_kernel<G>, dim3(e.n_seq * a.H * a.n_split * e.n_qt), dim3(256), 0, stream, e);
+  if (a.n_split > 0) {
+    const dim3 grid(e.n_seq * a.H * a.n_split * e.n_qt);
+    if (a.one_group)
+      hipLaunchKernelGGL((ext_int2_kernel<G, true>), grid, dim3(256), 0, stream, e);
+    else
+      hipLaunchKernelGGL((ext_int2_kernel<G, false>), grid, dim3(256), 0, stream, e);
+  }
   hipLaunchKernelGGL(ext_bf16_kernel<G>, dim3(e.n_seq * a.H * ((e.max_chunk + 3) / 4)), dim3(256), 0, stream, e);
   constexpr int GB = reduce_group<G>();
   hipLaunchKernelGGL((reduce_kernel<G, GB>), dim3(e.n_tok * a.H * (G / GB)), dim3(256), 0, stream, a);
@@ -1711,6 +1735,7 @@ int launch_extend(const ExtendLaunch& X, hipStream_t stream) {
   D.batch = X.num_tokens;
   D.sink = X.sink;
   D.recent = X.recent;
+  D.group = X.group;
   D.plan.pages_per_split = X.plan.pages_per_split;
   D.plan.n_split = X.plan.n_split;
   D.plan.n_bsplit = 1;

@@ -14,6 +14,7 @@ struct KvWriteLaunch {
   uint8_t* pages;
   const int32_t *seq_idx, *pos, *page_table, *seq_lens_after;
   int32_t num_tokens, num_kv_heads, max_pages, sink, recent;
+  int32_t group;   // 64 or 128 channels per quantization group
 };
 
 // Split-K plan of one decode call: the INT2 history of each (sequence, KV
@@ -48,6 +49,7 @@ struct DecodeLaunch {
   uint8_t* workspace;
   float sm_scale, clip_v;
   int32_t num_kv_heads, num_q_heads, max_pages, batch, sink, recent;
+  int32_t group;   // 64 or 128 channels per quantization group
   DecodePlan plan;
   // cascade decode only (n_groups == 0 otherwise)
   const int32_t *cu_groups, *group_pages;
@@ -94,6 +96,7 @@ struct ExtendLaunch {
   uint8_t* workspace;
   float sm_scale, clip_v;
   int32_t num_kv_heads, num_q_heads, max_pages, batch, num_tokens, max_chunk, sink, recent;
+  int32_t group;   // 64 or 128 channels per quantization group
   ExtendPlan plan;
 };
 

@@ -42,6 +42,9 @@ struct KvWriteArgs {
   const int32_t* lens_after;
   int32_t num_tokens, num_heads, max_pages, sink_len, recent, num_tiles;
   int32_t kind_of_z[2];
+  // page block format: 64-channel groups (1280 B, fp16 s0 z0 s1 z1 per slot) or one
+  // 128-channel group per token (1152 B, fp16 s z per slot)
+  int32_t one_group, block_bytes, params_off[2], param_bytes;
 };
 
 struct KvWriteSmem {
@@ -124,7 +127,8 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
   const float clip_s = a.clip[kind] * 11.313708498984761f;   // clip threshold before the 1/sqrt(128)
   uint16_t* sink_buf = a.sink[kind];
   uint16_t* ring_buf = a.ring[kind];
-  const int params_off = kind == 0 ? kKParams : kVParams;
+  const int params_off = a.params_off[kind];
+  const bool one_group = a.one_group;
 
 
   // The block walks tile groups bx, bx + gdx, ...: U^T is staged once per block.  Two tile
@@ -212,6 +216,10 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
       mn[g] = wave_min_xor(mn[g], 16, 32);
       mx[g] = wave_max_xor(mx[g], 16, 32);
     }
+    if (one_group) {   // one 128-channel group: both halves share its range
+      mn[0] = mn[1] = fminf(mn[0], mn[1]);
+      mx[0] = mx[1] = fmaxf(mx[0], mx[1]);
+    }
     uint32_t sbits[2], zbits[2];
     float sf[2], zf[2], inv[2];
 #pragma unroll
@@ -232,7 +240,7 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
     // whole aligned page written by this tile?
     const int b0 = __shfl(b, 0), p0 = __shfl(p, 0);
     const bool full_page = __all(is_int2 && b == b0 && p == p0 + n && (p0 & 15) == 0);
-    uint8_t* blk = a.pages + ((size_t)pid * a.num_heads + h) * kBlockBytes;   // used only if is_int2
+    uint8_t* blk = a.pages + ((size_t)pid * a.num_heads + h) * a.block_bytes;   // used only if is_int2
     const int slot = p & 15;
     if (kind == 0) {
       // K, token-major: post-rotation channel j = 64 r0 + 32 r1 + 16 q0 + 8 q1 + bitrev3(mt)
@@ -260,7 +268,7 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
       }
       wave_lds_sync();
       // every lane of the tile holds the same page: lane 0's id
-      const uint8_t* page_blk = a.pages + ((size_t)__shfl(pid, 0) * a.num_heads + h) * kBlockBytes;
+      const uint8_t* page_blk = a.pages + ((size_t)__shfl(pid, 0) * a.num_heads + h) * a.block_bytes;
       uint32_t words[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -292,7 +300,10 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
     }
     if (is_int2 && q == 0) {
       const uint32_t lo = sbits[0] | (zbits[0] << 16), hi = sbits[1] | (zbits[1] << 16);
-      *reinterpret_cast<uint2*>(blk + params_off + 8 * slot) = make_uint2(lo, hi);
+      if (one_group)
+        *reinterpret_cast<uint32_t*>(blk + params_off + 4 * slot) = lo;
+      else
+        *reinterpret_cast<uint2*>(blk + params_off + 8 * slot) = make_uint2(lo, hi);
     }
 
     // ---- bf16 copies (sink rows, recent ring), last: the sequence length they need was
@@ -349,6 +360,12 @@ inline bool kv_write_setup(const KvWriteLaunch& L, int cus, KvWriteArgs& a, dim3
   a.sink_len = L.sink;
   a.recent = L.recent;
   a.num_tiles = (L.num_tokens + 15) / 16;
+  const PageFormat f = page_format(L.group);
+  a.one_group = L.group == 128;
+  a.block_bytes = f.block_bytes;
+  a.params_off[0] = f.k_params;
+  a.params_off[1] = f.v_params;
+  a.param_bytes = f.param_bytes;
   const int n_groups = (a.num_tiles + 3) / 4;
   const int per_slice = std::max(1, (3 * cus + L.num_kv_heads * nz - 1) / (L.num_kv_heads * nz));
   grid = dim3(std::min(n_groups, per_slice), L.num_kv_heads, nz);

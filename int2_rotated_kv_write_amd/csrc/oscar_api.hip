@@ -21,7 +21,7 @@ int check_shape(const oscar_shape_t* s) {
   if (!s) return fail(OSCAR_EINVAL, "shape is NULL%s");
   if (s->head_dim != 128) return fail(OSCAR_EINVAL, "head_dim must be 128%s");
   if (s->page_size != 16) return fail(OSCAR_EINVAL, "page_size must be 16%s");
-  if (s->group != 64) return fail(OSCAR_EINVAL, "group must be 64%s");
+  if (s->group != 64 && s->group != 128) return fail(OSCAR_EINVAL, "group must be 64 or 128%s");
   if (s->num_kv_heads < 1) return fail(OSCAR_EINVAL, "num_kv_heads must be >= 1%s");
   if (s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads != 0)
     return fail(OSCAR_EINVAL, "num_q_heads must be a positive multiple of num_kv_heads%s");
@@ -97,6 +97,7 @@ int prepare_kv_write(const oscar_shape_t* shape, const oscar_layer_t* layer, con
   L.num_tokens = num_tokens;
   L.num_kv_heads = shape->num_kv_heads;
   L.max_pages = max_pages;
+  L.group = shape->group;
   L.sink = shape->sink;
   L.recent = shape->recent;
   return OSCAR_OK;
@@ -154,6 +155,7 @@ int prepare_decode(const oscar_shape_t* shape, const oscar_layer_t* layer, const
   L.batch = batch;
   L.sink = shape->sink;
   L.recent = shape->recent;
+  L.group = shape->group;
   L.plan = plan;
   return OSCAR_OK;
 }
@@ -378,6 +380,7 @@ int oscar_extend_attn(const oscar_shape_t* shape, const oscar_layer_t* layer, co
   L.max_chunk = max_chunk;
   L.sink = shape->sink;
   L.recent = shape->recent;
+  L.group = shape->group;
   L.plan = plan;
   if (oscar::launch_extend(L, stream)) return hip_fail("extend launch");
   return OSCAR_OK;

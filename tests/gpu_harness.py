@@ -94,19 +94,20 @@ def _near_code_boundary(t, slack=0.0):
     return near
 
 
-def _gpu_codes(pages, kind, pid, h, slot):
+def _gpu_codes(pages, kind, pid, h, slot, group=64):
     n = len(pid)
     hh = np.broadcast_to(h, (n,))
-    blk = pages[pid, hh]                                   # [n][1280]
+    blk = pages[pid, hh]                                   # [n][block bytes]
+    _, k_par, v_par, pb = O.block_layout(group)
     if kind == "K":
         kb = blk[np.arange(n)[:, None], O.K_CODES + 32 * slot[:, None] + np.arange(32)[None, :]]
         codes = O.unpack_k_codes(kb)
-        par = blk[np.arange(n)[:, None], O.K_PARAMS + 8 * slot[:, None] + np.arange(8)[None, :]]
+        par = blk[np.arange(n)[:, None], k_par + pb * slot[:, None] + np.arange(pb)[None, :]]
     else:
         words = np.ascontiguousarray(blk[:, O.V_CODES:O.V_CODES + 512]).view("<u4")
         codes = ((words >> (2 * slot[:, None]).astype(np.uint32)) & 3).astype(np.uint8)
-        par = blk[np.arange(n)[:, None], O.V_PARAMS + 8 * slot[:, None] + np.arange(8)[None, :]]
-    return codes, np.ascontiguousarray(par).view("<u2")     # [n][128], [n][4] s0 z0 s1 z1
+        par = blk[np.arange(n)[:, None], v_par + pb * slot[:, None] + np.arange(pb)[None, :]]
+    return codes, np.ascontiguousarray(par).view("<u2")     # [n][128], [n][2 per group]: s_g, z_g
 
 
 def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got_before: O.Cache):
@@ -117,6 +118,7 @@ def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got
     near-ties).  Returns counts of excused codes / parameters."""
     stats = dict(codes=0, codes_excused=0, codes_cond=0, params=0, params_excused=0, params_cond=0)
     H = shape.num_kv_heads
+    _, k_par, v_par, pb = O.block_layout(shape.group)
     assert np.array_equal(ref.k_sink, got.k_sink), "k_sink differs"
     assert np.array_equal(ref.v_sink, got.v_sink), "v_sink differs"
     assert np.array_equal(ref.k_ring, got.k_ring), "k_ring differs"
@@ -125,7 +127,7 @@ def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got
     for kind, d in info.items():
         pid, slot = d["page"], d["slot"]
         for h in range(H):
-            codes, par = _gpu_codes(got.pages, kind, pid, h, slot)
+            codes, par = _gpu_codes(got.pages, kind, pid, h, slot, shape.group)
             s_ref = d["s16"][:, h].view(np.uint16)              # [n][2]
             z_ref = d["z16"][:, h].view(np.uint16)
             s_got, z_got = par[:, 0::2], par[:, 1::2]
@@ -140,7 +142,7 @@ def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got
             for bad, what in ((bad_s, "scale"), (bad_z, "zero")):
                 if bad.any():
                     i, g = np.argwhere(bad)[0]
-                    seg = d["w"][i, h, 64 * g:64 * g + 64]
+                    seg = d["w"][i, h, shape.group * g:shape.group * (g + 1)]
                     raise AssertionError(
                         f"{kind} {what} mismatch h={h} at token {i} group {g} ({int(bad.sum())} total): "
                         f"s_pre={s_pre[i, g]!r} z_pre={z_pre[i, g]!r} ref s,z=0x{s_ref[i, g]:04x},0x{z_ref[i, g]:04x} "
@@ -150,7 +152,7 @@ def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got
             stats["params_excused"] += int((s_got != s_ref).sum() + (z_got != z_ref).sum())
             # reference codes, re-derived with the GPU's parameters where they differ
             w = d["w"][:, h]                                      # [n][128]
-            g = np.arange(128) // 64
+            g = np.arange(128) // shape.group
             sg = s_got.view(np.float16).astype(np.float64)[:, g]
             zg = z_got.view(np.float16).astype(np.float64)[:, g]
             t = np.where(sg == 0, 0.0, (w - zg) / np.where(sg == 0, 1.0, sg))
@@ -170,10 +172,10 @@ def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got
             if kind == "K":
                 cols = O.K_CODES + 32 * slot[:, None] + np.arange(32)[None, :]
                 touched[pid[:, None], hh[:, None], cols] = True
-                cols = O.K_PARAMS + 8 * slot[:, None] + np.arange(8)[None, :]
+                cols = k_par + pb * slot[:, None] + np.arange(pb)[None, :]
             else:
                 touched[pid[:, None], hh[:, None], O.V_CODES + np.arange(512)[None, :]] = True
-                cols = O.V_PARAMS + 8 * slot[:, None] + np.arange(8)[None, :]
+                cols = v_par + pb * slot[:, None] + np.arange(pb)[None, :]
             touched[pid[:, None], hh[:, None], cols] = True
     # V words: bits of slots not written by this call must be unchanged
     base = got_before.pages

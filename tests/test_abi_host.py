@@ -43,7 +43,7 @@ def good_shape(**kw):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(head_dim=64), dict(page_size=32), dict(group=128), dict(num_kv_heads=0),
+    dict(head_dim=64), dict(page_size=32), dict(group=32), dict(group=256), dict(num_kv_heads=0),
     dict(num_q_heads=30), dict(num_q_heads=8 * 9), dict(sink=10), dict(sink=2048),
     dict(recent=0), dict(recent=5000),
 ])
