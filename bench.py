@@ -19,6 +19,9 @@ Besides the headline line's fields, the JSON carries (unless --no-extras):
                     the shared reads save;
   kv_write_prefill  one kv_write of 100,000 prefill tokens x 8 KV heads;
   bf16_baseline     the all-BF16 paged decode at the headline shape;
+  concurrent_28x100k_group128  decode_attn at the headline shape and a 100K
+                    prefill kv_write in the 2.25-bit format (one 128-channel
+                    group per token);
   rotation_ablation attention-output error against BF16 of OSCAR,
                     Hadamard-only and naive INT2 rotations through the
                     library's kernels on two synthetic laws.
@@ -53,6 +56,10 @@ WORKLOADS = {
                                 table="contiguous", law="heavy"),
     "ragged_64x4k_128k": dict(batch=64, seq_len=(4096, 131072), q_heads=64, kv_heads=8, layers=1,
                               table="shared_prefix", law="outlier"),
+    # the headline shape in the 2.25-bit format (one 128-channel group per token), its 36
+    # layers cycled exactly as the headline's
+    "concurrent_28x100k_group128": dict(batch=28, seq_len=100_000, q_heads=32, kv_heads=8, layers=36,
+                                        table="permuted", law="heavy", group=128),
 }
 SHARED_PREFIX_TOKENS = 4096     # ragged workload: 25% of the sequences share their first 4,096 tokens
 SINK, RECENT = 64, 256
@@ -71,14 +78,15 @@ def bf16_tokens(L, sink=64, recent=256):
     return L if L <= sink else sink + (L - max(sink, L - recent))
 
 
-def decode_bytes(lens, H, Hq):
-    """Algorithmic HBM bytes of one decode_attn call: 80 B per INT2 token-head,
-    512 B per BF16 token-head, q and out, one page-table entry per INT2 page,
-    U_K and U_V."""
+def decode_bytes(lens, H, Hq, group=64):
+    """Algorithmic HBM bytes of one decode_attn call: 80 B per INT2 token-head
+    (72 B with one 128-channel group per token), 512 B per BF16 token-head, q
+    and out, one page-table entry per INT2 page, U_K and U_V."""
+    per_int2 = 72 if group == 128 else 80
     tot = 0
     for L in lens:
         ni = int2_tokens(int(L))
-        tot += H * (ni * 80 + bf16_tokens(int(L)) * 512)
+        tot += H * (ni * per_int2 + bf16_tokens(int(L)) * 512)
         tot += 4 * (math.ceil((64 + ni) / 16) - 4)
     tot += len(lens) * Hq * 128 * 2 * 2
     tot += 2 * H * 128 * 128 * 2
@@ -206,7 +214,7 @@ def build_workload(name, rng, gen, dev, n_fill_minus=0):
     else:
         lens = np.full(B, wl["seq_len"], np.int32)
     max_pages = int(math.ceil(lens.max() / 16))
-    shape = lib.CacheShape(H, Hq)
+    shape = lib.CacheShape(H, Hq, group=wl.get("group", 64))
     law = synth.heavy_tail_law(rng, H) if wl["law"] == "heavy" else synth.outlier_law(rng, H)
 
     # ---- offline calibration (host, native library), one set replicated per layer ----
@@ -376,6 +384,49 @@ def naive_basis():
     br = [int(format(i, "07b")[::-1], 2) for i in range(128)]
     return h[br, :] / math.sqrt(128)
 
+
+
+def bench_group128(rng, gen, dev):
+    """decode_attn at 28 x 100K in the 2.25-bit format (one fp16 scale and zero per
+    token and head), 36 layers' caches cycled as in the headline, and one kv_write
+    of 100,000 prefill tokens x 8 KV heads in that format."""
+    import torch
+
+    import int2_rotated_kv_write_amd as lib
+    import synth
+    from synth.device import sample_kv_device, sample_queries_device
+    name = "concurrent_28x100k_group128"
+    W = build_workload(name, rng, gen, dev)
+    q = sample_queries_device(W.B, W.Hq, gen, dev)
+    lens_d = torch.from_numpy(W.lens.astype(np.int32)).to(dev)
+    out = torch.empty((W.B, W.Hq, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.decode_workspace_bytes(W.shape, W.B, W.max_pages), dtype=torch.uint8, device=dev)
+    calls = [lib.prepare_decode_attn(W.shape, c, q, W.table_d, lens_d, out, ws, SIG) for c in W.caches]
+    mean, med = event_us(calls, 3 * len(calls))   # as the headline: 3 passes over the layers
+    nbytes = decode_bytes(W.lens, W.H, W.Hq, group=128)
+    gbs = nbytes / (mean * 1e-6) / 1e9
+    u_k, u_v, ck, cv = W.caches[0].u_k, W.caches[0].u_v, W.caches[0].clip_k, W.caches[0].clip_v
+    W.caches = None
+    torch.cuda.empty_cache()
+    n_pre = PREFILL_TOKENS
+    pre_pages = math.ceil(n_pre / 16)
+    pre_cache = lib.allocate_cache(W.shape, pre_pages, 1, dev, u_k=u_k, u_v=u_v, clip_k=ck, clip_v=cv)
+    pre_k = sample_kv_device(W.law, n_pre, gen, dev)
+    pre_v = sample_kv_device(W.law, n_pre, gen, dev)
+    pre_table = torch.arange(pre_pages, dtype=torch.int32, device=dev).view(1, pre_pages)
+    pre_write = lib.prepare_kv_write(W.shape, pre_cache, pre_k, pre_v,
+                                     torch.zeros(n_pre, dtype=torch.int32, device=dev),
+                                     torch.arange(n_pre, dtype=torch.int32, device=dev), pre_table,
+                                     torch.tensor([n_pre], dtype=torch.int32, device=dev))
+    w_mean, _ = event_us([pre_write], 10)
+    w_bytes = prefill_write_bytes(n_pre, W.H) - W.H * max(0, n_pre - SINK) * 8
+    log(f"{name}: decode_attn {mean:.1f} us ({gbs:.0f} GB/s), kv_write prefill {w_mean:.1f} us")
+    return {"workload": name, "batch": W.B, "seq_len": int(W.lens[0]), "num_q_heads": W.Hq, "num_kv_heads": W.H,
+            "group": 128, "bits_per_element": 2.25, "layers_cycled": W.NL,
+            "decode_attn": {"us": mean, "us_median": med, "bytes_per_launch": nbytes, "achieved_gbs": gbs,
+                            "frac": gbs / PEAK_HBM_GBS},
+            "kv_write_prefill": {"tokens": n_pre, "us": w_mean, "bytes": w_bytes,
+                                 "achieved_gbs": w_bytes / (w_mean * 1e-6) / 1e9}}
 
 def bench_ablation(rng, gen, dev):
     """Attention-output error against BF16 attention of three rotations, all through
@@ -627,6 +678,8 @@ def main():
         extras["single_1x100k"] = bench_single(rng, gen, dev)
         torch.cuda.empty_cache()
         extras["ragged_64x4k_128k"] = bench_ragged(rng, gen, dev)
+        torch.cuda.empty_cache()
+        extras["concurrent_28x100k_group128"] = bench_group128(rng, gen, dev)
         torch.cuda.empty_cache()
         extras["rotation_ablation"] = bench_ablation(rng, gen, dev)
         torch.cuda.empty_cache()
