@@ -38,13 +38,17 @@ def _head_layer(layer: O.Layer, h: int) -> O.Layer:
     return O.Layer(layer.u_k[h:h + 1], layer.u_v[h:h + 1], layer.clip_k, layer.clip_v)
 
 
-def test_qwen3_8b_layer_100k_full_compare(gpu):
+@pytest.mark.parametrize("law_name", ["heavy", "outlier"])
+def test_qwen3_8b_layer_100k_full_compare(gpu, law_name):
+    """Every byte a 100,000-token x 8-head kv_write stores, then decode over both
+    caches: with the heavy-tailed law of the single-layer decode workload and
+    with the outlier law of the 100K prefill write workload."""
     import torch
     import int2_rotated_kv_write_amd as lib
     rng = np.random.default_rng(0)
     H, Hq, L = 8, 32, 100_000
     shape = O.Shape(num_kv_heads=H, num_q_heads=Hq)
-    law = synth.heavy_tail_law(rng, H)
+    law = synth.heavy_tail_law(rng, H) if law_name == "heavy" else synth.outlier_law(rng, H)
     layer = _layer(rng, law, Hq // H)
     P = math.ceil(L / 16)
     table = synth.contiguous_page_table(1, P)
