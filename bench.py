@@ -102,17 +102,20 @@ def bf16_decode_bytes(lens, H, Hq):
     return tot + len(lens) * Hq * 128 * 2 * 2
 
 
-def write_bytes(n_tokens, H):
+def write_bytes(n_tokens, H, group=64):
     """kv_write of n decode tokens (K and V): read 2x256 B per token-head,
-    write 80 B INT2 + 2x256 B ring copy per token-head, U_K and U_V."""
-    return n_tokens * H * (512 + 80 + 512) + 2 * H * 128 * 128 * 2
+    write 80 B INT2 (72 B with 128-channel groups) + 2x256 B ring copy per
+    token-head, U_K and U_V."""
+    return n_tokens * H * (512 + (72 if group == 128 else 80) + 512) + 2 * H * 128 * 128 * 2
 
 
-def prefill_write_bytes(n_tokens, H, sink=64):
+def prefill_write_bytes(n_tokens, H, sink=64, group=64):
     """kv_write of positions [0, n) of one sequence (K and V): read 2x256 B
-    per token-head, write 80 B INT2 per token-head at pos >= sink and 2x256 B
-    BF16 per sink or recent token-head, U_K and U_V."""
-    return (H * (n_tokens * 512 + max(0, n_tokens - sink) * 80 + bf16_tokens(n_tokens) * 512)
+    per token-head, write 80 B INT2 (72 B with 128-channel groups) per
+    token-head at pos >= sink and 2x256 B BF16 per sink or recent token-head,
+    U_K and U_V."""
+    per_int2 = 72 if group == 128 else 80
+    return (H * (n_tokens * 512 + max(0, n_tokens - sink) * per_int2 + bf16_tokens(n_tokens) * 512)
             + 2 * H * 128 * 128 * 2)
 
 
@@ -419,7 +422,7 @@ def bench_group128(rng, gen, dev):
                                      torch.arange(n_pre, dtype=torch.int32, device=dev), pre_table,
                                      torch.tensor([n_pre], dtype=torch.int32, device=dev))
     w_mean, _ = event_us([pre_write], 10)
-    w_bytes = prefill_write_bytes(n_pre, W.H) - W.H * max(0, n_pre - SINK) * 8
+    w_bytes = prefill_write_bytes(n_pre, W.H, group=128)
     log(f"{name}: decode_attn {mean:.1f} us ({gbs:.0f} GB/s), kv_write prefill {w_mean:.1f} us")
     return {"workload": name, "batch": W.B, "seq_len": int(W.lens[0]), "num_q_heads": W.Hq, "num_kv_heads": W.H,
             "group": 128, "bits_per_element": 2.25, "layers_cycled": W.NL,
@@ -588,8 +591,9 @@ def main():
 
     ms_per_step = 1e3 * elapsed / args.steps
     tok_s = B * args.steps / elapsed
-    dbytes = decode_bytes(lens, H, Hq)
-    wbytes = write_bytes(B, H)
+    group = wl.get("group", 64)
+    dbytes = decode_bytes(lens, H, Hq, group)
+    wbytes = write_bytes(B, H, group)
     step_bytes = NL * (dbytes + wbytes)
     dec_avg_ms = statistics.mean(dec_ms)
     achieved = dbytes / (dec_avg_ms * 1e-3) / 1e9
@@ -624,7 +628,7 @@ def main():
         e1.record()
     torch.cuda.synchronize()
     pre_us = 1e3 * statistics.mean(e0.elapsed_time(e1) for e0, e1 in pev)
-    pre_bytes = prefill_write_bytes(n_pre, H)
+    pre_bytes = prefill_write_bytes(n_pre, H, group=group)
     pre_gbs = pre_bytes / (pre_us * 1e-6) / 1e9
     log(f"kv_write prefill of {n_pre} tokens x {H} heads: {pre_us:.1f} us, {pre_gbs:.0f} GB/s")
     del pre_cache, pre_k, pre_v
