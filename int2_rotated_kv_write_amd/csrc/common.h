@@ -95,6 +95,24 @@ struct PairConsts {
   }
 };
 
+// Non-temporal (streaming) loads of data read once per call: they bypass cache
+// allocation so the data that is reused stays resident.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t load_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
+// Masks of the value codes: dword d keeps bits 2d, 2d + 1 of each 16-bit half, which as
+// an fp16 is the subnormal code * 2^(2d - 24) (held in SGPRs).
+struct ValueMasks {
+  uint32_t m[4];
+  __device__ __forceinline__ ValueMasks() : m{0x00030003u, 0x000C000Cu, 0x00300030u, 0x00C000C0u} {
+    asm volatile("" : "+s"(m[0]), "+s"(m[1]), "+s"(m[2]), "+s"(m[3]));
+  }
+};
+
 __device__ __forceinline__ void unpack16(uint32_t x, uint32_t e[8], const PairConsts& k) {
   const uint32_t r6 = x >> 6, l6 = x << 6;
   e[0] = (x & k.m64) | k.b64;    // k = 2

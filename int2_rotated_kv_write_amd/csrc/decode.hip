@@ -361,12 +361,12 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
     if (j < nb) {
       const uint16_t* krow = kbuf(j) + row_offset(j) + 32 * q;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) in.kd[x] = reinterpret_cast<const uint4*>(krow)[x];
+      for (int x = 0; x < 4; ++x) in.kd[x] = load_nt(reinterpret_cast<const uint4*>(krow) + x);
     }
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
       const int jj = jbase + tt;
-      in.vv[tt] = jj < nb ? *reinterpret_cast<const uint32_t*>(vbuf(jj) + row_offset(jj) + 2 * lane) : 0u;
+      in.vv[tt] = jj < nb ? load_nt(reinterpret_cast<const uint32_t*>(vbuf(jj) + row_offset(jj) + 2 * lane)) : 0u;
     }
   };
   RoundIn nxt;
@@ -459,7 +459,10 @@ __device__ __forceinline__ half8 half8_of(uint4 u) { return __builtin_bit_cast(h
 // the statement, so whatever value the compiler keeps in it survives; one wait state
 // between each M0 write and the load that reads it (the compiler puts the same s_nop in
 // front of its own LDS-DMA loads; inline assembly is not checked for it).  A load reads
-// M0 when it issues, so M0 may be rewritten right after it.
+// M0 when it issues, so M0 may be rewritten right after it.  The page stream is loaded
+// non-temporal (nt): read once, it would otherwise displace from the caches what is
+// reused -- the split-K records, the q' records, U -- and measured 347 -> 328 us per
+// call at 28 x 100K.
 __device__ __forceinline__ void dma_page_to_lds(const void* sbase, uint32_t voff16, uint32_t voff4,
                                                 uint32_t lds_base, uint32_t lds_tail) {
   uint32_t saved;
@@ -467,10 +470,10 @@ __device__ __forceinline__ void dma_page_to_lds(const void* sbase, uint32_t voff
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
+      "global_load_lds_dwordx4 %1, %5 nt\n\t"
       "s_mov_b32 m0, %4\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %2, %5\n\t"
+      "global_load_lds_dword %2, %5 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff16), "v"(voff4), "s"(lds_base), "s"(lds_tail), "s"(sbase)
@@ -495,17 +498,34 @@ struct Int2Lane {
   uint32_t perm_sel;
   uint32_t wsel[4];
   PairConsts pk;
-  half2v nbase;
+  ValueMasks vm;
   float tau;
   half8 qb[NQ][2][2];
   float cinit[NQ], qs[NQ];
 };
 
-// Running softmax state of the lane's NQ quads: m (reference maximum), hm = -m / 2, the
-// lane's share of l, the zero-point sums and the value accumulators.
+// The value B operand's dword d holds the codes of token 4r + d as fp16 subnormals,
+// code 2^(2d - 24); that token's weights carry c_d = 2^(3 - 2d), so every product is
+// 2^-21 p s code.  c enters through the logit: each of the two group terms of token
+// 4r + d carries half of log2 c_d, so the lane of token 4r + 2 limb (+ 1) adds
+// hoff(limb, 0) (hoff(limb, 1)).  Both offsets and 1 / c are formed from the lane index
+// where they are used (the rescale branch, the start and the end of an item), not held in
+// registers through the page loop.
+__device__ __forceinline__ float hoff(int i) {
+  float limb = (float)((__lane_id() >> 1) & 1);
+  asm volatile("" : "+v"(limb));   // formed here, not hoisted into a register
+  return fmaf(-2.f, limb, i ? 0.5f : 1.5f);
+}
+__device__ __forceinline__ float inv_c() {   // 1 / c of the lane's token 4r + a4
+  return __builtin_amdgcn_ldexpf(1.f, 2 * (int)(__lane_id() & 3) - 3);
+}
+
+// Running softmax state of the lane's NQ quads: m (reference maximum), hm[i] = -m / 2 +
+// hoff(i), the lane's share of l, the zero-point sums and the value accumulators.  The
+// lane's l and zero-point shares are scaled by its c, the accumulators by 2^-21.
 template <int NQ>
 struct Int2State {
-  float m[NQ], hm[NQ], lsum[NQ], zs[NQ][2];
+  float m[NQ], hm[NQ][2], lsum[NQ], zs[NQ][2];
   f32x4 acc[NQ][8];
 };
 
@@ -525,9 +545,6 @@ __device__ __forceinline__ void int2_lane_init(Int2Lane<NQ>& L, int lane, float 
   L.off_vp = kOne ? kVParams128 + 4 * (4 * L.r + L.a4) : kVParams + 8 * (4 * L.r + L.a4);
   L.off_vw = kVCodes + 4 * n;                   // value code word of channel 16t + n at + 64t
   L.perm_sel = (uint32_t)L.r | (0x0Cu << 8) | ((4u + L.r) << 16) | (0x0Cu << 24);
-  // the value B operand's dword a4 carries fp16 base 64 (a4 even) or 16 (odd) on both
-  // halves: this lane's weights (dword a4 of A) pick up -base each
-  L.nbase = L.a4 & 1 ? half2v{(_Float16)-16.f, (_Float16)-16.f} : half2v{(_Float16)-64.f, (_Float16)-64.f};
   L.tau = tau;
   // byte selectors placing the weight limbs in the A operand (v_perm: bytes 4-7 = hi, 0-3 =
   // lo, 0x0C = zero): dword a4 takes the hi limb, dword (a4 + 1) % 4 the lo limb from lane a4 + 1
@@ -540,7 +557,8 @@ __device__ __forceinline__ void int2_state_init(Int2State<NQ>& st) {
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
     st.m[qd] = 0.f;   // set by the first pair, which always takes the rescale branch
-    st.hm[qd] = 0.f;
+    st.hm[qd][0] = hoff(0);
+    st.hm[qd][1] = hoff(1);
     st.lsum[qd] = 0.f;
     st.zs[qd][0] = st.zs[qd][1] = 0.f;
 #pragma unroll
@@ -611,8 +629,8 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
       const float u2 = d[2] + dpp<kQuadXor2>(d[2]), u3 = d[3] + dpp<kQuadXor2>(d[3]);
       const float y0 = L.limb ? u2 : u0, y1 = L.limb ? u3 : u1;
       // scale and zero-point term of group gp (tokens 4r + 2 limb, + 1)
-      const float x0 = fmaf(f16_bits_to_f32(P.kp[0]), y0, fmaf(f16_bits_to_f32(P.kp[0] >> 16), L.qs[qd], st.hm[qd]));
-      const float x1 = fmaf(f16_bits_to_f32(P.kp[1]), y1, fmaf(f16_bits_to_f32(P.kp[1] >> 16), L.qs[qd], st.hm[qd]));
+      const float x0 = fmaf(f16_bits_to_f32(P.kp[0]), y0, fmaf(f16_bits_to_f32(P.kp[0] >> 16), L.qs[qd], st.hm[qd][0]));
+      const float x1 = fmaf(f16_bits_to_f32(P.kp[1]), y1, fmaf(f16_bits_to_f32(P.kp[1] >> 16), L.qs[qd], st.hm[qd][1]));
       // groups: partner lane ^ 1 holds the other group of the same tokens
       const float v0 = x0 + dpp<kQuadXor1>(x0), v1 = x1 + dpp<kQuadXor1>(x1);
       lg[qd][k] = L.gp ? v1 : v0;
@@ -648,7 +666,8 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
       const float dm = first || pm > L.tau ? pm : 0.f;
       const float al = fast_exp2(-dm);
       st.m[qd] += dm;
-      st.hm[qd] = -0.5f * st.m[qd];
+      st.hm[qd][0] = fmaf(-0.5f, st.m[qd], hoff(0));
+      st.hm[qd][1] = fmaf(-0.5f, st.m[qd], hoff(1));
       lg[qd][0] -= dm;
       lg[qd][1] -= dm;
       st.lsum[qd] *= al;
@@ -684,9 +703,6 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
       const half2v hi2 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ps0, ps1));
       const half2v lo2 = half2v{(_Float16)fmaf(p0, (float)sz0[0], -(float)hi2[0]),
                                 (_Float16)fmaf(p1, (float)sz1[0], -(float)hi2[1])};
-      // the fp16 bases the value MFMA adds at this token's k-slot, times both limbs
-      st.zs[qd][g] = __builtin_amdgcn_fdot2(hi2, L.nbase, st.zs[qd][g], false);
-      st.zs[qd][g] = __builtin_amdgcn_fdot2(lo2, L.nbase, st.zs[qd][g], false);
       const uint32_t wh = __builtin_bit_cast(uint32_t, hi2);
       // lo of the next lane of the quad (every quad lane has a source)
       const uint32_t wl = (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, lo2), kQuadRot1, 0xF, 0xF, true);
@@ -698,11 +714,10 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
   // ---- values ----
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    // slots 4r + d of both pages: d = 0, 1 from x << 4 (bits 4-5, 6-7), d = 2, 3 from x
+    // slot 4r + d of both pages: the code at bits 2d, 2d + 1 of each half is the fp16
+    // subnormal code 2^(2d - 24)
     const uint32_t x = __builtin_amdgcn_perm(cur[1].vw[t], cur[0].vw[t], L.perm_sel);
-    const uint32_t l4 = x << 4;
-    const half8 bv = half8_of((l4 & L.pk.m64) | L.pk.b64, (l4 & L.pk.m16) | L.pk.b16, (x & L.pk.m64) | L.pk.b64,
-                              (x & L.pk.m16) | L.pk.b16);
+    const half8 bv = half8_of(x & L.vm.m[0], x & L.vm.m[1], x & L.vm.m[2], x & L.vm.m[3]);
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) st.acc[qd][t] = mfma16(A[qd][t >> 2], bv, st.acc[qd][t]);
   }
@@ -723,14 +738,20 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
 //   group's scale and zero-point term, and groups (lane ^ 1), after which lane
 //   (r, hh, a) holds the logit of token 4r + a of head hh: one value per lane.
 // Values, per page pair and quad: acc[(hh, j)][channel] += A[(hh, j)][k] *
-//   (base + code)[k][channel] with k running over the 32 tokens of the pair;
-//   row (hh, j) only carries the tokens 4r + j (A dword j holds the fp16
-//   weights p s_g of that token in both pages, the other dwords are zero), so
-//   each lane's own (token, head) weights feed the MFMA without any exchange;
-//   the four rows of a head are summed at the end.  B = channel-major code
-//   words of channel 16t + n, byte r of each page.  The base offsets are
-//   summed by one more MFMA per group against constant bases; the zero-point
-//   term sum p z_g is a per-head scalar.
+//   B[k][channel] with k running over the 32 tokens of the pair; row (hh, j)
+//   only carries the tokens 4r + j (A dword j holds the fp16 weights of that
+//   token in both pages, the other dwords are zero), so each lane's own
+//   (token, head) weights feed the MFMA without any exchange; the four rows of
+//   a head are summed at the end.  B = channel-major code words of channel
+//   16t + n, byte r of each page, masked in place: the code of token 4r + d
+//   sits at bits 2d, 2d + 1 of an fp16 half, i.e. it is the subnormal
+//   code 2^(2d - 24), taken exactly by the MFMA.  Token 4r + d's weights are
+//   c_d p s_g with c_d = 2^(3 - 2d), so every product is 2^-21 p s_g code and
+//   no term needs cancelling (all are >= 0).  c_d rides on p itself: the
+//   logit of token 4r + d carries log2 c_d (half on each group term), so the
+//   lane's shares of l and of the zero-point sums carry c_d too and are
+//   divided by it once at the end, where the accumulators are scaled by 2^21.
+//   The zero-point term sum p z_g is a per-head scalar.
 template <int G, bool kOne>
 __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int first, int end, int i_hi,
                           SplitSmem& sm) {
@@ -762,10 +783,9 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   }
   Int2Lane<NQ> ln;
   int2_lane_init<NQ, kOne>(ln, lane, a.resc_thr);
-  // zs[g]: per-head correction of group g's channels, sum over tokens of p z_g minus the
-  // fp16 bases the value MFMA adds (base * W_g), accumulated by v_dot2; m: running reference
-  // maximum of the head's logits, which are formed relative to it (each of the two group
-  // terms carries hm = -m / 2)
+  // zs[g]: per-head zero-point sum of group g's channels, sum over tokens of p z_g; m:
+  // running reference maximum of the head's logits, which are formed relative to it (each
+  // of the two group terms carries -m / 2)
   Int2State<NQ> st;
   int2_state_init(st);
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
@@ -921,7 +941,9 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
     // per-head totals over the 16 lanes of head hh (quad, then rows)
-    float L_h = st.lsum[qd], Z0 = st.zs[qd][0], Z1 = st.zs[qd][1];
+    // (the lane's shares carry its c; the accumulators 2^-21)
+    const float ic = inv_c();
+    float L_h = st.lsum[qd] * ic, Z0 = st.zs[qd][0] * ic, Z1 = st.zs[qd][1] * ic;
     L_h = rows_sum(quad_sum(L_h));
     Z0 = rows_sum(quad_sum(Z0));
     Z1 = rows_sum(quad_sum(Z1));
@@ -937,7 +959,7 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const float s = (st.acc[qd][t][0] + st.acc[qd][t][1]) + (st.acc[qd][t][2] + st.acc[qd][t][3]);
-        res.acc[row_head][16 * t + n] = s + (t < 4 ? z0 : z1);
+        res.acc[row_head][16 * t + n] = fmaf(s, 0x1p21f, t < 4 ? z0 : z1);
       }
     }
   }
@@ -1052,8 +1074,10 @@ __device__ void mq_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, i
   // ---- one record per (row, query head) ----
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
-    const float L_h = rows_sum(quad_sum(st.lsum[qd]));
-    const float Z0 = rows_sum(quad_sum(st.zs[qd][0])), Z1 = rows_sum(quad_sum(st.zs[qd][1]));
+    // (the lane's shares carry its c; the accumulators 2^-21)
+    const float ic = inv_c();
+    const float L_h = rows_sum(quad_sum(st.lsum[qd] * ic));
+    const float Z0 = rows_sum(quad_sum(st.zs[qd][0] * ic)), Z1 = rows_sum(quad_sum(st.zs[qd][1] * ic));
     const int e_q = e_wave + 4 * qd + hh;
     if (r == 0 && ln.a4 == 0 && e_q < n_e)
       a.part_ml[((size_t)(t0 + e_q / G) * a.Hq + h * G + e_q % G) * a.n_total + rec] = make_float2(st.m[qd], L_h);
@@ -1065,7 +1089,7 @@ __device__ void mq_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, i
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const float sum = (st.acc[qd][t][0] + st.acc[qd][t][1]) + (st.acc[qd][t][2] + st.acc[qd][t][3]);
-        dst[16 * t + n] = sum + (t < 4 ? z0 : z1);
+        dst[16 * t + n] = fmaf(sum, 0x1p21f, t < 4 ? z0 : z1);
       }
     }
   }
