@@ -103,6 +103,11 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ uint32_t load_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load_nt(const uint2* p) {
+  const u32x2_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p));
+  return make_uint2(v[0], v[1]);
+}
 
 // Masks of the value codes: dword d keeps bits 2d, 2d + 1 of each 16-bit half, which as
 // an fp16 is the subnormal code * 2^(2d - 24) (held in SGPRs).

@@ -57,11 +57,12 @@ struct B16Page {
   uint2 v[8];
 };
 
+// non-temporal: the pages are read once per call and would displace the records from the caches
 __device__ __forceinline__ void load_b16_page(B16Page& f, const uint8_t* blk, uint32_t koff, uint32_t voff) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) f.k[ks] = *reinterpret_cast<const uint4*>(blk + koff + 64 * ks);
+  for (int ks = 0; ks < 4; ++ks) f.k[ks] = load_nt(reinterpret_cast<const uint4*>(blk + koff + 64 * ks));
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) f.v[ct] = *reinterpret_cast<const uint2*>(blk + voff + 512 * ct);
+  for (int ct = 0; ct < 8; ++ct) f.v[ct] = load_nt(reinterpret_cast<const uint2*>(blk + voff + 512 * ct));
 }
 
 // high bf16 halves of two floats packed in one word (truncation)
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256) void b16_split_kernel(B16Args a) {
 
   // kB16Ahead pages in flight while one is processed; unrolled over the
   // buffers so each stays in fixed registers.  The prefetch is unconditional
-  // (past the wave's last page it reloads that page, which is still in L2):
+  // (past the wave's last page it reloads that page):
   // with a conditional one the compiler's wait before each page became
   // vmcnt(0), which also waited for the pages behind it.
   constexpr int NB = kB16Ahead + 1;
