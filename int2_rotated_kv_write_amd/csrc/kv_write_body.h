@@ -203,18 +203,19 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
     // ---- clip, group min/max (v holds the rotation times sqrt(128): the 1/sqrt(128)
     // goes into the clip threshold, the group parameters and the code scale below) ----
     // channel c = 16mt + 4q + r goes to post-rotation index j = bitrev7(c),
-    // whose group j/64 is bit 0 of c, i.e. r & 1.
+    // whose group j/64 is bit 0 of c, i.e. r & 1.  Clipping is monotone, so the group's
+    // clipped min/max are the clipped min/max of the raw values; the values themselves are
+    // clipped through their codes below.
     float mn[2] = {INFINITY, INFINITY}, mx[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      v[i] = __builtin_amdgcn_fmed3f(v[i], -clip_s, clip_s);
       mn[i & 1] = fminf(mn[i & 1], v[i]);
       mx[i & 1] = fmaxf(mx[i & 1], v[i]);
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      mn[g] = wave_min_xor(mn[g], 16, 32);
-      mx[g] = wave_max_xor(mx[g], 16, 32);
+      mn[g] = __builtin_amdgcn_fmed3f(wave_min_xor(mn[g], 16, 32), -clip_s, clip_s);
+      mx[g] = __builtin_amdgcn_fmed3f(wave_max_xor(mx[g], 16, 32), -clip_s, clip_s);
     }
     if (one_group) {   // one 128-channel group: both halves share its range
       mn[0] = mn[1] = fminf(mn[0], mn[1]);
@@ -232,9 +233,18 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
       zf[g] = -zf[g] * inv[g];          // t = w * inv - z * inv with w = v / sqrt(128)
       inv[g] = inv[g] * kInvSqrt128;
     }
+    // t(v) = fma(v, inv, zf) is non-decreasing in v, so the code of the clipped value,
+    // clamp(t(clip(v)), 0, 3), is t(v) clamped to [clamp(t(-c), 0, 3), clamp(t(c), 0, 3)]:
+    // one med3 per value, bit for bit the same (also where fp16 rounding put z beyond c)
+    float lo[2], hi[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      lo[g] = __builtin_amdgcn_fmed3f(fmaf(-clip_s, inv[g], zf[g]), 0.f, 3.f);
+      hi[g] = __builtin_amdgcn_fmed3f(fmaf(clip_s, inv[g], zf[g]), 0.f, 3.f);
+    }
     float tq[32];   // (w - z) / s clamped to [0, 3]; rounded to the code where it is stored
 #pragma unroll
-    for (int i = 0; i < 32; ++i) tq[i] = __builtin_amdgcn_fmed3f(fmaf(v[i], inv[i & 1], zf[i & 1]), 0.f, 3.f);
+    for (int i = 0; i < 32; ++i) tq[i] = __builtin_amdgcn_fmed3f(fmaf(v[i], inv[i & 1], zf[i & 1]), lo[i & 1], hi[i & 1]);
 
     // ---- store INT2 ----
     // whole aligned page written by this tile?

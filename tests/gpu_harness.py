@@ -163,8 +163,14 @@ def compare_kv_write(shape: O.Shape, ref: O.Cache, got: O.Cache, info: dict, got
             slack = np.where(sg == 0, 0.0, 4.0 * e_w / np.where(sg == 0, 1.0, sg))
             bad = mism & ~_near_code_boundary(t, slack)
             stats["codes_cond"] += int((mism & ~_near_code_boundary(t)).sum())
-            assert not bad.any(), (f"{kind} code mismatch h={h}: {int(bad.sum())} codes, e.g. "
-                                   f"t={t[bad][:4]}, gpu={codes[bad][:4]}, ref={code_ref[bad][:4]}")
+            if bad.any():
+                i, c = np.argwhere(bad)[0]
+                gg = c // shape.group
+                raise AssertionError(
+                    f"{kind} code mismatch h={h}: {int(bad.sum())} codes, e.g. t={t[bad][:4]}, gpu={codes[bad][:4]}, "
+                    f"ref={code_ref[bad][:4]}; token {i} group {gg}: gpu s,z=0x{s_got[i, gg]:04x},0x{z_got[i, gg]:04x} "
+                    f"ref s,z=0x{s_ref[i, gg]:04x},0x{z_ref[i, gg]:04x} w[min,max]=({w[i].min()!r},{w[i].max()!r}) "
+                    f"max|w_raw|={np.abs(d['w_raw'][i, h]).max()!r}")
             stats["codes"] += codes.size
             stats["codes_excused"] += int(mism.sum())
             # bytes this call may have written
