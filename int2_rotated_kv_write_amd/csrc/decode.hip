@@ -1193,6 +1193,25 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
       for (int ks = 0; ks < 4; ++ks)
         ub[t][ks] = *reinterpret_cast<const bf16x8*>(U + (32 * wave + 16 * t + n) * kHeadDim + 32 * ks + 8 * kg);
   }
+  // ---- requested before the sequence length is known: the records and (m, l) of a
+  // sequence whose every item holds tokens (record u at index u), the common case ----
+  constexpr int kBatch = GB == 1 ? 32 : 8;   // records per head requested at once by a wave
+  const float* head_base[GB];
+#pragma unroll
+  for (int g = 0; g < GB; ++g) head_base[g] = a.part + ((size_t)b * a.Hq + head0 + g) * a.n_total * kHeadDim;
+  const int n_all = a.ext ? a.n_total : a.n_bsplit + a.n_split;   // records of a full-length sequence
+  float2 v[GB][kBatch];
+#pragma unroll
+  for (int g = 0; g < GB; ++g)
+#pragma unroll
+    for (int d = 0; d < kBatch; ++d) {
+      const int u = wave + 4 * d;
+      v[g][d] = u < n_all ? *reinterpret_cast<const float2*>(head_base[g] + (u * kHeadDim + 2 * lane))
+                          : make_float2(0.f, 0.f);
+    }
+  const bool spec_ok = tid < GB * n_all;
+  const int sg = spec_ok ? tid / n_all : 0, su = spec_ok ? tid - sg * n_all : 0;
+  const float2 ml_spec = a.part_ml[((size_t)b * a.Hq + head0 + sg) * a.n_total + su];
   if (L == 0 && !a.ext) {
     for (int e = tid; e < GB * kHeadDim; e += 256) a.out[((size_t)b * a.Hq + head0) * kHeadDim + e] = 0;
     return;
@@ -1208,31 +1227,30 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
   // then from n_bsplit + n_split the shared ranges
   auto idx_of = [&](int u) { return u < n_b ? u : u < n_bi ? a.n_bsplit + (u - n_b) : a.n_bsplit + a.n_split + (u - n_bi); };
   auto rec_of = [&](int g, int u) { return ((size_t)b * a.Hq + head0 + g) * a.n_total + idx_of(u); };
-  // ---- this wave's records u = wave + 4 d, requested first (they do not depend on the maxima):
-  // per head one base address, the record index and lane in a 32-bit offset ----
-  constexpr int kBatch = GB == 1 ? 32 : 8;   // records per head requested at once by a wave
-  const float* head_base[GB];
-#pragma unroll
-  for (int g = 0; g < GB; ++g) head_base[g] = a.part + ((size_t)b * a.Hq + head0 + g) * a.n_total * kHeadDim;
-  auto load_batch = [&](int u0, float2 (&v)[GB][kBatch]) {
+  auto load_batch = [&](int u0, float2 (&vb)[GB][kBatch]) {
 #pragma unroll
     for (int g = 0; g < GB; ++g)
 #pragma unroll
       for (int d = 0; d < kBatch; ++d) {
         const int u = u0 + 4 * d;
         const int idx = idx_of(u);
-        v[g][d] = u < n_used ? *reinterpret_cast<const float2*>(head_base[g] + (idx * kHeadDim + 2 * lane))
-                             : make_float2(0.f, 0.f);
+        vb[g][d] = u < n_used ? *reinterpret_cast<const float2*>(head_base[g] + (idx * kHeadDim + 2 * lane))
+                              : make_float2(0.f, 0.f);
       }
   };
-  // ---- (m, l) of every record into LDS; each head's maximum.  The first 256 are requested
-  // before this wave's records, so the wait for them leaves the record loads in flight ----
-  const bool ml0_ok = tid < GB * n_used;
-  const int g0 = ml0_ok ? tid / n_used : 0, u0_ = ml0_ok ? tid - g0 * n_used : 0;
-  const float2 ml0 = a.part_ml[rec_of(g0, u0_)];
-  float2 v[GB][kBatch];
-  load_batch(wave, v);
-  if (ml0_ok) sm.ml[g0][u0_] = ml0;
+  // block-uniform: the speculative requests were the used records exactly
+  const bool full = !a.ext && n_b == a.n_bsplit && n_i == a.n_split && shared == 0;
+  if (full) {
+    if (spec_ok) sm.ml[sg][su] = ml_spec;
+  } else {
+    // (m, l) of every record into LDS; the first 256 are requested before this wave's records,
+    // so the wait for them leaves the record loads in flight
+    const bool ml0_ok = tid < GB * n_used;
+    const int g0 = ml0_ok ? tid / n_used : 0, u0_ = ml0_ok ? tid - g0 * n_used : 0;
+    const float2 ml0 = a.part_ml[rec_of(g0, u0_)];
+    load_batch(wave, v);
+    if (ml0_ok) sm.ml[g0][u0_] = ml0;
+  }
   for (int e = tid + 256; e < GB * n_used; e += 256) {   // more than 256 records: long sequences
     const int g = e / n_used, u = e - g * n_used;
     sm.ml[g][u] = a.part_ml[rec_of(g, u)];
