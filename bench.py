@@ -22,6 +22,9 @@ Besides the headline line's fields, the JSON carries (unless --no-extras):
   concurrent_28x100k_group128  decode_attn at the headline shape and a 100K
                     prefill kv_write in the 2.25-bit format (one 128-channel
                     group per token);
+  extend_1x100k_chunk1024  extend_attn (chunked prefill): 1,024 new tokens
+                    of one sequence over its cached 100,000-token prefix and
+                    causally over themselves, as attention TFLOP/s;
   rotation_ablation attention-output error against BF16 of OSCAR,
                     Hadamard-only and naive INT2 rotations through the
                     library's kernels on two synthetic laws.
@@ -60,7 +63,13 @@ WORKLOADS = {
     # layers cycled exactly as the headline's
     "concurrent_28x100k_group128": dict(batch=28, seq_len=100_000, q_heads=32, kv_heads=8, layers=36,
                                         table="permuted", law="heavy", group=128),
+    # chunked prefill: the cached 100,000-token prefix of one sequence, then one chunk of
+    # EXTEND_CHUNK new tokens through extend_attn
+    "extend_1x100k_chunk1024": dict(batch=1, seq_len=100_000, q_heads=32, kv_heads=8, layers=1,
+                                    table="permuted", law="heavy"),
 }
+EXTEND_CHUNK = 1024
+PEAK_F16_MFMA_TFLOPS = 2500.0   # dense fp16 MFMA peak of one MI355X
 SHARED_PREFIX_TOKENS = 4096     # ragged workload: 25% of the sequences share their first 4,096 tokens
 SINK, RECENT = 64, 256
 PREFILL_TOKENS = 100_000        # write-path workload: one kv_write of 100,000 prefill tokens x 8 KV heads
@@ -389,6 +398,42 @@ def naive_basis():
 
 
 
+def bench_extend(rng, gen, dev):
+    """Chunked prefill at long context: EXTEND_CHUNK new tokens of one sequence (32 query /
+    8 KV heads) attend to its cached 100,000-token prefix as stored (INT2 history through
+    the folded rotation, BF16 sink and ring) and causally to their own keys, in one
+    extend_attn call.  Its work is counted as the attention's QK and PV products (4 x 128
+    flops per query head and key) against the dense fp16 MFMA peak; the bytes are the
+    prefix cache read once plus the chunk's q, k, v and out."""
+    import torch
+
+    import int2_rotated_kv_write_amd as lib
+    from synth.device import sample_kv_device, sample_queries_device
+    name = "extend_1x100k_chunk1024"
+    W = build_workload(name, rng, gen, dev)
+    T, P = EXTEND_CHUNK, int(W.lens[0])
+    q = sample_queries_device(T, W.Hq, gen, dev)
+    k = sample_kv_device(W.law, T, gen, dev)
+    v = sample_kv_device(W.law, T, gen, dev)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    prefix = torch.tensor([P], dtype=torch.int32, device=dev)
+    out = torch.empty((T, W.Hq, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lib.extend_workspace_bytes(W.shape, T, W.max_pages, T), dtype=torch.uint8, device=dev)
+    call = lambda: lib.extend_attn(W.shape, W.caches[0], q, k, v, cu, prefix, W.table_d, out, ws, T, SIG)
+    mean, med = event_us([call], 10)
+    keys = T * P + T * (T + 1) // 2                  # (query row, key) pairs per query head
+    flops = 4 * 128 * W.Hq * keys
+    nbytes = decode_bytes(W.lens, W.H, W.Hq) - W.Hq * 128 * 2 * 2 + T * (W.Hq * 2 + W.H * 2) * 128 * 2
+    tflops = flops / (mean * 1e-6) / 1e12
+    log(f"{name}: extend_attn {mean:.1f} us (median {med:.1f}), {tflops:.1f} TFLOP/s")
+    return {"workload": name, "batch": 1, "prefix_len": P, "chunk_len": T, "num_q_heads": W.Hq,
+            "num_kv_heads": W.H, "page_table": "permuted",
+            "kernel": "extend_attn (rotate_q, extend INT2 ranges, extend BF16 rows, reduce)", "us": mean,
+            "us_median": med, "flops": flops, "achieved_tflops": tflops, "peak_tflops": PEAK_F16_MFMA_TFLOPS,
+            "frac": tflops / PEAK_F16_MFMA_TFLOPS, "bytes": nbytes,
+            "achieved_gbs": nbytes / (mean * 1e-6) / 1e9}
+
+
 def bench_group128(rng, gen, dev):
     """decode_attn at 28 x 100K in the 2.25-bit format (one fp16 scale and zero per
     token and head), 36 layers' caches cycled as in the headline, and one kv_write
@@ -508,6 +553,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the single-sequence and ragged workloads and the rotation ablation")
     ap.add_argument("--only-ablation", action="store_true", help="run the rotation ablation alone and print it")
+    ap.add_argument("--only-extend", action="store_true", help="run the chunked-prefill measurement alone and print it")
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -525,11 +571,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     lib.load()
-    if args.only_ablation:
+    if args.only_ablation or args.only_extend:
         rng = np.random.default_rng(args.seed)
         gen = torch.Generator(device=dev)
         gen.manual_seed(args.seed)
-        print(json.dumps({"rotation_ablation": bench_ablation(rng, gen, dev)}), flush=True)
+        if args.only_ablation:
+            print(json.dumps({"rotation_ablation": bench_ablation(rng, gen, dev)}), flush=True)
+        else:
+            print(json.dumps({"extend_1x100k_chunk1024": bench_extend(rng, gen, dev)}), flush=True)
         return
     wl = WORKLOADS[args.workload]
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -684,6 +733,8 @@ def main():
         extras["ragged_64x4k_128k"] = bench_ragged(rng, gen, dev)
         torch.cuda.empty_cache()
         extras["concurrent_28x100k_group128"] = bench_group128(rng, gen, dev)
+        torch.cuda.empty_cache()
+        extras["extend_1x100k_chunk1024"] = bench_extend(rng, gen, dev)
         torch.cuda.empty_cache()
         extras["rotation_ablation"] = bench_ablation(rng, gen, dev)
         torch.cuda.empty_cache()

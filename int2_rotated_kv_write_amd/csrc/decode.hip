@@ -1377,7 +1377,7 @@ struct ExtArgs {
   const int32_t *cu, *prefix_lens;
   int32_t* row_len;             // [T]: prefix length of the row's sequence (written by the BF16 kernel)
   int32_t n_seq, n_tok, max_chunk;
-  int32_t n_qt;                 // 16-query-head tiles per (sequence, KV head)
+  int32_t n_qt;                 // 32-query-head tiles per (sequence, KV head): 8 per wave (two quads)
 };
 
 // Sequence b's chunk: tokens t0 .. t0 + chunk - 1, clamped to [0, n_tok) and to at most
@@ -1398,7 +1398,7 @@ struct __attribute__((aligned(16))) MqSmem {
 // INT2 prefix pages of one range of one (sequence, KV head), read once per block for 16 query
 // heads of the sequence's chunk (query head e = chunk position * G + head in the group).
 template <int G, bool kOne>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void ext_int2_kernel(ExtArgs e) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void ext_int2_kernel(ExtArgs e) {
   __shared__ MqSmem sm;
   const DecodeArgs& a = e.d;
   int job = blockIdx.x;
@@ -1413,9 +1413,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   const int i_hi = int2_end(L, a.sink, a.recent);
   const int first = a.sink / kPage + split * a.P;
   const int end = min(first + a.P, (i_hi + kPage - 1) / kPage);
-  const int e_block = 16 * qt;
+  const int e_block = 32 * qt;
   if (i_hi <= a.sink || first >= end || e_block >= chunk * G) return;   // block-uniform
-  mq_int2_range<G, 1, kMqRing, kOne>(a, a.page_table + (size_t)b * a.max_pages, h, first, end - first, i_hi, t0, chunk * G,
+  mq_int2_range<G, 2, kMqRing, kOne>(a, a.page_table + (size_t)b * a.max_pages, h, first, end - first, i_hi, t0, chunk * G,
                                e_block, 1 + split, sm.ring);
 }
 
@@ -1727,7 +1727,7 @@ ExtendPlan make_extend_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   p.pages_per_split = (int)per;
   p.n_split = int2_pages > 0 ? (int)((int2_pages + per - 1) / per) : 0;
   p.n_total = 1 + p.n_split;
-  p.n_qt = (int)(((long long)max_chunk * (num_q_heads / num_kv_heads) + 15) / 16);
+  p.n_qt = (int)(((long long)max_chunk * (num_q_heads / num_kv_heads) + 31) / 32);
   const size_t rows = (size_t)num_tokens * num_q_heads;
   p.qrot_off = 0;
   p.part_off = (rows * kQrotBytes + 511) / 512 * 512;
