@@ -1095,6 +1095,250 @@ __device__ void mq_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, i
   }
 }
 
+// Many queries over one range of INT2 pages, flash style (chunked prefill): 16 query
+// vectors per wave (64 per block) against every page of the range, read once into an LDS
+// ring shared by the four waves (page j loaded by wave j % 4).  With queries in the MFMA's
+// column dimension a page's codes are unpacked once for 16 queries (the decode layout puts
+// (head, group, limb) there and serves 4 heads).  Lane l: n = l % 16 is the lane's query
+// (column), r = l / 16 its row group.
+//   logits, per page: D_g[token][query] = sum over group g's channels of (base + code) * q'
+//     with both limbs of q' accumulated into one D_g (4 MFMAs per group, started at minus
+//     the base sums); lane (n, r) gets tokens 4r .. 4r + 3 of query n and forms
+//     s_0 D_0 + s_1 D_1 + z_0 sum q'_0 + z_1 sum q'_1 for each.
+//   values, per page pair: O^T[channel][query] += V^T[channel][k] W^T[k][query] with the
+//     decode's k order (k-slots 8r .. 8r + 7 = tokens 4r .. 4r + 3 of both pages), so B is
+//     the lane's own weights W = c_i p s_g (hi and lo limbs as two MFMAs) and A the masked
+//     subnormal value codes; tiles 0-3 (group 0 channels) take s_0, tiles 4-7 s_1.
+//   c_i = 2^(3 - 2i) for token 4r + i enters through the logit (log2 c_i added); the
+//     lane's l and zero-point sums are kept per i and divided by c_i once at the end.
+constexpr int kFlashRing = 8;
+constexpr int kExtTile = 64;   // query vectors per block (16 per wave)
+
+template <int G, bool kOne>
+__device__ void flash_int2_range(const DecodeArgs& a, const int32_t* ptab, int h, int first, int np, int i_hi,
+                                 int t0, int n_e, int e_block, int rec, uint8_t (*ring)[kBlockBytes]) {
+  constexpr int R = kFlashRing;
+  static_assert(R % 4 == 0 && R * 8 <= 256, "whole rounds of the four waves; one thread per V-parameter line");
+  i_hi = __builtin_amdgcn_readfirstlane(i_hi);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, r = lane >> 4;
+  const int e_q = e_block + 16 * wave + n;   // this lane's query vector
+  const bool q_ok = e_q < n_e;
+  constexpr int kIdRegs = kMaxPagesPerSplit / 4 / 64;
+  static_assert(kIdRegs == 2, "page offsets in two registers");
+  uint32_t unit_reg[kIdRegs];
+  half8 qb[2][2][2];   // [group][half][limb]: q' of channels 32 (2g + kh) + 8r .. + 8
+  float init[2], qs[2];
+  {
+    constexpr uint32_t kUnits = (kOne ? kBlockBytes128 : kBlockBytes) / 128;
+    const uint32_t per_page = (uint32_t)a.H * kUnits, head_units = (uint32_t)h * kUnits;
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k)
+      unit_reg[k] = (uint32_t)ptab[first + min(wave + 4 * (lane + 64 * k), np - 1)] * per_page + head_units;
+    const int row = t0 + (q_ok ? e_q / G : 0), hq = h * G + (q_ok ? e_q % G : 0);
+    const QrotRecord* qr = a.qrot + ((size_t)row * a.Hq + hq);
+    uint4 qraw[2][2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int limb = 0; limb < 2; ++limb) qraw[g][kh][limb] = *reinterpret_cast<const uint4*>(&qr->frag[g][kh][limb][r][0]);
+    float nc[2][2], qsr[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      nc[g][0] = qr->negc[g][0];
+      nc[g][1] = qr->negc[g][1];
+      qsr[g] = qr->qsum[g];
+    }
+    // consumed here, before any page load: no wait for them lands in the page loop
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(unit_reg[k]));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int limb = 0; limb < 2; ++limb) {
+          asm volatile("" : "+v"(qraw[g][kh][limb].x), "+v"(qraw[g][kh][limb].y), "+v"(qraw[g][kh][limb].z),
+                       "+v"(qraw[g][kh][limb].w));
+          qb[g][kh][limb] = half8_of(q_ok ? qraw[g][kh][limb] : make_uint4(0, 0, 0, 0));
+        }
+      asm volatile("" : "+v"(nc[g][0]), "+v"(nc[g][1]), "+v"(qsr[g]));
+      init[g] = q_ok ? nc[g][0] + nc[g][1] : 0.f;
+      qs[g] = q_ok ? qsr[g] : 0.f;
+    }
+  }
+  const PairConsts pk;
+  const ValueMasks vm;
+  const uint32_t perm_sel = (uint32_t)r | (0x0Cu << 8) | ((4u + r) << 16) | (0x0Cu << 24);
+  const int off_kc = kKCodes + 32 * n + 4 * r;   // token n: code word r of group 0 (+16: group 1)
+  const int off_vw = kVCodes + 4 * n;            // value code word of channel 16t + n at + 64t
+  // running state: m (reference maximum), hmi[i] = log2 c_i - m, per-i shares of l and of
+  // the zero-point sums, the value accumulators (tile t: channels 16t + 4r + i of query n)
+  float m = 0.f, hmi[4], lsum[4], zs[2][4];
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hmi[i] = 3.f - 2.f * i;
+    lsum[i] = zs[0][i] = zs[1][i] = 0.f;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](int j) {   // page j of the range (first + j) into slot j % R, by wave j % 4
+    if ((j & 3) != wave) return;
+    const int mm = j >> 2;
+    const uint32_t u = __builtin_amdgcn_readlane(mm < 64 ? unit_reg[0] : unit_reg[1], mm & 63);
+    const uint8_t* blk = a.pages + ((uint64_t)u << 7);
+    const uint32_t dst = (uint32_t)(uintptr_t)&ring[j % R][0];
+    dma_page_to_lds(blk, 16 * lane, 1024 + 4 * (kOne ? (lane & 31) : lane), dst, dst + 1024);
+  };
+  // the V parameters of every slot start at zero (a missing second page of the last pair is
+  // read anyway and weighted 0; its scales must be finite)
+  if (threadIdx.x < R * 8)
+    *reinterpret_cast<uint4*>(&ring[threadIdx.x >> 3][(kOne ? kVParams128 : kVParams) + 16 * (threadIdx.x & 7)]) =
+        make_uint4(0, 0, 0, 0);
+  block_lds_barrier();
+  for (int j = 0; j < R - 2 && j < np; ++j) issue(j);
+  for (int j = 0; j < np; j += 2) {
+    mq_wait_own_pair<R>(j + R - 3 < np);
+    block_lds_barrier();   // pages j, j + 1 visible to every wave; slots of pair j - 2 no longer read
+    if (j + R - 2 < np) issue(j + R - 2);
+    if (j + R - 1 < np) issue(j + R - 1);
+    const uint8_t* blk[2] = {&ring[j % R][0], &ring[(j + 1) % R][0]};
+    const bool has1 = j + 1 < np;
+    const int pp = first + j;
+    // ---- logits of both pages: lane (n, r) holds tokens 4r + i of query n ----
+    float lg[2][4];
+    uint2 vpar[2][4];   // value (s0, z0), (s1, z1) of token 4r + i
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint8_t* bk = blk[k];
+      uint32_t e0[8], e1[8];
+      unpack16(*reinterpret_cast<const uint32_t*>(bk + off_kc), e0, pk);
+      unpack16(*reinterpret_cast<const uint32_t*>(bk + off_kc + 16), e1, pk);
+      const half8 a00 = half8_of(e0[0], e0[1], e0[2], e0[3]), a01 = half8_of(e0[4], e0[5], e0[6], e0[7]);
+      const half8 a10 = half8_of(e1[0], e1[1], e1[2], e1[3]), a11 = half8_of(e1[4], e1[5], e1[6], e1[7]);
+      f32x4 d0 = f32x4{init[0], init[0], init[0], init[0]}, d1 = f32x4{init[1], init[1], init[1], init[1]};
+      d0 = mfma16(a00, qb[0][0][0], d0);
+      d1 = mfma16(a10, qb[1][0][0], d1);
+      d0 = mfma16(a00, qb[0][0][1], d0);
+      d1 = mfma16(a10, qb[1][0][1], d1);
+      d0 = mfma16(a01, qb[0][1][0], d0);
+      d1 = mfma16(a11, qb[1][1][0], d1);
+      d0 = mfma16(a01, qb[0][1][1], d0);
+      d1 = mfma16(a11, qb[1][1][1], d1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * r + i;
+        uint32_t k0, k1;   // (s, z) of groups 0 and 1
+        if constexpr (kOne) {
+          k0 = k1 = *reinterpret_cast<const uint32_t*>(bk + kKParams + 4 * t);
+          vpar[k][i].x = vpar[k][i].y = *reinterpret_cast<const uint32_t*>(bk + kVParams128 + 4 * t);
+        } else {
+          const uint2 kk = *reinterpret_cast<const uint2*>(bk + kKParams + 8 * t);
+          k0 = kk.x;
+          k1 = kk.y;
+          vpar[k][i] = *reinterpret_cast<const uint2*>(bk + kVParams + 8 * t);
+        }
+        float x = fmaf(f16_bits_to_f32(k1 >> 16), qs[1], hmi[i]);
+        x = fmaf(f16_bits_to_f32(k0 >> 16), qs[0], x);
+        x = fmaf(f16_bits_to_f32(k1), d1[i], x);
+        lg[k][i] = fmaf(f16_bits_to_f32(k0), d0[i], x);
+      }
+    }
+    if (!has1 || (pp + 2) * kPage > i_hi) {   // wave-uniform: only the last pair can hold missing tokens
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (k == 0 || has1) && (pp + k) * kPage + 4 * r + i < i_hi;
+          lg[k][i] = ok ? lg[k][i] : -INFINITY;
+          vpar[k][i] = ok ? vpar[k][i] : make_uint2(0u, 0u);   // slots never written may hold anything
+        }
+    }
+    // ---- online softmax of query n (its 4 lanes hold the page's 16 tokens); rescale only
+    // when the maximum grows by more than tau ----
+    float pm = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
+                     fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
+    if (__any(j == 0 || pm > a.resc_thr)) {
+      pm = rows_max(pm);   // finite: every pair has a valid token
+      const float dm = j == 0 || pm > a.resc_thr ? pm : 0.f;
+      const float al = fast_exp2(-dm);
+      m += dm;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hmi[i] -= dm;
+        lg[0][i] -= dm;
+        lg[1][i] -= dm;
+        lsum[i] *= al;
+        zs[0][i] *= al;
+        zs[1][i] *= al;
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= al;
+    }
+    // ---- weights W_g = c_i p s_g as fp16 hi + lo of both pages (dword i: page 0, page 1) ----
+    uint32_t whi[2][4], wlo[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = fast_exp2(lg[0][i]), p1 = fast_exp2(lg[1][i]);
+      lsum[i] += p0 + p1;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t v0 = g ? vpar[0][i].y : vpar[0][i].x, v1 = g ? vpar[1][i].y : vpar[1][i].x;
+        const half2v sz0 = __builtin_bit_cast(half2v, v0), sz1 = __builtin_bit_cast(half2v, v1);
+        zs[g][i] = fmaf(p0, (float)sz0[1], fmaf(p1, (float)sz1[1], zs[g][i]));
+        const float ps0 = fmaf(p0, (float)sz0[0], 0.f), ps1 = fmaf(p1, (float)sz1[0], 0.f);
+        const half2v hi2 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ps0, ps1));
+        const half2v lo2 = half2v{(_Float16)fmaf(p0, (float)sz0[0], -(float)hi2[0]),
+                                  (_Float16)fmaf(p1, (float)sz1[0], -(float)hi2[1])};
+        whi[g][i] = __builtin_bit_cast(uint32_t, hi2);
+        wlo[g][i] = __builtin_bit_cast(uint32_t, lo2);
+      }
+    }
+    const half8 bhi[2] = {half8_of(whi[0][0], whi[0][1], whi[0][2], whi[0][3]),
+                          half8_of(whi[1][0], whi[1][1], whi[1][2], whi[1][3])};
+    const half8 blo[2] = {half8_of(wlo[0][0], wlo[0][1], wlo[0][2], wlo[0][3]),
+                          half8_of(wlo[1][0], wlo[1][1], wlo[1][2], wlo[1][3])};
+    // ---- values ----
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t x = __builtin_amdgcn_perm(*reinterpret_cast<const uint32_t*>(blk[1] + off_vw + 64 * t),
+                                               *reinterpret_cast<const uint32_t*>(blk[0] + off_vw + 64 * t), perm_sel);
+      const half8 av = half8_of(x & vm.m[0], x & vm.m[1], x & vm.m[2], x & vm.m[3]);
+      acc[t] = mfma16(av, bhi[t >> 2], acc[t]);
+      acc[t] = mfma16(av, blo[t >> 2], acc[t]);
+    }
+  }
+  // ---- one record per query vector: (m, l) and acc = 2^21 O + the zero-point sum of the
+  // channel's group; the lane's shares divided by c_i, summed over the query's 4 lanes ----
+  float L = 0.f, Z[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float ic = __builtin_amdgcn_ldexpf(1.f, 2 * i - 3);
+    L = fmaf(lsum[i], ic, L);
+    Z[0] = fmaf(zs[0][i], ic, Z[0]);
+    Z[1] = fmaf(zs[1][i], ic, Z[1]);
+  }
+  L = rows_sum(L);
+  Z[0] = rows_sum(Z[0]);
+  Z[1] = rows_sum(Z[1]);
+  if (q_ok) {
+    const size_t rr = ((size_t)(t0 + e_q / G) * a.Hq + h * G + e_q % G) * a.n_total + rec;
+    if (r == 0) a.part_ml[rr] = make_float2(m, L);
+    float* dst = a.part + rr * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float z = Z[t >> 2];
+      *reinterpret_cast<float4*>(dst + 16 * t + 4 * r) =
+          make_float4(fmaf(acc[t][0], 0x1p21f, z), fmaf(acc[t][1], 0x1p21f, z), fmaf(acc[t][2], 0x1p21f, z),
+                      fmaf(acc[t][3], 0x1p21f, z));
+    }
+  }
+}
+
 // Cascade block w (< n_cas): shared range k of group g, KV head h, query tile qt, with the
 // pages of the group's first member's table row.
 template <int G, bool kOne>
@@ -1377,7 +1621,7 @@ struct ExtArgs {
   const int32_t *cu, *prefix_lens;
   int32_t* row_len;             // [T]: prefix length of the row's sequence (written by the BF16 kernel)
   int32_t n_seq, n_tok, max_chunk;
-  int32_t n_qt;                 // 32-query-head tiles per (sequence, KV head): 8 per wave (two quads)
+  int32_t n_qt;                 // tiles of kExtTile query vectors per (sequence, KV head)
 };
 
 // Sequence b's chunk: tokens t0 .. t0 + chunk - 1, clamped to [0, n_tok) and to at most
@@ -1389,16 +1633,16 @@ __device__ __forceinline__ void chunk_of(const ExtArgs& e, int b, int& t0, int& 
   chunk = max(chunk, 0);
 }
 
-constexpr int kMqRing = 8;   // pages per block ring of the multi-query INT2 kernel
+constexpr int kMqRing = 8;   // pages per block ring of the multi-query INT2 kernels
+static_assert(kFlashRing == kMqRing, "one ring type");
 
 struct __attribute__((aligned(16))) MqSmem {
   uint8_t ring[kMqRing][kBlockBytes];
 };
 
-// INT2 prefix pages of one range of one (sequence, KV head), read once per block for 32 query
-// heads of the sequence's chunk (query head e = chunk position * G + head in the group), two
-// quads per wave (2 waves per SIMD: measured 7.7 against 8.5 ms with one quad per wave for a
-// 1,024-token chunk over a 100K prefix).
+// INT2 prefix pages of one range of one (sequence, KV head), read once per block for 64 query
+// vectors of the sequence's chunk (query vector e = chunk position * G + head in the group),
+// 16 per wave with the queries in the MFMA's column dimension.
 template <int G, bool kOne>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void ext_int2_kernel(ExtArgs e) {
   __shared__ MqSmem sm;
@@ -1415,10 +1659,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   const int i_hi = int2_end(L, a.sink, a.recent);
   const int first = a.sink / kPage + split * a.P;
   const int end = min(first + a.P, (i_hi + kPage - 1) / kPage);
-  const int e_block = 32 * qt;
+  const int e_block = kExtTile * qt;
   if (i_hi <= a.sink || first >= end || e_block >= chunk * G) return;   // block-uniform
-  mq_int2_range<G, 2, kMqRing, kOne>(a, a.page_table + (size_t)b * a.max_pages, h, first, end - first, i_hi, t0, chunk * G,
-                               e_block, 1 + split, sm.ring);
+  flash_int2_range<G, kOne>(a, a.page_table + (size_t)b * a.max_pages, h, first, end - first, i_hi, t0, chunk * G,
+                            e_block, 1 + split, sm.ring);
 }
 
 // BF16 keys of a chunk query: the prefix's sink rows [0, min(sink, L)), its ring rows
@@ -1729,7 +1973,7 @@ ExtendPlan make_extend_plan(int32_t num_kv_heads, int32_t num_q_heads, int32_t s
   p.pages_per_split = (int)per;
   p.n_split = int2_pages > 0 ? (int)((int2_pages + per - 1) / per) : 0;
   p.n_total = 1 + p.n_split;
-  p.n_qt = (int)(((long long)max_chunk * (num_q_heads / num_kv_heads) + 31) / 32);
+  p.n_qt = (int)(((long long)max_chunk * (num_q_heads / num_kv_heads) + kExtTile - 1) / kExtTile);
   const size_t rows = (size_t)num_tokens * num_q_heads;
   p.qrot_off = 0;
   p.part_off = (rows * kQrotBytes + 511) / 512 * 512;

@@ -77,7 +77,7 @@ struct B16Launch {
 };
 
 // Extend (chunked prefill) plan: the INT2 pages of a prefix in n_split ranges of
-// pages_per_split pages; n_qt tiles of 16 query heads per (sequence, KV head); every
+// pages_per_split pages; n_qt tiles of 64 query vectors per (sequence, KV head); every
 // (chunk token, query head) owns n_total = 1 + n_split partial records.
 struct ExtendPlan {
   int32_t pages_per_split, n_split, n_total, n_qt;
