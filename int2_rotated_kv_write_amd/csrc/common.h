@@ -110,11 +110,17 @@ __device__ __forceinline__ uint2 load_nt(const uint2* p) {
 }
 
 // Masks of the value codes: dword d keeps bits 2d, 2d + 1 of each 16-bit half, which as
-// an fp16 is the subnormal code * 2^(2d - 24) (held in SGPRs).
+// an fp16 is the subnormal code * 2^(2d - 24).  In VGPRs (kVgpr) the masking v_and_b32 issues
+// at the full rate (measured ~2.5 against ~4.7 cycles per wave64 instruction with an SGPR
+// operand); in SGPRs the four registers are saved where VGPRs are the tighter limit.
+template <bool kVgpr>
 struct ValueMasks {
   uint32_t m[4];
   __device__ __forceinline__ ValueMasks() : m{0x00030003u, 0x000C000Cu, 0x00300030u, 0x00C000C0u} {
-    asm volatile("" : "+s"(m[0]), "+s"(m[1]), "+s"(m[2]), "+s"(m[3]));
+    if constexpr (kVgpr)
+      asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]));
+    else
+      asm volatile("" : "+s"(m[0]), "+s"(m[1]), "+s"(m[2]), "+s"(m[3]));
   }
 };
 

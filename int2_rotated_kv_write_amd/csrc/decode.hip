@@ -498,7 +498,7 @@ struct Int2Lane {
   uint32_t perm_sel;
   uint32_t wsel[4];
   PairConsts pk;
-  ValueMasks vm;
+  ValueMasks<(NQ > 1)> vm;   // one quad: 128 VGPRs for 4 waves per SIMD, no room for them
   float tau;
   half8 qb[NQ][2][2];
   float cinit[NQ], qs[NQ];
@@ -701,8 +701,9 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
       // hi = fp16(p s) rounded toward zero (one packed conversion for both pages), lo = the
       // rest: hi + lo carries p s to about 2^-21 relative whatever hi's rounding
       const half2v hi2 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ps0, ps1));
-      const half2v lo2 = half2v{(_Float16)fmaf(p0, (float)sz0[0], -(float)hi2[0]),
-                                (_Float16)fmaf(p1, (float)sz1[0], -(float)hi2[1])};
+      // (the rest in fp32, then one packed conversion: cheaper than two fp16-result FMAs)
+      const half2v lo2 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(fmaf(p0, (float)sz0[0], -(float)hi2[0]),
+                                                                              fmaf(p1, (float)sz1[0], -(float)hi2[1])));
       const uint32_t wh = __builtin_bit_cast(uint32_t, hi2);
       // lo of the next lane of the quad (every quad lane has a source)
       const uint32_t wl = (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, lo2), kQuadRot1, 0xF, 0xF, true);
@@ -1170,7 +1171,7 @@ __device__ void flash_int2_range(const DecodeArgs& a, const int32_t* ptab, int h
     }
   }
   const PairConsts pk;
-  const ValueMasks vm;
+  const ValueMasks<true> vm;
   const uint32_t perm_sel = (uint32_t)r | (0x0Cu << 8) | ((4u + r) << 16) | (0x0Cu << 24);
   const int off_kc = kKCodes + 32 * n + 4 * r;   // token n: code word r of group 0 (+16: group 1)
   const int off_vw = kVCodes + 4 * n;            // value code word of channel 16t + n at + 64t
@@ -1292,8 +1293,8 @@ __device__ void flash_int2_range(const DecodeArgs& a, const int32_t* ptab, int h
         zs[g][i] = fmaf(p0, (float)sz0[1], fmaf(p1, (float)sz1[1], zs[g][i]));
         const float ps0 = fmaf(p0, (float)sz0[0], 0.f), ps1 = fmaf(p1, (float)sz1[0], 0.f);
         const half2v hi2 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ps0, ps1));
-        const half2v lo2 = half2v{(_Float16)fmaf(p0, (float)sz0[0], -(float)hi2[0]),
-                                  (_Float16)fmaf(p1, (float)sz1[0], -(float)hi2[1])};
+        const half2v lo2 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(fmaf(p0, (float)sz0[0], -(float)hi2[0]),
+                                                                                fmaf(p1, (float)sz1[0], -(float)hi2[1])));
         whi[g][i] = __builtin_bit_cast(uint32_t, hi2);
         wlo[g][i] = __builtin_bit_cast(uint32_t, lo2);
       }
