@@ -19,6 +19,7 @@
 // The extend and cascade kernels, whose blocks serve query heads of many rows,
 // read q' from records a separate rotate_q launch stores.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -724,6 +725,189 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
   }
 }
 
+// ---------------------------------------------------------------------------
+// Column layout of the INT2 page math for 5..8 query heads per KV head.  The 16 MFMA
+// columns are (head, limb): column n is head n % 8 with limb n / 8 of q' in the logit
+// MFMAs and limb n / 8 of the value weights in the value MFMAs, so no column holds zeros:
+// a page takes 4 logit MFMAs and a pair 8 value MFMAs for all the heads, half of what two
+// quads of the decode layout take.  Lane (n, r) gets tokens 4r .. 4r + 3 of its head: the
+// lanes n and n ^ 8 add their limbs' partial logits (one rotation of the 16-lane row by 8)
+// and then hold the same logits, softmax state and zero-point sums; lane n's value weights
+// are limb n / 8 of c_i p s_g (hi = fp16 rounded toward zero, lo = the rest), so the head's
+// output is the sum of the two limb lanes' accumulators, taken once at the end.
+// ---------------------------------------------------------------------------
+struct ColLane {
+  int r, hc, limb;
+  uint32_t lmask;   // all ones on the lo-limb lanes (n >= 8)
+  int off_kc, off_vw;
+  uint32_t perm_sel;
+  PairConsts pk;
+  ValueMasks<true> vm;
+  float tau;
+  half8 qb[2][2];   // [group][half]: limb `limb` of q' of head hc, channels 32 (2g + half) + 8r ..
+  float cinit[2], qs[2];
+};
+struct ColState {
+  float m, hm[4], lsum[4], zs[2][4];   // hm[i] = log2 c_i - m; the lane's shares carry its c_i
+  f32x4 acc[8];                        // tile t: channels 16t + 4r + i of column n
+};
+
+__device__ __forceinline__ void col_lane_init(ColLane& L, int lane, float tau) {
+  const int n = lane & 15;
+  L.r = lane >> 4;
+  L.hc = n & 7;
+  L.limb = n >> 3;
+  L.lmask = L.limb ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(L.lmask));
+  L.off_kc = kKCodes + 32 * n + 4 * L.r;   // token n: code word r of group 0 (+16: group 1)
+  L.off_vw = kVCodes + 4 * n;              // value code word of channel 16t + n at + 64t
+  L.perm_sel = (uint32_t)L.r | (0x0Cu << 8) | ((4u + L.r) << 16) | (0x0Cu << 24);
+  L.tau = tau;
+}
+
+__device__ __forceinline__ void col_state_init(ColState& st) {
+  st.m = 0.f;   // set by the first pair, which always takes the rescale branch
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.hm[i] = 3.f - 2.f * i;
+    st.lsum[i] = st.zs[0][i] = st.zs[1][i] = 0.f;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <bool kOne>
+__device__ __forceinline__ void col_pair(ColState& st, const ColLane& L, const uint8_t* blk0, const uint8_t* blk1,
+                                         bool has1, int pp, int i_hi, bool first) {
+  const uint8_t* blk[2] = {blk0, blk1};   // without page pp + 1 its block holds stale bytes
+  uint32_t kc[2][2];
+  uint32_t kp[2][4][2];   // [page][i][group]: key (s, z) of token 4r + i
+  uint32_t vp[2][4][2];   // [page][i][group]: value (s, z) of token 4r + i
+  uint32_t vw[2][8];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint8_t* bk = blk[k];
+    kc[k][0] = *reinterpret_cast<const uint32_t*>(bk + L.off_kc);
+    kc[k][1] = *reinterpret_cast<const uint32_t*>(bk + L.off_kc + 16);
+    if constexpr (kOne) {   // one (s, z) per token serves both groups
+      const uint4 kq = *reinterpret_cast<const uint4*>(bk + kKParams + 16 * L.r);
+      const uint4 vq = *reinterpret_cast<const uint4*>(bk + kVParams128 + 16 * L.r);
+      const uint32_t kk[4] = {kq.x, kq.y, kq.z, kq.w}, vv[4] = {vq.x, vq.y, vq.z, vq.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kp[k][i][0] = kp[k][i][1] = kk[i];
+        vp[k][i][0] = vp[k][i][1] = vv[i];
+      }
+    } else {
+      const uint4 ka = *reinterpret_cast<const uint4*>(bk + kKParams + 32 * L.r);
+      const uint4 kb = *reinterpret_cast<const uint4*>(bk + kKParams + 32 * L.r + 16);
+      const uint4 va = *reinterpret_cast<const uint4*>(bk + kVParams + 32 * L.r);
+      const uint4 vb = *reinterpret_cast<const uint4*>(bk + kVParams + 32 * L.r + 16);
+      const uint32_t kk[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+      const uint32_t vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          kp[k][i][g] = kk[2 * i + g];
+          vp[k][i][g] = vv[2 * i + g];
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) vw[k][t] = *reinterpret_cast<const uint32_t*>(bk + L.off_vw + 64 * t);
+  }
+  // ---- logits: lane (n, r) ends with tokens 4r + i of head n % 8 ----
+  f32x4 dq[2][2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    uint32_t e0[8], e1[8];
+    unpack16(kc[k][0], e0, L.pk);
+    unpack16(kc[k][1], e1, L.pk);
+    const half8 a00 = half8_of(e0[0], e0[1], e0[2], e0[3]), a01 = half8_of(e0[4], e0[5], e0[6], e0[7]);
+    const half8 a10 = half8_of(e1[0], e1[1], e1[2], e1[3]), a11 = half8_of(e1[4], e1[5], e1[6], e1[7]);
+    f32x4 d0 = f32x4{L.cinit[0], L.cinit[0], L.cinit[0], L.cinit[0]};
+    f32x4 d1 = f32x4{L.cinit[1], L.cinit[1], L.cinit[1], L.cinit[1]};
+    d0 = mfma16(a00, L.qb[0][0], d0);
+    d1 = mfma16(a10, L.qb[1][0], d1);
+    d0 = mfma16(a01, L.qb[0][1], d0);
+    d1 = mfma16(a11, L.qb[1][1], d1);
+    dq[k][0] = d0;
+    dq[k][1] = d1;
+  }
+  float lg[2][4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // the other limb of the same head sits in lane n ^ 8
+      const float y0 = dq[k][0][i] + dpp<kRowRor8>(dq[k][0][i]), y1 = dq[k][1][i] + dpp<kRowRor8>(dq[k][1][i]);
+      float x = fmaf(f16_bits_to_f32(kp[k][i][1] >> 16), L.qs[1], st.hm[i]);
+      x = fmaf(f16_bits_to_f32(kp[k][i][0] >> 16), L.qs[0], x);
+      x = fmaf(f16_bits_to_f32(kp[k][i][1]), y1, x);
+      lg[k][i] = fmaf(f16_bits_to_f32(kp[k][i][0]), y0, x);
+    }
+  if (!has1 || (pp + 2) * kPage > i_hi) {   // wave-uniform: only the last pair can hold missing tokens
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (k == 0 || has1) && (pp + k) * kPage + 4 * L.r + i < i_hi;
+        lg[k][i] = ok ? lg[k][i] : -INFINITY;
+        // slots at or past the sequence length were never written: s = z = 0 there
+        vp[k][i][0] = ok ? vp[k][i][0] : 0u;
+        vp[k][i][1] = ok ? vp[k][i][1] : 0u;
+      }
+  }
+  // ---- online softmax of the head (its 4 row lanes hold the pair's 32 tokens); rescale
+  // only when the maximum grows by more than tau ----
+  float pm = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
+                   fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
+  if (__any(first || pm > L.tau)) {
+    pm = rows_max(pm);   // finite: every pair has a valid token
+    const float dm = first || pm > L.tau ? pm : 0.f;
+    const float al = fast_exp2(-dm);
+    st.m += dm;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st.hm[i] -= dm;
+      lg[0][i] -= dm;
+      lg[1][i] -= dm;
+      st.lsum[i] *= al;
+      st.zs[0][i] *= al;
+      st.zs[1][i] *= al;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.acc[t] *= al;
+  }
+  // ---- value weights: dword i of group g = limb `limb` of c_i p s_g of token 4r + i in
+  // page 0 (low half) and page 1 (high half) ----
+  uint32_t w[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p0 = fast_exp2(lg[0][i]), p1 = fast_exp2(lg[1][i]);
+    st.lsum[i] += p0 + p1;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const half2v sz0 = __builtin_bit_cast(half2v, vp[0][i][g]), sz1 = __builtin_bit_cast(half2v, vp[1][i][g]);
+      st.zs[g][i] = fmaf(p0, (float)sz0[1], fmaf(p1, (float)sz1[1], st.zs[g][i]));
+      const float ps0 = fmaf(p0, (float)sz0[0], 0.f), ps1 = fmaf(p1, (float)sz1[0], 0.f);
+      // hi on the hi-limb lanes; on the lo-limb lanes hi is subtracted first, leaving lo
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ps0, ps1)) & L.lmask;
+      const half2v hs = __builtin_bit_cast(half2v, hi);
+      w[g][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(p0, (float)sz0[0], -(float)hs[0]),
+                                                                        fmaf(p1, (float)sz1[0], -(float)hs[1])));
+    }
+  }
+  const half8 bw[2] = {half8_of(w[0][0], w[0][1], w[0][2], w[0][3]), half8_of(w[1][0], w[1][1], w[1][2], w[1][3])};
+  // ---- values: A = the masked subnormal codes of channels 16t + row, B = the weights ----
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t x = __builtin_amdgcn_perm(vw[1][t], vw[0][t], L.perm_sel);
+    const half8 av = half8_of(x & L.vm.m[0], x & L.vm.m[1], x & L.vm.m[2], x & L.vm.m[3]);
+    st.acc[t] = mfma16(av, bw[t >> 2], st.acc[t]);
+  }
+}
+
 // INT2 history pages [first, end), two pages (32 tokens) per step; wave w
 // takes the pairs starting at first + 2w, + 8, ...  The G query heads are
 // handled in quads (NQ = ceil(G / 4)); lane l: n = l % 16, r = l / 16, and
@@ -757,10 +941,12 @@ template <int G, bool kOne>
 __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int first, int end, int i_hi,
                           SplitSmem& sm) {
   constexpr int NQ = (G + 3) / 4;
+  constexpr bool kCols = G > 4;   // (head, limb) columns; quads of heads otherwise
   i_hi = __builtin_amdgcn_readfirstlane(i_hi);   // block-uniform: keeps the tail test a scalar branch
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, r = lane >> 4;
   const int hh = n >> 2, a4 = n & 3, gp = a4 & 1, limb = a4 >> 1;
+  const int hc = n & 7, climb = n >> 3;   // column layout: head and limb of column n
 
   // The wave's pages: j -> first + 8 (j / 2) + 2 wave + (j % 2).
   const int base0 = first + 2 * wave;
@@ -782,13 +968,17 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
       pid_raw[k] = ptab[n_w > 0 ? page_of(min(j, n_w - 1)) : first];
     }
   }
-  Int2Lane<NQ> ln;
-  int2_lane_init<NQ, kOne>(ln, lane, a.resc_thr);
   // zs[g]: per-head zero-point sum of group g's channels, sum over tokens of p z_g; m:
-  // running reference maximum of the head's logits, which are formed relative to it (each
-  // of the two group terms carries -m / 2)
-  Int2State<NQ> st;
-  int2_state_init(st);
+  // running reference maximum of the head's logits, which are formed relative to it
+  std::conditional_t<kCols, ColLane, Int2Lane<NQ>> ln;
+  std::conditional_t<kCols, ColState, Int2State<NQ>> st;
+  if constexpr (kCols) {
+    col_lane_init(ln, lane, a.resc_thr);
+    col_state_init(st);
+  } else {
+    int2_lane_init<NQ, kOne>(ln, lane, a.resc_thr);
+    int2_state_init(st);
+  }
   // ---- page blocks stream through a per-wave LDS ring (direct global->LDS loads) ----
   // this lane's bytes of a page block: 16 at 16 lane, then 4 at 1024 + 4 lane (a 1152-byte
   // block's last 128 bytes are read twice, the copy landing past it in the 1280-byte slot)
@@ -852,26 +1042,74 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     block_lds_barrier();
     qrot_finish(a, qv);
     block_lds_barrier();
-    // B fragments of column n: head 4 qd + hh, group gp, limb; zero on the other group
-    // and beyond G
+    if constexpr (kCols) {
+      // B fragments of column n: limb climb of head hc, both groups; zero beyond G
+      const bool ok = hc < G;
+      const int hs = ok ? hc : 0;
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) {
-      const int head = 4 * qd + hh;
-      const bool ok = head < G;
-      const int hs = ok ? head : 0;
+      for (int g = 0; g < 2; ++g) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const uint4 f = make_uint4(qrot_frag_dword(qv, hs, gp, kh, limb, r, 0), qrot_frag_dword(qv, hs, gp, kh, limb, r, 1),
-                                   qrot_frag_dword(qv, hs, gp, kh, limb, r, 2), qrot_frag_dword(qv, hs, gp, kh, limb, r, 3));
-#pragma unroll
-        for (int g = 0; g < 2; ++g) ln.qb[qd][g][kh] = half8_of(ok && g == gp ? f : make_uint4(0, 0, 0, 0));
+        for (int kh = 0; kh < 2; ++kh) {
+          const uint4 f = make_uint4(qrot_frag_dword(qv, hs, g, kh, climb, r, 0), qrot_frag_dword(qv, hs, g, kh, climb, r, 1),
+                                     qrot_frag_dword(qv, hs, g, kh, climb, r, 2), qrot_frag_dword(qv, hs, g, kh, climb, r, 3));
+          ln.qb[g][kh] = half8_of(ok ? f : make_uint4(0, 0, 0, 0));
+        }
+        ln.cinit[g] = ok ? qv.negc[hs][g][climb] : 0.f;
+        ln.qs[g] = ok ? qv.qsum[hs][g] : 0.f;
       }
-      ln.cinit[qd] = ok ? qv.negc[hs][gp][limb] : 0.f;
-      ln.qs[qd] = ok ? qv.qsum[hs][gp] : 0.f;
+    } else {
+      // B fragments of column n: head 4 qd + hh, group gp, limb; zero on the other group
+      // and beyond G
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        const int head = 4 * qd + hh;
+        const bool ok = head < G;
+        const int hs = ok ? head : 0;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const uint4 f = make_uint4(qrot_frag_dword(qv, hs, gp, kh, limb, r, 0), qrot_frag_dword(qv, hs, gp, kh, limb, r, 1),
+                                     qrot_frag_dword(qv, hs, gp, kh, limb, r, 2), qrot_frag_dword(qv, hs, gp, kh, limb, r, 3));
+#pragma unroll
+          for (int g = 0; g < 2; ++g) ln.qb[qd][g][kh] = half8_of(ok && g == gp ? f : make_uint4(0, 0, 0, 0));
+        }
+        ln.cinit[qd] = ok ? qv.negc[hs][gp][limb] : 0.f;
+        ln.qs[qd] = ok ? qv.qsum[hs][gp] : 0.f;
+      }
     }
     block_lds_barrier();   // every wave holds its fragments: slots 4..7 are free
     zero_vparams(false, true);
     for (int j = 4; j < kRing - 2 && j < n_w; ++j) issue(unit_reg, j, j);
+  } else if constexpr (kCols) {
+    // ---- the q' fragments of column n from the stored record (limb climb of head hc, both
+    // groups; zero beyond G), loaded with the page ids ----
+    const bool ok = hc < G;
+    const QrotRecord* rec = a.qrot + ((size_t)b * a.Hq + h * G + (ok ? hc : 0));
+    uint4 qraw[2][2];
+    float craw[2], sraw[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) qraw[g][kh] = *reinterpret_cast<const uint4*>(&rec->frag[g][kh][climb][r][0]);
+      craw[g] = rec->negc[g][climb];
+      sraw[g] = rec->qsum[g];
+    }
+    // consume them all here: no wait for them may land inside the page loop
+#pragma unroll
+    for (int k = 0; k < kIdRegs; ++k) asm volatile("" : "+v"(pid_raw[k]));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        asm volatile("" : "+v"(qraw[g][kh].x), "+v"(qraw[g][kh].y), "+v"(qraw[g][kh].z), "+v"(qraw[g][kh].w));
+        ln.qb[g][kh] = half8_of(ok ? qraw[g][kh] : make_uint4(0, 0, 0, 0));
+      }
+      asm volatile("" : "+v"(craw[g]), "+v"(sraw[g]));
+      ln.cinit[g] = ok ? craw[g] : 0.f;
+      ln.qs[g] = ok ? sraw[g] : 0.f;
+    }
+    unit_offsets(unit_reg);
+    zero_vparams(true, true);
+    for (int j = 0; j < kRing - 2 && j < n_w; ++j) issue(unit_reg, j, j);
   } else {
     // ---- the q' fragments of column n from the stored records (head 4 qd + hh, group gp,
     // limb; zero beyond G), loaded with the page ids ----
@@ -934,33 +1172,70 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    int2_pair<NQ, kOne>(st, ln, &sm.ring[wave][2 * u][0], &sm.ring[wave][2 * u + 1][0], has1, pp, i_hi, j == 0);
+    if constexpr (kCols)
+      col_pair<kOne>(st, ln, &sm.ring[wave][2 * u][0], &sm.ring[wave][2 * u + 1][0], has1, pp, i_hi, j == 0);
+    else
+      int2_pair<NQ, kOne>(st, ln, &sm.ring[wave][2 * u][0], &sm.ring[wave][2 * u + 1][0], has1, pp, i_hi, j == 0);
   }
 
   // ---- finish the wave: its result goes to its own ring (all of its page loads have landed) ----
   WaveResult& res = wave_result(sm, wave);
+  if constexpr (kCols) {
+    // per-head totals over the 4 row lanes (the limb lanes n and n ^ 8 hold the same shares,
+    // which carry c_i; the accumulators 2^-21 and one limb each)
+    float L_h = 0.f, Z0 = 0.f, Z1 = 0.f;
 #pragma unroll
-  for (int qd = 0; qd < NQ; ++qd) {
-    // per-head totals over the 16 lanes of head hh (quad, then rows)
-    // (the lane's shares carry its c; the accumulators 2^-21)
-    const float ic = inv_c();
-    float L_h = st.lsum[qd] * ic, Z0 = st.zs[qd][0] * ic, Z1 = st.zs[qd][1] * ic;
-    L_h = rows_sum(quad_sum(L_h));
-    Z0 = rows_sum(quad_sum(Z0));
-    Z1 = rows_sum(quad_sum(Z1));
-    const int head = 4 * qd + hh;
-    if (r == 0 && a4 == 0 && head < G) {
-      res.m[head] = n_w > 0 ? st.m[qd] : -INFINITY;   // a wave without pages contributes nothing
-      res.l[head] = L_h;
+    for (int i = 0; i < 4; ++i) {
+      const float ic = __builtin_amdgcn_ldexpf(1.f, 2 * i - 3);
+      L_h = fmaf(st.lsum[i], ic, L_h);
+      Z0 = fmaf(st.zs[0][i], ic, Z0);
+      Z1 = fmaf(st.zs[1][i], ic, Z1);
     }
-    // accumulator rows of this lane: head 4 qd + r, subsets j = 0..3
-    const float z0 = __shfl(Z0, 4 * r), z1 = __shfl(Z1, 4 * r);
-    const int row_head = 4 * qd + r;
-    if (row_head < G) {
+    L_h = rows_sum(L_h);
+    Z0 = rows_sum(Z0);
+    Z1 = rows_sum(Z1);
+    float o[8][4];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[t][i] = st.acc[t][i] + dpp<kRowRor8>(st.acc[t][i]);
+    if (climb == 0 && hc < G) {
+      if (r == 0) {
+        res.m[hc] = n_w > 0 ? st.m : -INFINITY;   // a wave without pages contributes nothing
+        res.l[hc] = L_h;
+      }
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float s = (st.acc[qd][t][0] + st.acc[qd][t][1]) + (st.acc[qd][t][2] + st.acc[qd][t][3]);
-        res.acc[row_head][16 * t + n] = fmaf(s, 0x1p21f, t < 4 ? z0 : z1);
+        const float z = t < 4 ? Z0 : Z1;
+        *reinterpret_cast<float4*>(&res.acc[hc][16 * t + 4 * r]) =
+            make_float4(fmaf(o[t][0], 0x1p21f, z), fmaf(o[t][1], 0x1p21f, z), fmaf(o[t][2], 0x1p21f, z),
+                        fmaf(o[t][3], 0x1p21f, z));
+      }
+    }
+  } else {
+  #pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      // per-head totals over the 16 lanes of head hh (quad, then rows)
+      // (the lane's shares carry its c; the accumulators 2^-21)
+      const float ic = inv_c();
+      float L_h = st.lsum[qd] * ic, Z0 = st.zs[qd][0] * ic, Z1 = st.zs[qd][1] * ic;
+      L_h = rows_sum(quad_sum(L_h));
+      Z0 = rows_sum(quad_sum(Z0));
+      Z1 = rows_sum(quad_sum(Z1));
+      const int head = 4 * qd + hh;
+      if (r == 0 && a4 == 0 && head < G) {
+        res.m[head] = n_w > 0 ? st.m[qd] : -INFINITY;   // a wave without pages contributes nothing
+        res.l[head] = L_h;
+      }
+      // accumulator rows of this lane: head 4 qd + r, subsets j = 0..3
+      const float z0 = __shfl(Z0, 4 * r), z1 = __shfl(Z1, 4 * r);
+      const int row_head = 4 * qd + r;
+      if (row_head < G) {
+  #pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float s = (st.acc[qd][t][0] + st.acc[qd][t][1]) + (st.acc[qd][t][2] + st.acc[qd][t][3]);
+          res.acc[row_head][16 * t + n] = fmaf(s, 0x1p21f, t < 4 ? z0 : z1);
+        }
       }
     }
   }
@@ -1363,7 +1638,7 @@ __device__ void cascade_block(const DecodeArgs& a, int w, SplitSmem& sm) {
 }
 
 template <int G, bool kOne>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 3))) void split_kernel(DecodeArgs a) {
   __shared__ SplitSmem sm;
   // 1D grid: every (sequence, KV head)'s INT2 ranges first, then all BF16 chunks, which are
   // short and fill the block slots the last INT2 ranges leave idle (measured 1.7% faster
