@@ -64,7 +64,7 @@ struct DecodeArgs {
   // cascade decode: groups of sequences (batch entries cu_groups[g] .. cu_groups[g+1] - 1, at
   // most max_group of them) share their first group_pages[g] INT2 pages.  The first n_cas
   // split blocks read each shared range once for all members' query heads (n_cqt tiles of
-  // 16 NQ heads) into records n_bsplit + n_split + k; cas_eff[b] is the number of shared
+  // 16 NQ heads, or of 64 for more than 4 heads per KV head) into records n_bsplit + n_split + k; cas_eff[b] is the number of shared
   // pages sequence b takes from its group (0: none), written by the query rotation.
   const int32_t *cu_groups, *group_pages;
   int32_t* cas_eff;
@@ -1616,10 +1616,13 @@ __device__ void flash_int2_range(const DecodeArgs& a, const int32_t* ptab, int h
 }
 
 // Cascade block w (< n_cas): shared range k of group g, KV head h, query tile qt, with the
-// pages of the group's first member's table row.
+// pages of the group's first member's table row.  5..8 query heads per KV head: tiles of
+// 64 query vectors in the MFMA columns (the flash layout, which fits the 3 waves per SIMD
+// of that split kernel); up to 4: 16 query heads in quads (which fit its 4 waves per SIMD).
 template <int G, bool kOne>
 __device__ void cascade_block(const DecodeArgs& a, int w, SplitSmem& sm) {
   constexpr int NQ = (G + 3) / 4;
+  constexpr bool kFlash = G > 4;
   const int qt = w % a.n_cqt;
   w /= a.n_cqt;
   const int k = w % a.n_sh;
@@ -1629,12 +1632,16 @@ __device__ void cascade_block(const DecodeArgs& a, int w, SplitSmem& sm) {
   cascade_group(a, g, m0, members, shared);
   const int first = a.sink / kPage + k * a.P;
   const int end = min(first + a.P, a.sink / kPage + shared);
-  const int e_block = 16 * NQ * qt;
+  const int e_block = (kFlash ? kExtTile : 16 * NQ) * qt;
   if (first >= end || e_block >= members * G) return;   // block-uniform
   static_assert(sizeof(sm.ring) >= 16 * kBlockBytes, "a 16-slot ring inside the split kernel's LDS");
-  mq_int2_range<G, NQ, 16, kOne>(a, a.page_table + (size_t)m0 * a.max_pages, h, first, end - first,
-                           (a.sink / kPage + shared) * kPage, m0, members * G, e_block, a.n_bsplit + a.n_split + k,
-                           reinterpret_cast<uint8_t(*)[kBlockBytes]>(&sm.ring[0][0][0]));
+  const int32_t* ptab = a.page_table + (size_t)m0 * a.max_pages;
+  uint8_t(*ring)[kBlockBytes] = reinterpret_cast<uint8_t(*)[kBlockBytes]>(&sm.ring[0][0][0]);
+  const int i_hi = (a.sink / kPage + shared) * kPage, rec = a.n_bsplit + a.n_split + k;
+  if constexpr (kFlash)
+    flash_int2_range<G, kOne>(a, ptab, h, first, end - first, i_hi, m0, members * G, e_block, rec, ring);
+  else
+    mq_int2_range<G, NQ, 16, kOne>(a, ptab, h, first, end - first, i_hi, m0, members * G, e_block, rec, ring);
 }
 
 template <int G, bool kOne>
@@ -2195,13 +2202,14 @@ DecodeArgs make_decode_args(const DecodeLaunch& L) {
   if (L.n_groups > 0 && L.plan.n_sh > 0) {   // cascade decode
     constexpr int kHeadsPerTile = 16;          // per NQ: a block's 4 waves x 4 NQ query heads
     const int nq = (a.G + 3) / 4;
+    const int tile = a.G > 4 ? kExtTile : kHeadsPerTile * nq;   // query vectors per cascade block
     a.cu_groups = L.cu_groups;
     a.group_pages = L.group_pages;
     a.cas_eff = reinterpret_cast<int32_t*>(L.workspace + L.plan.eff_off);
     a.n_groups = L.n_groups;
     a.max_group = L.max_group;
     a.n_sh = L.plan.n_sh;
-    a.n_cqt = (L.max_group * a.G + kHeadsPerTile * nq - 1) / (kHeadsPerTile * nq);
+    a.n_cqt = (L.max_group * a.G + tile - 1) / tile;
     a.n_cas = L.n_groups * a.H * a.n_sh * a.n_cqt;
   }
   return a;
