@@ -730,16 +730,18 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
 // columns are (head, limb): column n is head n % 8 with limb n / 8 of q' in the logit
 // MFMAs and limb n / 8 of the value weights in the value MFMAs, so no column holds zeros:
 // a page takes 4 logit MFMAs and a pair 8 value MFMAs for all the heads, half of what two
-// quads of the decode layout take.  Lane (n, r) gets tokens 4r .. 4r + 3 of its head: the
-// lanes n and n ^ 8 add their limbs' partial logits (one rotation of the 16-lane row by 8)
-// and then hold the same logits, softmax state and zero-point sums; lane n's value weights
-// are limb n / 8 of c_i p s_g (hi = fp16 rounded toward zero, lo = the rest), so the head's
-// output is the sum of the two limb lanes' accumulators, taken once at the end.
+// quads of the decode layout take.  Lane (n, r) holds rows 4r .. 4r + 3 (tokens) of its
+// column; of those, the lane "owns" tokens 4r + 2 limb + j (j = 0, 1): it adds the other
+// limb's partial logit of those tokens from lane n ^ 8 (a rotation of the 16-lane row by 8),
+// forms their logits, probabilities and zero-point sums, and takes the other two tokens'
+// probabilities from lane n ^ 8, which owns them.  Lane n's value weights are limb n / 8 of
+// c_i p s_g for all four tokens (hi = fp16 rounded toward zero, lo = the rest), so the
+// head's output is the sum of its two limb lanes' accumulators, taken once at the end.
 // ---------------------------------------------------------------------------
 struct ColLane {
   int r, hc, limb;
   uint32_t lmask;   // all ones on the lo-limb lanes (n >= 8)
-  int off_kc, off_vw;
+  int off_kc, off_vw, off_po;   // off_po: byte offset of the own tokens' parameters
   uint32_t perm_sel;
   PairConsts pk;
   ValueMasks<true> vm;
@@ -748,10 +750,13 @@ struct ColLane {
   float cinit[2], qs[2];
 };
 struct ColState {
-  float m, hm[4], lsum[4], zs[2][4];   // hm[i] = log2 c_i - m; the lane's shares carry its c_i
-  f32x4 acc[8];                        // tile t: channels 16t + 4r + i of column n
+  // own token slots j (token 4r + 2 limb + j): hm[j] = log2 c - m, the lane's shares of l and
+  // of the zero-point sums (carrying c)
+  float m, hm[2], lsum[2], zs[2][2];
+  f32x4 acc[8];   // tile t: channels 16t + 4r + i of column n
 };
 
+template <bool kOne>
 __device__ __forceinline__ void col_lane_init(ColLane& L, int lane, float tau) {
   const int n = lane & 15;
   L.r = lane >> 4;
@@ -761,16 +766,19 @@ __device__ __forceinline__ void col_lane_init(ColLane& L, int lane, float tau) {
   asm volatile("" : "+v"(L.lmask));
   L.off_kc = kKCodes + 32 * n + 4 * L.r;   // token n: code word r of group 0 (+16: group 1)
   L.off_vw = kVCodes + 4 * n;              // value code word of channel 16t + n at + 64t
+  // (s, z) words of tokens 4r + 2 limb and + 1: 8 bytes per token (one 4-byte word with one
+  // 128-channel group per token), K at kKParams + off_po, V at the V parameters + off_po
+  L.off_po = (kOne ? 4 : 8) * (4 * L.r + 2 * L.limb);
   L.perm_sel = (uint32_t)L.r | (0x0Cu << 8) | ((4u + L.r) << 16) | (0x0Cu << 24);
   L.tau = tau;
 }
 
-__device__ __forceinline__ void col_state_init(ColState& st) {
+__device__ __forceinline__ void col_state_init(ColState& st, int limb) {
   st.m = 0.f;   // set by the first pair, which always takes the rescale branch
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st.hm[i] = 3.f - 2.f * i;
-    st.lsum[i] = st.zs[0][i] = st.zs[1][i] = 0.f;
+  for (int j = 0; j < 2; ++j) {
+    st.hm[j] = (float)(3 - 4 * limb - 2 * j);   // log2 c of token slot 2 limb + j
+    st.lsum[j] = st.zs[0][j] = st.zs[1][j] = 0.f;
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -780,9 +788,11 @@ template <bool kOne>
 __device__ __forceinline__ void col_pair(ColState& st, const ColLane& L, const uint8_t* blk0, const uint8_t* blk1,
                                          bool has1, int pp, int i_hi, bool first) {
   const uint8_t* blk[2] = {blk0, blk1};   // without page pp + 1 its block holds stale bytes
+  constexpr int kVp = kOne ? kVParams128 : kVParams;
   uint32_t kc[2][2];
-  uint32_t kp[2][4][2];   // [page][i][group]: key (s, z) of token 4r + i
-  uint32_t vp[2][4][2];   // [page][i][group]: value (s, z) of token 4r + i
+  uint32_t kpo[2][2][2];   // [page][j][group]: key (s, z) of own token j
+  uint32_t vpo[2][2][2];   // [page][j][group]: value (s, z) of own token j
+  uint32_t vp[2][4][2];    // [page][i][group]: value (s, z) of token 4r + i
   uint32_t vw[2][8];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -790,33 +800,39 @@ __device__ __forceinline__ void col_pair(ColState& st, const ColLane& L, const u
     kc[k][0] = *reinterpret_cast<const uint32_t*>(bk + L.off_kc);
     kc[k][1] = *reinterpret_cast<const uint32_t*>(bk + L.off_kc + 16);
     if constexpr (kOne) {   // one (s, z) per token serves both groups
-      const uint4 kq = *reinterpret_cast<const uint4*>(bk + kKParams + 16 * L.r);
-      const uint4 vq = *reinterpret_cast<const uint4*>(bk + kVParams128 + 16 * L.r);
-      const uint32_t kk[4] = {kq.x, kq.y, kq.z, kq.w}, vv[4] = {vq.x, vq.y, vq.z, vq.w};
+      const uint2 ko = *reinterpret_cast<const uint2*>(bk + kKParams + L.off_po);
+      const uint2 vo = *reinterpret_cast<const uint2*>(bk + kVp + L.off_po);
+      const uint4 vq = *reinterpret_cast<const uint4*>(bk + kVp + 16 * L.r);
+      const uint32_t vv[4] = {vq.x, vq.y, vq.z, vq.w};
+      kpo[k][0][0] = kpo[k][0][1] = ko.x;
+      kpo[k][1][0] = kpo[k][1][1] = ko.y;
+      vpo[k][0][0] = vpo[k][0][1] = vo.x;
+      vpo[k][1][0] = vpo[k][1][1] = vo.y;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kp[k][i][0] = kp[k][i][1] = kk[i];
-        vp[k][i][0] = vp[k][i][1] = vv[i];
-      }
+      for (int i = 0; i < 4; ++i) vp[k][i][0] = vp[k][i][1] = vv[i];
     } else {
-      const uint4 ka = *reinterpret_cast<const uint4*>(bk + kKParams + 32 * L.r);
-      const uint4 kb = *reinterpret_cast<const uint4*>(bk + kKParams + 32 * L.r + 16);
-      const uint4 va = *reinterpret_cast<const uint4*>(bk + kVParams + 32 * L.r);
-      const uint4 vb = *reinterpret_cast<const uint4*>(bk + kVParams + 32 * L.r + 16);
-      const uint32_t kk[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+      const uint4 ko = *reinterpret_cast<const uint4*>(bk + kKParams + L.off_po);
+      const uint4 vo = *reinterpret_cast<const uint4*>(bk + kVp + L.off_po);
+      const uint4 va = *reinterpret_cast<const uint4*>(bk + kVp + 32 * L.r);
+      const uint4 vb = *reinterpret_cast<const uint4*>(bk + kVp + 32 * L.r + 16);
+      kpo[k][0][0] = ko.x;
+      kpo[k][0][1] = ko.y;
+      kpo[k][1][0] = ko.z;
+      kpo[k][1][1] = ko.w;
+      vpo[k][0][0] = vo.x;
+      vpo[k][0][1] = vo.y;
+      vpo[k][1][0] = vo.z;
+      vpo[k][1][1] = vo.w;
       const uint32_t vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          kp[k][i][g] = kk[2 * i + g];
-          vp[k][i][g] = vv[2 * i + g];
-        }
+        for (int g = 0; g < 2; ++g) vp[k][i][g] = vv[2 * i + g];
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) vw[k][t] = *reinterpret_cast<const uint32_t*>(bk + L.off_vw + 64 * t);
   }
-  // ---- logits: lane (n, r) ends with tokens 4r + i of head n % 8 ----
+  // ---- logits of the own tokens of both pages ----
   f32x4 dq[2][2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -834,62 +850,92 @@ __device__ __forceinline__ void col_pair(ColState& st, const ColLane& L, const u
     dq[k][0] = d0;
     dq[k][1] = d1;
   }
-  float lg[2][4];
+  // (the lane's limb as an opaque mask: two-way selects, not an element index)
+  const bool lo_lane = L.lmask != 0u;
+  float lg[2][2];   // [page][j]
 #pragma unroll
   for (int k = 0; k < 2; ++k)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // the other limb of the same head sits in lane n ^ 8
-      const float y0 = dq[k][0][i] + dpp<kRowRor8>(dq[k][0][i]), y1 = dq[k][1][i] + dpp<kRowRor8>(dq[k][1][i]);
-      float x = fmaf(f16_bits_to_f32(kp[k][i][1] >> 16), L.qs[1], st.hm[i]);
-      x = fmaf(f16_bits_to_f32(kp[k][i][0] >> 16), L.qs[0], x);
-      x = fmaf(f16_bits_to_f32(kp[k][i][1]), y1, x);
-      lg[k][i] = fmaf(f16_bits_to_f32(kp[k][i][0]), y0, x);
+    for (int j = 0; j < 2; ++j) {
+      float y[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        // lane n ^ 8 holds the other limb; it owns the other two tokens
+        const float a = dq[k][g][j], b = dq[k][g][2 + j];
+        const float snd = lo_lane ? a : b, own = lo_lane ? b : a;
+        y[g] = own + dpp<kRowRor8>(snd);
+      }
+      float x = fmaf(f16_bits_to_f32(kpo[k][j][1] >> 16), L.qs[1], st.hm[j]);
+      x = fmaf(f16_bits_to_f32(kpo[k][j][0] >> 16), L.qs[0], x);
+      x = fmaf(f16_bits_to_f32(kpo[k][j][1]), y[1], x);
+      lg[k][j] = fmaf(f16_bits_to_f32(kpo[k][j][0]), y[0], x);
     }
   if (!has1 || (pp + 2) * kPage > i_hi) {   // wave-uniform: only the last pair can hold missing tokens
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 2; ++k) {
+      const bool page_ok = k == 0 || has1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool ok = page_ok && (pp + k) * kPage + 4 * L.r + 2 * L.limb + j < i_hi;
+        lg[k][j] = ok ? lg[k][j] : -INFINITY;
+        vpo[k][j][0] = ok ? vpo[k][j][0] : 0u;
+        vpo[k][j][1] = ok ? vpo[k][j][1] : 0u;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = (k == 0 || has1) && (pp + k) * kPage + 4 * L.r + i < i_hi;
-        lg[k][i] = ok ? lg[k][i] : -INFINITY;
         // slots at or past the sequence length were never written: s = z = 0 there
+        const bool ok = page_ok && (pp + k) * kPage + 4 * L.r + i < i_hi;
         vp[k][i][0] = ok ? vp[k][i][0] : 0u;
         vp[k][i][1] = ok ? vp[k][i][1] : 0u;
       }
+    }
   }
-  // ---- online softmax of the head (its 4 row lanes hold the pair's 32 tokens); rescale
-  // only when the maximum grows by more than tau ----
-  float pm = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
-                   fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
+  // ---- online softmax of the head (its 8 lanes hold the pair's 32 tokens); rescale only
+  // when the maximum grows by more than tau ----
+  float pm = fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[1][0], lg[1][1]));
   if (__any(first || pm > L.tau)) {
-    pm = rows_max(pm);   // finite: every pair has a valid token
+    pm = rows_max(fmaxf(pm, dpp<kRowRor8>(pm)));   // finite: every pair has a valid token
     const float dm = first || pm > L.tau ? pm : 0.f;
     const float al = fast_exp2(-dm);
     st.m += dm;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st.hm[i] -= dm;
-      lg[0][i] -= dm;
-      lg[1][i] -= dm;
-      st.lsum[i] *= al;
-      st.zs[0][i] *= al;
-      st.zs[1][i] *= al;
+    for (int j = 0; j < 2; ++j) {
+      st.hm[j] -= dm;
+      lg[0][j] -= dm;
+      lg[1][j] -= dm;
+      st.lsum[j] *= al;
+      st.zs[0][j] *= al;
+      st.zs[1][j] *= al;
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.acc[t] *= al;
+  }
+  // ---- probabilities: own tokens here, the other two from lane n ^ 8 ----
+  float pa[2][4];   // [page][i]: c_i p of token 4r + i
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float p0 = fast_exp2(lg[0][j]), p1 = fast_exp2(lg[1][j]);
+    st.lsum[j] += p0 + p1;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const half2v z0 = __builtin_bit_cast(half2v, vpo[0][j][g]), z1 = __builtin_bit_cast(half2v, vpo[1][j][g]);
+      st.zs[g][j] = fmaf(p0, (float)z0[1], fmaf(p1, (float)z1[1], st.zs[g][j]));
+    }
+    const float q0 = dpp<kRowRor8>(p0), q1 = dpp<kRowRor8>(p1);
+    pa[0][j] = lo_lane ? q0 : p0;
+    pa[1][j] = lo_lane ? q1 : p1;
+    pa[0][2 + j] = lo_lane ? p0 : q0;
+    pa[1][2 + j] = lo_lane ? p1 : q1;
   }
   // ---- value weights: dword i of group g = limb `limb` of c_i p s_g of token 4r + i in
   // page 0 (low half) and page 1 (high half) ----
   uint32_t w[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float p0 = fast_exp2(lg[0][i]), p1 = fast_exp2(lg[1][i]);
-    st.lsum[i] += p0 + p1;
+    const float p0 = pa[0][i], p1 = pa[1][i];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const half2v sz0 = __builtin_bit_cast(half2v, vp[0][i][g]), sz1 = __builtin_bit_cast(half2v, vp[1][i][g]);
-      st.zs[g][i] = fmaf(p0, (float)sz0[1], fmaf(p1, (float)sz1[1], st.zs[g][i]));
       const float ps0 = fmaf(p0, (float)sz0[0], 0.f), ps1 = fmaf(p1, (float)sz1[0], 0.f);
       // hi on the hi-limb lanes; on the lo-limb lanes hi is subtracted first, leaving lo
       const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ps0, ps1)) & L.lmask;
@@ -973,8 +1019,8 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   std::conditional_t<kCols, ColLane, Int2Lane<NQ>> ln;
   std::conditional_t<kCols, ColState, Int2State<NQ>> st;
   if constexpr (kCols) {
-    col_lane_init(ln, lane, a.resc_thr);
-    col_state_init(st);
+    col_lane_init<kOne>(ln, lane, a.resc_thr);
+    col_state_init(st, climb);
   } else {
     int2_lane_init<NQ, kOne>(ln, lane, a.resc_thr);
     int2_state_init(st);
@@ -1181,19 +1227,19 @@ __device__ void int2_item(const DecodeArgs& a, int b, int h, int split, int firs
   // ---- finish the wave: its result goes to its own ring (all of its page loads have landed) ----
   WaveResult& res = wave_result(sm, wave);
   if constexpr (kCols) {
-    // per-head totals over the 4 row lanes (the limb lanes n and n ^ 8 hold the same shares,
-    // which carry c_i; the accumulators 2^-21 and one limb each)
+    // per-head totals over the head's 8 lanes (4 rows x the two limb lanes, each holding the
+    // shares of its own tokens, which carry c; the accumulators 2^-21 and one limb each)
     float L_h = 0.f, Z0 = 0.f, Z1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ic = __builtin_amdgcn_ldexpf(1.f, 2 * i - 3);
-      L_h = fmaf(st.lsum[i], ic, L_h);
-      Z0 = fmaf(st.zs[0][i], ic, Z0);
-      Z1 = fmaf(st.zs[1][i], ic, Z1);
+    for (int j = 0; j < 2; ++j) {
+      const float ic = __builtin_amdgcn_ldexpf(1.f, 4 * climb + 2 * j - 3);
+      L_h = fmaf(st.lsum[j], ic, L_h);
+      Z0 = fmaf(st.zs[0][j], ic, Z0);
+      Z1 = fmaf(st.zs[1][j], ic, Z1);
     }
-    L_h = rows_sum(L_h);
-    Z0 = rows_sum(Z0);
-    Z1 = rows_sum(Z1);
+    L_h = rows_sum(L_h + dpp<kRowRor8>(L_h));
+    Z0 = rows_sum(Z0 + dpp<kRowRor8>(Z0));
+    Z1 = rows_sum(Z1 + dpp<kRowRor8>(Z1));
     float o[8][4];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
