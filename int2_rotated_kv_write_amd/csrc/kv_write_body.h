@@ -124,6 +124,13 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
     return *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kUtRow + 32 * ks + 8 * q]);
   };
 
+  // V: post-rotation channel j = bitrev7(c) of register i in this lane after the
+  // Walsh-Hadamard without swaps back: c = r + 4 (lane bit 5 + 2 (i bit 3)) + 16 (i bit 2 +
+  // 2 (lane bit 4) + 4 (i bit 4)), r = i & 3
+  auto vj = [&](int i) {
+    return 64 * (i & 1) + 32 * ((i >> 1) & 1) + 16 * (q >> 1) + 8 * ((i >> 3) & 1) + 4 * ((i >> 2) & 1) + 2 * (q & 1) +
+           ((i >> 4) & 1);
+  };
   const float clip_s = a.clip[kind] * 11.313708498984761f;   // clip threshold before the 1/sqrt(128)
   uint16_t* sink_buf = a.sink[kind];
   uint16_t* ring_buf = a.ring[kind];
@@ -179,25 +186,47 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
     // cross-lane bits: channel bit 2 = lane bit 4, channel bit 3 = lane bit 5.  Registers
     // x = v[i], y = v[i ^ 8] go through a permlane swap, which leaves in each lane the
     // (bit-clear, bit-set) partner values of one of them; sum and difference are the
-    // butterfly outputs, and a second swap of (sum, difference) puts every result back
-    // in the lane and register it came from.
+    // butterfly outputs.  For K a second swap of (sum, difference) puts every result back
+    // in the lane and register it came from (the K codes are packed per lane).  V codes go
+    // through LDS, where any placement is free, so V keeps the results where they are: after
+    // both stages register bit 3 holds channel bit 3, lane bit 5 channel bit 2 and lane bit
+    // 4 channel bit 5 (see vj below), and the 32 swaps back are saved.
+    if (kind == 0) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i & 8) continue;
-      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
-      const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
-      r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
-      v[i] = __uint_as_float(r[0]);
-      v[i | 8] = __uint_as_float(r[1]);
-    }
+      for (int i = 0; i < 32; ++i) {
+        if (i & 8) continue;
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
+        const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
+        r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
+        v[i] = __uint_as_float(r[0]);
+        v[i | 8] = __uint_as_float(r[1]);
+      }
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i & 8) continue;
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
-      const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
-      r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
-      v[i] = __uint_as_float(r[0]);
-      v[i | 8] = __uint_as_float(r[1]);
+      for (int i = 0; i < 32; ++i) {
+        if (i & 8) continue;
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
+        const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
+        r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
+        v[i] = __uint_as_float(r[0]);
+        v[i | 8] = __uint_as_float(r[1]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i & 8) continue;
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
+        const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
+        v[i] = a0 + b0;
+        v[i | 8] = a0 - b0;
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i & 8) continue;
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
+        const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
+        v[i] = a0 + b0;
+        v[i | 8] = a0 - b0;
+      }
     }
 
     // ---- clip, group min/max (v holds the rotation times sqrt(128): the 1/sqrt(128)
@@ -271,11 +300,7 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
       // byte is the low byte of tq + 2^23 (adding 2^23 rounds to the nearest integer, ties
       // to even, exactly like rint).
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int mt = i >> 2, r = i & 3;
-        const int j = 64 * (r & 1) + 32 * (r >> 1) + 16 * (q & 1) + 8 * (q >> 1) + bitrev3(mt);
-        vbytes[wave][vrow(j)][n] = (uint8_t)__float_as_uint(tq[i] + 8388608.0f);
-      }
+      for (int i = 0; i < 32; ++i) vbytes[wave][vrow(vj(i))][n] = (uint8_t)__float_as_uint(tq[i] + 8388608.0f);
       wave_lds_sync();
       // every lane of the tile holds the same page: lane 0's id
       const uint8_t* page_blk = a.pages + ((size_t)__shfl(pid, 0) * a.num_heads + h) * a.block_bytes;
@@ -301,8 +326,7 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
       const uint32_t clear = ~(3u << (2 * slot));
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const int mt = i >> 2, r = i & 3;
-        const int j = 64 * (r & 1) + 32 * (r >> 1) + 16 * (q & 1) + 8 * (q >> 1) + bitrev3(mt);
+        const int j = vj(i);
         const uint32_t code = (uint32_t)__builtin_rintf(tq[i]);
         atomicAnd(&words[j], clear);
         if (code) atomicOr(&words[j], code << (2 * slot));
