@@ -665,7 +665,7 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
       pm = fmaxf(pm, dpp<kQuadXor2>(pm));
       pm = rows_max(pm);   // finite: every pair has a valid token
       const float dm = first || pm > L.tau ? pm : 0.f;
-      const float al = fast_exp2(-dm);
+      const float al = first ? 0.f : fast_exp2(-dm);   // the state is still zero: 0, not 2^-dm (may overflow)
       st.m[qd] += dm;
       st.hm[qd][0] = fmaf(-0.5f, st.m[qd], hoff(0));
       st.hm[qd][1] = fmaf(-0.5f, st.m[qd], hoff(1));
@@ -896,7 +896,7 @@ __device__ __forceinline__ void col_pair(ColState& st, const ColLane& L, const u
   if (__any(first || pm > L.tau)) {
     pm = rows_max(fmaxf(pm, dpp<kRowRor8>(pm)));   // finite: every pair has a valid token
     const float dm = first || pm > L.tau ? pm : 0.f;
-    const float al = fast_exp2(-dm);
+    const float al = first ? 0.f : fast_exp2(-dm);   // the state is still zero: 0, not 2^-dm (may overflow)
     st.m += dm;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -1587,7 +1587,7 @@ __device__ void flash_int2_range(const DecodeArgs& a, const int32_t* ptab, int h
     if (__any(j == 0 || pm > a.resc_thr)) {
       pm = rows_max(pm);   // finite: every pair has a valid token
       const float dm = j == 0 || pm > a.resc_thr ? pm : 0.f;
-      const float al = fast_exp2(-dm);
+      const float al = j == 0 ? 0.f : fast_exp2(-dm);   // the state is still zero: 0, not 2^-dm (may overflow)
       m += dm;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1996,38 +1996,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 
 // BF16 keys of a chunk query: the prefix's sink rows [0, min(sink, L)), its ring rows
 // [max(sink, L - recent), L) as stored, and the chunk's keys 0..i from the input (causal).
-// Block (sequence, KV head, group of 4 chunk positions); wave w takes position 4 ig + w and
-// all G query heads, 16 keys per round (lane: key lane / 4, channels 32 (lane % 4) ..; for
-// the values channels 2 lane, + 1), the next round's rows requested before this round's math.
+// Flash layout on MFMA: block (sequence, KV head, tile of kExtTile query vectors), 16 query
+// vectors per wave in the MFMA columns (query vector e = chunk position * G + head), 16 keys
+// per round:
+//   logits: D[key][query] = K[key] . q (4 v_mfma_f32_16x16x32_bf16, A = the key rows straight
+//     from global memory, B = the queries' bf16 rows); lane (n, r) gets keys 4r .. 4r + 3 of
+//     query n and masks those past the query's causal end;
+//   values: O^T[channel][query] += V^T[channel][key] P^T[key][query]
+//     (v_mfma_f32_16x16x16_bf16, B = the lane's own probabilities as bf16 hi + lo limbs, A =
+//     the round's V rows gathered from an LDS copy), so each lane's rows are its own query's
+//     channels 16t + 4r .. 4r + 3 and a rescale needs no exchange.
+// The next round's key and value rows are requested before this round's math.
+constexpr int kExtVRow = kHeadDim + 8;   // bf16 per LDS row of the value copy (padded)
+
 struct __attribute__((aligned(16))) ExtB16Smem {
-  uint4 q[4][kMaxGqa][kHeadDim / 8];
-  float p[4][kMaxGqa][16];
+  uint16_t v[4][16][kExtVRow];
 };
+
+__device__ __forceinline__ uint32_t bf16_hi_pair(float a, float b) {   // truncated bf16 of a (lo), b (hi)
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
 
 template <int G>
 __global__ __launch_bounds__(256) void ext_bf16_kernel(ExtArgs e) {
+  typedef short short4v __attribute__((ext_vector_type(4)));
   __shared__ ExtB16Smem sm;
   const DecodeArgs& a = e.d;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tt = lane >> 2, q4 = lane & 3;
-  const int n_ig = (e.max_chunk + 3) / 4;   // groups of 4 positions per (sequence, KV head)
+  const int n = lane & 15, r = lane >> 4;
   int job = blockIdx.x;
-  const int ig = job % n_ig;
-  job /= n_ig;
+  const int qt = job % e.n_qt;
+  job /= e.n_qt;
   const int h = job % a.H, b = job / a.H;
   int t0, chunk;
   chunk_of(e, b, t0, chunk);
   const int L = clamp_len(scalar_load_i32(e.prefix_lens, b), a.max_pages);
-  const int i = 4 * ig + wave;
-  if (i >= chunk) return;   // wave-uniform; nothing below synchronises the block
-  const int t = t0 + i;
-  if (h == 0 && lane == 0) e.row_len[t] = L;
+  const int n_e = chunk * G;
+  const int e_wave = kExtTile * qt + 16 * wave;
+  if (e_wave >= n_e) return;   // wave-uniform; nothing below synchronises the block
+  const int e_q = e_wave + n;
+  const bool q_ok = e_q < n_e;
+  const int i_q = q_ok ? e_q / G : 0, g_q = q_ok ? e_q % G : 0;
+  if (h == 0 && r == 0 && q_ok && g_q == 0) e.row_len[t0 + i_q] = L;
   const int ns = min(a.sink, L);
   const int r_lo = L > a.sink ? max(a.sink, L - a.recent) : L;
   const int nr = L - r_lo;
-  const int nk = ns + nr + i + 1;
-  const size_t head_row = (size_t)b * a.H + h;
   const int ring0 = a.recent > 0 ? r_lo % a.recent : 0;
+  const int nk_q = ns + nr + i_q + 1;   // keys of this lane's query (a padding column: 1 + ...)
+  const int nk = __builtin_amdgcn_readfirstlane(ns + nr + (min(e_wave + 15, n_e - 1) / G) + 1);   // wave's keys
+  const size_t head_row = (size_t)b * a.H + h;
   auto key_row = [&](int j, const uint16_t* sink_buf, const uint16_t* ring_buf, const uint16_t* chunk_buf) {
     if (j < ns) return sink_buf + (head_row * a.sink + j) * kHeadDim;
     if (j < ns + nr) {
@@ -2037,83 +2054,93 @@ __global__ __launch_bounds__(256) void ext_bf16_kernel(ExtArgs e) {
     }
     return chunk_buf + ((size_t)(t0 + j - ns - nr) * a.H + h) * kHeadDim;
   };
+  // this lane's query as B fragments (channels 32 ks + 8 r ..)
+  bf16x8 qf[4];
   {
-    const uint4* qg = reinterpret_cast<const uint4*>(a.q + ((size_t)t * a.Hq + h * G) * kHeadDim);
-    for (int x = lane; x < G * kHeadDim / 8; x += 64) (&sm.q[wave][0][0])[x] = qg[x];
-  }
-  float m[G], lsum[G], acc[G][2];
+    const uint16_t* qrow = a.q + ((size_t)(t0 + i_q) * a.Hq + h * G + g_q) * kHeadDim + 8 * r;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    lsum[g] = 0.f;
-    acc[g][0] = acc[g][1] = 0.f;
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   }
   struct RoundIn {
-    uint4 kd[4];
-    uint32_t vv[16];
+    uint4 k[4];   // key row jbase + n, channels 32 ks + 8 r ..
+    uint4 v[4];   // value row jbase + lane / 4, channels 32 (lane % 4) ..
   };
   auto load_round = [&](int jbase, RoundIn& in) {
-    const int j = jbase + tt;
-    const uint16_t* krow = key_row(min(j, nk - 1), a.k_sink, a.k_ring, e.k_new) + 32 * q4;
+    const uint16_t* krow = key_row(min(jbase + n, nk - 1), a.k_sink, a.k_ring, e.k_new) + 8 * r;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) in.kd[x] = reinterpret_cast<const uint4*>(krow)[x];
+    for (int ks = 0; ks < 4; ++ks) in.k[ks] = *reinterpret_cast<const uint4*>(krow + 32 * ks);
+    const uint16_t* vrow = key_row(min(jbase + (lane >> 2), nk - 1), a.v_sink, a.v_ring, e.v_new) + 32 * (lane & 3);
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      in.vv[u] = *reinterpret_cast<const uint32_t*>(key_row(min(jbase + u, nk - 1), a.v_sink, a.v_ring, e.v_new) +
-                                                    2 * lane);
+    for (int x = 0; x < 4; ++x) in.v[x] = *reinterpret_cast<const uint4*>(vrow + 8 * x);
   };
+  float m = 0.f, lsum = 0.f;   // m: reference maximum (set by the first round)
+  f32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t(*vs)[kExtVRow] = sm.v[wave];
   RoundIn nxt;
   load_round(0, nxt);
-  wave_lds_sync();   // the query rows are in LDS
   for (int jbase = 0; jbase < nk; jbase += 16) {
     const RoundIn cur = nxt;
     if (jbase + 16 < nk) load_round(jbase + 16, nxt);
-    const bool valid = jbase + tt < nk;
-    float lg[G];
+    // the round's value rows into this wave's LDS copy (the previous round's reads of it
+    // were issued before these writes, and LDS serves one wave's operations in order)
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float d = 0.f;
+    for (int x = 0; x < 4; ++x) *reinterpret_cast<uint4*>(&vs[lane >> 2][32 * (lane & 3) + 8 * x]) = cur.v[x];
+    // ---- logits of keys jbase + 4r + i for query n ----
+    f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const uint4 qd = sm.q[wave][g][4 * q4 + x];
-        d = dot2_bf16(qd.x, cur.kd[x].x, d);
-        d = dot2_bf16(qd.y, cur.kd[x].y, d);
-        d = dot2_bf16(qd.z, cur.kd[x].z, d);
-        d = dot2_bf16(qd.w, cur.kd[x].w, d);
-      }
-      d += __shfl_xor(d, 1);
-      d += __shfl_xor(d, 2);
-      lg[g] = valid ? d * a.sl2e : -INFINITY;
+    for (int ks = 0; ks < 4; ++ks)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[ks]), qf[ks], d, 0, 0, 0);
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = jbase + 4 * r + i;
+      x[i] = j < (q_ok ? nk_q : 1) ? fmaf(d[i], a.sl2e, -m) : -INFINITY;
     }
-    wave_lds_sync();   // the previous round's weights have been read
+    // ---- online softmax of query n; rescale only when the maximum grows by more than 8 ----
+    float pm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__any(jbase == 0 || pm > 8.f)) {
+      pm = rows_max(pm);   // finite: key 0 is valid for every query
+      const float dm = jbase == 0 || pm > 8.f ? pm : 0.f;
+      const float al = jbase == 0 ? 0.f : fast_exp2(-dm);   // the state is still zero: 0, not 2^-dm (may overflow)
+      m += dm;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m_new = fmaxf(m[g], wave_max_xor(lg[g], 4, 32));   // finite: the round has a key
-      const float al = exp2f(m[g] - m_new);
-      const float p = valid ? exp2f(lg[g] - m_new) : 0.f;
-      lsum[g] = lsum[g] * al + wave_sum_xor(p, 4, 32);
-      acc[g][0] *= al;
-      acc[g][1] *= al;
-      m[g] = m_new;
-      if (q4 == 0) sm.p[wave][g][tt] = p;
+      for (int i = 0; i < 4; ++i) x[i] -= dm;
+      lsum *= al;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= al;
     }
-    wave_lds_sync();
+    float p[4], lo[4];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const float v0 = bf16_bits_to_f32(cur.vv[u] & 0xFFFFu), v1 = bf16_bits_to_f32(cur.vv[u] >> 16);
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(x[i]);
+      lo[i] = p[i] - __uint_as_float(__float_as_uint(p[i]) & 0xFFFF0000u);
+    }
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    // B fragment: k = keys 4r .. 4r + 3 of query n, as truncated bf16 hi and lo limbs
+    const short4v bhi = __builtin_bit_cast(short4v, make_uint2(bf16_hi_pair(p[0], p[1]), bf16_hi_pair(p[2], p[3])));
+    const short4v blo = __builtin_bit_cast(short4v, make_uint2(bf16_hi_pair(lo[0], lo[1]), bf16_hi_pair(lo[2], lo[3])));
+    wave_lds_sync();   // the value rows are in LDS
+    // ---- values: A row = channel 16t + n, k = keys 4r .. 4r + 3 ----
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = sm.p[wave][g][u];   // 0 beyond the last key
-        acc[g][0] = fmaf(p, v0, acc[g][0]);
-        acc[g][1] = fmaf(p, v1, acc[g][1]);
-      }
+    for (int t = 0; t < 8; ++t) {
+      const int c = 16 * t + n;
+      const uint32_t w0 = (uint32_t)vs[4 * r][c] | ((uint32_t)vs[4 * r + 1][c] << 16);
+      const uint32_t w1 = (uint32_t)vs[4 * r + 2][c] | ((uint32_t)vs[4 * r + 3][c] << 16);
+      const short4v av = __builtin_bit_cast(short4v, make_uint2(w0, w1));
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bhi, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, blo, acc[t], 0, 0, 0);
     }
   }
+  // ---- record 0 of each query vector: (m, l) and the unnormalised sum ----
+  const float lq = rows_sum(lsum);
+  if (q_ok) {
+    const size_t rec = ((size_t)(t0 + i_q) * a.Hq + h * G + g_q) * a.n_total;   // record 0: the BF16 keys
+    if (r == 0) a.part_ml[rec] = make_float2(m, lq);
+    float* dst = a.part + rec * kHeadDim;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const size_t rec = ((size_t)t * a.Hq + h * G + g) * a.n_total;   // record 0: the BF16 keys
-    *reinterpret_cast<float2*>(a.part + rec * kHeadDim + 2 * lane) = make_float2(acc[g][0], acc[g][1]);
-    if (lane == 0) a.part_ml[rec] = make_float2(m[g], lsum[g]);
+    for (int t = 0; t < 8; ++t) *reinterpret_cast<float4*>(dst + 16 * t + 4 * r) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
   }
 }
 
@@ -2326,7 +2353,7 @@ void launch_extend_g(const ExtArgs& e, hipStream_t stream) {
     else
       hipLaunchKernelGGL((ext_int2_kernel<G, false>), grid, dim3(256), 0, stream, e);
   }
-  hipLaunchKernelGGL(ext_bf16_kernel<G>, dim3(e.n_seq * a.H * ((e.max_chunk + 3) / 4)), dim3(256), 0, stream, e);
+  hipLaunchKernelGGL(ext_bf16_kernel<G>, dim3(e.n_seq * a.H * e.n_qt), dim3(256), 0, stream, e);
   constexpr int GB = reduce_group<G>();
   hipLaunchKernelGGL((reduce_kernel<G, GB>), dim3(e.n_tok * a.H * (G / GB)), dim3(256), 0, stream, a);
 }
