@@ -740,7 +740,8 @@ __device__ __forceinline__ void int2_pair(Int2State<NQ>& st, const Int2Lane<NQ>&
 // ---------------------------------------------------------------------------
 struct ColLane {
   int r, hc, limb;
-  uint32_t lmask;   // all ones on the lo-limb lanes (n >= 8)
+  uint32_t lmask;     // all ones on the lo-limb lanes (n >= 8)
+  uint32_t lmask13;   // the sign, exponent and top 10 mantissa bits of an fp32 on the lo-limb lanes
   int off_kc, off_vw, off_po;   // off_po: byte offset of the own tokens' parameters
   uint32_t perm_sel;
   PairConsts pk;
@@ -763,7 +764,8 @@ __device__ __forceinline__ void col_lane_init(ColLane& L, int lane, float tau) {
   L.hc = n & 7;
   L.limb = n >> 3;
   L.lmask = L.limb ? 0xFFFFFFFFu : 0u;
-  asm volatile("" : "+v"(L.lmask));
+  L.lmask13 = L.limb ? 0xFFFFE000u : 0u;
+  asm volatile("" : "+v"(L.lmask), "+v"(L.lmask13));
   L.off_kc = kKCodes + 32 * n + 4 * L.r;   // token n: code word r of group 0 (+16: group 1)
   L.off_vw = kVCodes + 4 * n;              // value code word of channel 16t + n at + 64t
   // (s, z) words of tokens 4r + 2 limb and + 1: 8 bytes per token (one 4-byte word with one
@@ -937,11 +939,12 @@ __device__ __forceinline__ void col_pair(ColState& st, const ColLane& L, const u
     for (int g = 0; g < 2; ++g) {
       const half2v sz0 = __builtin_bit_cast(half2v, vp[0][i][g]), sz1 = __builtin_bit_cast(half2v, vp[1][i][g]);
       const float ps0 = fmaf(p0, (float)sz0[0], 0.f), ps1 = fmaf(p1, (float)sz1[0], 0.f);
-      // hi on the hi-limb lanes; on the lo-limb lanes hi is subtracted first, leaving lo
-      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ps0, ps1)) & L.lmask;
-      const half2v hs = __builtin_bit_cast(half2v, hi);
-      w[g][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fmaf(p0, (float)sz0[0], -(float)hs[0]),
-                                                                        fmaf(p1, (float)sz1[0], -(float)hs[1])));
+      // hi-limb lanes: fp16(ps) rounded toward zero.  lo-limb lanes: ps less ps with its low 13
+      // mantissa bits cleared (exact), i.e. less the hi lane's fp16 -- the same value wherever ps
+      // is in fp16's normal range; below it the two differ by under 2^-24
+      const float t0 = ps0 - __uint_as_float(__float_as_uint(ps0) & L.lmask13);
+      const float t1 = ps1 - __uint_as_float(__float_as_uint(ps1) & L.lmask13);
+      w[g][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(t0, t1));
     }
   }
   const half8 bw[2] = {half8_of(w[0][0], w[0][1], w[0][2], w[0][3]), half8_of(w[1][0], w[1][1], w[1][2], w[1][3])};
