@@ -124,7 +124,7 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
     return *reinterpret_cast<const bf16x8*>(&ut[(16 * mt + n) * kUtRow + 32 * ks + 8 * q]);
   };
 
-  // V: post-rotation channel j = bitrev7(c) of register i in this lane after the
+  // post-rotation channel j = bitrev7(c) of register i in this lane after the
   // Walsh-Hadamard without swaps back: c = r + 4 (lane bit 5 + 2 (i bit 3)) + 16 (i bit 2 +
   // 2 (lane bit 4) + 4 (i bit 4)), r = i & 3
   auto vj = [&](int i) {
@@ -186,47 +186,25 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
     // cross-lane bits: channel bit 2 = lane bit 4, channel bit 3 = lane bit 5.  Registers
     // x = v[i], y = v[i ^ 8] go through a permlane swap, which leaves in each lane the
     // (bit-clear, bit-set) partner values of one of them; sum and difference are the
-    // butterfly outputs.  For K a second swap of (sum, difference) puts every result back
-    // in the lane and register it came from (the K codes are packed per lane).  V codes go
-    // through LDS, where any placement is free, so V keeps the results where they are: after
-    // both stages register bit 3 holds channel bit 3, lane bit 5 channel bit 2 and lane bit
-    // 4 channel bit 5 (see vj below), and the 32 swaps back are saved.
-    if (kind == 0) {
+    // butterfly outputs, kept where the swap leaves them: after both stages register bit 3
+    // holds channel bit 3, lane bit 5 channel bit 2 and lane bit 4 channel bit 5 (vj above).
+    // The codes are placed by that map (V through LDS, K by halfwords merged across the
+    // lane pair), so no swap puts a result back.
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i & 8) continue;
-        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
-        const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
-        r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
-        v[i] = __uint_as_float(r[0]);
-        v[i | 8] = __uint_as_float(r[1]);
-      }
+    for (int i = 0; i < 32; ++i) {
+      if (i & 8) continue;
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
+      const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
+      v[i] = a0 + b0;
+      v[i | 8] = a0 - b0;
+    }
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i & 8) continue;
-        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
-        const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
-        r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0 + b0), __float_as_uint(a0 - b0), false, false);
-        v[i] = __uint_as_float(r[0]);
-        v[i | 8] = __uint_as_float(r[1]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i & 8) continue;
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
-        const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
-        v[i] = a0 + b0;
-        v[i | 8] = a0 - b0;
-      }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i & 8) continue;
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
-        const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
-        v[i] = a0 + b0;
-        v[i | 8] = a0 - b0;
-      }
+    for (int i = 0; i < 32; ++i) {
+      if (i & 8) continue;
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i | 8]), false, false);
+      const float a0 = __uint_as_float(r[0]), b0 = __uint_as_float(r[1]);
+      v[i] = a0 + b0;
+      v[i | 8] = a0 - b0;
     }
 
     // ---- clip, group min/max (v holds the rotation times sqrt(128): the 1/sqrt(128)
@@ -282,25 +260,43 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
     uint8_t* blk = a.pages + ((size_t)pid * a.num_heads + h) * a.block_bytes;   // used only if is_int2
     const int slot = p & 15;
     if (kind == 0) {
-      // K, token-major: post-rotation channel j = 64 r0 + 32 r1 + 16 q0 + 8 q1 + bitrev3(mt)
-      // -> halfword (j / 8) = 8 r0 + 4 r1 + 2 q0 + q1, bit 2 * bitrev3(mt).
+      // K, token-major: channel j = vj(i) is code j % 8 = 4 i2 + 2 (q & 1) + i4 of halfword
+      // j / 8 = 8 i0 + 4 i1 + 2 (q >> 1) + i3 (i_k = bit k of i).  A lane holds four codes of
+      // each of eight halfwords, the lane 16 apart (the other q & 1) the other four: each
+      // lane sums its codes into halfwords (code * 4^position: exact in fp32), pairs them
+      // into the dwords of halfwords (2m, 2m + 1), and one permlane swap per two dwords
+      // gives each lane of the pair both halves of one of them.
+      float w4[4];   // 4^position of code (i2, i4) = k >> 1, k & 1 in this lane
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w4[k] = (float)(1u << (2 * (4 * (k >> 1) + 2 * (q & 1) + (k & 1))));
+      float hf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // [i0 + 2 i1 + 4 i3]
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int u = (i & 3) | (((i >> 3) & 1) << 2), k = (((i >> 2) & 1) << 1) | ((i >> 4) & 1);
+        hf[u] = fmaf(__builtin_rintf(tq[i]), w4[k], hf[u]);
+      }
+      uint32_t d[4];   // [m = i0 + 2 i1]: halfwords with i3 = 0 (low) and 1 (high)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) d[m] = (uint32_t)hf[m] | ((uint32_t)hf[m + 4] << 16);
+      // lane bit 4 clear: dwords m = 0, 2 of the pair; set: m = 1, 3
+      const auto s01 = __builtin_amdgcn_permlane16_swap(d[0], d[1], false, false);
+      const auto s23 = __builtin_amdgcn_permlane16_swap(d[2], d[3], false, false);
       if (is_int2) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float hf = 0.f;   // sum of code * 4^k: exact in fp32 (16 bits)
-#pragma unroll
-          for (int mt = 0; mt < 8; ++mt) hf = fmaf(__builtin_rintf(tq[4 * mt + r]), (float)(1 << (2 * bitrev3(mt))), hf);
-          const uint32_t hw = (uint32_t)hf;
-          const int hidx = 8 * (r & 1) + 4 * (r >> 1) + 2 * (q & 1) + (q >> 1);
-          *reinterpret_cast<uint16_t*>(blk + kKCodes + 32 * slot + 2 * hidx) = (uint16_t)hw;
-        }
+        // dword m at byte 2 (8 i0 + 4 i1 + 2 (q >> 1)) of the token's codes, i0 = q & 1
+        uint8_t* row = blk + kKCodes + 32 * slot + 16 * (q & 1) + 4 * (q >> 1);
+        *reinterpret_cast<uint32_t*>(row) = s01[0] | s01[1];
+        *reinterpret_cast<uint32_t*>(row + 8) = s23[0] | s23[1];
       }
     } else if (full_page) {
       // V, channel-major, whole page: transpose through LDS, write whole words.  The code
       // byte is the low byte of tq + 2^23 (adding 2^23 rounds to the nearest integer, ties
       // to even, exactly like rint).
+      {
+        float c23 = 8388608.0f;   // held in a register: a literal operand costs a slower issue
+        asm volatile("" : "+v"(c23));
 #pragma unroll
-      for (int i = 0; i < 32; ++i) vbytes[wave][vrow(vj(i))][n] = (uint8_t)__float_as_uint(tq[i] + 8388608.0f);
+        for (int i = 0; i < 32; ++i) vbytes[wave][vrow(vj(i))][n] = (uint8_t)__float_as_uint(tq[i] + c23);
+      }
       wave_lds_sync();
       // every lane of the tile holds the same page: lane 0's id
       const uint8_t* page_blk = a.pages + ((size_t)__shfl(pid, 0) * a.num_heads + h) * a.block_bytes;
