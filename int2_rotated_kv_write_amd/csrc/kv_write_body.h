@@ -294,8 +294,12 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
       {
         float c23 = 8388608.0f;   // held in a register: a literal operand costs a slower issue
         asm volatile("" : "+v"(c23));
+        // token n's byte at 4 (n % 4) + n / 4 of the row: dword d then holds tokens d, d + 4,
+        // d + 8, d + 12 in bytes 0..3, and shifting it left by 2 d puts each token t's code at
+        // bits 2 t of the page word
+        const int vpos = ((n & 3) << 2) | (n >> 2);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) vbytes[wave][vrow(vj(i))][n] = (uint8_t)__float_as_uint(tq[i] + c23);
+        for (int i = 0; i < 32; ++i) vbytes[wave][vrow(vj(i))][vpos] = (uint8_t)__float_as_uint(tq[i] + c23);
       }
       wave_lds_sync();
       // every lane of the tile holds the same page: lane 0's id
@@ -304,15 +308,7 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const uint4 by = *reinterpret_cast<const uint4*>(&vbytes[wave][vrow(2 * lane + c)][0]);
-        const uint32_t parts[4] = {by.x, by.y, by.z, by.w};
-        uint32_t wv = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t y = parts[k] | (parts[k] >> 6);
-          y = (y | (y >> 12)) & 0xFFu;   // 4 two-bit codes -> one byte
-          wv |= y << (8 * k);
-        }
-        words[c] = wv;
+        words[c] = by.x | (by.y << 2) | (by.z << 4) | (by.w << 6);   // codes are 0..3: no carries
       }
       *reinterpret_cast<uint2*>(const_cast<uint8_t*>(page_blk) + kVCodes + 8 * lane) = make_uint2(words[0], words[1]);
       wave_lds_sync();
