@@ -18,7 +18,9 @@
 namespace oscar {
 namespace {
 
-constexpr int kUtRow = kHeadDim + 8;   // U^T row stride in LDS (272 B): conflict-free fragment reads
+// U^T row stride in LDS (288 B): the fragment reads count no LDS bank conflicts on gfx950
+// (SQ_LDS_BANK_CONFLICT 0; at 272 B, 4 conflict cycles per 16-byte fragment read)
+constexpr int kUtRow = kHeadDim + 16;
 constexpr float kInvSqrt128 = 0.08838834764831845f;
 
 // LDS row of channel j in the V transposition buffer: channel bits 3, 4 (the lane's
