@@ -143,18 +143,6 @@ __host__ __device__ constexpr int bitrev7(int x) {
          ((x >> 6) & 1);
 }
 
-__device__ __forceinline__ float wave_sum_xor(float v, int from, int to) {
-  for (int m = from; m <= to; m <<= 1) v += __shfl_xor(v, m);
-  return v;
-}
-__device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
-  for (int m = from; m <= to; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
-__device__ __forceinline__ float wave_min_xor(float v, int from, int to) {
-  for (int m = from; m <= to; m <<= 1) v = fminf(v, __shfl_xor(v, m));
-  return v;
-}
 
 // ---------------------------------------------------------------------------
 // Cross-lane reductions without LDS traffic: DPP inside a 16-lane row, the
@@ -167,6 +155,47 @@ __device__ __forceinline__ float dpp(float x) {
 }
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
 constexpr int kQuadRot1 = 0x39;   // quad_perm [1, 2, 3, 0]: lane i of a quad reads lane (i + 1) % 4
+constexpr int kRowRor12 = 0x12C;   // row_ror:n: lane l of a row reads lane (l - n) % 16
+
+// The value held by lane ^ m, m one of 1, 2, 4, 8, 16, 32 (a constant once inlined), from the
+// vector ALU alone: DPP inside a row, permlane swaps across rows.  Every lane of the wave must
+// be active.
+__device__ __forceinline__ float lane_xor(float x, int m) {
+  const int lane = threadIdx.x & 63;
+  switch (m) {
+    case 1: return dpp<kQuadXor1>(x);
+    case 2: return dpp<kQuadXor2>(x);
+    case 4: {
+      const float up = dpp<kRowRor4>(x), down = dpp<kRowRor12>(x);   // lanes l - 4, l + 4
+      return (lane & 4) ? up : down;
+    }
+    case 8: return dpp<kRowRor8>(x);
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    }
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+      return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    }
+  }
+}
+// butterfly reductions over lane bits from .. to (powers of two): every lane gets the result
+__device__ __forceinline__ float wave_sum_xor(float v, int from, int to) {
+#pragma unroll
+  for (int m = from; m <= to; m <<= 1) v += lane_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
+#pragma unroll
+  for (int m = from; m <= to; m <<= 1) v = fmaxf(v, lane_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_min_xor(float v, int from, int to) {
+#pragma unroll
+  for (int m = from; m <= to; m <<= 1) v = fminf(v, lane_xor(v, m));
+  return v;
+}
 
 __device__ __forceinline__ float swap16(float x, bool is_max) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -186,8 +186,8 @@ __device__ __forceinline__ void qrot_finish(const DecodeArgs& a, QRotLds v) {
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {           // stages 2 .. 64: lane bit m
       const float sgn = (lane & m) ? -1.f : 1.f;   // upper partner: partner - own
-      y0 = fmaf(sgn, y0, __shfl_xor(y0, m));
-      y1 = fmaf(sgn, y1, __shfl_xor(y1, m));
+      y0 = fmaf(sgn, y0, lane_xor(y0, m));
+      y1 = fmaf(sgn, y1, lane_xor(y1, m));
     }
     *reinterpret_cast<float2*>(&v.y[g][2 * lane]) = make_float2(y0, y1);
     wave_lds_sync();
@@ -400,8 +400,8 @@ __device__ void bf16_item(const DecodeArgs& a, int b, int h, int chunk, int L, S
         d = dot2_bf16(qd.z, kd[x].z, d);
         d = dot2_bf16(qd.w, kd[x].w, d);
       }
-      d += __shfl_xor(d, 1);
-      d += __shfl_xor(d, 2);
+      d += lane_xor(d, 1);
+      d += lane_xor(d, 2);
       lg[hh] = valid ? d * a.sl2e : -INFINITY;
     }
     wave_lds_sync();   // the previous group's weights have been read
@@ -1885,8 +1885,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeArgs a) {
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       const float sgn = (lane & m) ? -1.f : 1.f;   // upper partner: partner - own
-      y0 = fmaf(sgn, y0, __shfl_xor(y0, m));
-      y1 = fmaf(sgn, y1, __shfl_xor(y1, m));
+      y0 = fmaf(sgn, y0, lane_xor(y0, m));
+      y1 = fmaf(sgn, y1, lane_xor(y1, m));
     }
     // three bf16 limbs of each value: rows 4 g + limb of the A operand
     const float ys[2] = {y0, y1};

@@ -221,10 +221,14 @@ __device__ __forceinline__ void kv_write_block(const KvWriteArgs& a, KvWriteSmem
       mn[i & 1] = fminf(mn[i & 1], v[i]);
       mx[i & 1] = fmaxf(mx[i & 1], v[i]);
     }
+    // across the four quarters through the LDS crossbar (ds_bpermute): this kernel is bound
+    // by its vector-ALU issue, and permlane swaps here measured 2-4% slower
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      mn[g] = __builtin_amdgcn_fmed3f(wave_min_xor(mn[g], 16, 32), -clip_s, clip_s);
-      mx[g] = __builtin_amdgcn_fmed3f(wave_max_xor(mx[g], 16, 32), -clip_s, clip_s);
+      mn[g] = fminf(mn[g], __shfl_xor(mn[g], 16));
+      mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], 16));
+      mn[g] = __builtin_amdgcn_fmed3f(fminf(mn[g], __shfl_xor(mn[g], 32)), -clip_s, clip_s);
+      mx[g] = __builtin_amdgcn_fmed3f(fmaxf(mx[g], __shfl_xor(mx[g], 32)), -clip_s, clip_s);
     }
     if (one_group) {   // one 128-channel group: both halves share its range
       mn[0] = mn[1] = fminf(mn[0], mn[1]);
